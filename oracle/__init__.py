@@ -1,0 +1,257 @@
+"""Python wrapper around the C oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the oracle is the slow, obviously-correct CPU
+reference that the HIP library is checked against.  Only the tests, the smoke
+check and the benchmark's CPU-baseline leg import this package.  It imports
+nothing from the product package and shares no code with it.
+
+Every function here is argument marshalling around one C routine; the
+arithmetic lives in oracle.c, whose header cites the page passages each step
+follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, building it with gcc first if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+
+            _b.build()
+        _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _declare(L):
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    L.orc_f32_to_f16.restype = ctypes.c_uint16
+    L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    L.orc_f16_to_f32.restype = ctypes.c_float
+    L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+    for name in ("orc_f32_to_f16_n", "orc_f16_to_f32_n", "orc_bf16_to_f32_n", "orc_f32_to_bf16_n"):
+        getattr(L, name).restype = None
+        getattr(L, name).argtypes = [P, P, i64]
+    L.orc_fwht_f32.restype = None
+    L.orc_fwht_f32.argtypes = [P, i32]
+    L.orc_rotate_f64.restype = None
+    L.orc_rotate_f64.argtypes = [P, P, i32]
+    L.orc_quantize_group.restype = None
+    L.orc_quantize_group.argtypes = [P, i32, i32, P, P, P, P, P]
+    L.orc_num_quantized.restype = i64
+    L.orc_num_quantized.argtypes = [i64, i32, i32]
+    L.orc_encode_slice.restype = i64
+    L.orc_encode_slice.argtypes = [P, P, i32, i64, i32, i32, i32, i32, i32, i32] + [P] * 8
+    L.orc_pack_codes.restype = None
+    L.orc_pack_codes.argtypes = [P, i64, i32, i32, P]
+    L.orc_unpack_codes.restype = None
+    L.orc_unpack_codes.argtypes = [P, i64, i32, i32, P]
+    L.orc_attend_partial.restype = None
+    L.orc_attend_partial.argtypes = [P, i32, i64, i32, i32, i32] + [P] * 8 + [i64, i64, P, P, P]
+    L.orc_attend_slice.restype = None
+    L.orc_attend_slice.argtypes = [P, i32, i64, i32, i32, i32] + [P] * 8 + [P]
+    L.orc_merge_partials.restype = None
+    L.orc_merge_partials.argtypes = [i32, i32, i32, P, P, P, P]
+    L.orc_bits_per_element.restype = f64
+    L.orc_bits_per_element.argtypes = [i64, i32, i32, i32, i32, f64]
+    return L
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------- conversions
+def f32_to_f16_bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_f32_to_f16_n(_p(x), _p(out), x.size)
+    return out
+
+
+def f16_bits_to_f32(h) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().orc_f16_to_f32_n(_p(h), _p(out), h.size)
+    return out
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    out = np.empty(b.shape, np.float32)
+    lib().orc_bf16_to_f32_n(_p(b), _p(out), b.size)
+    return out
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_f32_to_bf16_n(_p(x), _p(out), x.size)
+    return out
+
+
+def input_to_f64(a, dtype: str) -> np.ndarray:
+    """Widen stored input elements (f32 values, or f16/bf16 bit patterns) to fp64 exactly."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "f16":
+        return f16_bits_to_f32(a).astype(np.float64)
+    return bf16_bits_to_f32(a).astype(np.float64)
+
+
+# ---------------------------------------------------------------- rotation
+def fwht_f32(y) -> np.ndarray:
+    y = np.array(y, dtype=np.float32, copy=True, order="C")
+    lib().orc_fwht_f32(_p(y), y.size)
+    return y
+
+
+def rotate_f64(q) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    out = np.empty_like(q)
+    lib().orc_rotate_f64(_p(q), _p(out), q.size)
+    return out
+
+
+# ---------------------------------------------------------------- quantizer
+def quantize_group(x, bits: int):
+    """Quantize one group of fp16-valued binary32 numbers.
+
+    Returns (codes uint16[count], s_f32, mn_f32, scale16_bits, zero16_bits)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(x.size, np.uint16)
+    s = np.zeros(1, np.float32)
+    mn = np.zeros(1, np.float32)
+    sc = np.zeros(1, np.uint16)
+    zr = np.zeros(1, np.uint16)
+    lib().orc_quantize_group(_p(x), x.size, bits, _p(codes), _p(s), _p(mn), _p(sc), _p(zr))
+    return codes, np.float32(s[0]), np.float32(mn[0]), int(sc[0]), int(zr[0])
+
+
+def num_quantized(n: int, G: int, R: int) -> int:
+    return int(lib().orc_num_quantized(n, G, R))
+
+
+def encode_slice(k, v, dtype: str, D: int, kbits: int, vbits: int, G: int, R: int, rotate: bool):
+    """Encode one (batch, kv-head) slice.  k, v: [n][D] in the input dtype
+    (float32 values for "f32", uint16 bit patterns for "f16"/"bf16").
+
+    Returns a dict of canonical arrays (codes unpacked, one per uint16)."""
+    np_dt = np.float32 if dtype == "f32" else np.uint16
+    k = np.ascontiguousarray(k, dtype=np_dt).reshape(-1, D)
+    v = np.ascontiguousarray(v, dtype=np_dt).reshape(-1, D)
+    n = k.shape[0]
+    nq = num_quantized(n, G, R)
+    nr = n - nq
+    out = {
+        "k_codes": np.zeros((nq, D), np.uint16),
+        "k_scale": np.zeros((nq // G, D), np.uint16),
+        "k_zero": np.zeros((nq // G, D), np.uint16),
+        "v_codes": np.zeros((nq, D), np.uint16),
+        "v_scale": np.zeros((nq, D // G), np.uint16),
+        "v_zero": np.zeros((nq, D // G), np.uint16),
+        "k_resid": np.zeros((nr, D), np.uint16),
+        "v_resid": np.zeros((nr, D), np.uint16),
+    }
+    r = lib().orc_encode_slice(
+        _p(k), _p(v), DTYPE_CODE[dtype], n, D, kbits, vbits, G, R, int(bool(rotate)),
+        *(_p(out[key]) for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")),
+    )
+    if r < 0:
+        raise ValueError("orc_encode_slice rejected its arguments")
+    out["nq"] = nq
+    out["n"] = n
+    return out
+
+
+def pack_codes(codes, bits: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint16)
+    rows, D = codes.shape
+    out = np.zeros((rows, (D * bits + 7) // 8), np.uint8)
+    lib().orc_pack_codes(_p(codes), rows, D, bits, _p(out))
+    return out
+
+
+def unpack_codes(packed, D: int, bits: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    out = np.zeros((rows, D), np.uint16)
+    lib().orc_unpack_codes(_p(packed), rows, D, bits, _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- attention
+_CACHE_KEYS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")
+
+
+def _cache_ptrs(cache):
+    arrs = [np.ascontiguousarray(cache[k], dtype=np.uint16) for k in _CACHE_KEYS]
+    return arrs, [_p(a) for a in arrs]
+
+
+def attend_slice(q, cache, D: int, G: int, R: int) -> np.ndarray:
+    """fp64 attention of q[nh][D] (fp64, rotated already if keys were) over a canonical slice."""
+    q = np.ascontiguousarray(q, dtype=np.float64).reshape(-1, D)
+    nh = q.shape[0]
+    out = np.zeros((nh, D), np.float64)
+    keep, ptrs = _cache_ptrs(cache)
+    lib().orc_attend_slice(_p(q), nh, int(cache["n"]), D, G, R, *ptrs, _p(out))
+    del keep
+    return out
+
+
+def attend_partial(q, cache, D: int, G: int, R: int, t0: int, t1: int):
+    q = np.ascontiguousarray(q, dtype=np.float64).reshape(-1, D)
+    nh = q.shape[0]
+    m = np.zeros(nh, np.float64)
+    l = np.zeros(nh, np.float64)
+    o = np.zeros((nh, D), np.float64)
+    keep, ptrs = _cache_ptrs(cache)
+    lib().orc_attend_partial(_p(q), nh, int(cache["n"]), D, G, R, *ptrs, t0, t1, _p(m), _p(l), _p(o))
+    del keep
+    return m, l, o
+
+
+def merge_partials(m, l, o) -> np.ndarray:
+    m = np.ascontiguousarray(m, dtype=np.float64)
+    l = np.ascontiguousarray(l, dtype=np.float64)
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    S, nh, D = o.shape
+    out = np.zeros((nh, D), np.float64)
+    lib().orc_merge_partials(S, nh, D, _p(m), _p(l), _p(o), _p(out))
+    return out
+
+
+def attend_slices_parallel(jobs, threads: int):
+    """Run attend_slice over many (q, cache, D, G, R) jobs on `threads` host
+    threads (ctypes releases the GIL during each C call)."""
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(lambda j: attend_slice(*j), jobs))
+
+
+# ---------------------------------------------------------------- accounting
+def bits_per_element(n: int, kbits: int, vbits: int, G: int, R: int, overhead_bits: float = 32.0) -> float:
+    return float(lib().orc_bits_per_element(n, kbits, vbits, G, R, overhead_bits))
+
+
+def kv_cache_bytes(layers: int, hidden: int, tokens: int, bits_per_elem: float) -> float:
+    """K and V of `layers` layers with `hidden` channels each, `tokens` tokens,
+    at `bits_per_elem` bits per stored element (section 5.4 memory model of
+    "Asymmetric Key-Value Quantization ...")."""
+    return 2.0 * layers * hidden * tokens * bits_per_elem / 8.0

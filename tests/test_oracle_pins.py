@@ -1,0 +1,429 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself
+(library routines, closed forms printed on the pages, invariants, brute force
+in exact arithmetic).  CPU only."""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- conversions
+def test_f16_to_f32_exhaustive(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.f16_bits_to_f32(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _f32_probe_values():
+    rng = np.random.default_rng(7)
+    vals = [rng.standard_normal(200000).astype(np.float32) * np.float32(s) for s in (1e-6, 1e-4, 1e-2, 1, 100, 3e4)]
+    # every binary16 value and every midpoint between neighbours (exact ties), nudged both ways
+    h = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = ((h[:-1] + h[1:]) / 2).astype(np.float32)
+    vals += [h.astype(np.float32), mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf))]
+    special = np.array([65504, 65519.996, 65520, 65536, 1e9, 2.0 ** -25, 3 * 2.0 ** -25, 2.0 ** -26,
+                        2.0 ** -14, 2.0 ** -24, 0.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, np.inf], dtype=np.float32)
+    vals.append(special)
+    v = np.concatenate(vals)
+    return np.concatenate([v, -v])
+
+
+def test_f32_to_f16_matches_numpy_rne(orc):
+    x = _f32_probe_values()
+    got = orc.f32_to_f16_bits(x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_f32_to_bf16_matches_torch_rne(orc):
+    x = _f32_probe_values()
+    got = orc.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+    back = orc.bf16_bits_to_f32(ref)
+    assert np.array_equal(back, torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+# ----------------------------------------------------------------- Hadamard
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32, 64, 128])
+def test_fwht_matches_sylvester_matrix(orc, n):
+    rng = np.random.default_rng(n)
+    H = scipy.linalg.hadamard(n).astype(np.float64) / math.sqrt(n)
+    for _ in range(20):
+        x = (rng.standard_normal(n) * np.exp(rng.standard_normal(n))).astype(np.float32)
+        y = orc.fwht_f32(x).astype(np.float64)
+        ref = H @ x.astype(np.float64)
+        assert np.max(np.abs(y - ref)) <= 1e-6 * np.linalg.norm(x.astype(np.float64))
+        assert np.allclose(orc.rotate_f64(x.astype(np.float64)), ref, rtol=0, atol=1e-12 * np.linalg.norm(x))
+
+
+def test_fwht_basis_vector_and_constant(orc):
+    # H e0 = (1/sqrt(128)) * ones, with the binary32 constant nearest 1/sqrt(128)
+    e0 = np.zeros(128, np.float32)
+    e0[0] = 1.0
+    y = orc.fwht_f32(e0)
+    assert set(y.view(np.uint32).tolist()) == {0x3DB504F3}
+    # the row pattern of H e_i is the Sylvester sign pattern
+    H = scipy.linalg.hadamard(128)
+    for i in (1, 5, 77, 127):
+        e = np.zeros(128, np.float32)
+        e[i] = 1.0
+        y = orc.fwht_f32(e)
+        assert np.array_equal(np.sign(y), H[:, i].astype(np.float32))
+
+
+def test_fwht_is_involution_and_preserves_dot(orc):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(128).astype(np.float32)
+    z = rng.standard_normal(128).astype(np.float32)
+    xx = orc.fwht_f32(orc.fwht_f32(x))
+    assert np.max(np.abs(xx - x)) < 1e-5
+    qx, qz = orc.rotate_f64(x.astype(np.float64)), orc.rotate_f64(z.astype(np.float64))
+    assert abs(qx @ qz - x.astype(np.float64) @ z.astype(np.float64)) < 1e-12 * np.linalg.norm(x) * np.linalg.norm(z)
+
+
+# ----------------------------------------------------------------- quantizer
+def _fp16_values(rng, n, scale=1.0):
+    return (rng.standard_normal(n) * scale).astype(np.float16).astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", list(range(1, 17)))
+def test_quantizer_range_and_error_bound(orc, bits):
+    rng = np.random.default_rng(100 + bits)
+    L = 2 ** bits - 1
+    for trial in range(300):
+        scale = float(np.exp(rng.uniform(-6, 6)))
+        x = _fp16_values(rng, int(rng.integers(2, 129)), scale)
+        if trial % 7 == 0:
+            x[int(rng.integers(0, x.size))] *= 50  # an outlier
+            x = x.astype(np.float16).astype(np.float32)
+        codes, s, mn, sc16, zr16 = orc.quantize_group(x, bits)
+        assert codes.max() <= L
+        xs = x.astype(np.float64)
+        assert float(mn) == xs.min()
+        s64 = float(s)
+        err = np.abs(xs - (float(mn) + codes.astype(np.float64) * s64))
+        assert err.max() <= s64 * (0.5 + 2.0 ** (bits - 23)) + 1e-300
+        # fp16 storage: zero16 is exact, scale16 within half an fp16 ulp
+        assert orc.f16_bits_to_f32(np.array([zr16], np.uint16))[0] == mn
+        s16 = float(orc.f16_bits_to_f32(np.array([sc16], np.uint16))[0])
+        if s64 >= 2.0 ** -14 and bits <= 8:
+            err16 = np.abs(xs - (float(mn) + codes.astype(np.float64) * s16))
+            assert err16.max() <= s64 * (0.5 + 2.0 ** (bits - 23) + L * 2.0 ** -11)
+
+
+def _brute_codes(x, mn, s, bits):
+    """Nearest level mn + c*s by exact rational search, ties to even c.
+    Returns per element the set of acceptable codes: one code unless the
+    exact quotient is within 2^-20 of a half-integer without being one."""
+    out = []
+    mnf, sf = Fraction(float(mn)), Fraction(float(s))
+    for xi in x:
+        xf = Fraction(float(xi))
+        d = [abs(xf - mnf - c * sf) for c in range(2 ** bits)]
+        best = min(d)
+        cands = [c for c in range(2 ** bits) if d[c] == best]
+        exact = [c for c in cands if c % 2 == 0] if len(cands) > 1 else cands
+        q = (xf - mnf) / sf
+        frac = q - math.floor(q)
+        if frac != Fraction(1, 2) and abs(frac - Fraction(1, 2)) < Fraction(1, 2 ** 20):
+            out.append({math.floor(q), math.floor(q) + 1})
+        else:
+            out.append(set(exact))
+    return out
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_quantizer_brute_force_small(orc, bits):
+    rng = np.random.default_rng(bits)
+    for _ in range(400):
+        g = int(rng.integers(2, 9))
+        x = _fp16_values(rng, g, float(np.exp(rng.uniform(-3, 3))))
+        codes, s, mn, _, _ = orc.quantize_group(x, bits)
+        if s == 0:
+            assert not codes.any()
+            continue
+        ok = _brute_codes(x, mn, s, bits)
+        assert all(int(c) in o for c, o in zip(codes, ok)), (x, codes, ok)
+
+
+def test_quantizer_ties_go_to_even(orc):
+    x = np.array([0.0, 3.0, 0.5, 1.5, 2.5], np.float32)  # b=2: s = 1 exactly
+    codes, s, mn, _, _ = orc.quantize_group(x, 2)
+    assert s == 1.0 and mn == 0.0
+    assert codes.tolist() == [0, 3, 0, 2, 2]
+
+
+def test_quantizer_one_bit_limit(orc):
+    codes, s, mn, _, _ = orc.quantize_group(np.array([0, 1, 0.5, 0.5], np.float32), 1)
+    assert codes.tolist() == [0, 1, 0, 0]  # midpoint to the even code
+    a, b = -1.5, 2.25
+    x = np.array([a, b, a, b, b], np.float32)
+    codes, s, mn, sc16, zr16 = orc.quantize_group(x, 1)
+    rec = orc.f16_bits_to_f32(np.array([zr16], np.uint16))[0] + codes * orc.f16_bits_to_f32(np.array([sc16], np.uint16))[0]
+    assert np.array_equal(rec, x)  # a two-valued group reconstructs exactly
+
+
+def test_quantizer_sixteen_bit_limit(orc):
+    rng = np.random.default_rng(16)
+    for _ in range(50):
+        x = _fp16_values(rng, 64, 3.0)
+        codes, s, mn, _, _ = orc.quantize_group(x, 16)
+        err = np.abs(x.astype(np.float64) - (float(mn) + codes * float(s)))
+        assert err.max() <= float(s) * (0.5 + 2.0 ** -7)
+
+
+def test_quantizer_constant_group_and_signed_zero(orc):
+    for val in (0.0, -0.0, 1.25, -7.5):
+        codes, s, mn, sc16, zr16 = orc.quantize_group(np.full(32, val, np.float32), 2)
+        assert not codes.any() and s == 0 and sc16 == 0
+        assert zr16 == (0 if val == 0 else int(np.float16(val).view(np.uint16)))
+    codes, s, mn, sc16, zr16 = orc.quantize_group(np.array([-0.0, 0.0, -0.0], np.float32), 4)
+    assert (sc16, zr16) == (0, 0)
+
+
+# ----------------------------------------------------------------- window bookkeeping
+@pytest.mark.parametrize("G,R", [(32, 32), (64, 128), (32, 128), (32, 0), (64, 64)])
+def test_window_bookkeeping(orc, G, R):
+    prev = 0
+    flushes = 0
+    for n in range(0, 700):
+        nq = orc.num_quantized(n, G, R)
+        assert nq % G == 0 and 0 <= nq <= n
+        nr = n - nq
+        assert min(n, R) <= nr <= R + G - 1
+        if nq != prev:
+            assert nq - prev == G and nr == R  # a flush leaves exactly R recent tokens
+            flushes += 1
+        prev = nq
+    assert flushes == max(0, (699 - R) // G)
+
+
+# ----------------------------------------------------------------- slice encoding
+def test_encode_axes_and_window(orc):
+    D, G, R, n = 64, 32, 32, 100
+    alpha = np.linspace(-3, 3, D).astype(np.float16).astype(np.float32)
+    beta = np.linspace(-2, 5, n).astype(np.float16).astype(np.float32)
+    k = np.tile(alpha, (n, 1))           # constant along tokens in each channel
+    v = np.tile(beta[:, None], (1, D))   # constant along channels in each token
+    enc = orc.encode_slice(k, v, "f32", D, 2, 2, G, R, False)
+    nq = enc["nq"]
+    assert nq == 64 and enc["k_resid"].shape == (36, D)
+    assert not enc["k_codes"].any() and not enc["k_scale"].any()
+    assert np.array_equal(enc["k_zero"], np.tile(alpha.astype(np.float16).view(np.uint16), (nq // G, 1)))
+    assert not enc["v_codes"].any() and not enc["v_scale"].any()
+    assert np.array_equal(enc["v_zero"], np.tile(beta[:nq, None].astype(np.float16).view(np.uint16), (1, D // G)))
+    assert np.array_equal(enc["v_resid"], v[nq:].astype(np.float16).view(np.uint16))
+
+
+def test_encode_prefix_consistency(orc):
+    rng = np.random.default_rng(11)
+    D, G, R = 64, 32, 32
+    k = rng.standard_normal((300, D)).astype(np.float32)
+    v = rng.standard_normal((300, D)).astype(np.float32)
+    full = orc.encode_slice(k, v, "f32", D, 2, 4, G, R, False)
+    for n in (1, 31, 32, 63, 64, 65, 95, 96, 97, 200, 299):
+        part = orc.encode_slice(k[:n], v[:n], "f32", D, 2, 4, G, R, False)
+        nq = part["nq"]
+        for key in ("k_codes", "v_codes", "v_scale", "v_zero"):
+            assert np.array_equal(part[key], full[key][:nq])
+        for key in ("k_scale", "k_zero"):
+            assert np.array_equal(part[key], full[key][: nq // G])
+        assert np.array_equal(part["k_resid"], k[nq:n].astype(np.float16).view(np.uint16))
+
+
+def test_encode_entry_rounding_bf16(orc):
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy(rng.standard_normal((40, 64)).astype(np.float32)).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    enc = orc.encode_slice(bits, bits, "bf16", 64, 2, 2, 32, 32, False)
+    assert enc["nq"] == 0
+    assert np.array_equal(enc["k_resid"], x.float().numpy().astype(np.float16).view(np.uint16))
+
+
+def test_encode_rotation_sign_pattern(orc):
+    D = 128
+    H = scipy.linalg.hadamard(D)
+    k = np.zeros((3, D), np.float32)
+    for t, i in enumerate((0, 9, 100)):
+        k[t, i] = 2.0
+    enc = orc.encode_slice(k, k, "f32", D, 2, 2, 32, 32, True)
+    c16 = np.float16(2.0 * np.float32(1 / math.sqrt(128)))
+    for t, i in enumerate((0, 9, 100)):
+        ref = (H[:, i] * c16).astype(np.float16).view(np.uint16)
+        assert np.array_equal(enc["k_resid"][t], ref)
+    assert np.array_equal(enc["v_resid"], k.astype(np.float16).view(np.uint16))  # values are not rotated
+
+
+# ----------------------------------------------------------------- packing
+def test_pack_worked_examples(orc):
+    assert orc.pack_codes(np.array([[1, 2, 3, 0]]), 2).tolist() == [[0x39]]
+    assert orc.pack_codes(np.array([[0xA, 0x5]]), 4).tolist() == [[0x5A]]
+    assert orc.pack_codes(np.array([[1, 0, 1, 1, 0, 0, 0, 1]]), 1).tolist() == [[0x8D]]
+    assert orc.pack_codes(np.array([[0x1234, 0xBEEF]]), 16).tolist() == [[0x34, 0x12, 0xEF, 0xBE]]
+    assert orc.pack_codes(np.array([[7, 1, 6]]), 3).tolist() == [[0x8F, 0x01]]  # 111 | 001<<3 | 110<<6
+
+
+@pytest.mark.parametrize("bits", list(range(1, 17)))
+def test_pack_unpack_roundtrip(orc, bits):
+    rng = np.random.default_rng(bits)
+    D = 64
+    codes = rng.integers(0, 2 ** bits, size=(37, D)).astype(np.uint16)
+    packed = orc.pack_codes(codes, bits)
+    assert packed.shape == (37, (D * bits + 7) // 8)
+    assert np.array_equal(orc.unpack_codes(packed, D, bits), codes)
+
+
+# ----------------------------------------------------------------- attention
+def _decode(cache, D, G):
+    """Dequantized keys/values (fp64) of a canonical slice, for closed-form checks."""
+    f = lambda a: np.asarray(a, np.uint16).view(np.float16).astype(np.float64)
+    nq = cache["nq"]
+    kq = f(cache["k_zero"]).repeat(G, 0)[:nq] + cache["k_codes"] * f(cache["k_scale"]).repeat(G, 0)[:nq]
+    vq = f(cache["v_zero"]).repeat(G, 1) + cache["v_codes"] * f(cache["v_scale"]).repeat(G, 1)
+    return np.concatenate([kq, f(cache["k_resid"])]), np.concatenate([vq, f(cache["v_resid"])])
+
+
+def _decimal_attention(q, K, V):
+    getcontext().prec = 50
+    D = q.shape[1]
+    out = []
+    for qh in q:
+        sig = [sum(Decimal(float(qh[c])) * Decimal(float(K[t, c])) for c in range(D)) / Decimal(D).sqrt()
+               for t in range(len(K))]
+        m = max(sig)
+        w = [(s - m).exp() for s in sig]
+        L = sum(w)
+        out.append([float(sum(w[t] * Decimal(float(V[t, c])) for t in range(len(K))) / L) for c in range(D)])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("n,G,R", [(8, 2, 2), (7, 2, 0), (5, 4, 8), (8, 4, 0)])
+def test_attention_brute_force_decimal(orc, n, G, R):
+    rng = np.random.default_rng(n * 10 + G)
+    D = 4
+    k = rng.standard_normal((n, D)).astype(np.float32) * 2
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    cache = orc.encode_slice(k, v, "f32", D, 2, 2, G, R, False)
+    q = rng.standard_normal((3, D))
+    got = orc.attend_slice(q, cache, D, G, R)
+    K, V = _decode(cache, D, G)
+    ref = _decimal_attention(q, K, V)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attention_closed_forms(orc):
+    rng = np.random.default_rng(21)
+    D, G, R, n = 64, 32, 32, 200
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    cache = orc.encode_slice(k, v, "f32", D, 2, 2, G, R, False)
+    K, V = _decode(cache, D, G)
+    # q = 0: uniform weights, the mean of the decoded values
+    out = orc.attend_slice(np.zeros((1, D)), cache, D, G, R)
+    assert np.max(np.abs(out[0] - V.mean(0))) < 1e-12
+    # constant values: weights sum to one
+    ones = orc.encode_slice(k, np.ones((n, D), np.float32), "f32", D, 2, 2, G, R, False)
+    out = orc.attend_slice(rng.standard_normal((4, D)) * 3, ones, D, G, R)
+    assert np.max(np.abs(out - 1.0)) < 1e-14
+    # one dominant key: output is that token's decoded value
+    t_star = 17
+    qq = K[t_star][None, :] * 1e4 / np.linalg.norm(K[t_star]) ** 2 * math.sqrt(D)
+    out = orc.attend_slice(qq, cache, D, G, R)
+    assert np.max(np.abs(out[0] - V[t_star])) < 1e-9
+
+
+def test_attention_identical_keys_give_mean(orc):
+    rng = np.random.default_rng(22)
+    D, G, R, n = 64, 32, 32, 160
+    krow = rng.standard_normal(D).astype(np.float32)
+    k = np.tile(krow, (n, 1))
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    cache = orc.encode_slice(k, v, "f32", D, 2, 2, G, R, False)
+    _, V = _decode(cache, D, G)
+    out = orc.attend_slice(rng.standard_normal((2, D)) * 5, cache, D, G, R)
+    assert np.max(np.abs(out - V.mean(0)[None])) < 1e-12
+
+
+def test_attention_permutation_invariance(orc):
+    rng = np.random.default_rng(23)
+    D, n = 64, 40
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    perm = rng.permutation(n)
+    a = orc.encode_slice(k, v, "f32", D, 2, 2, 32, 64, False)  # all tokens in the window
+    b = orc.encode_slice(k[perm], v[perm], "f32", D, 2, 2, 32, 64, False)
+    q = rng.standard_normal((3, D))
+    assert np.max(np.abs(orc.attend_slice(q, a, D, 32, 64) - orc.attend_slice(q, b, D, 32, 64))) < 1e-12
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 0])
+def test_split_merge_matches_full(orc, S):
+    rng = np.random.default_rng(24)
+    D, G, R, n = 64, 32, 32, 237
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    cache = orc.encode_slice(k, v, "f32", D, 4, 2, G, R, False)
+    q = rng.standard_normal((4, D)) * 2
+    full = orc.attend_slice(q, cache, D, G, R)
+    S = n if S == 0 else S
+    cuts = sorted(set([0, n] + rng.choice(np.arange(1, n), size=S - 1, replace=False).tolist())) if S > 1 else [0, n]
+    parts = [orc.attend_partial(q, cache, D, G, R, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+    # an empty split contributes nothing
+    parts.append(orc.attend_partial(q, cache, D, G, R, 5, 5))
+    m = np.stack([p[0] for p in parts])
+    l = np.stack([p[1] for p in parts])
+    o = np.stack([p[2] for p in parts])
+    assert np.isneginf(m[-1]).all() and not l[-1].any()
+    assert np.max(np.abs(orc.merge_partials(m, l, o) - full)) < 1e-12
+
+
+# ----------------------------------------------------------------- accounting
+def test_compression_table_from_pages(orc):
+    g = json.load(open(os.path.join(GOLDEN, "akvq_compression_table.json")))
+    for row in g["rows"]:
+        assert round(g["fp16_bits"] / row["avg_bits"], 1) == row["compression"]
+        if row["key_bits"] is not None:
+            bpe = orc.bits_per_element(4096, row["key_bits"], row["value_bits"], 64, 0, overhead_bits=0.0)
+            assert bpe == row["avg_bits"]
+
+
+def test_memory_numbers_from_pages(orc):
+    g = json.load(open(os.path.join(GOLDEN, "akvq_memory_7b_262k.json")))
+    fp16_printed = g["rows"][0]["gb"]
+    for row in g["rows"]:
+        gb = orc.kv_cache_bytes(g["layers"], g["hidden"], g["tokens"], row["bits"]) / 1e9
+        assert abs(gb - row["gb"]) <= 0.06, (row, gb)
+        # the page's quantized rows scale its rounded fp16 figure by bits/16
+        assert round(fp16_printed * row["bits"] / 16, 1) == row["gb"]
+    assert round(orc.kv_cache_bytes(g["layers"], g["hidden"], g["tokens"], 16) / 1e9, 1) == fp16_printed
+
+
+@pytest.mark.parametrize("kb,vb,G,R,n", [(2, 2, 32, 128, 8192), (4, 2, 64, 128, 32768 // 8), (2, 2, 32, 32, 1000), (2, 2, 32, 64, 777)])
+def test_bits_per_element_counts_encoded_bytes(orc, kb, vb, G, R, n):
+    rng = np.random.default_rng(n)
+    D = 128
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    cache = orc.encode_slice(k, k, "f32", D, kb, vb, G, R, False)
+    bits = (orc.pack_codes(cache["k_codes"], kb).size + orc.pack_codes(cache["v_codes"], vb).size) * 8
+    bits += 16 * sum(cache[x].size for x in ("k_scale", "k_zero", "v_scale", "v_zero", "k_resid", "v_resid"))
+    assert bits / (2 * n * D) == pytest.approx(orc.bits_per_element(n, kb, vb, G, R), rel=1e-12)
+
+
+def test_window_default_from_pages():
+    g = json.load(open(os.path.join(GOLDEN, "kivi_window_defaults.json")))
+    from synth import WORKLOADS
+
+    assert WORKLOADS[0].R == g["window_tokens"] and WORKLOADS[0].kbits == g["bits"] == WORKLOADS[0].vbits
