@@ -1,0 +1,29 @@
+"""MI355X-native asymmetric low-bit KV-cache quantization fused into decode attention.
+
+The compute path is libkvq.so (hand-written HIP kernels for gfx950 behind the
+C ABI in include/kvq.h); this package is the ctypes binding over it.
+"""
+from .kvq import (  # noqa: F401
+    Config,
+    KVQCache,
+    KVQError,
+    cache_bytes,
+    check,
+    lib,
+    workspace_bytes,
+    KVQ_OK,
+    KVQ_E_ARG,
+    KVQ_E_UNSUPPORTED,
+    KVQ_E_CAPACITY,
+    KVQ_E_DEVICE,
+    KVQ_E_STATE,
+)
+
+
+def config_for(w, max_tokens: int | None = None) -> "Config":
+    """Library config for a synthetic workload description (synth.Workload)."""
+    return Config(
+        batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+        max_tokens=max_tokens or w.N, k_bits=w.kbits, v_bits=w.vbits, group_size=w.G,
+        residual=w.R, rotate=w.rotate, in_dtype=w.dtype,
+    )

@@ -1,0 +1,427 @@
+// kvq_api.cpp -- host side of libkvq: validation, layout planning, host-side
+// token counters, split choice, launches, canonical export/import.
+//
+// The window bookkeeping follows "[Framework] The Asymmetric Key-Value Cache
+// Compression", section III (a full-precision window of the most recent
+// tokens): after n tokens, floor(max(0, n - R) / G) * G tokens are quantized
+// in whole groups aligned to token 0 and the rest stay in fp16, so a group is
+// flushed whenever the window reaches R + G tokens.  All sequences advance in
+// lockstep, so the host knows every count without reading the device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+using kvq::Layout;
+
+struct kvq_cache {
+  kvq_config cfg;
+  Layout L;
+  uint8_t* buf;
+  int64_t n;
+  bool poisoned;
+  int cu_count;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char msg[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, sizeof msg, fmt, ap);
+  va_end(ap);
+  g_err = msg;
+  return st;
+}
+
+kvq_status ok() { return KVQ_OK; }
+
+kvq_status validate(const kvq_config* c) {
+  if (!c) return fail(KVQ_E_ARG, "config is NULL");
+  if (c->struct_size != sizeof(kvq_config))
+    return fail(KVQ_E_ARG, "config.struct_size %u != sizeof(kvq_config) %zu", c->struct_size, sizeof(kvq_config));
+  if (c->batch < 1 || c->num_kv_heads < 1 || c->num_q_heads < 1 || c->max_tokens < 1)
+    return fail(KVQ_E_ARG, "batch, heads and max_tokens must be positive");
+  if (c->num_q_heads % c->num_kv_heads != 0)
+    return fail(KVQ_E_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", c->num_q_heads, c->num_kv_heads);
+  int gqa = c->num_q_heads / c->num_kv_heads;
+  if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8 && gqa != 16)
+    return fail(KVQ_E_UNSUPPORTED, "query heads per kv head %d not in {1,2,4,8,16}", gqa);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(KVQ_E_UNSUPPORTED, "head_dim %d not in {64,128}", c->head_dim);
+  if ((c->k_bits != 2 && c->k_bits != 4) || (c->v_bits != 2 && c->v_bits != 4))
+    return fail(KVQ_E_UNSUPPORTED, "k_bits %d / v_bits %d not in {2,4}", c->k_bits, c->v_bits);
+  if ((c->group_size != 32 && c->group_size != 64) || c->group_size > c->head_dim)
+    return fail(KVQ_E_UNSUPPORTED, "group_size %d not in {32,64} or larger than head_dim", c->group_size);
+  if (c->residual < 0 || c->residual > 1024 || c->residual % 32 != 0)
+    return fail(KVQ_E_UNSUPPORTED, "residual %d must be a multiple of 32 in [0, 1024]", c->residual);
+  if (c->rotate != 0 && c->rotate != 1) return fail(KVQ_E_ARG, "rotate must be 0 or 1");
+  if (c->in_dtype < KVQ_F32 || c->in_dtype > KVQ_BF16) return fail(KVQ_E_ARG, "in_dtype %d unknown", c->in_dtype);
+  if (!kvq::decode_supported(c->head_dim, c->k_bits, c->v_bits, c->group_size))
+    return fail(KVQ_E_UNSUPPORTED, "no kernel for this (head_dim, bits, group) combination");
+  return KVQ_OK;
+}
+
+Layout layout_of(const kvq_config* c) {
+  return kvq::make_layout(c->batch, c->num_kv_heads, c->head_dim, c->max_tokens, c->k_bits, c->v_bits, c->group_size,
+                          c->residual);
+}
+
+int max_splits(const kvq_config* c) {
+  int64_t slices = static_cast<int64_t>(c->batch) * c->num_kv_heads;
+  int64_t s = (16384 + slices - 1) / slices;
+  return static_cast<int>(std::min<int64_t>(256, std::max<int64_t>(1, s)));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+kvq_status check_handle(const kvq_cache* h) {
+  if (!h) return fail(KVQ_E_ARG, "handle is NULL");
+  if (h->poisoned) return fail(KVQ_E_STATE, "handle poisoned by an earlier device error");
+  return KVQ_OK;
+}
+
+kvq_status device_error(kvq_cache* h, hipError_t e, const char* what) {
+  h->poisoned = true;
+  return fail(KVQ_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t ngroups_of(const kvq_cache* h) { return kvq::num_quantized(h->n, h->cfg.group_size, h->cfg.residual) / h->cfg.group_size; }
+
+int choose_splits(kvq_cache* h) {
+  if (h->cu_count <= 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      h->cu_count = cus;
+    else
+      h->cu_count = 256;
+  }
+  int64_t slices = h->L.slices;
+  int64_t target = static_cast<int64_t>(h->cu_count) * 16;  // about four waves per SIMD
+  int64_t s = (target + slices - 1) / slices;
+  int64_t ng = ngroups_of(h);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, ng / 2));
+  s = std::min<int64_t>(s, max_splits(&h->cfg));
+  return static_cast<int>(std::max<int64_t>(1, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+size_t kvq_cache_bytes(const kvq_config* cfg) {
+  if (validate(cfg) != KVQ_OK) return 0;
+  return static_cast<size_t>(layout_of(cfg).total_bytes);
+}
+
+size_t kvq_workspace_bytes(const kvq_config* cfg) {
+  if (validate(cfg) != KVQ_OK) return 0;
+  return static_cast<size_t>(cfg->batch) * cfg->num_q_heads * max_splits(cfg) * (cfg->head_dim + 4) * sizeof(float);
+}
+
+kvq_status kvq_create(const kvq_config* cfg, void* cache_buf, size_t cache_bytes, kvq_cache** out) {
+  kvq_status st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_E_ARG, "out is NULL");
+  if (!cache_buf || !aligned(cache_buf, 256)) return fail(KVQ_E_ARG, "cache buffer NULL or not 256-byte aligned");
+  Layout L = layout_of(cfg);
+  if (cache_bytes < static_cast<size_t>(L.total_bytes))
+    return fail(KVQ_E_ARG, "cache buffer holds %zu bytes, %lld needed", cache_bytes, (long long)L.total_bytes);
+  kvq_cache* h = new (std::nothrow) kvq_cache{};
+  if (!h) return fail(KVQ_E_ARG, "out of host memory");
+  h->cfg = *cfg;
+  h->L = L;
+  h->buf = static_cast<uint8_t*>(cache_buf);
+  h->n = 0;
+  h->poisoned = false;
+  h->cu_count = 0;
+  *out = h;
+  return ok();
+}
+
+kvq_status kvq_destroy(kvq_cache* h) {
+  delete h;
+  return ok();
+}
+
+kvq_status kvq_reset(kvq_cache* h) {
+  if (!h) return fail(KVQ_E_ARG, "handle is NULL");
+  h->n = 0;
+  return ok();
+}
+
+int64_t kvq_num_tokens(const kvq_cache* h) { return h ? h->n : -1; }
+
+int64_t kvq_num_quantized(const kvq_cache* h) {
+  return h ? kvq::num_quantized(h->n, h->cfg.group_size, h->cfg.residual) : -1;
+}
+
+kvq_status kvq_append(kvq_cache* h, const void* k, const void* v, int32_t n_tokens, void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  if (n_tokens < 0) return fail(KVQ_E_ARG, "n_tokens %d < 0", n_tokens);
+  if (n_tokens == 0) return ok();
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_E_ARG, "k/v NULL or not 16-byte aligned");
+  const int64_t n_new = h->n + n_tokens;
+  if (n_new > h->cfg.max_tokens)
+    return fail(KVQ_E_CAPACITY, "append of %d tokens to %lld exceeds max_tokens %d", n_tokens, (long long)h->n,
+                h->cfg.max_tokens);
+  const int G = h->cfg.group_size, R = h->cfg.residual;
+  const int64_t nq_old = kvq::num_quantized(h->n, G, R), nq_new = kvq::num_quantized(n_new, G, R);
+  kvq::AppendArgs a{};
+  a.cache = h->buf;
+  a.L = h->L;
+  a.k = k;
+  a.v = v;
+  a.in_dtype = h->cfg.in_dtype;
+  a.rotate = h->cfg.rotate;
+  a.Hkv = h->cfg.num_kv_heads;
+  a.T = n_tokens;
+  a.n_old = h->n;
+  a.g_first = nq_old / G;
+  a.n_flush = (nq_new - nq_old) / G;
+  a.w_first = std::max(h->n, nq_new);
+  a.n_write = n_new - a.w_first;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // flush before the window write: the write may reuse ring slots the flush reads
+  hipError_t e = kvq::launch_flush(a, s);
+  if (e != hipSuccess) return device_error(h, e, "flush kernel launch");
+  e = kvq::launch_window_write(a, s);
+  if (e != hipSuccess) return device_error(h, e, "window write kernel launch");
+  h->n = n_new;
+  return ok();
+}
+
+int32_t kvq_default_splits(const kvq_cache* h) {
+  if (!h) return 0;
+  return choose_splits(const_cast<kvq_cache*>(h));
+}
+
+kvq_status kvq_decode_attn_splits(kvq_cache* h, const void* q, float* out, void* ws, size_t ws_bytes,
+                                  int32_t num_splits, void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  if (h->n <= 0) return fail(KVQ_E_STATE, "decode on an empty cache");
+  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return fail(KVQ_E_ARG, "q/out NULL or not 16-byte aligned");
+  if (num_splits < 1) return fail(KVQ_E_ARG, "num_splits %d < 1", num_splits);
+  if (num_splits > max_splits(&h->cfg))
+    return fail(KVQ_E_ARG, "num_splits %d above the workspace maximum %d", num_splits, max_splits(&h->cfg));
+  const kvq_config& c = h->cfg;
+  const int64_t ng = ngroups_of(h);
+  int64_t S = std::min<int64_t>(num_splits, std::max<int64_t>(1, ng));
+  int64_t gps = ng > 0 ? (ng + S - 1) / S : 0;
+  if (gps > 0) S = (ng + gps - 1) / gps;  // no empty split
+  const int64_t rows = static_cast<int64_t>(c.batch) * c.num_q_heads;
+  if (S > 1) {
+    size_t need = static_cast<size_t>(rows * S * (c.head_dim + 4) * sizeof(float));
+    if (!ws || !aligned(ws, 16) || ws_bytes < need)
+      return fail(KVQ_E_ARG, "workspace NULL, misaligned or %zu < %zu bytes", ws_bytes, need);
+  }
+  kvq::DecodeArgs a{};
+  a.cache = h->buf;
+  a.L = h->L;
+  a.q = q;
+  a.in_dtype = c.in_dtype;
+  a.rotate = c.rotate;
+  a.gqa = c.num_q_heads / c.num_kv_heads;
+  a.Hq = c.num_q_heads;
+  a.Hkv = c.num_kv_heads;
+  a.n = h->n;
+  a.ngroups = ng;
+  a.splits = static_cast<int>(S);
+  a.groups_per_split = gps;
+  a.rc0 = kvq::num_quantized(h->n, c.group_size, c.residual) / kvq::kChunk;
+  a.rc1 = (h->n + kvq::kChunk - 1) / kvq::kChunk;
+  a.partial = static_cast<float*>(ws);
+  a.out = out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = kvq::launch_decode(a, s);
+  if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
+  if (S > 1) {
+    e = kvq::launch_merge(static_cast<float*>(ws), out, static_cast<int>(rows), static_cast<int>(S), c.head_dim, s);
+    if (e != hipSuccess) return device_error(h, e, "merge kernel launch");
+  }
+  return ok();
+}
+
+kvq_status kvq_decode_attn(kvq_cache* h, const void* q, float* out, void* ws, size_t ws_bytes, void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  return kvq_decode_attn_splits(h, q, out, ws, ws_bytes, choose_splits(h), stream);
+}
+
+// ---------------------------------------------------------------- export / import
+
+kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void* k_scale, void* k_zero,
+                      void* v_codes, void* v_scale, void* v_zero, void* k_resid, void* v_resid, void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = h->cfg;
+  if (b0 < 0 || bc < 0 || b0 + bc > c.batch) return fail(KVQ_E_ARG, "batch range [%d, %d) out of [0, %d)", b0, b0 + bc, c.batch);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(h, e, "stream synchronize");
+  const Layout& L = h->L;
+  const int D = c.head_dim, G = c.group_size, kb = c.k_bits, vb = c.v_bits, ncg = D / G;
+  const int64_t nq = kvq::num_quantized(h->n, G, c.residual), nr = h->n - nq, ng = nq / G;
+  const int64_t krow = D * kb / 8, vrow = D * vb / 8;
+  std::vector<uint8_t> pages(static_cast<size_t>(ng * L.page_bytes));
+  std::vector<uint8_t> ring(static_cast<size_t>(L.ring_chunks * L.ring_chunk_bytes));
+  for (int64_t bi = 0; bi < bc; ++bi)
+    for (int64_t hk = 0; hk < c.num_kv_heads; ++hk) {
+      const int64_t slice = (b0 + bi) * c.num_kv_heads + hk;
+      const int64_t oi = bi * c.num_kv_heads + hk;  // output slice index
+      if (ng > 0) {
+        e = hipMemcpy(pages.data(), h->buf + kvq::page_offset(L, slice, 0), pages.size(), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return device_error(h, e, "export copy");
+      }
+      e = hipMemcpy(ring.data(), h->buf + L.ring_offset + slice * L.ring_chunks * L.ring_chunk_bytes, ring.size(),
+                    hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return device_error(h, e, "export copy");
+      for (int64_t t = 0; t < nq; ++t) {
+        const uint8_t* page = pages.data() + (t / G) * L.page_bytes;
+        const int ch = static_cast<int>((t % G) / kvq::kChunk), tt = static_cast<int>(t % kvq::kChunk);
+        if (k_codes) {
+          uint8_t* row = static_cast<uint8_t*>(k_codes) + (oi * nq + t) * krow;
+          std::memset(row, 0, static_cast<size_t>(krow));
+          for (int cc = 0; cc < D; ++cc) {
+            int64_t byte; int bit;
+            kvq::kcode_loc(L, tt, cc, &byte, &bit);
+            uint32_t w;
+            std::memcpy(&w, page + L.off_kcodes + ch * L.kc_chunk_bytes + byte, 4);
+            uint32_t code = (w >> bit) & ((1u << kb) - 1u);
+            row[(cc * kb) / 8] |= static_cast<uint8_t>(code << ((cc * kb) % 8));
+          }
+        }
+        if (v_codes) {
+          uint8_t* row = static_cast<uint8_t*>(v_codes) + (oi * nq + t) * vrow;
+          std::memset(row, 0, static_cast<size_t>(vrow));
+          for (int cc = 0; cc < D; ++cc) {
+            int64_t byte; int bit;
+            kvq::vcode_loc(L, tt, cc, &byte, &bit);
+            uint32_t w;
+            std::memcpy(&w, page + L.off_vcodes + ch * L.vc_chunk_bytes + byte, 4);
+            uint32_t code = (w >> bit) & ((1u << vb) - 1u);
+            row[(cc * vb) / 8] |= static_cast<uint8_t>(code << ((cc * vb) % 8));
+          }
+        }
+        for (int cg = 0; cg < ncg; ++cg) {
+          uint32_t w;
+          std::memcpy(&w, page + L.off_vparams + ch * L.vp_chunk_bytes + 4 * kvq::vparam_index(L, tt, cg), 4);
+          if (v_scale) static_cast<uint16_t*>(v_scale)[(oi * nq + t) * ncg + cg] = static_cast<uint16_t>(w);
+          if (v_zero) static_cast<uint16_t*>(v_zero)[(oi * nq + t) * ncg + cg] = static_cast<uint16_t>(w >> 16);
+        }
+      }
+      for (int64_t g = 0; g < ng; ++g) {
+        const uint16_t* kp = reinterpret_cast<const uint16_t*>(pages.data() + g * L.page_bytes + L.off_kparams);
+        for (int cc = 0; cc < D; ++cc) {
+          int pi = kvq::kparam_index(L, cc);
+          if (k_scale) static_cast<uint16_t*>(k_scale)[(oi * ng + g) * D + cc] = kp[pi];
+          if (k_zero) static_cast<uint16_t*>(k_zero)[(oi * ng + g) * D + cc] = kp[D + pi];
+        }
+      }
+      for (int64_t t = 0; t < nr; ++t) {
+        const int64_t pos = nq + t;
+        const uint8_t* rc = ring.data() + ((pos / kvq::kChunk) % L.ring_chunks) * L.ring_chunk_bytes;
+        const int tt = static_cast<int>(pos % kvq::kChunk);
+        for (int cc = 0; cc < D; ++cc) {
+          uint16_t kvb, vvb;
+          std::memcpy(&kvb, rc + kvq::ring_k_offset(L, tt, cc), 2);
+          std::memcpy(&vvb, rc + kvq::ring_v_offset(L, tt, cc), 2);
+          if (k_resid) static_cast<uint16_t*>(k_resid)[(oi * nr + t) * D + cc] = kvb;
+          if (v_resid) static_cast<uint16_t*>(v_resid)[(oi * nr + t) * D + cc] = vvb;
+        }
+      }
+    }
+  return ok();
+}
+
+kvq_status kvq_import(kvq_cache* h, int64_t n_tokens, int32_t b0, int32_t bc, const void* k_codes,
+                      const void* k_scale, const void* k_zero, const void* v_codes, const void* v_scale,
+                      const void* v_zero, const void* k_resid, const void* v_resid, void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = h->cfg;
+  if (n_tokens < 0) return fail(KVQ_E_ARG, "n_tokens < 0");
+  if (n_tokens > c.max_tokens) return fail(KVQ_E_CAPACITY, "n_tokens %lld > max_tokens %d", (long long)n_tokens, c.max_tokens);
+  if (b0 < 0 || bc < 0 || b0 + bc > c.batch) return fail(KVQ_E_ARG, "batch range out of bounds");
+  if (!k_codes || !k_scale || !k_zero || !v_codes || !v_scale || !v_zero || !k_resid || !v_resid)
+    return fail(KVQ_E_ARG, "import arrays must not be NULL");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(h, e, "stream synchronize");
+  const Layout& L = h->L;
+  const int D = c.head_dim, G = c.group_size, kb = c.k_bits, vb = c.v_bits, ncg = D / G;
+  const int64_t nq = kvq::num_quantized(n_tokens, G, c.residual), nr = n_tokens - nq, ng = nq / G;
+  const int64_t krow = D * kb / 8, vrow = D * vb / 8;
+  std::vector<uint8_t> pages(static_cast<size_t>(ng * L.page_bytes));
+  std::vector<uint8_t> ring(static_cast<size_t>(L.ring_chunks * L.ring_chunk_bytes));
+  for (int64_t bi = 0; bi < bc; ++bi)
+    for (int64_t hk = 0; hk < c.num_kv_heads; ++hk) {
+      const int64_t slice = (b0 + bi) * c.num_kv_heads + hk;
+      const int64_t oi = bi * c.num_kv_heads + hk;
+      std::fill(pages.begin(), pages.end(), 0);
+      std::fill(ring.begin(), ring.end(), 0);
+      for (int64_t t = 0; t < nq; ++t) {
+        uint8_t* page = pages.data() + (t / G) * L.page_bytes;
+        const int ch = static_cast<int>((t % G) / kvq::kChunk), tt = static_cast<int>(t % kvq::kChunk);
+        const uint8_t* krw = static_cast<const uint8_t*>(k_codes) + (oi * nq + t) * krow;
+        const uint8_t* vrw = static_cast<const uint8_t*>(v_codes) + (oi * nq + t) * vrow;
+        for (int cc = 0; cc < D; ++cc) {
+          int64_t byte; int bit; uint32_t w;
+          uint32_t code = (krw[(cc * kb) / 8] >> ((cc * kb) % 8)) & ((1u << kb) - 1u);
+          kvq::kcode_loc(L, tt, cc, &byte, &bit);
+          uint8_t* dst = page + L.off_kcodes + ch * L.kc_chunk_bytes + byte;
+          std::memcpy(&w, dst, 4); w |= code << bit; std::memcpy(dst, &w, 4);
+          code = (vrw[(cc * vb) / 8] >> ((cc * vb) % 8)) & ((1u << vb) - 1u);
+          kvq::vcode_loc(L, tt, cc, &byte, &bit);
+          dst = page + L.off_vcodes + ch * L.vc_chunk_bytes + byte;
+          std::memcpy(&w, dst, 4); w |= code << bit; std::memcpy(dst, &w, 4);
+        }
+        for (int cg = 0; cg < ncg; ++cg) {
+          uint32_t w = static_cast<uint32_t>(static_cast<const uint16_t*>(v_scale)[(oi * nq + t) * ncg + cg]) |
+                       (static_cast<uint32_t>(static_cast<const uint16_t*>(v_zero)[(oi * nq + t) * ncg + cg]) << 16);
+          std::memcpy(page + L.off_vparams + ch * L.vp_chunk_bytes + 4 * kvq::vparam_index(L, tt, cg), &w, 4);
+        }
+      }
+      for (int64_t g = 0; g < ng; ++g) {
+        uint16_t* kp = reinterpret_cast<uint16_t*>(pages.data() + g * L.page_bytes + L.off_kparams);
+        for (int cc = 0; cc < D; ++cc) {
+          int pi = kvq::kparam_index(L, cc);
+          kp[pi] = static_cast<const uint16_t*>(k_scale)[(oi * ng + g) * D + cc];
+          kp[D + pi] = static_cast<const uint16_t*>(k_zero)[(oi * ng + g) * D + cc];
+        }
+      }
+      for (int64_t t = 0; t < nr; ++t) {
+        const int64_t pos = nq + t;
+        uint8_t* rc = ring.data() + ((pos / kvq::kChunk) % L.ring_chunks) * L.ring_chunk_bytes;
+        const int tt = static_cast<int>(pos % kvq::kChunk);
+        for (int cc = 0; cc < D; ++cc) {
+          std::memcpy(rc + kvq::ring_k_offset(L, tt, cc), static_cast<const uint16_t*>(k_resid) + (oi * nr + t) * D + cc, 2);
+          std::memcpy(rc + kvq::ring_v_offset(L, tt, cc), static_cast<const uint16_t*>(v_resid) + (oi * nr + t) * D + cc, 2);
+        }
+      }
+      if (ng > 0) {
+        e = hipMemcpy(h->buf + kvq::page_offset(L, slice, 0), pages.data(), pages.size(), hipMemcpyHostToDevice);
+        if (e != hipSuccess) return device_error(h, e, "import copy");
+      }
+      e = hipMemcpy(h->buf + L.ring_offset + slice * L.ring_chunks * L.ring_chunk_bytes, ring.data(), ring.size(),
+                    hipMemcpyHostToDevice);
+      if (e != hipSuccess) return device_error(h, e, "import copy");
+    }
+  h->n = n_tokens;
+  return ok();
+}
+
+}  // extern "C"

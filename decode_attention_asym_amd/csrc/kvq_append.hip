@@ -1,0 +1,260 @@
+// kvq_append.hip -- quantize-and-pack kernels of kvq_append.
+//
+// Entry conversion, the fp16 window and the group flush follow
+// "[Framework] The Asymmetric Key-Value Cache Compression", section III (keys
+// per channel, values per token, recent tokens kept in fp16) and section IV
+// (Walsh-Hadamard rotation of keys, fused here into the append).  The
+// quantizer is the asymmetric min/max uniform quantizer: scale =
+// (max - min) / (2^b - 1) and code = round-half-even((x - min) / scale), both
+// in IEEE binary32, so the codes are reproducible bit for bit on any IEEE
+// machine.  This file is built with -ffp-contract=off and relies on hipcc's
+// default correctly rounded binary32 division.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+__device__ __forceinline__ float load_in(const void* p, int dtype, int64_t i) {
+  if (dtype == 0) return static_cast<const float*>(p)[i];
+  uint16_t u = static_cast<const uint16_t*>(p)[i];
+  if (dtype == 1) return __half2float(__ushort_as_half(u));
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+__device__ __forceinline__ float round_fp16(float x) { return __half2float(__float2half_rn(x)); }
+
+__device__ __forceinline__ uint16_t fp16_bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
+
+// code = clamp(rne((x - mn) / s), 0, levels); 0 when the group is constant.
+__device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float levels) {
+  if (s == 0.0f) return 0u;
+  float q = rintf((x - mn) / s);
+  q = fminf(fmaxf(q, 0.0f), levels);
+  return static_cast<uint32_t>(q);
+}
+
+constexpr float kInvSqrt128 = 0.08838834764831845f;  // nearest binary32 to 1/sqrt(128)
+constexpr float kInvSqrt64 = 0.125f;
+
+// Fast Walsh-Hadamard transform of `rows` rows of D fp32 values in LDS:
+// butterflies (a + b, a - b) with span 1, 2, ..., D/2 in Sylvester order,
+// then one multiply by the binary32 constant nearest 1/sqrt(D).  Every output
+// depends only on the fixed butterfly sequence, so the result is independent
+// of how threads share the work.
+template <int D>
+__device__ void fwht_rows(float* x, int rows, int tid, int nthreads) {
+  for (int h = 1; h < D; h <<= 1) {
+    for (int k = tid; k < rows * (D / 2); k += nthreads) {
+      int r = k / (D / 2), p = k % (D / 2);
+      int i0 = (p / h) * 2 * h + (p % h);
+      float a = x[r * D + i0], b = x[r * D + i0 + h];
+      x[r * D + i0] = a + b;
+      x[r * D + i0 + h] = a - b;
+    }
+    __syncthreads();
+  }
+  const float c = D == 128 ? kInvSqrt128 : kInvSqrt64;
+  for (int k = tid; k < rows * D; k += nthreads) x[k] = x[k] * c;
+  __syncthreads();
+}
+
+// One block per (flushed group, slice): gathers the group's G tokens (from
+// the fp16 window ring, or from the input for tokens of this call), computes
+// per-channel key and per-token value parameters, and writes the page.
+template <int D, int KB, int VB, int G>
+__global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
+  constexpr int NKB = D / 32, NCG = D / G;
+  constexpr int CPG = G / kChunk;
+  __shared__ float kx[G * D];
+  __shared__ __half vx[G * D];  // values are fp16 after entry conversion
+  __shared__ float ks[D], kmn[D];
+  __shared__ float vs[G * NCG], vmn[G * NCG];
+
+  const Layout& L = a.L;
+  const int tid = threadIdx.x;
+  const int64_t g = a.g_first + blockIdx.x;
+  const int64_t slice = blockIdx.y;
+  const int64_t in_base = slice * a.T * D;  // [B][H_kv] flattened == slice
+  uint8_t* ring = a.cache;
+
+  // 1. gather (entry conversion of new tokens; window tokens are fp16 already)
+  bool any_new = false;
+  for (int idx = tid; idx < G * D; idx += blockDim.x) {
+    int i = idx / D, c = idx % D;
+    int64_t p = g * G + i;
+    if (p >= a.n_old) {
+      int64_t src = in_base + (p - a.n_old) * D + c;
+      kx[idx] = load_in(a.k, a.in_dtype, src);
+      vx[idx] = __float2half_rn(load_in(a.v, a.in_dtype, src));
+    } else {
+      const uint8_t* rc = ring + ring_chunk_offset(L, slice, p);
+      int t = static_cast<int>(p % kChunk);
+      kx[idx] = __half2float(*reinterpret_cast<const __half*>(rc + ring_k_offset(L, t, c)));
+      vx[idx] = *reinterpret_cast<const __half*>(rc + ring_v_offset(L, t, c));
+    }
+  }
+  any_new = (g * G + G) > a.n_old;
+  __syncthreads();
+  if (any_new) {
+    // rows [first_new, G) come from the input: rotate (keys) then round to fp16
+    int first_new = a.n_old > g * G ? static_cast<int>(a.n_old - g * G) : 0;
+    if (a.rotate) fwht_rows<D>(kx + first_new * D, G - first_new, tid, blockDim.x);
+    for (int idx = first_new * D + tid; idx < G * D; idx += blockDim.x) kx[idx] = round_fp16(kx[idx]);
+    __syncthreads();
+  }
+
+  uint8_t* page = a.cache + page_offset(L, slice, g);
+
+  // 2. parameters: keys per channel over G tokens, values per token over G channels
+  for (int c = tid; c < D; c += blockDim.x) {
+    float mn = kx[c], mx = kx[c];
+    for (int i = 1; i < G; ++i) {
+      float x = kx[i * D + c];
+      mn = x < mn ? x : mn;
+      mx = x > mx ? x : mx;
+    }
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
+    float s = (mx - mn) / static_cast<float>((1 << KB) - 1);
+    ks[c] = s;
+    kmn[c] = mn;
+    uint16_t* kp = reinterpret_cast<uint16_t*>(page + L.off_kparams);
+    int pi = kparam_index(L, c);
+    kp[pi] = fp16_bits(s);
+    kp[D + pi] = fp16_bits(mn);
+  }
+  for (int task = tid; task < G * NCG; task += blockDim.x) {
+    int i = task / NCG, cg = task % NCG;
+    const __half* row = vx + i * D + cg * G;
+    float mn = __half2float(row[0]), mx = mn;
+    for (int c = 1; c < G; ++c) {
+      float x = __half2float(row[c]);
+      mn = x < mn ? x : mn;
+      mx = x > mx ? x : mx;
+    }
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
+    float s = (mx - mn) / static_cast<float>((1 << VB) - 1);
+    vs[task] = s;
+    vmn[task] = mn;
+    uint32_t* vp = reinterpret_cast<uint32_t*>(page + L.off_vparams + (i / kChunk) * L.vp_chunk_bytes);
+    vp[vparam_index(L, i % kChunk, cg)] = static_cast<uint32_t>(fp16_bits(s)) |
+                                          (static_cast<uint32_t>(fp16_bits(mn)) << 16);
+  }
+  __syncthreads();
+
+  // 3. key codes: each task assembles one dword of one lane of one chunk
+  {
+    constexpr int KW = 2 * NKB * KB / 4;
+    constexpr float KL = static_cast<float>((1 << KB) - 1);
+    for (int task = tid; task < CPG * kLanes * KW; task += blockDim.x) {
+      int ch = task / (kLanes * KW);
+      int l = (task / KW) % kLanes;
+      int d = task % KW;
+      int l16 = l & 15, j = l >> 4;
+      uint32_t word = 0;
+      constexpr int SUBS = KB == 4 ? 1 : 2;
+      for (int sub = 0; sub < SUBS; ++sub) {
+        int combo = KB == 4 ? d : 2 * d + sub;
+        int mt = combo / NKB, kb = combo % NKB;
+        int i = ch * kChunk + 16 * mt + l16;  // token within the group
+        for (int e = 0; e < 8; ++e) {
+          int c = 32 * kb + 8 * j + e;
+          uint32_t code = quant_code(kx[i * D + c], kmn[c], ks[c], KL);
+          int bit = KB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
+          word |= code << bit;
+        }
+      }
+      *reinterpret_cast<uint32_t*>(page + L.off_kcodes + ch * L.kc_chunk_bytes + lane_dword_offset(KW, l, d)) = word;
+    }
+  }
+  // 4. value codes
+  {
+    constexpr int NMT = D / 16;
+    constexpr int VW = NMT * VB / 4;
+    constexpr float VL = static_cast<float>((1 << VB) - 1);
+    for (int task = tid; task < CPG * kLanes * VW; task += blockDim.x) {
+      int ch = task / (kLanes * VW);
+      int l = (task / VW) % kLanes;
+      int d = task % VW;
+      int l16 = l & 15, j = l >> 4;
+      uint32_t word = 0;
+      constexpr int SUBS = VB == 4 ? 1 : 2;
+      for (int sub = 0; sub < SUBS; ++sub) {
+        int mt = VB == 4 ? d : 2 * d + sub;
+        int c = 16 * mt + l16;
+        int cg = c / G;
+        for (int e = 0; e < 8; ++e) {
+          int i = ch * kChunk + tau(j, e);
+          uint32_t code = quant_code(__half2float(vx[i * D + c]), vmn[i * NCG + cg], vs[i * NCG + cg], VL);
+          int bit = VB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
+          word |= code << bit;
+        }
+      }
+      *reinterpret_cast<uint32_t*>(page + L.off_vcodes + ch * L.vc_chunk_bytes + lane_dword_offset(VW, l, d)) = word;
+    }
+  }
+}
+
+// One block of D threads per (window position written, slice).
+template <int D>
+__global__ __launch_bounds__(128) void window_write_kernel(AppendArgs a) {
+  __shared__ float kx[D];
+  const Layout& L = a.L;
+  const int c = threadIdx.x;
+  const int64_t p = a.w_first + blockIdx.x;
+  const int64_t slice = blockIdx.y;
+  const int64_t src = (slice * a.T + (p - a.n_old)) * D + c;
+  kx[c] = load_in(a.k, a.in_dtype, src);
+  float v = round_fp16(load_in(a.v, a.in_dtype, src));
+  __syncthreads();
+  if (a.rotate) fwht_rows<D>(kx, 1, c, D);
+  uint8_t* rc = a.cache + ring_chunk_offset(L, slice, p);
+  int t = static_cast<int>(p % kChunk);
+  *reinterpret_cast<__half*>(rc + ring_k_offset(L, t, c)) = __float2half_rn(kx[c]);
+  *reinterpret_cast<__half*>(rc + ring_v_offset(L, t, c)) = __float2half_rn(v);
+}
+
+template <int D, int KB, int VB, int G>
+hipError_t flush_t(const AppendArgs& a, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(a.n_flush), static_cast<unsigned>(a.L.slices));
+  hipLaunchKernelGGL((flush_kernel<D, KB, VB, G>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int KB, int VB>
+hipError_t flush_g(const AppendArgs& a, hipStream_t s) {
+  return a.L.G == 32 ? flush_t<D, KB, VB, 32>(a, s) : flush_t<D, KB, VB, 64>(a, s);
+}
+
+template <int D, int KB>
+hipError_t flush_v(const AppendArgs& a, hipStream_t s) {
+  return a.L.vbits == 2 ? flush_g<D, KB, 2>(a, s) : flush_g<D, KB, 4>(a, s);
+}
+
+template <int D>
+hipError_t flush_k(const AppendArgs& a, hipStream_t s) {
+  return a.L.kbits == 2 ? flush_v<D, 2>(a, s) : flush_v<D, 4>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_flush(const AppendArgs& a, hipStream_t s) {
+  if (a.n_flush <= 0) return hipSuccess;
+  return a.L.D == 64 ? flush_k<64>(a, s) : flush_k<128>(a, s);
+}
+
+hipError_t launch_window_write(const AppendArgs& a, hipStream_t s) {
+  if (a.n_write <= 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(a.n_write), static_cast<unsigned>(a.L.slices));
+  if (a.L.D == 64)
+    hipLaunchKernelGGL((window_write_kernel<64>), grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((window_write_kernel<128>), grid, dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

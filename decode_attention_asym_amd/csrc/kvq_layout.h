@@ -1,0 +1,191 @@
+// kvq_layout.h -- device memory layout of the packed KV cache.
+//
+// The cache is laid out so that every wave of the decode kernel reads each
+// 32-token chunk with one 16-byte load per lane per 1 KiB, and so that the
+// dwords a lane receives are exactly its operands of the
+// v_mfma_f32_16x16x32_f16 instruction after a two-operation unpack.
+//
+// MFMA operand convention used throughout (wave64, lane l, l16 = l % 16,
+// j = l / 16, element e = 0..7 of the lane's eight fp16 operand values):
+//   A (16 x 32, M x K): row l16, column 8j + e
+//   B (32 x 16, K x N): row 8j + e, column l16
+//   C (16 x 16):        rows 4j + r (r = 0..3), column l16
+//
+// Keys (QK^T): A = key codes, rows = 16 tokens of an M-tile mt (0 or 1 of a
+// 32-token chunk), columns = 32 channels of k-block kb; B = scaled queries,
+// columns = query heads.  C row 4j + r of tile mt is token 16 mt + 4j + r.
+//
+// Values (PV): A = value codes transposed, rows = 16 channels of M-tile mt,
+// columns = the 32 tokens of the chunk in the order tau(j, e) below; B =
+// softmax weights times value scales, columns = query heads.  tau makes lane
+// (head l16, j) own exactly the tokens whose scores it holds in the C tiles
+// of the QK step, so no data moves between lanes between the two products:
+//   tau(j, e) = 4j + e           for e < 4
+//             = 16 + 4j + e - 4  for e >= 4
+//
+// Code unpack: a 32-bit word w holds fields for two fp16 lanes of a half8
+// (low half -> even e, high half -> odd e).  (w & mask) | 0x64006400 turns a
+// b-bit field at bit position p of each half into the fp16 value
+// 1024 + 2^p * code, exactly; a shift by 8 brings the upper byte of each half
+// down.  The 2^p factors are folded into the other operand (powers of two,
+// exact) and the 1024 offsets are removed by a per-group correction.
+//
+//   4-bit word, operand pair i = e >> 1: field at 4 * (i & 1) after shifting
+//     by 8 * (i >> 1); multiplier 16^(i & 1).  Bit of element e:
+//     16 * (e & 1) + 4 * (e >> 1).
+//   2-bit word holds two sub-blocks s (low byte, high byte of each half):
+//     element e of sub-block s at bit 16 * (e & 1) + 8 * s + 2 * (e >> 1);
+//     multiplier 4^(e >> 1).
+#pragma once
+
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define KVQ_HD __host__ __device__ __forceinline__
+#else
+#define KVQ_HD inline
+#endif
+
+namespace kvq {
+
+constexpr int kChunk = 32;     // tokens per chunk (the K of the PV MFMA)
+constexpr int kLanes = 64;
+
+struct Layout {
+  int D, kbits, vbits, G, R;
+  int nkb, nmt, ncg;            // D/32 key k-blocks, D/16 value M-tiles, D/G value groups
+  int chunks_per_group;         // G / 32
+  int kw, vw;                   // dwords per lane per chunk of key / value codes
+  int64_t kc_chunk_bytes;       // key code bytes of one chunk
+  int64_t vc_chunk_bytes;
+  int64_t vp_chunk_bytes;       // value scale/zero bytes of one chunk
+  int64_t kp_bytes;             // key scale + zero bytes of one group
+  int64_t off_kcodes, off_kparams, off_vcodes, off_vparams, page_bytes;
+  int64_t pages;                // pages (token groups) per slice
+  int cap;                      // window ring slots per slice (R + G)
+  int ring_chunks;              // cap / 32
+  int64_t ring_chunk_bytes;     // K part then V part, fp16, 32 * D * 2 each
+  int64_t slices;               // B * H_kv
+  int64_t pages_offset, ring_offset, total_bytes;
+};
+
+KVQ_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int vbits, int G, int R) {
+  Layout L{};
+  L.D = D; L.kbits = kbits; L.vbits = vbits; L.G = G; L.R = R;
+  L.nkb = D / 32; L.nmt = D / 16; L.ncg = D / G;
+  L.chunks_per_group = G / kChunk;
+  L.kw = 2 * L.nkb * kbits / 4;            // 4-bit: one dword per (mt, kb); 2-bit: half of that
+  L.vw = L.nmt * vbits / 4;                // 4-bit: one dword per mt; 2-bit: half
+  L.kc_chunk_bytes = (int64_t)kLanes * L.kw * 4;
+  L.vc_chunk_bytes = (int64_t)kLanes * L.vw * 4;
+  L.vp_chunk_bytes = (int64_t)kChunk * L.ncg * 4;
+  L.kp_bytes = (int64_t)D * 4;
+  L.off_kcodes = 0;
+  L.off_kparams = L.off_kcodes + L.chunks_per_group * L.kc_chunk_bytes;
+  L.off_vcodes = L.off_kparams + L.kp_bytes;
+  L.off_vparams = L.off_vcodes + L.chunks_per_group * L.vc_chunk_bytes;
+  L.page_bytes = L.off_vparams + L.chunks_per_group * L.vp_chunk_bytes;
+  int64_t over = (int64_t)max_tokens - R;
+  L.pages = over > 0 ? over / G : 0;
+  L.cap = R + G;
+  L.ring_chunks = L.cap / kChunk;
+  L.ring_chunk_bytes = (int64_t)kChunk * D * 2 * 2;
+  L.slices = (int64_t)B * Hkv;
+  L.pages_offset = 0;
+  L.ring_offset = align_up(L.slices * L.pages * L.page_bytes, 256);
+  L.total_bytes = align_up(L.ring_offset + L.slices * L.ring_chunks * L.ring_chunk_bytes, 256);
+  return L;
+}
+
+// ---- token order of the PV step -------------------------------------------
+KVQ_HD int tau(int j, int e) { return e < 4 ? 4 * j + e : 16 + 4 * j + (e - 4); }
+KVQ_HD void tau_inv(int t, int* j, int* e) {
+  if (t < 16) { *j = t >> 2; *e = t & 3; }
+  else { *j = (t - 16) >> 2; *e = 4 + (t & 3); }
+}
+
+// Byte offset, inside a chunk's code block, of dword d of lane l when each
+// lane holds w dwords stored as 16-byte vectors (w >= 4) or one w-dword vector.
+KVQ_HD int64_t lane_dword_offset(int w, int l, int d) {
+  int vw = w >= 4 ? 4 : w;
+  return (int64_t)(d / vw) * (kLanes * vw * 4) + (int64_t)l * vw * 4 + (d % vw) * 4;
+}
+
+// Location of the key code of token t (0..31 within its chunk), channel c.
+KVQ_HD void kcode_loc(const Layout& L, int t, int c, int64_t* byte, int* bit) {
+  int mt = t >> 4, t16 = t & 15;
+  int kb = c >> 5, j = (c >> 3) & 3, e = c & 7;
+  int l = j * 16 + t16;
+  int combo = mt * L.nkb + kb;
+  if (L.kbits == 4) {
+    *byte = lane_dword_offset(L.kw, l, combo);
+    *bit = 16 * (e & 1) + 4 * (e >> 1);
+  } else {
+    *byte = lane_dword_offset(L.kw, l, combo >> 1);
+    *bit = 16 * (e & 1) + 8 * (combo & 1) + 2 * (e >> 1);
+  }
+}
+
+// Location of the value code of token t (0..31 within its chunk), channel c.
+KVQ_HD void vcode_loc(const Layout& L, int t, int c, int64_t* byte, int* bit) {
+  int mt = c >> 4, c16 = c & 15;
+  int j, e;
+  tau_inv(t, &j, &e);
+  int l = j * 16 + c16;
+  if (L.vbits == 4) {
+    *byte = lane_dword_offset(L.vw, l, mt);
+    *bit = 16 * (e & 1) + 4 * (e >> 1);
+  } else {
+    *byte = lane_dword_offset(L.vw, l, mt >> 1);
+    *bit = 16 * (e & 1) + 8 * (mt & 1) + 2 * (e >> 1);
+  }
+}
+
+// Index (in fp16 elements) of channel c's key scale within a group's scale
+// row; the zero row follows the scale row (D elements later).  Lane group j
+// reads its 8 * nkb channels {32 kb + 8 j + e} as one contiguous run.
+KVQ_HD int kparam_index(const Layout& L, int c) {
+  int kb = c >> 5, j = (c >> 3) & 3, e = c & 7;
+  return j * (L.D / 4) + kb * 8 + e;
+}
+
+// Dword index, inside a chunk's value-parameter block, of (token t, value
+// group cg); the dword holds scale (low half) and zero (high half).
+KVQ_HD int vparam_index(const Layout& L, int t, int cg) {
+  int j, e;
+  tau_inv(t, &j, &e);
+  return (j * 8 + e) * L.ncg + cg;
+}
+
+// Byte offsets inside a ring chunk of the fp16 window copy of token t, channel c.
+// Keys are stored as the QK A operand, values as the PV A operand.
+KVQ_HD int64_t ring_k_offset(const Layout& L, int t, int c) {
+  int mt = t >> 4, t16 = t & 15;
+  int kb = c >> 5, j = (c >> 3) & 3, e = c & 7;
+  int l = j * 16 + t16;
+  return ((int64_t)(mt * L.nkb + kb) * kLanes + l) * 16 + e * 2;
+}
+KVQ_HD int64_t ring_v_offset(const Layout& L, int t, int c) {
+  int mt = c >> 4, c16 = c & 15;
+  int j, e;
+  tau_inv(t, &j, &e);
+  int l = j * 16 + c16;
+  return (int64_t)kChunk * L.D * 2 + ((int64_t)mt * kLanes + l) * 16 + e * 2;
+}
+
+// Address helpers (byte offsets from the cache base).
+KVQ_HD int64_t page_offset(const Layout& L, int64_t slice, int64_t g) {
+  return L.pages_offset + (slice * L.pages + g) * L.page_bytes;
+}
+KVQ_HD int64_t ring_chunk_offset(const Layout& L, int64_t slice, int64_t pos) {
+  return L.ring_offset + (slice * L.ring_chunks + (pos / kChunk) % L.ring_chunks) * L.ring_chunk_bytes;
+}
+
+KVQ_HD int64_t num_quantized(int64_t n, int G, int R) {
+  int64_t over = n - R;
+  return over > 0 ? over / G * G : 0;
+}
+
+}  // namespace kvq

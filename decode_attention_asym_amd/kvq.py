@@ -1,0 +1,223 @@
+"""Thin ctypes binding of libkvq.so (include/kvq.h): argument marshalling only.
+
+Every step of the quantize-append and decode-attention path runs in the HIP
+kernels behind the C ABI; PyTorch provides device memory and streams.  If the
+library is not built this module raises on import -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+KVQ_OK, KVQ_E_ARG, KVQ_E_UNSUPPORTED, KVQ_E_CAPACITY, KVQ_E_DEVICE, KVQ_E_STATE = range(6)
+STATUS_NAMES = ["KVQ_OK", "KVQ_E_ARG", "KVQ_E_UNSUPPORTED", "KVQ_E_CAPACITY", "KVQ_E_DEVICE", "KVQ_E_STATE"]
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+
+# entry points declared in include/kvq.h, with (restype, argtypes)
+_P, _SZ, _I32, _I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32),
+        ("k_bits", ctypes.c_int32),
+        ("v_bits", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("residual", ctypes.c_int32),
+        ("rotate", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+    ]
+
+
+_CFG_P = ctypes.POINTER(kvq_config)
+SIGNATURES = {
+    "kvq_cache_bytes": (_SZ, [_CFG_P]),
+    "kvq_workspace_bytes": (_SZ, [_CFG_P]),
+    "kvq_create": (ctypes.c_int, [_CFG_P, _P, _SZ, ctypes.POINTER(_P)]),
+    "kvq_append": (ctypes.c_int, [_P, _P, _P, _I32, _P]),
+    "kvq_decode_attn": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
+    "kvq_decode_attn_splits": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _I32, _P]),
+    "kvq_default_splits": (_I32, [_P]),
+    "kvq_num_tokens": (_I64, [_P]),
+    "kvq_num_quantized": (_I64, [_P]),
+    "kvq_reset": (ctypes.c_int, [_P]),
+    "kvq_destroy": (ctypes.c_int, [_P]),
+    "kvq_last_error": (ctypes.c_char_p, []),
+    "kvq_export": (ctypes.c_int, [_P, _I32, _I32] + [_P] * 8 + [_P]),
+    "kvq_import": (ctypes.c_int, [_P, _I64, _I32, _I32] + [_P] * 8 + [_P]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(or python decode_attention_asym_amd/build.py). There is no CPU fallback."
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class KVQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.kvq_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {STATUS_NAMES[status] if 0 <= status < 6 else status}: {msg}")
+
+
+def check(status: int, where: str) -> None:
+    if status != KVQ_OK:
+        raise KVQError(status, where)
+
+
+@dataclass
+class Config:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    max_tokens: int
+    k_bits: int
+    v_bits: int
+    group_size: int
+    residual: int
+    rotate: bool = False
+    in_dtype: str = "bf16"
+
+    def c(self) -> kvq_config:
+        return kvq_config(
+            ctypes.sizeof(kvq_config), self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
+            self.max_tokens, self.k_bits, self.v_bits, self.group_size, self.residual, int(bool(self.rotate)),
+            DTYPES[self.in_dtype],
+        )
+
+
+def cache_bytes(cfg: Config) -> int:
+    c = cfg.c()
+    return int(lib.kvq_cache_bytes(ctypes.byref(c)))
+
+
+def workspace_bytes(cfg: Config) -> int:
+    c = cfg.c()
+    return int(lib.kvq_workspace_bytes(ctypes.byref(c)))
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+
+        return int(torch.cuda.current_stream().cuda_stream)
+    return int(stream)
+
+
+class KVQCache:
+    """A quantized KV cache in a torch-allocated device buffer.
+
+    append(k, v): k, v [B, H_kv, T, D] contiguous tensors of the config dtype.
+    decode(q, out=None): q [B, H_q, D]; returns out [B, H_q, D] float32.
+    """
+
+    def __init__(self, cfg: Config, device="cuda"):
+        import torch
+
+        self.cfg = cfg
+        nbytes = cache_bytes(cfg)
+        if nbytes == 0:
+            raise KVQError(KVQ_E_UNSUPPORTED if lib.kvq_last_error() else KVQ_E_ARG, "kvq_cache_bytes")
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(max(workspace_bytes(cfg), 16), dtype=torch.uint8, device=device)
+        h = ctypes.c_void_p()
+        c = cfg.c()
+        check(lib.kvq_create(ctypes.byref(c), self.buf.data_ptr(), nbytes, ctypes.byref(h)), "kvq_create")
+        self.h = h
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h:
+            lib.kvq_destroy(h)
+            self.h = None
+
+    @property
+    def num_tokens(self) -> int:
+        return int(lib.kvq_num_tokens(self.h))
+
+    @property
+    def num_quantized(self) -> int:
+        return int(lib.kvq_num_quantized(self.h))
+
+    def default_splits(self) -> int:
+        return int(lib.kvq_default_splits(self.h))
+
+    def append(self, k, v, stream=None) -> None:
+        T = k.shape[2]
+        check(lib.kvq_append(self.h, _ptr(k), _ptr(v), T, _stream(stream)), "kvq_append")
+
+    def decode(self, q, out=None, splits: int | None = None, stream=None):
+        import torch
+
+        if out is None:
+            out = torch.empty((self.cfg.batch, self.cfg.num_q_heads, self.cfg.head_dim), dtype=torch.float32,
+                              device=q.device)
+        if splits is None:
+            st = lib.kvq_decode_attn(self.h, _ptr(q), _ptr(out), _ptr(self.ws), self.ws.numel(), _stream(stream))
+        else:
+            st = lib.kvq_decode_attn_splits(self.h, _ptr(q), _ptr(out), _ptr(self.ws), self.ws.numel(), splits,
+                                            _stream(stream))
+        check(st, "kvq_decode_attn")
+        return out
+
+    def reset(self) -> None:
+        check(lib.kvq_reset(self.h), "kvq_reset")
+
+    def export(self, batch_begin: int = 0, batch_count: int | None = None, stream=None):
+        """Canonical host arrays (numpy) for sequences [batch_begin, batch_begin + batch_count)."""
+        import numpy as np
+
+        c = self.cfg
+        bc = c.batch - batch_begin if batch_count is None else batch_count
+        nq, n = self.num_quantized, self.num_tokens
+        nr, D, G, H = n - nq, c.head_dim, c.group_size, c.num_kv_heads
+        out = {
+            "k_codes": np.zeros((bc, H, nq, D * c.k_bits // 8), np.uint8),
+            "k_scale": np.zeros((bc, H, nq // G, D), np.uint16),
+            "k_zero": np.zeros((bc, H, nq // G, D), np.uint16),
+            "v_codes": np.zeros((bc, H, nq, D * c.v_bits // 8), np.uint8),
+            "v_scale": np.zeros((bc, H, nq, D // G), np.uint16),
+            "v_zero": np.zeros((bc, H, nq, D // G), np.uint16),
+            "k_resid": np.zeros((bc, H, nr, D), np.uint16),
+            "v_resid": np.zeros((bc, H, nr, D), np.uint16),
+        }
+        keys = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")
+        check(lib.kvq_export(self.h, batch_begin, bc, *(out[k].ctypes.data for k in keys), _stream(stream)),
+              "kvq_export")
+        out["nq"], out["n"] = nq, n
+        return out
+
+    def import_(self, arrays, n_tokens: int, batch_begin: int = 0, stream=None) -> None:
+        import numpy as np
+
+        keys = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")
+        arrs = [np.ascontiguousarray(arrays[k]) for k in keys]
+        bc = arrs[0].shape[0]
+        check(lib.kvq_import(self.h, n_tokens, batch_begin, bc, *(a.ctypes.data for a in arrs), _stream(stream)),
+              "kvq_import")

@@ -1,0 +1,172 @@
+/*
+ * kvq.h -- C ABI of libkvq: asymmetric low-bit KV-cache quantization fused
+ * into single-query decode attention, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (pages cited by title and section):
+ *   - Keys are quantized per channel, with min/max statistics over groups of
+ *     G consecutive tokens; values are quantized per token, with statistics
+ *     over groups of G consecutive channels; the most recent tokens stay in
+ *     an fp16 window and are never quantized.  "[Framework] The Asymmetric
+ *     Key-Value Cache Compression", section III (KIVI partitioning);
+ *     "Asymmetric Key-Value Quantization: 2-Bit Values and 4-Bit Keys under
+ *     Long-Context Drift", section 3.1 (keys per channel at 4 bits, values
+ *     per token at 2 bits).
+ *   - Each group stores an fp16 scale and an fp16 zero (the group minimum);
+ *     codes are round-half-even((x - min) / scale) with scale =
+ *     (max - min) / (2^b - 1) in IEEE binary32 (the textbook asymmetric
+ *     uniform quantizer; the pages name the scheme but print no formula).
+ *   - Optionally keys (at append) and queries (at decode) are rotated by the
+ *     normalized Walsh-Hadamard transform, "[Framework] ...", section IV
+ *     (stage 1, Y = X H, computed with the fast transform).
+ *   - Decode attention is softmax(q K^T / sqrt(d)) V over every cached token,
+ *     "Asymmetric Key-Value Quantization ...", section 1, computed directly
+ *     on the packed cache (split over the token axis, merged with the
+ *     online-softmax rule).
+ *
+ * Conventions for every entry point:
+ *   - All device buffers are owned by the caller.  The library never
+ *     allocates or frees device memory; a handle holds host metadata only.
+ *   - Device pointers must be 16-byte aligned (the cache buffer 256-byte
+ *     aligned) unless stated otherwise.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Device work is enqueued on it and the call returns without waiting,
+ *     except kvq_export / kvq_import, which synchronize the stream.
+ *   - Every call validates its arguments before enqueueing anything.  Errors
+ *     are returned as kvq_status; nothing is thrown or aborted across the ABI.
+ *     kvq_last_error() gives a message for the calling thread's last error.
+ *   - After a device launch error (KVQ_E_DEVICE) the handle is poisoned:
+ *     later calls on it return KVQ_E_STATE.  A handle is not thread-safe.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_E_ARG = 1,         /* null / misaligned pointer, bad size, workspace too small */
+  KVQ_E_UNSUPPORTED = 2, /* configuration outside what the kernels implement */
+  KVQ_E_CAPACITY = 3,    /* append would exceed max_tokens; nothing was changed */
+  KVQ_E_DEVICE = 4,      /* a HIP call or kernel launch failed; handle poisoned */
+  KVQ_E_STATE = 5        /* handle poisoned, or an operation invalid in this state */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_F16 = 1, KVQ_BF16 = 2 } kvq_dtype;
+
+typedef struct {
+  uint32_t struct_size; /* must equal sizeof(kvq_config) */
+  int32_t batch;        /* B >= 1 sequences, advancing in lockstep */
+  int32_t num_q_heads;  /* H_q; a multiple of num_kv_heads, H_q / H_kv in {1, 2, 4, 8, 16} */
+  int32_t num_kv_heads; /* H_kv >= 1; query head h uses kv head h / (H_q / H_kv) */
+  int32_t head_dim;     /* D in {64, 128} */
+  int32_t max_tokens;   /* capacity per sequence, >= 1 */
+  int32_t k_bits;       /* key code width in {2, 4} */
+  int32_t v_bits;       /* value code width in {2, 4} */
+  int32_t group_size;   /* G in {32, 64}: tokens per key group, channels per value group; G <= D */
+  int32_t residual;     /* R: recent tokens kept in fp16; a multiple of 32, 0 <= R <= 1024 */
+  int32_t rotate;       /* 0 or 1: Walsh-Hadamard rotation of keys (append) and queries (decode) */
+  int32_t in_dtype;     /* kvq_dtype of the k, v and q buffers passed in */
+} kvq_config;
+
+/* Device bytes the cache buffer must hold for `cfg`, or 0 if `cfg` is
+ * invalid or unsupported (kvq_last_error says why). */
+size_t kvq_cache_bytes(const kvq_config* cfg);
+
+/* Device bytes of workspace kvq_decode_attn may need for `cfg` at any split
+ * count it chooses (split partials: B * H_q * S_max * (D + 2) floats).
+ * 0 if `cfg` is invalid. */
+size_t kvq_workspace_bytes(const kvq_config* cfg);
+
+/* Create a handle over the caller's device buffer `cache_buf` of
+ * `cache_bytes` >= kvq_cache_bytes(cfg) bytes (256-byte aligned).  The cache
+ * starts empty (0 tokens per sequence).  No device work is done.  The buffer
+ * contents need no initialization.  On success *out receives the handle. */
+kvq_status kvq_create(const kvq_config* cfg, void* cache_buf, size_t cache_bytes, kvq_cache** out);
+
+/* Append n_tokens tokens to every sequence.
+ *   k, v: device, [B][H_kv][n_tokens][D] contiguous, elements of in_dtype.
+ * Each element is widened to fp32; keys are rotated if cfg.rotate; then every
+ * element is rounded to fp16 (round-to-nearest-even) and lands in the fp16
+ * window.  Whenever the window holds R + G tokens the oldest G are quantized
+ * (keys per channel, values per token) into packed codes with fp16
+ * scale/zero, so after n tokens floor(max(0, n - R) / G) * G tokens are
+ * quantized and the rest are in the window.  A prefill is one call with
+ * n_tokens = N; a decode step appends 1.  Appending one token at a time gives
+ * bit-identical cache contents to one call with all of them.
+ * n_tokens == 0 is a no-op.  Exceeding max_tokens returns KVQ_E_CAPACITY
+ * and changes nothing.  The k and v buffers may be reused once the work
+ * enqueued on `stream` has completed. */
+kvq_status kvq_append(kvq_cache* cache, const void* k, const void* v, int32_t n_tokens, void* stream);
+
+/* Decode attention of one query per head over all cached tokens.
+ *   q:   device, [B][H_q][D] contiguous, elements of in_dtype.
+ *   out: device, [B][H_q][D] fp32, out = softmax(q K^T / sqrt(D)) V with K, V
+ *        the dequantized cache (keys rotated and q rotated when cfg.rotate).
+ *   workspace: device scratch of ws_bytes >= kvq_workspace_bytes(cfg); its
+ *        contents on entry do not matter and are clobbered.
+ * The split count over the token axis is chosen from the cache shape and the
+ * number of compute units.  Requires at least one cached token
+ * (KVQ_E_STATE otherwise). */
+kvq_status kvq_decode_attn(kvq_cache* cache, const void* q, float* out, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/* As kvq_decode_attn with an explicit split count 1 <= num_splits <= the
+ * S_max sized by kvq_workspace_bytes (values above the number of token
+ * groups are clamped).  Any split count gives the same result up to
+ * floating-point summation order. */
+kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, void* workspace, size_t ws_bytes,
+                                  int32_t num_splits, void* stream);
+
+/* Split count kvq_decode_attn would use for the current token count. */
+int32_t kvq_default_splits(const kvq_cache* cache);
+
+/* Tokens per sequence currently cached, and how many of them are quantized. */
+int64_t kvq_num_tokens(const kvq_cache* cache);
+int64_t kvq_num_quantized(const kvq_cache* cache);
+
+/* Forget all tokens (n = 0).  No device work. */
+kvq_status kvq_reset(kvq_cache* cache);
+
+/* Free the host handle (never the caller's device buffers).  NULL is a no-op. */
+kvq_status kvq_destroy(kvq_cache* cache);
+
+/* Message for the calling thread's most recent non-OK status ("" if none). */
+const char* kvq_last_error(void);
+
+/* Canonical (layout-independent) form of the cache for sequences
+ * [batch_begin, batch_begin + batch_count), all kv heads, with
+ * nq = kvq_num_quantized, nr = n - nq.  Host buffers; any may be NULL to skip:
+ *   k_codes  uint8  [bc][H_kv][nq][D*k_bits/8]  codes packed along channels,
+ *                   little-endian: channel c at bit k_bits*(c mod (8/k_bits))
+ *                   of byte floor(k_bits*c/8)
+ *   k_scale, k_zero uint16 fp16 bits [bc][H_kv][nq/G][D]   (per channel, per token group)
+ *   v_codes  uint8  [bc][H_kv][nq][D*v_bits/8]
+ *   v_scale, v_zero uint16 fp16 bits [bc][H_kv][nq][D/G]   (per token, per channel group)
+ *   k_resid, v_resid uint16 fp16 bits [bc][H_kv][nr][D]     (the fp16 window, oldest first)
+ * Synchronizes `stream`, then copies and converts.  For checkpoints and tests. */
+kvq_status kvq_export(kvq_cache* cache, int32_t batch_begin, int32_t batch_count, void* k_codes, void* k_scale,
+                      void* k_zero, void* v_codes, void* v_scale, void* v_zero, void* k_resid, void* v_resid,
+                      void* stream);
+
+/* Inverse of kvq_export: write canonical arrays (same shapes, none NULL) for
+ * sequences [batch_begin, batch_begin + batch_count) holding n_tokens tokens
+ * each into the device cache, and set the cache's token count to n_tokens
+ * (every sequence shares one count, so import every sequence before decoding).
+ * Synchronizes `stream`.  KVQ_E_CAPACITY if n_tokens > max_tokens. */
+kvq_status kvq_import(kvq_cache* cache, int64_t n_tokens, int32_t batch_begin, int32_t batch_count,
+                      const void* k_codes, const void* k_scale, const void* k_zero, const void* v_codes,
+                      const void* v_scale, const void* v_zero, const void* k_resid, const void* v_resid,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

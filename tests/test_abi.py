@@ -1,0 +1,110 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point
+include/kvq.h declares, and validates arguments on the host (no device work,
+no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared()
+    for n in ("kvq_create", "kvq_append", "kvq_decode_attn"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    from decode_attention_asym_amd import kvq
+
+    raw = ctypes.CDLL(kvq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert set(_declared()) == set(kvq.SIGNATURES), "binding and header disagree"
+
+
+def _cfg(**kw):
+    from decode_attention_asym_amd import Config
+
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, max_tokens=1000, k_bits=4, v_bits=2,
+                group_size=64, residual=128, rotate=False, in_dtype="bf16")
+    base.update(kw)
+    return Config(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(head_dim=96), dict(k_bits=3), dict(v_bits=8), dict(group_size=16), dict(residual=48),
+    dict(num_q_heads=6, num_kv_heads=2), dict(num_q_heads=64, num_kv_heads=2),
+    dict(batch=0), dict(max_tokens=0), dict(head_dim=64, group_size=128),
+])
+def test_invalid_configs_rejected(bad):
+    import decode_attention_asym_amd as kvq
+
+    assert kvq.cache_bytes(_cfg(**bad)) == 0
+    assert kvq.lib.kvq_last_error()
+
+
+def test_cache_bytes_matches_bit_accounting():
+    """Quantized pages hold exactly codes + fp16 scale/zero (the oracle's bits
+    per element), plus a fp16 window ring of R + G tokens per slice."""
+    import decode_attention_asym_amd as kvq
+    import oracle
+
+    for kb, vb, G, R, D in ((4, 2, 64, 128, 128), (2, 2, 32, 32, 128), (2, 4, 32, 64, 64)):
+        n = 10000
+        c = _cfg(k_bits=kb, v_bits=vb, group_size=G, residual=R, head_dim=D, max_tokens=n,
+                 num_q_heads=2, num_kv_heads=2)
+        nq = oracle.num_quantized(n, G, R)
+        quant_bits = oracle.bits_per_element(n, kb, vb, G, R) * 2 * n * D - 2 * 16 * (n - nq) * D
+        ring = (R + G) * D * 2 * 2
+        total = kvq.cache_bytes(c)
+        slices = c.batch * c.num_kv_heads
+        assert total >= slices * (quant_bits / 8 + ring)
+        assert total <= slices * (quant_bits / 8 + ring) + 512
+
+
+def test_host_validation_without_device_work():
+    import decode_attention_asym_amd as kvq
+    from decode_attention_asym_amd.kvq import lib
+
+    c = _cfg()
+    cc = c.c()
+    need = kvq.cache_bytes(c)
+    fake = 1 << 40  # never dereferenced: every call below fails or returns before device work
+    h = ctypes.c_void_p()
+    assert lib.kvq_create(ctypes.byref(cc), None, need, ctypes.byref(h)) == kvq.KVQ_E_ARG
+    assert lib.kvq_create(ctypes.byref(cc), fake + 16, need, ctypes.byref(h)) == kvq.KVQ_E_ARG  # misaligned
+    assert lib.kvq_create(ctypes.byref(cc), fake, need - 1, ctypes.byref(h)) == kvq.KVQ_E_ARG   # too small
+    assert lib.kvq_create(ctypes.byref(cc), fake, need, ctypes.byref(h)) == kvq.KVQ_OK
+    try:
+        assert lib.kvq_num_tokens(h) == 0
+        assert lib.kvq_append(h, fake, fake, 0, None) == kvq.KVQ_OK  # no-op
+        assert lib.kvq_append(h, fake, fake, -1, None) == kvq.KVQ_E_ARG
+        assert lib.kvq_append(h, None, fake, 5, None) == kvq.KVQ_E_ARG
+        assert lib.kvq_append(h, fake, fake, 1001, None) == kvq.KVQ_E_CAPACITY
+        assert lib.kvq_num_tokens(h) == 0
+        assert lib.kvq_decode_attn(h, fake, fake, fake, 1 << 30, None) == kvq.KVQ_E_STATE  # empty cache
+        assert b"empty" in lib.kvq_last_error()
+        assert lib.kvq_reset(h) == kvq.KVQ_OK
+    finally:
+        assert lib.kvq_destroy(h) == kvq.KVQ_OK
+    assert lib.kvq_destroy(None) == kvq.KVQ_OK
+    cc.struct_size = 4
+    assert lib.kvq_create(ctypes.byref(cc), fake, need, ctypes.byref(h)) == kvq.KVQ_E_ARG
+
+
+def test_workspace_bounds_split_request():
+    import decode_attention_asym_amd as kvq
+
+    for w in ("tiny", "big"):
+        c = _cfg(batch=1 if w == "tiny" else 64, num_kv_heads=8, num_q_heads=32)
+        ws = kvq.workspace_bytes(c)
+        assert ws > 0 and ws % 16 == 0

@@ -1,0 +1,172 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the
+same seeded inputs.  Codes, fp16 scales/zeros and the fp16 window must match
+bit for bit; attention must be within relative L2 2e-3 of the oracle's fp64
+attention on the exported (dequantized) cache."""
+import numpy as np
+import pytest
+import torch
+
+from _parity import (TOL_REL_L2, assert_export_matches, log, oracle_encode_slices, oracle_rows, rel_l2)
+from synth import WORKLOADS, Synth, to_oracle_input
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import decode_attention_asym_amd as kvq
+
+    return kvq
+
+
+def _run_prefill(w, max_tokens=None, seed_positions=None):
+    kvq = _lib()
+    syn = Synth(w, "cuda", positions=seed_positions)
+    K, V = syn.kv_all()
+    cache = kvq.KVQCache(kvq.config_for(w, max_tokens))
+    cache.append(K, V)
+    q = syn.q()
+    return syn, K, V, q, cache
+
+
+def _check_full(w, splits=None, check_codes=True, batches=None):
+    log(f"[parity] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} N={w.N} K{w.kbits}V{w.vbits} G={w.G} R={w.R} "
+        f"rot={w.rotate} {w.dtype} splits={splits}")
+    syn, K, V, q, cache = _run_prefill(w)
+    out = cache.decode(q, splits=splits)
+    torch.cuda.synchronize()
+    batches = list(range(w.B)) if batches is None else batches
+    q_host = to_oracle_input(q, w.dtype)
+    res = []
+    for b in batches:
+        exp = cache.export(b, 1)
+        if check_codes:
+            encs = oracle_encode_slices(w, K, V, [(b, h) for h in range(w.Hkv)])
+            assert_export_matches(w, exp, b, encs)
+        ref = oracle_rows(w, exp, b, q_host, [b])[b]
+        res.append((out[b].double().cpu().numpy(), ref))
+    got = np.stack([r[0] for r in res])
+    ref = np.stack([r[1] for r in res])
+    err, worst = rel_l2(got, ref)
+    log(f"[parity] {w.name}: rel L2 {err:.3e} (worst row {worst:.3e}) over batches {batches[:4]}...")
+    assert err <= TOL_REL_L2
+    return cache, K, V, q, out
+
+
+SMALL = [
+    WORKLOADS[0],
+    WORKLOADS[2].replace(name="k4v2-g64-drift-ragged", B=2, N=4096 + 77),
+    WORKLOADS[3].replace(name="gqa8-r32-ragged", B=1, N=8192 + 45),
+    WORKLOADS[4].replace(name="mha-fwht-ragged", B=2, Hq=8, Hkv=8, N=2048 + 13),
+    WORKLOADS[1].replace(name="d64-k4v4-g64-gqa2-f16", B=3, Hq=4, Hkv=2, D=64, N=1000, kbits=4, vbits=4, G=64, R=64, dtype="f16"),
+    WORKLOADS[1].replace(name="k2v4-g32-gqa16-r0", B=1, Hq=32, Hkv=2, N=700, kbits=2, vbits=4, G=32, R=0),
+    WORKLOADS[0].replace(name="d64-rot-k4v2-g32", B=2, Hq=4, Hkv=4, N=333, kbits=4, vbits=2, rotate=True),
+    WORKLOADS[1].replace(name="window-only", B=2, N=100, R=128),
+    WORKLOADS[1].replace(name="single-token", B=2, N=1, R=32),
+    WORKLOADS[1].replace(name="window-full", B=2, N=128 + 31, R=128),
+    WORKLOADS[1].replace(name="first-flush", B=2, N=128 + 32, R=128),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_prefill_bitexact_and_decode(w):
+    _check_full(w)
+
+
+def test_llama8b_8k_full():
+    """The 8B-shaped 8k workload at full size: every slice bit-exact, every row checked."""
+    _check_full(WORKLOADS[1])
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 16])
+def test_split_counts_agree(splits):
+    w = WORKLOADS[1].replace(name="splits", B=2, N=3000 + 17)
+    _check_full(w, splits=splits, check_codes=(splits == 1))
+
+
+def test_stepwise_append_equals_prefill():
+    kvq = _lib()
+    w = WORKLOADS[2].replace(name="stepwise", B=2, Hkv=2, Hq=8, N=700)
+    syn = Synth(w, "cuda")
+    K, V = syn.kv_all()
+    a = kvq.KVQCache(kvq.config_for(w))
+    a.append(K, V)
+    b = kvq.KVQCache(kvq.config_for(w))
+    sizes = [1, 1, 7, 64, 1, 100, 3, 128, 65, 1, 1, 200]
+    sizes.append(w.N - sum(sizes))
+    t = 0
+    for s in sizes:
+        b.append(K[:, :, t:t + s].contiguous(), V[:, :, t:t + s].contiguous())
+        t += s
+    assert a.num_tokens == b.num_tokens == w.N
+    ea, eb = a.export(), b.export()
+    for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid"):
+        assert np.array_equal(ea[key], eb[key]), key
+    encs = oracle_encode_slices(w, K, V, [(bb, h) for bb in range(w.B) for h in range(w.Hkv)])
+    assert_export_matches(w, ea, 0, encs)
+
+
+def test_import_then_decode_matches_oracle():
+    """Decode on a cache the oracle encoded (imported), independent of the GPU quantizer."""
+    kvq = _lib()
+    w = WORKLOADS[1].replace(name="import", B=2, N=2000 + 5)
+    syn = Synth(w, "cpu")
+    K, V = syn.kv_all()
+    encs = oracle_encode_slices(w, K, V, [(b, h) for b in range(w.B) for h in range(w.Hkv)])
+    import oracle
+
+    arrays = {}
+    for key, bits in (("k_codes", w.kbits), ("v_codes", w.vbits)):
+        arrays[key] = np.stack([np.stack([oracle.pack_codes(encs[(b, h)][key], bits) for h in range(w.Hkv)])
+                                for b in range(w.B)])
+    for key in ("k_scale", "k_zero", "v_scale", "v_zero", "k_resid", "v_resid"):
+        arrays[key] = np.stack([np.stack([encs[(b, h)][key] for h in range(w.Hkv)]) for b in range(w.B)])
+    cache = kvq.KVQCache(kvq.config_for(w))
+    cache.import_(arrays, w.N)
+    exp = cache.export()
+    for key in arrays:
+        assert np.array_equal(exp[key], arrays[key]), key
+    q = syn.q().cuda()
+    out = cache.decode(q)
+    ref = oracle_rows(w, exp, 0, to_oracle_input(q, w.dtype), range(w.B))
+    err, worst = rel_l2(out.double().cpu().numpy(), np.stack([ref[b] for b in range(w.B)]))
+    log(f"[parity] import: rel L2 {err:.3e} worst row {worst:.3e}")
+    assert err <= TOL_REL_L2
+
+
+def test_identical_keys_give_mean_of_values():
+    kvq = _lib()
+    w = WORKLOADS[1].replace(name="identical-keys", B=1, Hq=4, Hkv=1, N=900)
+    syn = Synth(w, "cuda")
+    K, V = syn.kv_all()
+    K = K[:, :, :1, :].expand(-1, -1, w.N, -1).contiguous()
+    cache = kvq.KVQCache(kvq.config_for(w))
+    cache.append(K, V)
+    out = cache.decode(syn.q() * 4)
+    exp = cache.export()
+    # dequantized values: per token zero + code * scale
+    import oracle
+
+    codes = oracle.unpack_codes(exp["v_codes"][0, 0], w.D, w.vbits).astype(np.float64)
+    f = lambda a: a.view(np.float16).astype(np.float64)
+    vq = f(exp["v_zero"][0, 0]).repeat(w.G, 1) + codes * f(exp["v_scale"][0, 0]).repeat(w.G, 1)
+    mean = np.concatenate([vq, f(exp["v_resid"][0, 0])]).mean(0)
+    err = np.abs(out[0].double().cpu().numpy() - mean[None]).max()
+    assert err < 1e-3 * np.abs(mean).max() + 1e-4
+
+
+def test_capacity_and_empty_errors():
+    kvq = _lib()
+    w = WORKLOADS[0].replace(name="cap", N=64)
+    syn = Synth(w, "cuda")
+    K, V = syn.kv_all()
+    cache = kvq.KVQCache(kvq.config_for(w, max_tokens=100))
+    with pytest.raises(kvq.KVQError) as ei:
+        cache.decode(syn.q())
+    assert ei.value.status == kvq.KVQ_E_STATE
+    cache.append(K, V)
+    with pytest.raises(kvq.KVQError) as ei:
+        cache.append(K, V)  # 128 > 100
+    assert ei.value.status == kvq.KVQ_E_CAPACITY
+    assert cache.num_tokens == 64
+    out = cache.decode(syn.q())
+    assert torch.isfinite(out).all()
