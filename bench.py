@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the quantized-KV decode attention path on one MI355X.
+
+A step is one pass of the whole hot path on one batch: append one token per
+sequence (entry conversion, fp16 window write, and a group flush whenever the
+window fills) and decode attention of one query per head over the whole
+cache (split kernel + cross-split merge).  Inputs are seeded synthetic
+tensors already resident in HBM; the cache is prefilled before timing.
+
+Prints one JSON line.  `value` is achieved HBM throughput of the whole step
+(algorithmic bytes: packed codes + fp16 scales/zeros + fp16 window + q + out
++ the append's own bytes, divided by the measured step time).  `roofline`
+covers the dominant kernel (the split decode kernel), timed with HIP events
+on the stream it runs on; `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized-KV decode attention: µs/step + achieved HBM GB/s (8B-shape, 32k ctx)"
+HBM_PEAK_GBS = 8000.0
+
+
+def in_bytes(w) -> int:
+    return 4 if w.dtype == "f32" else 2
+
+
+def decode_bytes(w, n: int) -> int:
+    """Algorithmic bytes of one decode over n cached tokens per sequence."""
+    nq = (max(0, n - w.R) // w.G) * w.G
+    nr = n - nq
+    per_quant_token = w.D * (w.kbits + w.vbits) // 8 + 4 * w.D // w.G + 4 * (w.D // w.G)
+    per_window_token = 4 * w.D  # fp16 K and V
+    cache = w.B * w.Hkv * (nq * per_quant_token + nr * per_window_token)
+    return cache + w.B * w.Hq * w.D * (in_bytes(w) + 4)
+
+
+def append_bytes(w, n_before: int) -> int:
+    """Algorithmic bytes of appending one token to sequences holding n_before."""
+    slices = w.B * w.Hkv
+    b = slices * w.D * (2 * in_bytes(w) + 4)  # read k, v; write both as fp16
+    nq0 = (max(0, n_before - w.R) // w.G) * w.G
+    nq1 = (max(0, n_before + 1 - w.R) // w.G) * w.G
+    if nq1 > nq0:  # one group flushed: read its fp16 tokens, write the page
+        page = w.G * w.D * (w.kbits + w.vbits) // 8 + 4 * w.D + w.G * 4 * (w.D // w.G)
+        b += slices * (w.G * w.D * 4 + page)
+    return b
+
+
+def cpu_baseline(w, K_host, V_host, q_host, batches, threads: int) -> dict:
+    """Time the oracle's decode step (fp64 dequant + attention) on the sampled
+    batch rows (all kv heads), then scale to the full step."""
+    import oracle
+    from synth import to_oracle_input
+
+    pairs = [(b, h) for b in batches for h in range(w.Hkv)]
+    from concurrent.futures import ThreadPoolExecutor
+
+    def enc(bh):
+        b, h = bh
+        return oracle.encode_slice(to_oracle_input(K_host[b][h], w.dtype), to_oracle_input(V_host[b][h], w.dtype),
+                                   w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate)
+
+    with ThreadPoolExecutor(threads) as ex:
+        encs = list(ex.map(enc, pairs))
+    jobs = []
+    for (b, h), e in zip(pairs, encs):
+        q = oracle.input_to_f64(to_oracle_input(q_host[b], w.dtype), w.dtype).reshape(w.Hq, w.D)
+        if w.rotate:
+            import numpy as np
+
+            q = np.stack([oracle.rotate_f64(x) for x in q])
+        jobs.append((q[h * w.gqa:(h + 1) * w.gqa], e, w.D, w.G, w.R))
+    t0 = time.perf_counter()
+    oracle.attend_slices_parallel(jobs, threads)
+    dt = time.perf_counter() - t0
+    full = dt * (w.B * w.Hkv) / len(pairs)
+    return {
+        "value": round(decode_bytes(w, w.N) / full / 1e9, 3),
+        "unit": "GB/s",
+        "us_per_step": round(full * 1e6, 1),
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"decode step (fp64 dequant + attention) over {len(pairs)} of {w.B * w.Hkv} (batch, kv-head) "
+                  f"slices at {w.N} tokens, {dt:.2f} s wall on {threads} threads, scaled by slice count",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64, help="timed steps (64 spans one group flush at G=64)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 32k K4/V2 layer)")
+    ap.add_argument("--splits", type=int, default=0, help="split count (0: the library's default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-batches", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (this path has no multi-GPU "
+              f"mode: every (batch, kv-head) slice is independent, see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import decode_attention_asym_amd as kvq
+    from decode_attention_asym_amd.kvq import merge_partials
+    from synth import WORKLOADS, Synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = WORKLOADS[args.workload]
+    total = args.warmup + args.steps
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    syn = Synth(w, dev, positions=w.N + total + 1)
+    cache = kvq.KVQCache(kvq.config_for(w, max_tokens=w.N + total), device=dev)
+
+    print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
+    K, V = syn.kv_all()
+    batches = list(range(min(args.cpu_sample_batches, w.B)))
+    K_host = [K[b].cpu() for b in batches] if not args.no_cpu_baseline else None
+    V_host = [V[b].cpu() for b in batches] if not args.no_cpu_baseline else None
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cache.append(K, V)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    del K, V
+    torch.cuda.empty_cache()
+    print(f"[bench] prefill {w.N} tokens: {prefill_ms:.2f} ms", file=sys.stderr, flush=True)
+
+    step_kv = [syn.step_kv(i) for i in range(total)]
+    qs = [syn.q(i) for i in range(total)]
+    rows = w.B * w.Hq
+    S = args.splits or cache.default_splits()
+    partials = torch.empty((rows, S, w.D + 4), dtype=torch.float32, device=dev)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+
+    def step(i, evs=None):
+        k, v = step_kv[i]
+        cache.append(k, v)
+        if evs:
+            evs[0].record()
+        if S > 1:
+            _, used = cache.decode_partials(qs[i], partials, splits=S)
+            if evs:
+                evs[1].record()
+            merge_partials(partials, out, rows, used, w.D)
+        else:
+            cache.decode(qs[i], out, splits=1)
+            if evs:
+                evs[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n0 = cache.num_tokens
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    step_bytes = [decode_bytes(w, n0 + i + 1) + append_bytes(w, n0 + i) for i in range(args.steps)]
+    dec_bytes = [decode_bytes(w, n0 + i + 1) for i in range(args.steps)]
+    value = sum(step_bytes) / (ms_total * 1e-3) / 1e9
+    achieved = (sum(dec_bytes) / len(dec_bytes)) / (dec_avg_ms * 1e-3) / 1e9
+    assert torch.isfinite(out).all()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from synth import to_oracle_input  # noqa: F401
+
+        threads = min(16, len(os.sched_getaffinity(0)))
+        print(f"[bench] cpu baseline on {threads} threads", file=sys.stderr, flush=True)
+        q0 = syn.q(0).cpu()
+        cpu = cpu_baseline(w, K_host, V_host, q0, batches, threads)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "dtype_detail": f"u{w.kbits}/u{w.vbits} codes and fp16 scale/zero/window; fp16 MFMA operands, fp32 accumulate and softmax; {w.dtype} inputs",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+            "context": w.N, "k_bits": w.kbits, "v_bits": w.vbits, "group": w.G, "residual": w.R,
+            "rotate": w.rotate, "splits": S, "parallelism": "single-gpu",
+        },
+        "roofline": {
+            "kernel": "decode_kernel (split dequant-attention)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_us": round(dec_avg_ms * 1e3, 2),
+            "bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes)),
+        },
+        "prefill_ms": round(prefill_ms, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

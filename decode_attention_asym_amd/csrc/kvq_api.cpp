@@ -210,12 +210,15 @@ int32_t kvq_default_splits(const kvq_cache* h) {
   return choose_splits(const_cast<kvq_cache*>(h));
 }
 
-kvq_status kvq_decode_attn_splits(kvq_cache* h, const void* q, float* out, void* ws, size_t ws_bytes,
-                                  int32_t num_splits, void* stream) {
+namespace {
+
+// Validate and launch the split kernel; write_final selects direct output (S == 1).
+kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partials, size_t bytes, int32_t num_splits,
+                         bool allow_final, int32_t* splits_used, hipStream_t s) {
   kvq_status st = check_handle(h);
   if (st != KVQ_OK) return st;
   if (h->n <= 0) return fail(KVQ_E_STATE, "decode on an empty cache");
-  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return fail(KVQ_E_ARG, "q/out NULL or not 16-byte aligned");
+  if (!q || !aligned(q, 16)) return fail(KVQ_E_ARG, "q NULL or not 16-byte aligned");
   if (num_splits < 1) return fail(KVQ_E_ARG, "num_splits %d < 1", num_splits);
   if (num_splits > max_splits(&h->cfg))
     return fail(KVQ_E_ARG, "num_splits %d above the workspace maximum %d", num_splits, max_splits(&h->cfg));
@@ -225,10 +228,13 @@ kvq_status kvq_decode_attn_splits(kvq_cache* h, const void* q, float* out, void*
   int64_t gps = ng > 0 ? (ng + S - 1) / S : 0;
   if (gps > 0) S = (ng + gps - 1) / gps;  // no empty split
   const int64_t rows = static_cast<int64_t>(c.batch) * c.num_q_heads;
-  if (S > 1) {
+  const bool final = allow_final && S == 1;
+  if (final) {
+    if (!out || !aligned(out, 16)) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
+  } else {
     size_t need = static_cast<size_t>(rows * S * (c.head_dim + 4) * sizeof(float));
-    if (!ws || !aligned(ws, 16) || ws_bytes < need)
-      return fail(KVQ_E_ARG, "workspace NULL, misaligned or %zu < %zu bytes", ws_bytes, need);
+    if (!partials || !aligned(partials, 16) || bytes < need)
+      return fail(KVQ_E_ARG, "workspace/partials NULL, misaligned or %zu < %zu bytes", bytes, need);
   }
   kvq::DecodeArgs a{};
   a.cache = h->buf;
@@ -245,15 +251,43 @@ kvq_status kvq_decode_attn_splits(kvq_cache* h, const void* q, float* out, void*
   a.groups_per_split = gps;
   a.rc0 = kvq::num_quantized(h->n, c.group_size, c.residual) / kvq::kChunk;
   a.rc1 = (h->n + kvq::kChunk - 1) / kvq::kChunk;
-  a.partial = static_cast<float*>(ws);
+  a.partial = partials;
   a.out = out;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  a.write_final = final ? 1 : 0;
   hipError_t e = kvq::launch_decode(a, s);
   if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
-  if (S > 1) {
-    e = kvq::launch_merge(static_cast<float*>(ws), out, static_cast<int>(rows), static_cast<int>(S), c.head_dim, s);
-    if (e != hipSuccess) return device_error(h, e, "merge kernel launch");
-  }
+  if (splits_used) *splits_used = static_cast<int32_t>(S);
+  return ok();
+}
+
+}  // namespace
+
+kvq_status kvq_decode_attn_splits(kvq_cache* h, const void* q, float* out, void* ws, size_t ws_bytes,
+                                  int32_t num_splits, void* stream) {
+  if (!out || !aligned(out, 16)) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t S = 0;
+  kvq_status st = launch_splits(h, q, out, static_cast<float*>(ws), ws_bytes, num_splits, true, &S, s);
+  if (st != KVQ_OK || S == 1) return st;
+  const int64_t rows = static_cast<int64_t>(h->cfg.batch) * h->cfg.num_q_heads;
+  hipError_t e = kvq::launch_merge(static_cast<float*>(ws), out, static_cast<int>(rows), S, h->cfg.head_dim, s);
+  if (e != hipSuccess) return device_error(h, e, "merge kernel launch");
+  return ok();
+}
+
+kvq_status kvq_decode_partials(kvq_cache* h, const void* q, float* partials, size_t bytes, int32_t num_splits,
+                               int32_t* splits_used, void* stream) {
+  return launch_splits(h, q, nullptr, partials, bytes, num_splits, false, splits_used, static_cast<hipStream_t>(stream));
+}
+
+kvq_status kvq_merge_partials(const float* partials, float* out, int32_t rows, int32_t splits, int32_t head_dim,
+                              void* stream) {
+  if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16))
+    return fail(KVQ_E_ARG, "partials/out NULL or not 16-byte aligned");
+  if (rows < 1 || splits < 1) return fail(KVQ_E_ARG, "rows and splits must be positive");
+  if (head_dim != 64 && head_dim != 128) return fail(KVQ_E_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  hipError_t e = kvq::launch_merge(partials, out, rows, splits, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVQ_E_DEVICE, "merge kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -318,10 +352,9 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
           }
         }
         for (int cg = 0; cg < ncg; ++cg) {
-          uint32_t w;
-          std::memcpy(&w, page + L.off_vparams + ch * L.vp_chunk_bytes + 4 * kvq::vparam_index(L, tt, cg), 4);
-          if (v_scale) static_cast<uint16_t*>(v_scale)[(oi * nq + t) * ncg + cg] = static_cast<uint16_t>(w);
-          if (v_zero) static_cast<uint16_t*>(v_zero)[(oi * nq + t) * ncg + cg] = static_cast<uint16_t>(w >> 16);
+          const uint16_t* vpp = reinterpret_cast<const uint16_t*>(page + L.off_vparams + ch * L.vp_chunk_bytes);
+          if (v_scale) static_cast<uint16_t*>(v_scale)[(oi * nq + t) * ncg + cg] = vpp[kvq::vparam_scale_elem(L, tt, cg)];
+          if (v_zero) static_cast<uint16_t*>(v_zero)[(oi * nq + t) * ncg + cg] = vpp[kvq::vparam_zero_elem(L, tt, cg)];
         }
       }
       for (int64_t g = 0; g < ng; ++g) {
@@ -390,9 +423,9 @@ kvq_status kvq_import(kvq_cache* h, int64_t n_tokens, int32_t b0, int32_t bc, co
           std::memcpy(&w, dst, 4); w |= code << bit; std::memcpy(dst, &w, 4);
         }
         for (int cg = 0; cg < ncg; ++cg) {
-          uint32_t w = static_cast<uint32_t>(static_cast<const uint16_t*>(v_scale)[(oi * nq + t) * ncg + cg]) |
-                       (static_cast<uint32_t>(static_cast<const uint16_t*>(v_zero)[(oi * nq + t) * ncg + cg]) << 16);
-          std::memcpy(page + L.off_vparams + ch * L.vp_chunk_bytes + 4 * kvq::vparam_index(L, tt, cg), &w, 4);
+          uint16_t* vpp = reinterpret_cast<uint16_t*>(page + L.off_vparams + ch * L.vp_chunk_bytes);
+          vpp[kvq::vparam_scale_elem(L, tt, cg)] = static_cast<const uint16_t*>(v_scale)[(oi * nq + t) * ncg + cg];
+          vpp[kvq::vparam_zero_elem(L, tt, cg)] = static_cast<const uint16_t*>(v_zero)[(oi * nq + t) * ncg + cg];
         }
       }
       for (int64_t g = 0; g < ng; ++g) {

@@ -140,9 +140,9 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
     float s = (mx - mn) / static_cast<float>((1 << VB) - 1);
     vs[task] = s;
     vmn[task] = mn;
-    uint32_t* vp = reinterpret_cast<uint32_t*>(page + L.off_vparams + (i / kChunk) * L.vp_chunk_bytes);
-    vp[vparam_index(L, i % kChunk, cg)] = static_cast<uint32_t>(fp16_bits(s)) |
-                                          (static_cast<uint32_t>(fp16_bits(mn)) << 16);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(page + L.off_vparams + (i / kChunk) * L.vp_chunk_bytes);
+    vp[vparam_scale_elem(L, i % kChunk, cg)] = fp16_bits(s);
+    vp[vparam_zero_elem(L, i % kChunk, cg)] = fp16_bits(mn);
   }
   __syncthreads();
 

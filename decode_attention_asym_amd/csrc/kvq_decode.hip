@@ -139,59 +139,163 @@ __device__ __forceinline__ float load_q(const void* p, int dtype, int64_t i) {
 __device__ __forceinline__ float h2f_lo(uint32_t w) { return __half2float(__ushort_as_half(static_cast<uint16_t>(w))); }
 __device__ __forceinline__ float h2f_hi(uint32_t w) { return __half2float(__ushort_as_half(static_cast<uint16_t>(w >> 16))); }
 
-template <int D, int KB, int VB, int G>
+// All arithmetic helpers below are plain C++ (no inline assembly), so the
+// compiler sees every VGPR they write and inserts the wait states an MFMA
+// needs before reading a freshly written operand.
+__device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
+__device__ __forceinline__ uint32_t as_u32(half2v x) { return __builtin_bit_cast(uint32_t, x); }
+// fp16 pair (fp16(a0 * s.lo), fp16(a1 * s.hi)) from fp32 a and an fp16 pair s,
+// each rounded once (fma with +0 keeps the product and selects v_fma_mix*).
+__device__ __forceinline__ uint32_t mix_mul2(float a0, float a1, uint32_t s) {
+  const half2v sv = as_h2(s);
+  const half2v r = {static_cast<_Float16>(__builtin_fmaf(a0, static_cast<float>(sv[0]), 0.0f)),
+                    static_cast<_Float16>(__builtin_fmaf(a1, static_cast<float>(sv[1]), 0.0f))};
+  return as_u32(r);
+}
+// fp16 pair (fp16(a0 * s.lo + c.lo), fp16(a1 * s.hi + c.hi)), one rounding each.
+__device__ __forceinline__ uint32_t mix_fma2(float a0, float a1, uint32_t s, uint32_t c) {
+  const half2v sv = as_h2(s), cv = as_h2(c);
+  const half2v r = {static_cast<_Float16>(__builtin_fmaf(a0, static_cast<float>(sv[0]), static_cast<float>(cv[0]))),
+                    static_cast<_Float16>(__builtin_fmaf(a1, static_cast<float>(sv[1]), static_cast<float>(cv[1])))};
+  return as_u32(r);
+}
+__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) { return as_u32(as_h2(a) * as_h2(b)); }
+// Sum with the lane 8 places away inside each row of 16 (row_ror:8): lanes h
+// and h + 8 both receive x_h + x_{h+8}.
+__device__ __forceinline__ float add_ror8(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+
+// ---- LDS staging of the code stream ----------------------------------------
+// Chunks are copied global -> LDS with gfx950's direct loads (no VGPRs held
+// while in flight), several chunks ahead of the one being processed.  The
+// copies are issued from inline assembly so the compiler neither reorders nor
+// conservatively waits for them; the kernel waits with explicit vmcnt values
+// (every vector-memory instruction of the main loop is one of these copies,
+// issued in a fixed pattern, and vector memory returns in order).
+#define KVQ_AS3 __attribute__((address_space(3)))
+
+// The destination LDS address is taken from M0; an LDS-DMA instruction that
+// reads M0 right after an SALU write of it needs a wait state (s_nop) or it
+// may see the previous value.  Outstanding LDS reads are drained first so a
+// slot is never overwritten while still being read.
+// 1 KiB: lane l copies global [base + 16 l, +16) to LDS [lds + 16 l, +16)
+__device__ __forceinline__ void dma_1k(const uint8_t* gbase, uint32_t lane16, uint32_t lds) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(lane16), "s"(gbase), "s"(lds) : "memory", "m0");
+}
+// 256 B: lane l copies global [base + 4 l, +4) to LDS [lds + 4 l, +4)
+__device__ __forceinline__ void dma_256(const uint8_t* gbase, uint32_t lane4, uint32_t lds) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(lane4), "s"(gbase), "s"(lds) : "memory", "m0");
+}
+template <int BYTES>
+__device__ __forceinline__ void dma_block(const uint8_t* g, uint32_t lane16, uint32_t lane4, uint32_t lds) {
+  static_assert(BYTES % 256 == 0, "DMA blocks are whole 256-byte units");
+#pragma unroll
+  for (int o = 0; o + 1024 <= BYTES; o += 1024) dma_1k(g + o, lane16, lds + o);
+#pragma unroll
+  for (int o = BYTES / 1024 * 1024; o < BYTES; o += 256) dma_256(g + o, lane4, lds + o);
+}
+template <int BYTES>
+constexpr int dma_count() { return BYTES / 1024 + (BYTES % 1024) / 256; }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Two-part fp16 operand of x = a * s (a fp32, s an fp16 pair): part 0 = fp16(x),
+// part 1 = fp16(x - fp16(x)).  In column-split mode each lane produces the
+// part selected by negf (0: part 0, fp16 -1 pair: part 1); otherwise both.
+__device__ __forceinline__ uint32_t split_part(float a0, float a1, uint32_t s, uint32_t negf) {
+  uint32_t t = mix_mul2(a0, a1, s);
+  return mix_fma2(a0, a1, s, pk_mul_f16(t, negf));
+}
+
+// Running-max slack of the online softmax (base-2 units): the accumulators
+// are rescaled only when a chunk's maximum exceeds the running maximum by more
+// than this, so weights stay <= 2^0.5 and the fp16 PV operand p * scale stays
+// below 65504 for any scale of fp16 data.
+constexpr float kMaxSlack = 0.5f;
+
+template <int D, int KB, int VB, int G, bool CS>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   constexpr int NKB = D / 32, NMT = D / 16, NCG = D / G, CPG = G / kChunk;
-  constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4;
+  constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4, VPW = 8 * NCG;
+  // B operands carry each value as two fp16 parts (hi + lo) so the folded
+  // products keep ~22 bits: in CS mode (at most 8 heads) hi sits in columns
+  // 0-7 and lo in columns 8-15 of one MFMA; otherwise two MFMAs.
+  constexpr int NP = CS ? 1 : 2;
   const Layout& L = a.L;
   const int l = threadIdx.x, l16 = l & 15, j = l >> 4;
   const int S = a.splits;
   const int64_t slice = blockIdx.x / S;
   const int s = static_cast<int>(blockIdx.x % S);
   const int b = static_cast<int>(slice / a.Hkv), hkv = static_cast<int>(slice % a.Hkv);
-  const bool hv = l16 < a.gqa;
-  const int hq = hkv * a.gqa + (hv ? l16 : 0);
+  const int h = CS ? (l16 & 7) : l16;
+  const bool lo_lane = CS && l16 >= 8;
+  const bool hv = h < a.gqa;
+  const int hq = hkv * a.gqa + (hv ? h : 0);
+  const uint32_t negf_p0 = lo_lane ? 0xBC00BC00u : 0u;  // this lane's part (CS mode)
 
-  // ---- query: lane owns channels 32 kb + 8 j + e of head l16, times log2(e)/sqrt(D)
-  float qv[NKB][8];
+  // ---- query: lane owns channels 32 kb + 8 j + e of head h, times log2(e)/sqrt(D)
+  float qm[NKB][8];
   const float qscale = kLog2e * (D == 128 ? 0.08838834764831845f : 0.125f);
   if (a.rotate) {
     extern __shared__ float qsh[];  // gqa * D floats, sized at launch
     const int64_t base = (static_cast<int64_t>(b) * a.Hq + hkv * a.gqa) * D;
     for (int idx = l; idx < a.gqa * D; idx += kLanes) qsh[idx] = load_q(a.q, a.in_dtype, base + idx);
     __syncthreads();
-    for (int h = 1; h < D; h <<= 1) {
+    for (int hh = 1; hh < D; hh <<= 1) {
       for (int k = l; k < a.gqa * (D / 2); k += kLanes) {
         int r = k / (D / 2), p = k % (D / 2);
-        int i0 = r * D + (p / h) * 2 * h + (p % h);
-        float x0 = qsh[i0], x1 = qsh[i0 + h];
+        int i0 = r * D + (p / hh) * 2 * hh + (p % hh);
+        float x0 = qsh[i0], x1 = qsh[i0 + hh];
         qsh[i0] = x0 + x1;
-        qsh[i0 + h] = x0 - x1;
+        qsh[i0 + hh] = x0 - x1;
       }
       __syncthreads();
     }
+    const float rs = qscale * (D == 128 ? 0.08838834764831845f : 0.125f);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        qv[kb][e] = hv ? qsh[(hv ? l16 : 0) * D + 32 * kb + 8 * j + e] * (qscale * (D == 128 ? 0.08838834764831845f : 0.125f)) : 0.0f;
+        qm[kb][e] = hv ? qsh[(hv ? h : 0) * D + 32 * kb + 8 * j + e] * rs : 0.0f;
   } else {
     const int64_t base = (static_cast<int64_t>(b) * a.Hq + hq) * D;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[kb][e] = hv ? load_q(a.q, a.in_dtype, base + 32 * kb + 8 * j + e) * qscale : 0.0f;
+      for (int e = 0; e < 8; ++e) qm[kb][e] = hv ? load_q(a.q, a.in_dtype, base + 32 * kb + 8 * j + e) * qscale : 0.0f;
   }
-  // qm = q / mult: the B operand of QK^T is fp16(qm * key scale)
-  float qm[NKB][8];
+  // B operand of the zero-point term (the query itself, two parts): once per split
+  uint32_t bqv[NP][NKB][4];
+  {
+    const uint32_t one = 0x3C003C00u;  // fp16 1.0 pair
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (CS) {
+          bqv[0][kb][i] = split_part(qm[kb][2 * i], qm[kb][2 * i + 1], one, negf_p0);
+        } else {
+          uint32_t t = mix_mul2(qm[kb][2 * i], qm[kb][2 * i + 1], one);
+          bqv[0][kb][i] = t;
+          bqv[NP - 1][kb][i] = mix_fma2(qm[kb][2 * i], qm[kb][2 * i + 1], one, pk_mul_f16(t, 0xBC00BC00u));
+        }
+      }
+  }
+  // qm = q / mult: the folded B operand of QK^T is qm * key scale
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qm[kb][e] = qv[kb][e] * (1.0f / code_mult<KB>(e));
+    for (int e = 0; e < 8; ++e) qm[kb][e] *= (1.0f / code_mult<KB>(e));
 
   const Unpack uk = make_unpack<KB>();
   const Unpack uv = make_unpack<VB>();
-  const half2v neg1024 = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-1024.0f)};
+  const half8 aneg = __builtin_bit_cast(half8, u32x4{0xE400E400u, 0xE400E400u, 0xE400E400u, 0xE400E400u});
 
   float m = -INFINITY, lsum = 0.0f;
   f32x4 acc[NMT];
@@ -203,11 +307,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
   // online softmax over one chunk's 8 scores per lane (tokens tau(j, e))
   auto softmax_step = [&](float (&sc)[8], float (&p)[8]) {
-    float cmax = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, sc[e]);
+    float cmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     cmax = wave_max_j(cmax);
-    if (__any(cmax > m)) {
+    if (__any(cmax > m + kMaxSlack)) {
       float mnew = fmaxf(m, cmax);
       float al = __builtin_amdgcn_exp2f(m - mnew);
 #pragma unroll
@@ -224,108 +326,216 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  const int64_t g0 = static_cast<int64_t>(s) * a.groups_per_split;
-  const int64_t g1 = g0 + a.groups_per_split < a.ngroups ? g0 + a.groups_per_split : a.ngroups;
-  for (int64_t g = g0; g < g1; ++g) {
-    const uint8_t* page = a.cache + page_offset(L, slice, g);
-    // B operand of QK^T for this group and the per-head bias
-    half8 bq[NKB];
-    float bacc[4] = {0.f, 0.f, 0.f, 0.f};
-    float corr = 0.0f;
-    {
-      const u32x4* kps = reinterpret_cast<const u32x4*>(page + L.off_kparams) + j * NKB;
-      const u32x4* kpz = reinterpret_cast<const u32x4*>(page + L.off_kparams + 2 * D) + j * NKB;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        u32x4 sw = kps[kb], zw = kpz[kb];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t sv = sw[e >> 1], zv = zw[e >> 1];
-          float sf = (e & 1) ? h2f_hi(sv) : h2f_lo(sv);
-          float zf = (e & 1) ? h2f_hi(zv) : h2f_lo(zv);
-          bq[kb][e] = static_cast<_Float16>(qm[kb][e] * sf);
-          bacc[e >> 1] += qm[kb][e] * zf;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          half2v pr = {bq[kb][2 * i], bq[kb][2 * i + 1]};
-          corr = __builtin_amdgcn_fdot2(pr, neg1024, corr, false);
-        }
-      }
-    }
-    float bias = corr;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bias += bacc[i] * code_mult<KB>(2 * i);
-    bias = wave_sum_j(bias);
+  const int64_t nchunks = a.ngroups * CPG;
+  const int64_t cb = static_cast<int64_t>(s) * a.groups_per_split * CPG;
+  const int64_t ce = cb + a.groups_per_split * CPG < nchunks ? cb + a.groups_per_split * CPG : nchunks;
 
-#pragma unroll
-    for (int ch = 0; ch < CPG; ++ch) {
-      uint32_t kw[KW], vw[VW];
-      load_lane_words<KW>(page + L.off_kcodes + ch * L.kc_chunk_bytes, l, kw);
-      load_lane_words<VW>(page + L.off_vcodes + ch * L.vc_chunk_bytes, l, vw);
-      uint32_t vp[8 * NCG];
-      {
-        const u32x4* vpp = reinterpret_cast<const u32x4*>(page + L.off_vparams + ch * L.vp_chunk_bytes) + j * 2 * NCG;
-#pragma unroll
-        for (int v = 0; v < 2 * NCG; ++v) {
-          u32x4 x = vpp[v];
-          vp[4 * v] = x[0]; vp[4 * v + 1] = x[1]; vp[4 * v + 2] = x[2]; vp[4 * v + 3] = x[3];
-        }
-      }
-      // QK^T: two 16-token tiles
-      f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+  // ---- LDS ring of NBUF chunk slots: [key codes][value codes][value params][key params]
+  constexpr int KC = kChunk * D * KB / 8, VC = kChunk * D * VB / 8;
+  constexpr int VPB = (kChunk * NCG * 4 + 255) / 256 * 256, KPB = 4 * D;
+  constexpr int SLOT = KC + VC + VPB + KPB;
+  constexpr int NBUF = 4;
+  constexpr int NBASE = dma_count<KC>() + dma_count<VC>() + dma_count<VPB>(), NKP = dma_count<KPB>();
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF * SLOT];
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((KVQ_AS3 uint8_t*)ring));
+  const uint32_t lane16 = static_cast<uint32_t>(l) * 16, lane4 = static_cast<uint32_t>(l) * 4;
+
+  // copy virtual chunk cv (clamped to the split, so the copy count per issue
+  // slot never changes) into slot cv % NBUF; a group's first chunk also
+  // carries the group's key scale/zero rows
+  auto issue = [&](int64_t cv, bool with_kp) {
+    const int64_t c = cv < ce ? cv : ce - 1;
+    const uint8_t* page = a.cache + page_offset(L, slice, c / CPG);
+    const int ch = static_cast<int>(c % CPG);
+    const uint32_t sl = ring_lds + static_cast<uint32_t>(cv % NBUF) * SLOT;
+    dma_block<KC>(page + L.off_kcodes + ch * KC, lane16, lane4, sl);
+    dma_block<VC>(page + L.off_vcodes + ch * VC, lane16, lane4, sl + KC);
+    dma_block<VPB>(page + L.off_vparams + ch * VPB, lane16, lane4, sl + KC + VC);
+    if (with_kp) dma_block<KPB>(page + L.off_kparams, lane16, lane4, sl + KC + VC + VPB);
+  };
+
+  uint32_t bq[NP][NKB][4];  // B operand of QK^T (fp16 pairs), per part
+  f32x4 cbias = {0.f, 0.f, 0.f, 0.f};  // QK accumulator start: zero-point term and offset removal
+
+  auto process = [&](const uint8_t* sl, bool group_start) {
+    if (group_start) {
+      // B operand from this group's key scales, and the bias tile (every row:
+      // sum_c q_c z_c - 1024 sum_c bq_c) by MFMA
+      const u32x4* ps = reinterpret_cast<const u32x4*>(sl + KC + VC + VPB) + j * NKB;
+      const u32x4* pz = reinterpret_cast<const u32x4*>(sl + KC + VC + VPB + 2 * D) + j * NKB;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand<KB, 8>(kw, kb, uk), bq[kb], c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand<KB, 8>(kw, NKB + kb, uk), bq[kb], c1, 0, 0, 0);
-      }
-      float sc[8], p[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sc[r] = c0[r] + bias;
-        sc[4 + r] = c1[r] + bias;
-      }
-      softmax_step(sc, p);
-      // PV B operands, one per value group, and the zero-point / offset sums
-      half8 bp[NCG];
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
-        float zsum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t w = vp[e * NCG + cg];
-          bp[cg][e] = static_cast<_Float16>(p[e] * (1.0f / code_mult<VB>(e)) * h2f_lo(w));
-          zsum += p[e] * h2f_hi(w);
-        }
+        const u32x4 sw = ps[kb];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          half2v pr = {bp[cg][2 * i], bp[cg][2 * i + 1]};
-          zsum = __builtin_amdgcn_fdot2(pr, neg1024, zsum, false);
+          const float q0 = qm[kb][2 * i], q1 = qm[kb][2 * i + 1];
+          if (CS) {
+            bq[0][kb][i] = split_part(q0, q1, sw[i], negf_p0);
+          } else {
+            uint32_t t = mix_mul2(q0, q1, sw[i]);
+            bq[0][kb][i] = t;
+            bq[NP - 1][kb][i] = mix_fma2(q0, q1, sw[i], pk_mul_f16(t, 0xBC00BC00u));
+          }
         }
-        zacc[cg] += zsum;
       }
+      cbias = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand<VB, 8>(vw, mt, uv), bp[(16 * mt) / G], acc[mt], 0, 0, 0);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const half8 az = __builtin_bit_cast(half8, pz[kb]);
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          const half8 bz = __builtin_bit_cast(half8, u32x4{bqv[pp][kb][0], bqv[pp][kb][1], bqv[pp][kb][2], bqv[pp][kb][3]});
+          const half8 bb = __builtin_bit_cast(half8, u32x4{bq[pp][kb][0], bq[pp][kb][1], bq[pp][kb][2], bq[pp][kb][3]});
+          cbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bz, cbias, 0, 0, 0);
+          cbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(aneg, bb, cbias, 0, 0, 0);
+        }
+      }
     }
+    uint32_t kw[KW], vw[VW], vp[VPW];
+    if constexpr (KW >= 4) {
+#pragma unroll
+      for (int v = 0; v < KW / 4; ++v) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(sl + v * (kLanes * 16) + l * 16);
+        kw[4 * v] = x[0]; kw[4 * v + 1] = x[1]; kw[4 * v + 2] = x[2]; kw[4 * v + 3] = x[3];
+      }
+    } else {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(sl + l * 8);
+      kw[0] = x[0]; kw[1] = x[1];
+    }
+    if constexpr (VW >= 4) {
+#pragma unroll
+      for (int v = 0; v < VW / 4; ++v) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(sl + KC + v * (kLanes * 16) + l * 16);
+        vw[4 * v] = x[0]; vw[4 * v + 1] = x[1]; vw[4 * v + 2] = x[2]; vw[4 * v + 3] = x[3];
+      }
+    } else {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(sl + KC + l * 8);
+      vw[0] = x[0]; vw[1] = x[1];
+    }
+    {
+      const u32x4* vpp = reinterpret_cast<const u32x4*>(sl + KC + VC) + j * (VPW / 4);
+#pragma unroll
+      for (int v = 0; v < VPW / 4; ++v) {
+        const u32x4 x = vpp[v];
+        vp[4 * v] = x[0]; vp[4 * v + 1] = x[1]; vp[4 * v + 2] = x[2]; vp[4 * v + 3] = x[3];
+      }
+    }
+    // QK^T: two 16-token tiles, accumulated on top of the bias tile
+    f32x4 c0 = cbias, c1 = cbias;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const half8 a0 = a_operand<KB, 8>(kw, kb, uk);
+      const half8 a1 = a_operand<KB, 8>(kw, NKB + kb, uk);
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const half8 bb = __builtin_bit_cast(half8, u32x4{bq[pp][kb][0], bq[pp][kb][1], bq[pp][kb][2], bq[pp][kb][3]});
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bb, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bb, c1, 0, 0, 0);
+      }
+    }
+    float sc[8], p[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = c0[r];
+      sc[4 + r] = c1[r];
+    }
+    if (CS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc[e] = add_ror8(sc[e]);
+    }
+    softmax_step(sc, p);
+    // PV B operands (p * value scale / mult, two parts) and the zero-point sums
+    float pm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pm[e] = p[e] * (1.0f / code_mult<VB>(e));
+    uint32_t bp[NP][NCG][4];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      float zsum = zacc[cg];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t sp = vp[cg * 8 + i], zp = vp[cg * 8 + 4 + i];
+        if (CS) {
+          bp[0][cg][i] = split_part(pm[2 * i], pm[2 * i + 1], sp, negf_p0);
+        } else {
+          uint32_t t = mix_mul2(pm[2 * i], pm[2 * i + 1], sp);
+          bp[0][cg][i] = t;
+          bp[NP - 1][cg][i] = mix_fma2(pm[2 * i], pm[2 * i + 1], sp, pk_mul_f16(t, 0xBC00BC00u));
+        }
+        zsum += p[2 * i] * h2f_lo(zp);
+        zsum += p[2 * i + 1] * h2f_hi(zp);
+      }
+      zacc[cg] = zsum;
+    }
+    // PV: codes enter as 1024 + mult * code; the constant -1024 operand removes
+    // the offset inside the same accumulator every chunk
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const half8 av = a_operand<VB, 8>(vw, mt, uv);
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const uint32_t* bw = bp[pp][(16 * mt) / G];
+        const half8 bb = __builtin_bit_cast(half8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aneg, bb, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bb, acc[mt], 0, 0, 0);
+      }
+    }
+  };
+
+  if (ce > cb) {
+    // prologue: NBUF - 1 chunks in flight (split boundaries are group-aligned)
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k) issue(cb + k, k % CPG == 0);
+    for (int64_t g = cb / CPG; g < ce / CPG; ++g) {
+#pragma unroll
+      for (int ch = 0; ch < CPG; ++ch) {
+        const int64_t c = g * CPG + ch;
+        issue(c + NBUF - 1, (ch + NBUF - 1) % CPG == 0);
+        // copies issued after chunk c's: chunks c+1 .. c+NBUF-1, NBASE each,
+        // plus NKP for each that starts a group
+        constexpr int kp_after_0 = ((1) % CPG == 0) + ((2) % CPG == 0) + ((3) % CPG == 0);
+        constexpr int kp_after_1 = ((2) % CPG == 0) + ((3) % CPG == 0) + ((4) % CPG == 0);
+        static_assert(NBUF == 4, "wait counts below assume four slots");
+        if (ch == 0)
+          wait_vmcnt<(NBUF - 1) * NBASE + kp_after_0 * NKP>();
+        else
+          wait_vmcnt<(NBUF - 1) * NBASE + kp_after_1 * NKP>();
+        process(ring + static_cast<uint32_t>(c % NBUF) * SLOT, ch == 0);
+      }
+    }
+    wait_vmcnt<0>();  // no copy into LDS outlives the loop
   }
 
   // ---- fp16 window chunks: the last split
   if (s == S - 1 && a.rc1 > a.rc0) {
-    half8 bqr[NKB];
+    uint32_t bqr[NP][NKB][4];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bqr[kb][e] = static_cast<_Float16>(qv[kb][e]);
+      for (int i = 0; i < 4; ++i) {
+        const float q0 = qm[kb][2 * i] * code_mult<KB>(2 * i), q1 = qm[kb][2 * i + 1] * code_mult<KB>(2 * i + 1);
+        const uint32_t one = 0x3C003C00u;  // fp16 1.0 pair
+        if (CS) {
+          bqr[0][kb][i] = split_part(q0, q1, one, negf_p0);
+        } else {
+          uint32_t t = mix_mul2(q0, q1, one);
+          bqr[0][kb][i] = t;
+          bqr[NP - 1][kb][i] = mix_fma2(q0, q1, one, pk_mul_f16(t, 0xBC00BC00u));
+        }
+      }
     for (int64_t rc = a.rc0; rc < a.rc1; ++rc) {
       const uint8_t* rch = a.cache + ring_chunk_offset(L, slice, rc * kChunk);
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        half8 a0 = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(rch + ((0 * NKB + kb) * kLanes + l) * 16));
-        half8 a1 = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(rch + ((1 * NKB + kb) * kLanes + l) * 16));
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bqr[kb], c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bqr[kb], c1, 0, 0, 0);
+        const half8 a0 = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(rch + ((0 * NKB + kb) * kLanes + l) * 16));
+        const half8 a1 = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(rch + ((1 * NKB + kb) * kLanes + l) * 16));
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          const half8 bb = __builtin_bit_cast(half8, u32x4{bqr[pp][kb][0], bqr[pp][kb][1], bqr[pp][kb][2], bqr[pp][kb][3]});
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bb, c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bb, c1, 0, 0, 0);
+        }
       }
       const int64_t pos0 = rc * kChunk;
       const bool partial = pos0 + kChunk > a.n;
@@ -335,37 +545,59 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         sc[r] = c0[r];
         sc[4 + r] = c1[r];
       }
+      if (CS) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = add_ror8(sc[e]);
+      }
       uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
       if (partial) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          bool valid = pos0 + tau(j, e) < a.n;
-          if (!valid) {
+          if (pos0 + tau(j, e) >= a.n) {
             sc[e] = -INFINITY;
             vmask[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
           }
         }
       }
       softmax_step(sc, p);
-      half8 bp;
+      uint32_t bpr[NP][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bp[e] = static_cast<_Float16>(p[e]);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t one = 0x3C003C00u;
+        if (CS) {
+          bpr[0][i] = split_part(p[2 * i], p[2 * i + 1], one, negf_p0);
+        } else {
+          uint32_t t = mix_mul2(p[2 * i], p[2 * i + 1], one);
+          bpr[0][i] = t;
+          bpr[NP - 1][i] = mix_fma2(p[2 * i], p[2 * i + 1], one, pk_mul_f16(t, 0xBC00BC00u));
+        }
+      }
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         u32x4 vwd = *reinterpret_cast<const u32x4*>(rch + kChunk * D * 2 + (mt * kLanes + l) * 16);
         vwd[0] &= vmask[0]; vwd[1] &= vmask[1]; vwd[2] &= vmask[2]; vwd[3] &= vmask[3];
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, vwd), bp, acc[mt], 0, 0, 0);
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          const half8 bb = __builtin_bit_cast(half8, u32x4{bpr[pp][0], bpr[pp][1], bpr[pp][2], bpr[pp][3]});
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, vwd), bb, acc[mt], 0, 0, 0);
+        }
       }
     }
   }
 
-  // ---- finalize
+  // ---- finalize: combine the two parts (CS), reduce over lane groups, write
+  if (CS) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[mt][r] = add_ror8(acc[mt][r]);
+  }
   lsum = wave_sum_j(lsum);
 #pragma unroll
   for (int i = 0; i < NCG; ++i) zacc[i] = wave_sum_j(zacc[i]);
-  if (hv) {
+  if (hv && !lo_lane) {
     const int64_t row = static_cast<int64_t>(b) * a.Hq + hq;
-    if (S == 1) {
+    if (a.write_final) {
       const float inv = 1.0f / lsum;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
@@ -414,7 +646,10 @@ template <int D, int KB, int VB, int G>
 hipError_t decode_t(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(a.L.slices * a.splits));
   const size_t lds = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
-  hipLaunchKernelGGL((decode_kernel<D, KB, VB, G>), grid, dim3(kLanes), lds, s, a);
+  if (a.gqa <= 8)
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, true>), grid, dim3(kLanes), lds, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, false>), grid, dim3(kLanes), lds, s, a);
   return hipGetLastError();
 }
 template <int D, int KB, int VB>

@@ -37,8 +37,9 @@ struct DecodeArgs {
   int splits;
   int64_t groups_per_split;
   int64_t rc0, rc1;     // window chunks [rc0, rc1) (absolute 32-token chunk indices)
-  float* partial;       // [B*H_q][splits][D + 2] when splits > 1
-  float* out;           // [B][H_q][D] when splits == 1
+  float* partial;       // [B*H_q][splits][D + 4] when !write_final
+  float* out;           // [B][H_q][D] when write_final (splits == 1)
+  int write_final;
 };
 
 // Both return hipSuccess or the launch error.

@@ -80,7 +80,7 @@ inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int 
   L.vw = L.nmt * vbits / 4;                // 4-bit: one dword per mt; 2-bit: half
   L.kc_chunk_bytes = (int64_t)kLanes * L.kw * 4;
   L.vc_chunk_bytes = (int64_t)kLanes * L.vw * 4;
-  L.vp_chunk_bytes = (int64_t)kChunk * L.ncg * 4;
+  L.vp_chunk_bytes = align_up((int64_t)kChunk * L.ncg * 4, 256);  // whole 256-byte DMA blocks
   L.kp_bytes = (int64_t)D * 4;
   L.off_kcodes = 0;
   L.off_kparams = L.off_kcodes + L.chunks_per_group * L.kc_chunk_bytes;
@@ -151,13 +151,17 @@ KVQ_HD int kparam_index(const Layout& L, int c) {
   return j * (L.D / 4) + kb * 8 + e;
 }
 
-// Dword index, inside a chunk's value-parameter block, of (token t, value
-// group cg); the dword holds scale (low half) and zero (high half).
-KVQ_HD int vparam_index(const Layout& L, int t, int cg) {
+// fp16 element index, inside a chunk's value-parameter block, of the scale of
+// (token t, value group cg); the zero is 8 elements (4 dwords) later.  Lane
+// group j reads its run of 8 * ncg dwords: per group cg four dwords of scale
+// pairs (tokens tau(j, 2i), tau(j, 2i + 1)) then four dwords of zero pairs,
+// so each dword is one fp16 pair of a PV B operand as it is.
+KVQ_HD int vparam_scale_elem(const Layout& L, int t, int cg) {
   int j, e;
   tau_inv(t, &j, &e);
-  return (j * 8 + e) * L.ncg + cg;
+  return ((j * L.ncg + cg) * 8 + (e >> 1)) * 2 + (e & 1);
 }
+KVQ_HD int vparam_zero_elem(const Layout& L, int t, int cg) { return vparam_scale_elem(L, t, cg) + 8; }
 
 // Byte offsets inside a ring chunk of the fp16 window copy of token t, channel c.
 // Keys are stored as the QK A operand, values as the PV A operand.

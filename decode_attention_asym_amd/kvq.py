@@ -47,6 +47,8 @@ SIGNATURES = {
     "kvq_decode_attn": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
     "kvq_decode_attn_splits": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _I32, _P]),
     "kvq_default_splits": (_I32, [_P]),
+    "kvq_decode_partials": (ctypes.c_int, [_P, _P, _P, _SZ, _I32, ctypes.POINTER(_I32), _P]),
+    "kvq_merge_partials": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P]),
     "kvq_num_tokens": (_I64, [_P]),
     "kvq_num_quantized": (_I64, [_P]),
     "kvq_reset": (ctypes.c_int, [_P]),
@@ -130,6 +132,12 @@ def _stream(stream) -> int:
     return int(stream)
 
 
+def merge_partials(partials, out, rows: int, splits: int, head_dim: int, stream=None):
+    check(lib.kvq_merge_partials(_ptr(partials), _ptr(out), rows, splits, head_dim, _stream(stream)),
+          "kvq_merge_partials")
+    return out
+
+
 class KVQCache:
     """A quantized KV cache in a torch-allocated device buffer.
 
@@ -185,6 +193,19 @@ class KVQCache:
                                             _stream(stream))
         check(st, "kvq_decode_attn")
         return out
+
+    def decode_partials(self, q, partials=None, splits: int | None = None, stream=None):
+        """Split partials [B*H_q, S, D+4] (o unnormalized, m, l in base 2); returns (partials, S)."""
+        import torch
+
+        S_req = self.default_splits() if splits is None else splits
+        rows = self.cfg.batch * self.cfg.num_q_heads
+        if partials is None:
+            partials = torch.empty((rows, S_req, self.cfg.head_dim + 4), dtype=torch.float32, device=q.device)
+        used = ctypes.c_int32(0)
+        check(lib.kvq_decode_partials(self.h, _ptr(q), _ptr(partials), partials.numel() * 4, S_req,
+                                      ctypes.byref(used), _stream(stream)), "kvq_decode_partials")
+        return partials, int(used.value)
 
     def reset(self) -> None:
         check(lib.kvq_reset(self.h), "kvq_reset")

@@ -80,7 +80,7 @@ typedef struct {
 size_t kvq_cache_bytes(const kvq_config* cfg);
 
 /* Device bytes of workspace kvq_decode_attn may need for `cfg` at any split
- * count it chooses (split partials: B * H_q * S_max * (D + 2) floats).
+ * count it chooses (split partials: B * H_q * S_max * (D + 4) floats).
  * 0 if `cfg` is invalid. */
 size_t kvq_workspace_bytes(const kvq_config* cfg);
 
@@ -123,6 +123,29 @@ kvq_status kvq_decode_attn(kvq_cache* cache, const void* q, float* out, void* wo
  * floating-point summation order. */
 kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, void* workspace, size_t ws_bytes,
                                   int32_t num_splits, void* stream);
+
+/* The two halves of kvq_decode_attn, for callers that merge partial results
+ * themselves (e.g. several caches holding disjoint token ranges of the same
+ * sequences, as when a long context is sharded over devices).
+ *
+ * kvq_decode_partials: split the cached tokens into num_splits ranges
+ * (clamped as in kvq_decode_attn_splits; *splits_used receives the count S)
+ * and write, for every row r = b * H_q + h and split s, at
+ * partials + (r * S + s) * (D + 4) floats:
+ *   [0, D)  o = sum_t 2^(x_t - m) v_t   (unnormalized)
+ *   D       m = max_t x_t               (-inf for an empty split)
+ *   D + 1   l = sum_t 2^(x_t - m)
+ * with x_t = log2(e) * q . k_t / sqrt(D) (scores in the base-2 domain).
+ * bytes must be >= H_q * B * S * (D + 4) * 4.  Requires a non-empty cache. */
+kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials, size_t bytes, int32_t num_splits,
+                               int32_t* splits_used, void* stream);
+
+/* Merge `splits` partials per row (layout above, `rows` rows) into
+ * out[rows][head_dim] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+ * M = max_s m_s; splits with m_s = -inf contribute nothing, and a row whose
+ * splits are all empty yields NaN.  head_dim in {64, 128}. */
+kvq_status kvq_merge_partials(const float* partials, float* out, int32_t rows, int32_t splits, int32_t head_dim,
+                              void* stream);
 
 /* Split count kvq_decode_attn would use for the current token count. */
 int32_t kvq_default_splits(const kvq_cache* cache);
