@@ -94,6 +94,21 @@ def cpu_baseline(w, K_host, V_host, q_host, batches, threads: int) -> dict:
     }
 
 
+def copy_calibration(gib: float) -> int:
+    """Device-to-device copies of exactly `gib` GiB (reads and writes that many
+    bytes each time): the reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    n = int(gib * (1 << 30)) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,7 +118,12 @@ def main() -> int:
     ap.add_argument("--splits", type=int, default=0, help="split count (0: the library's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="instead of the benchmark, copy GIB GiB device-to-device 3 times (a plain copy of known "
+                         "size, used to scale HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration > 0:
+        return copy_calibration(args.copy_calibration)
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (this path has no multi-GPU "

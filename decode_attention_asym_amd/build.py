@@ -23,7 +23,9 @@ COMMON = [
 # hipcc's default correctly rounded division is relied on.
 SOURCES = {
     "kvq_append.hip": ["-ffp-contract=off"],
-    "kvq_decode.hip": [],
+    # MFMA accumulators in ArchVGPRs: the softmax rescale multiplies them with
+    # VALU, which otherwise costs AGPR<->VGPR copies every chunk
+    "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
     "kvq_api.cpp": ["-ffp-contract=off"],
 }
 

@@ -199,6 +199,14 @@ __device__ __forceinline__ void dma_block(const uint8_t* g, uint32_t lane16, uin
 }
 template <int BYTES>
 constexpr int dma_count() { return BYTES / 1024 + (BYTES % 1024) / 256; }
+// Number of chunks among the NBUF - 1 issued after chunk position ch (mod
+// CPG) that start a group, i.e. that also carry key parameters.
+template <int NBUF, int CPG>
+constexpr int kp_after(int ch) {
+  int n = 0;
+  for (int k = 1; k < NBUF; ++k) n += ((ch + k) % CPG) == 0;
+  return n;
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
@@ -334,7 +342,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   constexpr int KC = kChunk * D * KB / 8, VC = kChunk * D * VB / 8;
   constexpr int VPB = (kChunk * NCG * 4 + 255) / 256 * 256, KPB = 4 * D;
   constexpr int SLOT = KC + VC + VPB + KPB;
-  constexpr int NBUF = 4;
+  // Slots per wave: three chunks in flight when the ring stays small enough
+  // for three waves per SIMD (12 per CU within 160 KiB of LDS), else two.
+  constexpr int NBUF = 4 * SLOT <= 13 * 1024 ? 4 : 3;
   constexpr int NBASE = dma_count<KC>() + dma_count<VC>() + dma_count<VPB>(), NKP = dma_count<KPB>();
   __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF * SLOT];
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((KVQ_AS3 uint8_t*)ring));
@@ -492,14 +502,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         const int64_t c = g * CPG + ch;
         issue(c + NBUF - 1, (ch + NBUF - 1) % CPG == 0);
         // copies issued after chunk c's: chunks c+1 .. c+NBUF-1, NBASE each,
-        // plus NKP for each that starts a group
-        constexpr int kp_after_0 = ((1) % CPG == 0) + ((2) % CPG == 0) + ((3) % CPG == 0);
-        constexpr int kp_after_1 = ((2) % CPG == 0) + ((3) % CPG == 0) + ((4) % CPG == 0);
-        static_assert(NBUF == 4, "wait counts below assume four slots");
+        // plus NKP for each of them that starts a group
         if (ch == 0)
-          wait_vmcnt<(NBUF - 1) * NBASE + kp_after_0 * NKP>();
+          wait_vmcnt<(NBUF - 1) * NBASE + kp_after<NBUF, CPG>(0) * NKP>();
         else
-          wait_vmcnt<(NBUF - 1) * NBASE + kp_after_1 * NKP>();
+          wait_vmcnt<(NBUF - 1) * NBASE + kp_after<NBUF, CPG>(1) * NKP>();
         process(ring + static_cast<uint32_t>(c % NBUF) * SLOT, ch == 0);
       }
     }
