@@ -19,11 +19,14 @@
 // so both products run on raw integer codes: (q_c s_gc) is the B operand of
 // QK^T once per token group, (p_t s_tj) the B operand of PV once per chunk,
 // and the zero-point sums are added as per-head biases.  Codes enter the MFMA
-// as fp16 1024 + 2^p code (see kvq_layout.h); the 2^p are folded into the B
-// operands and the 1024 offsets are subtracted using the same fp16 B values.
-// Softmax runs in the log2 domain (exp2), log2(e)/sqrt(D) folded into q.
+// as fp16 subnormals 2^-24 * 2^p * code (see kvq_layout.h): the 2^p factors
+// are folded into the B operands and the 2^-24 into the scores and the final
+// output, all exact.  Softmax runs in the log2 domain (exp2), log2(e)/sqrt(D)
+// folded into q.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kvq_internal.h"
 
@@ -37,55 +40,64 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTwo24 = 16777216.0f;  // undoes the 2^-24 of subnormal code operands
 
-// Constants kept out of the optimizer's sight so that (w & mask) | magic
-// selects one v_and_or_b32 with the mask in an SGPR and the magic in a VGPR
-// (gfx9 VOP3 encodings take no literal operands).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Field masks kept in SGPRs (v_and_b32 with an SGPR operand instead of a
+// 32-bit literal per instruction).
 __device__ __forceinline__ uint32_t sgpr_const(uint32_t x) {
   uint32_t r;
   asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(x));
   return r;
 }
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t x) {
-  uint32_t r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(x));
-  return r;
-}
-
-struct Unpack {
-  uint32_t magic;   // 0x64006400: fp16 1024 in both halves
-  uint32_t m[4];    // field masks
-};
 
 template <int BITS>
-__device__ __forceinline__ Unpack make_unpack() {
-  Unpack u;
-  u.magic = vgpr_const(0x64006400u);
-  if (BITS == 4) {
-    u.m[0] = sgpr_const(0x000F000Fu);
-    u.m[1] = sgpr_const(0x00F000F0u);
-    u.m[2] = u.m[0];
-    u.m[3] = u.m[1];
-  } else {
-    u.m[0] = sgpr_const(0x00030003u);
-    u.m[1] = sgpr_const(0x000C000Cu);
-    u.m[2] = sgpr_const(0x00300030u);
-    u.m[3] = sgpr_const(0x00C000C0u);
+struct CodeMasks {
+  uint32_t m[4];
+  __device__ __forceinline__ CodeMasks() {
+    if (BITS == 4) {
+      m[0] = sgpr_const(0x000F000Fu);
+      m[1] = sgpr_const(0x00F000F0u);
+      m[2] = m[0];
+      m[3] = m[1];
+    } else {
+      m[0] = sgpr_const(0x00030003u);
+      m[1] = sgpr_const(0x000C000Cu);
+      m[2] = sgpr_const(0x00300030u);
+      m[3] = sgpr_const(0x00C000C0u);
+    }
   }
-  return u;
-}
+};
 
-// 4-bit word -> 8 fp16 values 1024 + mult(e) * code_e, mult = 1, 1, 16, 16, 1, 1, 16, 16.
-__device__ __forceinline__ half8 unpack4(uint32_t w, const Unpack& u) {
-  uint32_t w8 = w >> 8;
-  u32x4 r = {(w & u.m[0]) | u.magic, (w & u.m[1]) | u.magic, (w8 & u.m[0]) | u.magic, (w8 & u.m[1]) | u.magic};
-  return __builtin_bit_cast(half8, r);
+// A b-bit field at bit p of a 16-bit half, with every other bit of the half
+// clear, is the fp16 subnormal 2^(p - 24) * code exactly.
+//
+// Precision note (measured on gfx950): the matrix cores' fp32 result of a
+// 32-product sum is biased low by a few ulp (about -4e-6 relative) when an
+// input is a small subnormal, and equally so when a large offset is added
+// and cancelled (the 1024 + code encoding); only sums of normal-range inputs
+// are unbiased.  The PV code sum is then amplified by its cancellation
+// against the zero-point sum (|sum p s code| / |output| is 30-70 on long
+// diffuse contexts), which puts the attention output's relative error at
+// 1e-4 .. 1.5e-3 against exact arithmetic.  Normal-range code operands would
+// cost one more VALU operation per operand dword (about a quarter more VALU
+// work per chunk).
+// 4-bit word -> 8 values 2^-24 * mult(e) * code_e, mult = 1, 1, 16, 16, 1, 1, 16, 16.
+__device__ __forceinline__ half8 unpack4(uint32_t w, const CodeMasks<4>& u) {
+  const uint32_t w8 = w >> 8;
+  return __builtin_bit_cast(half8, u32x4{w & u.m[0], w & u.m[1], w8 & u.m[0], w8 & u.m[1]});
 }
-// One 2-bit sub-block (the low byte of each half of w) -> 8 fp16 values
-// 1024 + 4^(e>>1) * code_e.
-__device__ __forceinline__ half8 unpack2(uint32_t w, const Unpack& u) {
-  u32x4 r = {(w & u.m[0]) | u.magic, (w & u.m[1]) | u.magic, (w & u.m[2]) | u.magic, (w & u.m[3]) | u.magic};
-  return __builtin_bit_cast(half8, r);
+// One 2-bit sub-block (the low byte of each half of w) -> 8 values
+// 2^-24 * 4^(e>>1) * code_e.
+__device__ __forceinline__ half8 unpack2(uint32_t w, const CodeMasks<2>& u) {
+  return __builtin_bit_cast(half8, u32x4{w & u.m[0], w & u.m[1], w & u.m[2], w & u.m[3]});
 }
 
 template <int BITS>
@@ -93,40 +105,31 @@ __host__ __device__ constexpr float code_mult(int e) {
   return BITS == 4 ? (((e >> 1) & 1) ? 16.0f : 1.0f) : static_cast<float>(1 << (2 * (e >> 1)));
 }
 
-template <int W>
-__device__ __forceinline__ void load_lane_words(const uint8_t* base, int l, uint32_t (&w)[W]) {
-  if constexpr (W >= 4) {
-#pragma unroll
-    for (int v = 0; v < W / 4; ++v) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(base + v * (kLanes * 16) + l * 16);
-      w[4 * v + 0] = x[0]; w[4 * v + 1] = x[1]; w[4 * v + 2] = x[2]; w[4 * v + 3] = x[3];
-    }
-  } else {
-    u32x2 x = *reinterpret_cast<const u32x2*>(base + l * 8);
-    w[0] = x[0]; w[1] = x[1];
-  }
-}
-
-template <int BITS, int NPER>
-__device__ __forceinline__ half8 a_operand(const uint32_t* words, int idx, const Unpack& u) {
+template <int BITS>
+__device__ __forceinline__ half8 a_operand(const uint32_t* words, int idx, const CodeMasks<BITS>& u) {
   // idx-th 8-element operand of a lane: 4-bit -> one word each; 2-bit -> two per word
   if constexpr (BITS == 4) {
     return unpack4(words[idx], u);
   } else {
-    uint32_t w = words[idx >> 1];
+    const uint32_t w = words[idx >> 1];
     return unpack2((idx & 1) ? (w >> 8) : w, u);
   }
 }
 
-__device__ __forceinline__ float wave_sum_j(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
+// Reductions over the four lane groups j of a column (lanes l16, l16 + 16,
+// l16 + 32, l16 + 48), on the VALU with gfx950's lane swaps.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_fmaxf(a, b); }
 __device__ __forceinline__ float wave_max_j(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_sum_j(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float load_q(const void* p, int dtype, int64_t i) {
@@ -152,14 +155,29 @@ __device__ __forceinline__ uint32_t mix_mul2(float a0, float a1, uint32_t s) {
                     static_cast<_Float16>(__builtin_fmaf(a1, static_cast<float>(sv[1]), 0.0f))};
   return as_u32(r);
 }
-// fp16 pair (fp16(a0 * s.lo + c.lo), fp16(a1 * s.hi + c.hi)), one rounding each.
-__device__ __forceinline__ uint32_t mix_fma2(float a0, float a1, uint32_t s, uint32_t c) {
+// fp16 pair (fp16(a0 * s.lo - c.lo), fp16(a1 * s.hi - c.hi)), one rounding each.
+__device__ __forceinline__ uint32_t mix_fms2(float a0, float a1, uint32_t s, uint32_t c) {
   const half2v sv = as_h2(s), cv = as_h2(c);
-  const half2v r = {static_cast<_Float16>(__builtin_fmaf(a0, static_cast<float>(sv[0]), static_cast<float>(cv[0]))),
-                    static_cast<_Float16>(__builtin_fmaf(a1, static_cast<float>(sv[1]), static_cast<float>(cv[1])))};
+  const half2v r = {static_cast<_Float16>(__builtin_fmaf(a0, static_cast<float>(sv[0]), -static_cast<float>(cv[0]))),
+                    static_cast<_Float16>(__builtin_fmaf(a1, static_cast<float>(sv[1]), -static_cast<float>(cv[1])))};
   return as_u32(r);
 }
-__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) { return as_u32(as_h2(a) * as_h2(b)); }
+// Two-part fp16 operand of x = a * s (a fp32, s an fp16 pair): part 0 =
+// fp16(x), part 1 = fp16(x - part 0).  In column-split mode a lane produces
+// the part its columns hold: mask 0 gives part 0, all-ones part 1.
+__device__ __forceinline__ uint32_t split_part(float a0, float a1, uint32_t s, uint32_t mask) {
+  return mix_fms2(a0, a1, s, mix_mul2(a0, a1, s) & mask);
+}
+// Exact-residual product of fp16 pairs: with x = fp16(a * s), the fp16 fma
+// a * s - x is exact (the rounding error of a product of two fp16 values is
+// an fp16 value), so fp16(b * s + (a * s - x)) is the second part of
+// (a + b) * s for a two-part a + b.
+__device__ __forceinline__ half2v pk_mul(half2v a, half2v b) { return a * b; }
+__device__ __forceinline__ half2v pk_fma(half2v a, half2v b, half2v c) { return __builtin_elementwise_fma(a, b, c); }
+__device__ __forceinline__ uint32_t pack_h2(float x0, float x1) {
+  const half2v r = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
+  return as_u32(r);
+}
 // Sum with the lane 8 places away inside each row of 16 (row_ror:8): lanes h
 // and h + 8 both receive x_h + x_{h+8}.
 __device__ __forceinline__ float add_ror8(float x) {
@@ -174,21 +192,24 @@ __device__ __forceinline__ float add_ror8(float x) {
 // (every vector-memory instruction of the main loop is one of these copies,
 // issued in a fixed pattern, and vector memory returns in order).
 #define KVQ_AS3 __attribute__((address_space(3)))
+// M0 is named as clobbered by the copies below; the compiler reserves M0 and
+// warns about it, but nothing else in these kernels uses M0.
+#pragma clang diagnostic ignored "-Winline-asm"
 
 // The destination LDS address is taken from M0; an LDS-DMA instruction that
-// reads M0 right after an SALU write of it needs a wait state (s_nop) or it
-// may see the previous value.  Outstanding LDS reads are drained first so a
-// slot is never overwritten while still being read.
+// reads M0 right after an SALU write of it needs a wait state (s_nop).
 // 1 KiB: lane l copies global [base + 16 l, +16) to LDS [lds + 16 l, +16)
 __device__ __forceinline__ void dma_1k(const uint8_t* gbase, uint32_t lane16, uint32_t lds) {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(lane16), "s"(gbase), "s"(lds) : "memory", "m0");
 }
 // 256 B: lane l copies global [base + 4 l, +4) to LDS [lds + 4 l, +4)
 __device__ __forceinline__ void dma_256(const uint8_t* gbase, uint32_t lane4, uint32_t lds) {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dword %0, %1"
                :: "v"(lane4), "s"(gbase), "s"(lds) : "memory", "m0");
 }
+// Outstanding LDS reads are drained before a slot is overwritten.
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 template <int BYTES>
 __device__ __forceinline__ void dma_block(const uint8_t* g, uint32_t lane16, uint32_t lane4, uint32_t lds) {
   static_assert(BYTES % 256 == 0, "DMA blocks are whole 256-byte units");
@@ -213,23 +234,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// Two-part fp16 operand of x = a * s (a fp32, s an fp16 pair): part 0 = fp16(x),
-// part 1 = fp16(x - fp16(x)).  In column-split mode each lane produces the
-// part selected by negf (0: part 0, fp16 -1 pair: part 1); otherwise both.
-__device__ __forceinline__ uint32_t split_part(float a0, float a1, uint32_t s, uint32_t negf) {
-  uint32_t t = mix_mul2(a0, a1, s);
-  return mix_fma2(a0, a1, s, pk_mul_f16(t, negf));
-}
+// Page geometry of one token group (the same numbers as make_layout's,
+// as compile-time constants of the kernel instance).
+template <int D, int KB, int VB, int G>
+struct PageShape {
+  static constexpr int NCG = D / G, CPG = G / kChunk;
+  static constexpr int KC = kChunk * D * KB / 8, VC = kChunk * D * VB / 8;
+  static constexpr int VPB = (kChunk * NCG * 4 + 255) / 256 * 256, KPB = 4 * D;
+  static constexpr int OFF_KC = 0, OFF_KP = CPG * KC, OFF_VC = OFF_KP + KPB, OFF_VP = OFF_VC + CPG * VC;
+  static constexpr int BYTES = OFF_VP + CPG * VPB;
+};
 
 // Running-max slack of the online softmax (base-2 units): the accumulators
 // are rescaled only when a chunk's maximum exceeds the running maximum by more
 // than this, so weights stay <= 2^0.5 and the fp16 PV operand p * scale stays
 // below 65504 for any scale of fp16 data.
 constexpr float kMaxSlack = 0.5f;
+#ifndef KVQ_PV_SPLIT
+#define KVQ_PV_SPLIT 1
+#endif
 
 template <int D, int KB, int VB, int G, bool CS>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-  constexpr int NKB = D / 32, NMT = D / 16, NCG = D / G, CPG = G / kChunk;
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CS ? 3 : 2)))
+void decode_kernel(DecodeArgs a) {
+  using PS = PageShape<D, KB, VB, G>;
+  constexpr int NKB = D / 32, NMT = D / 16, NCG = PS::NCG, CPG = PS::CPG;
   constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4, VPW = 8 * NCG;
   // B operands carry each value as two fp16 parts (hi + lo) so the folded
   // products keep ~22 bits: in CS mode (at most 8 heads) hi sits in columns
@@ -245,7 +274,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const bool lo_lane = CS && l16 >= 8;
   const bool hv = h < a.gqa;
   const int hq = hkv * a.gqa + (hv ? h : 0);
-  const uint32_t negf_p0 = lo_lane ? 0xBC00BC00u : 0u;  // this lane's part (CS mode)
+  const uint32_t part_mask = lo_lane ? 0xFFFFFFFFu : 0u;  // this lane's part (CS mode)
 
   // ---- query: lane owns channels 32 kb + 8 j + e of head h, times log2(e)/sqrt(D)
   float qm[NKB][8];
@@ -278,34 +307,41 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qm[kb][e] = hv ? load_q(a.q, a.in_dtype, base + 32 * kb + 8 * j + e) * qscale : 0.0f;
   }
-  // B operand of the zero-point term (the query itself, two parts): once per split
-  uint32_t bqv[NP][NKB][4];
-  {
-    const uint32_t one = 0x3C003C00u;  // fp16 1.0 pair
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (CS) {
-          bqv[0][kb][i] = split_part(qm[kb][2 * i], qm[kb][2 * i + 1], one, negf_p0);
-        } else {
-          uint32_t t = mix_mul2(qm[kb][2 * i], qm[kb][2 * i + 1], one);
-          bqv[0][kb][i] = t;
-          bqv[NP - 1][kb][i] = mix_fma2(qm[kb][2 * i], qm[kb][2 * i + 1], one, pk_mul_f16(t, 0xBC00BC00u));
-        }
-      }
-  }
-  // qm = q / mult: the folded B operand of QK^T is qm * key scale
+  // Per-split fp16 parts of the query (part 1 = fp16(x - part 0)):
+  //   qz: q itself, the B operand of the key zero-point bias and of the window;
+  //   qh / ql: q / mult (the code multipliers of the key operand), from which
+  //   the per-group B operand q * scale / mult is formed by exact-residual fp16
+  //   products.  In CS mode ql holds part 0 on hi lanes (so the same
+  //   instructions produce each lane's own part).
+  uint32_t qz[NP][NKB][4], qh[NKB][4], ql[NKB][4];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qm[kb][e] *= (1.0f / code_mult<KB>(e));
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = qm[kb][2 * i], x1 = qm[kb][2 * i + 1];
+      const float h0 = static_cast<float>(static_cast<_Float16>(x0)), h1 = static_cast<float>(static_cast<_Float16>(x1));
+      const uint32_t z_hi = pack_h2(x0, x1), z_lo = pack_h2(x0 - h0, x1 - h1);
+      const float d0 = x0 * (1.0f / code_mult<KB>(2 * i)), d1 = x1 * (1.0f / code_mult<KB>(2 * i + 1));
+      const float e0 = static_cast<float>(static_cast<_Float16>(d0)), e1 = static_cast<float>(static_cast<_Float16>(d1));
+      const uint32_t d_hi = pack_h2(d0, d1), d_lo = pack_h2(d0 - e0, d1 - e1);
+      if (CS) {
+        qz[0][kb][i] = lo_lane ? z_lo : z_hi;
+        ql[kb][i] = lo_lane ? d_lo : d_hi;
+      } else {
+        qz[0][kb][i] = z_hi;
+        qz[NP - 1][kb][i] = z_lo;
+        ql[kb][i] = d_lo;
+      }
+      qh[kb][i] = d_hi;
+    }
 
-  const Unpack uk = make_unpack<KB>();
-  const Unpack uv = make_unpack<VB>();
-  const half8 aneg = __builtin_bit_cast(half8, u32x4{0xE400E400u, 0xE400E400u, 0xE400E400u, 0xE400E400u});
+  const CodeMasks<KB> uk;
+  const CodeMasks<VB> uv;
 
-  float m = -INFINITY, lsum = 0.0f;
+  // Online-softmax state (per column, uniform over j).  m is the running max
+  // in log2 units; acc holds the PV sums in units of 2^-24 while quantized
+  // chunks are processed (subnormal code operands), real units afterwards.
+  float m = -INFINITY, mslack = -INFINITY, lsum = 0.0f;
   f32x4 acc[NMT];
 #pragma unroll
   for (int i = 0; i < NMT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -313,34 +349,23 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < NCG; ++i) zacc[i] = 0.0f;
 
-  // online softmax over one chunk's 8 scores per lane (tokens tau(j, e))
-  auto softmax_step = [&](float (&sc)[8], float (&p)[8]) {
-    float cmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    cmax = wave_max_j(cmax);
-    if (__any(cmax > m + kMaxSlack)) {
-      float mnew = fmaxf(m, cmax);
-      float al = __builtin_amdgcn_exp2f(m - mnew);
+  // (called wave-uniformly; mnew = max(m, chunk max) per column)
+  auto rescale = [&](float mnew) __attribute__((always_inline)) {
+    const float al = __builtin_amdgcn_exp2f(m - mnew);
 #pragma unroll
-      for (int i = 0; i < NMT; ++i) acc[i] *= al;
+    for (int i = 0; i < NMT; ++i) acc[i] *= al;
 #pragma unroll
-      for (int i = 0; i < NCG; ++i) zacc[i] *= al;
-      lsum *= al;
-      m = mnew;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(sc[e] - m);
-      lsum += p[e];
-    }
+    for (int i = 0; i < NCG; ++i) zacc[i] *= al;
+    lsum *= al;
+    m = mnew;
+    mslack = mnew + kMaxSlack;
   };
 
-  const int64_t nchunks = a.ngroups * CPG;
-  const int64_t cb = static_cast<int64_t>(s) * a.groups_per_split * CPG;
-  const int64_t ce = cb + a.groups_per_split * CPG < nchunks ? cb + a.groups_per_split * CPG : nchunks;
+  const int g0 = s * static_cast<int>(a.groups_per_split);
+  const int g1 = min(g0 + static_cast<int>(a.groups_per_split), static_cast<int>(a.ngroups));
 
   // ---- LDS ring of NBUF chunk slots: [key codes][value codes][value params][key params]
-  constexpr int KC = kChunk * D * KB / 8, VC = kChunk * D * VB / 8;
-  constexpr int VPB = (kChunk * NCG * 4 + 255) / 256 * 256, KPB = 4 * D;
+  constexpr int KC = PS::KC, VC = PS::VC, VPB = PS::VPB, KPB = PS::KPB;
   constexpr int SLOT = KC + VC + VPB + KPB;
   // Slots per wave: three chunks in flight when the ring stays small enough
   // for three waves per SIMD (12 per CU within 160 KiB of LDS), else two.
@@ -350,186 +375,189 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((KVQ_AS3 uint8_t*)ring));
   const uint32_t lane16 = static_cast<uint32_t>(l) * 16, lane4 = static_cast<uint32_t>(l) * 4;
 
-  // copy virtual chunk cv (clamped to the split, so the copy count per issue
-  // slot never changes) into slot cv % NBUF; a group's first chunk also
-  // carries the group's key scale/zero rows
-  auto issue = [&](int64_t cv, bool with_kp) {
-    const int64_t c = cv < ce ? cv : ce - 1;
-    const uint8_t* page = a.cache + page_offset(L, slice, c / CPG);
-    const int ch = static_cast<int>(c % CPG);
-    const uint32_t sl = ring_lds + static_cast<uint32_t>(cv % NBUF) * SLOT;
-    dma_block<KC>(page + L.off_kcodes + ch * KC, lane16, lane4, sl);
-    dma_block<VC>(page + L.off_vcodes + ch * VC, lane16, lane4, sl + KC);
-    dma_block<VPB>(page + L.off_vparams + ch * VPB, lane16, lane4, sl + KC + VC);
-    if (with_kp) dma_block<KPB>(page + L.off_kparams, lane16, lane4, sl + KC + VC + VPB);
-  };
+  if (g1 > g0) {
+    const uint8_t* slice_pages = a.cache + page_offset(L, slice, 0);
 
-  uint32_t bq[NP][NKB][4];  // B operand of QK^T (fp16 pairs), per part
-  f32x4 cbias = {0.f, 0.f, 0.f, 0.f};  // QK accumulator start: zero-point term and offset removal
+    // copy position chi of group gi into the slot at LDS address sl; a group's
+    // first chunk also carries the group's key scale/zero rows
+    auto issue = [&](int gi, auto chi_c, uint32_t sl) __attribute__((always_inline)) {
+      constexpr int chi = decltype(chi_c)::value;
+      const uint8_t* page = slice_pages + static_cast<int64_t>(gi) * PS::BYTES;
+      lds_reads_done();
+      dma_block<KC>(page + PS::OFF_KC + chi * KC, lane16, lane4, sl);
+      dma_block<VC>(page + PS::OFF_VC + chi * VC, lane16, lane4, sl + KC);
+      dma_block<VPB>(page + PS::OFF_VP + chi * VPB, lane16, lane4, sl + KC + VC);
+      if constexpr (chi == 0) dma_block<KPB>(page + PS::OFF_KP, lane16, lane4, sl + KC + VC + VPB);
+    };
 
-  auto process = [&](const uint8_t* sl, bool group_start) {
-    if (group_start) {
-      // B operand from this group's key scales, and the bias tile (every row:
-      // sum_c q_c z_c - 1024 sum_c bq_c) by MFMA
-      const u32x4* ps = reinterpret_cast<const u32x4*>(sl + KC + VC + VPB) + j * NKB;
-      const u32x4* pz = reinterpret_cast<const u32x4*>(sl + KC + VC + VPB + 2 * D) + j * NKB;
+    uint32_t bq[NP][NKB][4];  // B operand of QK^T (fp16 pairs), per part
+    float cb = 0.0f;          // this group's zero-point score bias (log2 units)
+
+    auto process = [&](const uint8_t* sl, bool group_start) __attribute__((always_inline)) {
+      if (group_start) {
+        // B operand from this group's key scales: q * s / mult in two parts
+        // (exact-residual fp16 products), and the bias sum_c q_c z_c by MFMA
+        // (every row of the bias tile is the same sum)
+        const u32x4* ps = reinterpret_cast<const u32x4*>(sl + KC + VC + VPB) + j * NKB;
+        const u32x4* pz = reinterpret_cast<const u32x4*>(sl + KC + VC + VPB + 2 * D) + j * NKB;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 sw = ps[kb];
+        for (int kb = 0; kb < NKB; ++kb) {
+          const u32x4 sw = ps[kb];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float q0 = qm[kb][2 * i], q1 = qm[kb][2 * i + 1];
-          if (CS) {
-            bq[0][kb][i] = split_part(q0, q1, sw[i], negf_p0);
-          } else {
-            uint32_t t = mix_mul2(q0, q1, sw[i]);
-            bq[0][kb][i] = t;
-            bq[NP - 1][kb][i] = mix_fma2(q0, q1, sw[i], pk_mul_f16(t, 0xBC00BC00u));
+          for (int i = 0; i < 4; ++i) {
+            const half2v sv = as_h2(sw[i]), hh = as_h2(qh[kb][i]);
+            const half2v x = pk_mul(hh, sv);
+            const half2v y = pk_fma(hh, sv, -x);  // exact: hh * sv - x
+            if (CS) {
+              bq[0][kb][i] = as_u32(pk_fma(as_h2(ql[kb][i]), sv, as_h2(as_u32(y) & part_mask)));
+            } else {
+              bq[0][kb][i] = as_u32(x);
+              bq[NP - 1][kb][i] = as_u32(pk_fma(as_h2(ql[kb][i]), sv, y));
+            }
           }
         }
+        f32x4 cbt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const half8 az = __builtin_bit_cast(half8, pz[kb]);
+#pragma unroll
+          for (int pp = 0; pp < NP; ++pp) {
+            const half8 bz = __builtin_bit_cast(half8, u32x4{qz[pp][kb][0], qz[pp][kb][1], qz[pp][kb][2], qz[pp][kb][3]});
+            cbt = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bz, cbt, 0, 0, 0);
+          }
+        }
+        cb = CS ? add_ror8(cbt[0]) : cbt[0];
       }
-      cbias = f32x4{0.f, 0.f, 0.f, 0.f};
+      uint32_t kw[KW], vw[VW], vp[VPW];
+      if constexpr (KW >= 4) {
+#pragma unroll
+        for (int v = 0; v < KW / 4; ++v) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(sl + v * (kLanes * 16) + l * 16);
+          kw[4 * v] = x[0]; kw[4 * v + 1] = x[1]; kw[4 * v + 2] = x[2]; kw[4 * v + 3] = x[3];
+        }
+      } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(sl + l * 8);
+        kw[0] = x[0]; kw[1] = x[1];
+      }
+      if constexpr (VW >= 4) {
+#pragma unroll
+        for (int v = 0; v < VW / 4; ++v) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(sl + KC + v * (kLanes * 16) + l * 16);
+          vw[4 * v] = x[0]; vw[4 * v + 1] = x[1]; vw[4 * v + 2] = x[2]; vw[4 * v + 3] = x[3];
+        }
+      } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(sl + KC + l * 8);
+        vw[0] = x[0]; vw[1] = x[1];
+      }
+      {
+        const u32x4* vpp = reinterpret_cast<const u32x4*>(sl + KC + VC) + j * (VPW / 4);
+#pragma unroll
+        for (int v = 0; v < VPW / 4; ++v) {
+          const u32x4 x = vpp[v];
+          vp[4 * v] = x[0]; vp[4 * v + 1] = x[1]; vp[4 * v + 2] = x[2]; vp[4 * v + 3] = x[3];
+        }
+      }
+      // QK^T: two 16-token tiles; C = 2^-24 * (score - bias)
+      f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const half8 az = __builtin_bit_cast(half8, pz[kb]);
+        const half8 a0 = a_operand<KB>(kw, kb, uk);
+        const half8 a1 = a_operand<KB>(kw, NKB + kb, uk);
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp) {
-          const half8 bz = __builtin_bit_cast(half8, u32x4{bqv[pp][kb][0], bqv[pp][kb][1], bqv[pp][kb][2], bqv[pp][kb][3]});
           const half8 bb = __builtin_bit_cast(half8, u32x4{bq[pp][kb][0], bq[pp][kb][1], bq[pp][kb][2], bq[pp][kb][3]});
-          cbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bz, cbias, 0, 0, 0);
-          cbias = __builtin_amdgcn_mfma_f32_16x16x32_f16(aneg, bb, cbias, 0, 0, 0);
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bb, c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bb, c1, 0, 0, 0);
         }
       }
-    }
-    uint32_t kw[KW], vw[VW], vp[VPW];
-    if constexpr (KW >= 4) {
+      float t[8];
 #pragma unroll
-      for (int v = 0; v < KW / 4; ++v) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(sl + v * (kLanes * 16) + l * 16);
-        kw[4 * v] = x[0]; kw[4 * v + 1] = x[1]; kw[4 * v + 2] = x[2]; kw[4 * v + 3] = x[3];
+      for (int r = 0; r < 4; ++r) {
+        t[r] = CS ? add_ror8(c0[r]) : c0[r];
+        t[4 + r] = CS ? add_ror8(c1[r]) : c1[r];
       }
-    } else {
-      const u32x2 x = *reinterpret_cast<const u32x2*>(sl + l * 8);
-      kw[0] = x[0]; kw[1] = x[1];
-    }
-    if constexpr (VW >= 4) {
+      // online softmax over the chunk's 8 scores per lane (tokens tau(j, e))
+      const float tmax = fmax2(fmax2(fmax2(t[0], t[1]), fmax2(t[2], t[3])), fmax2(fmax2(t[4], t[5]), fmax2(t[6], t[7])));
+      const float cmax = wave_max_j(__builtin_fmaf(tmax, kTwo24, cb));
+      if (__builtin_amdgcn_ballot_w64(cmax > mslack)) rescale(fmax2(m, cmax));
+      const float bm = cb - m;
+      float p[8];
 #pragma unroll
-      for (int v = 0; v < VW / 4; ++v) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(sl + KC + v * (kLanes * 16) + l * 16);
-        vw[4 * v] = x[0]; vw[4 * v + 1] = x[1]; vw[4 * v + 2] = x[2]; vw[4 * v + 3] = x[3];
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[e], kTwo24, bm));
+        lsum += p[e];
       }
-    } else {
-      const u32x2 x = *reinterpret_cast<const u32x2*>(sl + KC + l * 8);
-      vw[0] = x[0]; vw[1] = x[1];
-    }
-    {
-      const u32x4* vpp = reinterpret_cast<const u32x4*>(sl + KC + VC) + j * (VPW / 4);
+      // PV B operands (p * value scale / mult, two parts) and the zero-point sums
+      float pm[8];
 #pragma unroll
-      for (int v = 0; v < VPW / 4; ++v) {
-        const u32x4 x = vpp[v];
-        vp[4 * v] = x[0]; vp[4 * v + 1] = x[1]; vp[4 * v + 2] = x[2]; vp[4 * v + 3] = x[3];
-      }
-    }
-    // QK^T: two 16-token tiles, accumulated on top of the bias tile
-    f32x4 c0 = cbias, c1 = cbias;
+      for (int e = 0; e < 8; ++e) pm[e] = p[e] * (1.0f / code_mult<VB>(e));
+      uint32_t bp[NP][NCG][4];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const half8 a0 = a_operand<KB, 8>(kw, kb, uk);
-      const half8 a1 = a_operand<KB, 8>(kw, NKB + kb, uk);
+      for (int cg = 0; cg < NCG; ++cg) {
+        float zsum = zacc[cg];
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        const half8 bb = __builtin_bit_cast(half8, u32x4{bq[pp][kb][0], bq[pp][kb][1], bq[pp][kb][2], bq[pp][kb][3]});
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bb, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bb, c1, 0, 0, 0);
-      }
-    }
-    float sc[8], p[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[r] = c0[r];
-      sc[4 + r] = c1[r];
-    }
-    if (CS) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sc[e] = add_ror8(sc[e]);
-    }
-    softmax_step(sc, p);
-    // PV B operands (p * value scale / mult, two parts) and the zero-point sums
-    float pm[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pm[e] = p[e] * (1.0f / code_mult<VB>(e));
-    uint32_t bp[NP][NCG][4];
-#pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      float zsum = zacc[cg];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t sp = vp[cg * 8 + i], zp = vp[cg * 8 + 4 + i];
-        if (CS) {
-          bp[0][cg][i] = split_part(pm[2 * i], pm[2 * i + 1], sp, negf_p0);
-        } else {
-          uint32_t t = mix_mul2(pm[2 * i], pm[2 * i + 1], sp);
-          bp[0][cg][i] = t;
-          bp[NP - 1][cg][i] = mix_fma2(pm[2 * i], pm[2 * i + 1], sp, pk_mul_f16(t, 0xBC00BC00u));
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t sp = vp[cg * 8 + i], zp = vp[cg * 8 + 4 + i];
+          if (CS && !KVQ_PV_SPLIT) {
+            bp[0][cg][i] = mix_mul2(pm[2 * i], pm[2 * i + 1], sp) & ~part_mask;
+          } else if (CS) {
+            bp[0][cg][i] = split_part(pm[2 * i], pm[2 * i + 1], sp, part_mask);
+          } else {
+            const uint32_t hi = mix_mul2(pm[2 * i], pm[2 * i + 1], sp);
+            bp[0][cg][i] = hi;
+            bp[NP - 1][cg][i] = mix_fms2(pm[2 * i], pm[2 * i + 1], sp, hi);
+          }
+          zsum += p[2 * i] * h2f_lo(zp);
+          zsum += p[2 * i + 1] * h2f_hi(zp);
         }
-        zsum += p[2 * i] * h2f_lo(zp);
-        zsum += p[2 * i + 1] * h2f_hi(zp);
+        zacc[cg] = zsum;
       }
-      zacc[cg] = zsum;
-    }
-    // PV: codes enter as 1024 + mult * code; the constant -1024 operand removes
-    // the offset inside the same accumulator every chunk
+      // PV on the subnormal code operands
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      const half8 av = a_operand<VB, 8>(vw, mt, uv);
+      for (int mt = 0; mt < NMT; ++mt) {
+        const half8 av = a_operand<VB>(vw, mt, uv);
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        const uint32_t* bw = bp[pp][(16 * mt) / G];
-        const half8 bb = __builtin_bit_cast(half8, u32x4{bw[0], bw[1], bw[2], bw[3]});
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aneg, bb, acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bb, acc[mt], 0, 0, 0);
+        for (int pp = 0; pp < NP; ++pp) {
+          const uint32_t* bw = bp[pp][(16 * mt) / G];
+          const half8 bb = __builtin_bit_cast(half8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bb, acc[mt], 0, 0, 0);
+        }
       }
-    }
-  };
+    };
 
-  if (ce > cb) {
-    // prologue: NBUF - 1 chunks in flight (split boundaries are group-aligned)
-#pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k) issue(cb + k, k % CPG == 0);
-    for (int64_t g = cb / CPG; g < ce / CPG; ++g) {
-#pragma unroll
-      for (int ch = 0; ch < CPG; ++ch) {
-        const int64_t c = g * CPG + ch;
-        issue(c + NBUF - 1, (ch + NBUF - 1) % CPG == 0);
+    // Ring slots rotate through LDS addresses ring_lds + k * SLOT; chunk c of
+    // the split sits in slot c % NBUF.  Slot of the chunk processed next and
+    // of the next chunk to copy (NBUF - 1 ahead).
+    uint32_t sl_proc = ring_lds, sl_issue = ring_lds + (NBUF - 1) * SLOT;
+    auto next_slot = [&](uint32_t x) { return x + SLOT == ring_lds + NBUF * SLOT ? ring_lds : x + SLOT; };
+    // prologue: NBUF - 1 chunks in flight (split boundaries are group-aligned;
+    // copies past the split's end repeat its last group, so the number of
+    // copies per issue never changes)
+    static_for<0, NBUF - 1>([&](auto k) {
+      constexpr int K = decltype(k)::value;
+      issue(min(g0 + K / CPG, g1 - 1), std::integral_constant<int, K % CPG>{}, ring_lds + K * SLOT);
+    });
+    for (int g = g0; g < g1; ++g) {
+      static_for<0, CPG>([&](auto chc) {
+        constexpr int ch = decltype(chc)::value;
+        constexpr int ahead = ch + NBUF - 1;
+        issue(min(g + ahead / CPG, g1 - 1), std::integral_constant<int, ahead % CPG>{}, sl_issue);
         // copies issued after chunk c's: chunks c+1 .. c+NBUF-1, NBASE each,
         // plus NKP for each of them that starts a group
-        if (ch == 0)
-          wait_vmcnt<(NBUF - 1) * NBASE + kp_after<NBUF, CPG>(0) * NKP>();
-        else
-          wait_vmcnt<(NBUF - 1) * NBASE + kp_after<NBUF, CPG>(1) * NKP>();
-        process(ring + static_cast<uint32_t>(c % NBUF) * SLOT, ch == 0);
-      }
+        wait_vmcnt<(NBUF - 1) * NBASE + kp_after<NBUF, CPG>(ch) * NKP>();
+        process(ring + (sl_proc - ring_lds), ch == 0);
+        sl_proc = next_slot(sl_proc);
+        sl_issue = next_slot(sl_issue);
+      });
     }
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
   }
+  // quantized-chunk sums to real units
+#pragma unroll
+  for (int i = 0; i < NMT; ++i) acc[i] *= kTwo24;
 
   // ---- fp16 window chunks: the last split
   if (s == S - 1 && a.rc1 > a.rc0) {
-    uint32_t bqr[NP][NKB][4];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float q0 = qm[kb][2 * i] * code_mult<KB>(2 * i), q1 = qm[kb][2 * i + 1] * code_mult<KB>(2 * i + 1);
-        const uint32_t one = 0x3C003C00u;  // fp16 1.0 pair
-        if (CS) {
-          bqr[0][kb][i] = split_part(q0, q1, one, negf_p0);
-        } else {
-          uint32_t t = mix_mul2(q0, q1, one);
-          bqr[0][kb][i] = t;
-          bqr[NP - 1][kb][i] = mix_fma2(q0, q1, one, pk_mul_f16(t, 0xBC00BC00u));
-        }
-      }
     for (int64_t rc = a.rc0; rc < a.rc1; ++rc) {
       const uint8_t* rch = a.cache + ring_chunk_offset(L, slice, rc * kChunk);
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
@@ -539,22 +567,18 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         const half8 a1 = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(rch + ((1 * NKB + kb) * kLanes + l) * 16));
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp) {
-          const half8 bb = __builtin_bit_cast(half8, u32x4{bqr[pp][kb][0], bqr[pp][kb][1], bqr[pp][kb][2], bqr[pp][kb][3]});
+          const half8 bb = __builtin_bit_cast(half8, u32x4{qz[pp][kb][0], qz[pp][kb][1], qz[pp][kb][2], qz[pp][kb][3]});
           c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bb, c0, 0, 0, 0);
           c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bb, c1, 0, 0, 0);
         }
       }
       const int64_t pos0 = rc * kChunk;
       const bool partial = pos0 + kChunk > a.n;
-      float sc[8], p[8];
+      float sc[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sc[r] = c0[r];
-        sc[4 + r] = c1[r];
-      }
-      if (CS) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = add_ror8(sc[e]);
+        sc[r] = CS ? add_ror8(c0[r]) : c0[r];
+        sc[4 + r] = CS ? add_ror8(c1[r]) : c1[r];
       }
       uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
       if (partial) {
@@ -566,17 +590,25 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
           }
         }
       }
-      softmax_step(sc, p);
+      float cmax = fmax2(fmax2(fmax2(sc[0], sc[1]), fmax2(sc[2], sc[3])), fmax2(fmax2(sc[4], sc[5]), fmax2(sc[6], sc[7])));
+      cmax = wave_max_j(cmax);
+      if (__builtin_amdgcn_ballot_w64(cmax > mslack)) rescale(fmax2(m, cmax));
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(sc[e] - m);
+        lsum += p[e];
+      }
       uint32_t bpr[NP][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t one = 0x3C003C00u;
+        const uint32_t one = 0x3C003C00u;  // fp16 1.0 pair
         if (CS) {
-          bpr[0][i] = split_part(p[2 * i], p[2 * i + 1], one, negf_p0);
+          bpr[0][i] = split_part(p[2 * i], p[2 * i + 1], one, part_mask);
         } else {
-          uint32_t t = mix_mul2(p[2 * i], p[2 * i + 1], one);
-          bpr[0][i] = t;
-          bpr[NP - 1][i] = mix_fma2(p[2 * i], p[2 * i + 1], one, pk_mul_f16(t, 0xBC00BC00u));
+          const uint32_t hi = mix_mul2(p[2 * i], p[2 * i + 1], one);
+          bpr[0][i] = hi;
+          bpr[NP - 1][i] = mix_fms2(p[2 * i], p[2 * i + 1], one, hi);
         }
       }
 #pragma unroll
