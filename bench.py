@@ -11,8 +11,10 @@ Prints one JSON line.  `value` is achieved HBM throughput of the whole step
 (algorithmic bytes: packed codes + fp16 scales/zeros + fp16 window + q + out
 + the append's own bytes, divided by the measured step time).  `roofline`
 covers the dominant kernel (the split decode kernel), timed with HIP events
-on the stream it runs on; `cpu_baseline` is the CPU oracle timed on a
-bounded sample of the same workload on this host's cores.
+on the stream it runs on; its `traffic` is the HBM bytes per launch measured
+with rocprofv3 counters (profiles/), reported only while the kernel sources
+are unchanged since.  `cpu_baseline` is the CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -92,6 +94,42 @@ def cpu_baseline(w, K_host, V_host, q_host, batches, threads: int) -> dict:
         "sample": f"decode step (fp64 dequant + attention) over {len(pairs)} of {w.B * w.Hkv} (batch, kv-head) "
                   f"slices at {w.N} tokens, {dt:.2f} s wall on {threads} threads, scaled by slice count",
     }
+
+
+def source_fingerprint(paths) -> str:
+    """sha256 of the given sources with comments and whitespace removed."""
+    import hashlib
+    import re
+
+    parts = []
+    for rel in paths:
+        with open(os.path.join(ROOT, rel)) as f:
+            t = f.read()
+        t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", "", t)
+        parts.append(re.sub(r"\s+", "", t))
+    return hashlib.sha256("".join(parts).encode()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the rocprofv3 counter summary for this
+    workload (profiles/decode_kernel_traffic_<workload>.md), or None when there
+    is none or the decode kernel sources changed since the counters were taken."""
+    import glob
+    import re
+
+    for path in glob.glob(os.path.join(ROOT, "profiles", "decode_kernel_traffic_*.md")):
+        with open(path) as f:
+            m = re.search(r"```json\s*(\{.*?\})\s*```", f.read(), flags=re.S)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("workload") != workload:
+            continue
+        if source_fingerprint(rec["fingerprint_of"]) != rec["source_fingerprint"]:
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    return None
 
 
 def copy_calibration(gib: float) -> int:
@@ -243,7 +281,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "avg_us": round(dec_avg_ms * 1e3, 2),
             "bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes)),
         },

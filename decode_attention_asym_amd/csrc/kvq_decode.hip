@@ -6,8 +6,9 @@
 // keys quantized per channel and values quantized per token ("[Framework] The
 // Asymmetric Key-Value Cache Compression", section III), plus the fp16
 // window of recent tokens.  Decode attention is bound by reading the cache
-// (the "Loading ... takes longer than computing" remark of the NOVA-KV
-// abstract), so the kernel is built to stream every byte once.
+// (the NOVA-KV abstract on the page "WUSH-KV: KV Cache Quantization with
+// Data-Adaptive Transforms" makes this point), so the kernel is built to
+// stream every byte once.
 //
 // Per wave: one (batch, kv head) slice and one contiguous range of token
 // groups (a split).  The GQA query heads of the slice are the 16 columns of
