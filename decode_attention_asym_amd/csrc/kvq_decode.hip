@@ -408,7 +408,7 @@ void decode_kernel(DecodeArgs a) {
       for (int c = 0; c < NI; ++c) bmc[c] = (cb - m) - (VB == 4 ? 4.0f * (c & 1) : 2.0f * c);
     };
 
-    auto process = [&](const uint8_t* sl, bool group_start) __attribute__((always_inline)) {
+    auto process = [&](const uint8_t* sl, bool group_start, auto&& refill) __attribute__((always_inline)) {
       if (group_start) {
         // B operand from this group's key scales: q * s / mult in two parts
         // (exact-residual fp16 products), and the bias sum_c q_c z_c by MFMA
@@ -521,6 +521,9 @@ void decode_kernel(DecodeArgs a) {
           z = __builtin_fmaf(pm[2 * i + 1], h2f_hi(zp), z);
         }
       }
+      // the slot's data has long been read into registers: refill it with a
+      // later chunk before the PV products
+      refill();
       // PV on the subnormal code operands
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
@@ -532,28 +535,30 @@ void decode_kernel(DecodeArgs a) {
     };
 
     // Ring slots rotate through LDS addresses ring_lds + k * SLOT; chunk c of
-    // the split sits in slot c % NBUF.  Slot of the chunk processed next and
-    // of the next chunk to copy (NBUF - 1 ahead).
-    uint32_t sl_proc = ring_lds, sl_issue = ring_lds + (NBUF - 1) * SLOT;
+    // the split sits in slot c % NBUF.  Once chunk c's data is in registers its
+    // slot is refilled with chunk c + NBUF, so NBUF chunks are in flight while
+    // one is being computed.
+    uint32_t sl_proc = ring_lds;
     auto next_slot = [&](uint32_t x) { return x + SLOT == ring_lds + NBUF * SLOT ? ring_lds : x + SLOT; };
-    // prologue: NBUF - 1 chunks in flight (split boundaries are group-aligned;
+    // prologue: NBUF chunks in flight (split boundaries are group-aligned;
     // copies past the split's end repeat its last group, so the number of
     // copies per issue never changes)
-    static_for<0, NBUF - 1>([&](auto k) {
+    static_for<0, NBUF>([&](auto k) {
       constexpr int K = decltype(k)::value;
       issue(min(g0 + K / CPG, g1 - 1), std::integral_constant<int, K % CPG>{}, ring_lds + K * SLOT);
     });
     for (int g = g0; g < g1; ++g) {
       static_for<0, CPG>([&](auto chc) {
         constexpr int ch = decltype(chc)::value;
-        constexpr int ahead = ch + NBUF - 1;
-        issue(min(g + ahead / CPG, g1 - 1), std::integral_constant<int, ahead % CPG>{}, sl_issue);
+        constexpr int ahead = ch + NBUF;
         // copies issued after chunk c's: chunks c+1 .. c+NBUF-1, NBASE each,
         // plus NKP for each of them that starts a group
         wait_vmcnt<(NBUF - 1) * NBASE + kp_after<NBUF, CPG>(ch) * NKP>();
-        process(ring + (sl_proc - ring_lds), ch == 0);
+        const uint32_t sl = sl_proc;
+        process(ring + (sl - ring_lds), ch == 0, [&]() __attribute__((always_inline)) {
+          issue(min(g + ahead / CPG, g1 - 1), std::integral_constant<int, ahead % CPG>{}, sl);
+        });
         sl_proc = next_slot(sl_proc);
-        sl_issue = next_slot(sl_issue);
       });
     }
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
