@@ -10,6 +10,7 @@ from .kvq import (  # noqa: F401
     cache_bytes,
     check,
     lib,
+    merge_partials,
     workspace_bytes,
     KVQ_OK,
     KVQ_E_ARG,

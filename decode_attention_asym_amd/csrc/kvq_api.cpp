@@ -285,6 +285,7 @@ kvq_status kvq_merge_partials(const float* partials, float* out, int32_t rows, i
   if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16))
     return fail(KVQ_E_ARG, "partials/out NULL or not 16-byte aligned");
   if (rows < 1 || splits < 1) return fail(KVQ_E_ARG, "rows and splits must be positive");
+  if (splits > 256) return fail(KVQ_E_ARG, "splits %d above 256", splits);
   if (head_dim != 64 && head_dim != 128) return fail(KVQ_E_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
   hipError_t e = kvq::launch_merge(partials, out, rows, splits, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVQ_E_DEVICE, "merge kernel launch: %s", hipGetErrorString(e));

@@ -133,9 +133,13 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, v
  * and write, for every row r = b * H_q + h and split s, at
  * partials + (r * S + s) * (D + 4) floats:
  *   [0, D)  o = sum_t 2^(x_t - m) v_t   (unnormalized)
- *   D       m = max_t x_t               (-inf for an empty split)
+ *   D       m, a reference point with max_t x_t - 0.5 <= m <= max_t x_t
+ *           (the kernel moves it lazily; -inf for an empty split)
  *   D + 1   l = sum_t 2^(x_t - m)
  * with x_t = log2(e) * q . k_t / sqrt(D) (scores in the base-2 domain).
+ * Split s covers the contiguous token groups [s * c, min(ng, (s + 1) * c))
+ * with c = ceil(ng / S) (ng quantized groups); the last split also covers
+ * the fp16 window.
  * bytes must be >= H_q * B * S * (D + 4) * 4.  Requires a non-empty cache. */
 kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials, size_t bytes, int32_t num_splits,
                                int32_t* splits_used, void* stream);
@@ -143,7 +147,8 @@ kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials,
 /* Merge `splits` partials per row (layout above, `rows` rows) into
  * out[rows][head_dim] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
  * M = max_s m_s; splits with m_s = -inf contribute nothing, and a row whose
- * splits are all empty yields NaN.  head_dim in {64, 128}. */
+ * splits are all empty yields NaN.  head_dim in {64, 128}; 1 <= splits <= 256
+ * (the most kvq_workspace_bytes ever provides for), else KVQ_E_ARG. */
 kvq_status kvq_merge_partials(const float* partials, float* out, int32_t rows, int32_t splits, int32_t head_dim,
                               void* stream);
 

@@ -97,6 +97,11 @@ def test_host_validation_without_device_work():
     finally:
         assert lib.kvq_destroy(h) == kvq.KVQ_OK
     assert lib.kvq_destroy(None) == kvq.KVQ_OK
+    # merge: argument checks before any launch
+    assert lib.kvq_merge_partials(fake, fake, 4, 257, 128, None) == kvq.KVQ_E_ARG
+    assert lib.kvq_merge_partials(fake, fake, 4, 0, 128, None) == kvq.KVQ_E_ARG
+    assert lib.kvq_merge_partials(fake + 4, fake, 4, 8, 128, None) == kvq.KVQ_E_ARG
+    assert lib.kvq_merge_partials(fake, fake, 4, 8, 96, None) == kvq.KVQ_E_UNSUPPORTED
     cc.struct_size = 4
     assert lib.kvq_create(ctypes.byref(cc), fake, need, ctypes.byref(h)) == kvq.KVQ_E_ARG
 

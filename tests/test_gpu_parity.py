@@ -83,6 +83,95 @@ def test_split_counts_agree(splits):
     _check_full(w, splits=splits, check_codes=(splits == 1))
 
 
+def _split_ranges(n, ng, G, S_req):
+    """Token ranges of the splits: contiguous, group-aligned runs of
+    ceil(ng / S) groups; the last split also takes the fp16 window."""
+    S = min(S_req, max(1, ng))
+    gps = -(-ng // S) if ng else 0
+    if gps:
+        S = -(-ng // gps)
+    cuts = [min(ng, s * gps) * G for s in range(S)] + [n]
+    return S, list(zip(cuts[:-1], cuts[1:]))
+
+
+def test_decode_partials_per_split_match_oracle():
+    """kvq_decode_partials: every split's (m, l, o) against the oracle's partial
+    attention over the same token range; kvq_merge_partials of them equals
+    kvq_decode_attn_splits with the same split count, bit for bit."""
+    kvq = _lib()
+    import oracle
+    from _parity import canonical_slice, oracle_queries
+
+    w = WORKLOADS[2].replace(name="partials", B=2, Hq=8, Hkv=2, N=64 * 9 + 128 + 21)
+    syn, K, V, q, cache = _run_prefill(w)
+    S_req = 4
+    partials, S = cache.decode_partials(q, splits=S_req)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    kvq.merge_partials(partials, out, w.B * w.Hq, S, w.D)
+    full = cache.decode(q, splits=S_req)
+    torch.cuda.synchronize()
+    assert torch.equal(out, full)
+    exp = cache.export()
+    ng = exp["nq"] // w.G
+    S_exp, ranges = _split_ranges(w.N, ng, w.G, S_req)
+    assert S == S_exp
+    P = partials.reshape(-1)[:w.B * w.Hq * S * (w.D + 4)].double().cpu().numpy().reshape(w.B, w.Hq, S, w.D + 4)
+    q_host = to_oracle_input(q, w.dtype)
+    log2e = 1.0 / np.log(2.0)
+    for b in range(w.B):
+        qb = oracle_queries(w, q_host[b])
+        for h in range(w.Hkv):
+            sl = canonical_slice(exp, b, h, w.D, w.kbits, w.vbits)
+            hq = slice(h * w.gqa, (h + 1) * w.gqa)
+            for s, (t0, t1) in enumerate(ranges):
+                m, l, o = oracle.attend_partial(qb[hq], sl, w.D, w.G, w.R, t0, t1)
+                got = P[b, hq, s]
+                # m is the kernel's lazily moved reference point: at most 0.5 below the max
+                mx = m * log2e
+                assert np.all(got[:, w.D] <= mx + 1e-3) and np.all(got[:, w.D] >= mx - 0.5 - 1e-3), (b, h, s)
+                l_at_max = got[:, w.D + 1] * np.exp2(got[:, w.D] - mx)
+                assert np.all(np.abs(l_at_max / l - 1.0) <= 2e-3), (b, h, s)
+                err, _ = rel_l2(got[:, :w.D] / got[:, w.D + 1:w.D + 2], o / l[:, None])
+                assert err <= TOL_REL_L2, (b, h, s, err)
+
+
+@pytest.mark.parametrize("D,S", [(128, 1), (128, 8), (64, 13), (128, 100), (64, 256), (128, 256)])
+def test_merge_partials_against_oracle(D, S):
+    """kvq_merge_partials on seeded partials (wide score ranges, empty splits
+    whose o and l hold NaN) against the oracle's split merge."""
+    kvq = _lib()
+    import oracle
+
+    rows = 37
+    rng = np.random.default_rng(1000 + 7 * D + S)
+    m2 = rng.standard_normal((rows, S)) * 20.0
+    empty = rng.random((rows, S)) < 0.2
+    empty[:, 0] = False
+    m2[empty] = -np.inf
+    l = rng.uniform(0.5, 50.0, (rows, S))
+    o = rng.standard_normal((rows, S, D)) * l[..., None]
+    rec = np.zeros((rows, S, D + 4), np.float32)
+    rec[..., :D] = o
+    rec[..., D] = m2
+    rec[..., D + 1] = l
+    rec[..., D + 2:] = np.nan
+    rec[empty, :D] = np.nan
+    rec[empty, D + 1] = np.nan
+    part = torch.from_numpy(rec).cuda()
+    out = torch.empty((rows, D), dtype=torch.float32, device="cuda")
+    kvq.merge_partials(part, out, rows, S, D)
+    torch.cuda.synchronize()
+    r32 = rec.astype(np.float64)
+    ln2 = np.log(2.0)
+    o_ref = np.where(empty[..., None], 0.0, r32[..., :D])
+    l_ref = np.where(empty, 0.0, r32[..., D + 1])
+    ref = oracle.merge_partials((r32[..., D] * ln2).T, l_ref.T, o_ref.transpose(1, 0, 2))
+    got = out.double().cpu().numpy()
+    assert np.isfinite(got).all()
+    err, worst = rel_l2(got, ref)
+    assert worst <= 1e-5, (err, worst)
+
+
 def test_stepwise_append_equals_prefill():
     kvq = _lib()
     w = WORKLOADS[2].replace(name="stepwise", B=2, Hkv=2, Hq=8, N=700)
