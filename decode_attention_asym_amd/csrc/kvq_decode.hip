@@ -11,8 +11,9 @@
 // stream every byte once.
 //
 // Per wave: one (batch, kv head) slice and one contiguous range of token
-// groups (a split).  The GQA query heads of the slice are the 16 columns of
-// the MFMA B operand (unused columns compute on zeros).
+// groups (a split).  The GQA query heads of the slice are columns of the MFMA
+// B operand, replicated across the 16 columns so that the per-score softmax
+// work is shared out over the replicas (see decode_kernel).
 //
 // Scale folding (exact in real arithmetic):
 //   keys, per channel c of group g:  q . khat_t = sum_c (q_c s_gc) code_tc + sum_c q_c z_gc
@@ -119,7 +120,12 @@ __device__ __forceinline__ half8 a_operand(const uint32_t* words, int idx, const
 
 // Reductions over the four lane groups j of a column (lanes l16, l16 + 16,
 // l16 + 32, l16 + 48), on the VALU with gfx950's lane swaps.
-__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_fmaxf(a, b); }
+// max(a, b) as the median of (a, b, +inf): one v_med3_f32, with none of the
+// input canonicalization fmaxf needs (+inf comes from an SGPR so the compiler
+// does not turn the median back into fmaxf)
+__device__ __forceinline__ float fmax2(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, __uint_as_float(sgpr_const(0x7f800000u)));
+}
 __device__ __forceinline__ float wave_max_j(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -163,12 +169,6 @@ __device__ __forceinline__ uint32_t mix_fms2(float a0, float a1, uint32_t s, uin
                     static_cast<_Float16>(__builtin_fmaf(a1, static_cast<float>(sv[1]), -static_cast<float>(cv[1])))};
   return as_u32(r);
 }
-// Two-part fp16 operand of x = a * s (a fp32, s an fp16 pair): part 0 =
-// fp16(x), part 1 = fp16(x - part 0).  In column-split mode a lane produces
-// the part its columns hold: mask 0 gives part 0, all-ones part 1.
-__device__ __forceinline__ uint32_t split_part(float a0, float a1, uint32_t s, uint32_t mask) {
-  return mix_fms2(a0, a1, s, mix_mul2(a0, a1, s) & mask);
-}
 // Exact-residual product of fp16 pairs: with x = fp16(a * s), the fp16 fma
 // a * s - x is exact (the rounding error of a product of two fp16 values is
 // an fp16 value), so fp16(b * s + (a * s - x)) is the second part of
@@ -179,12 +179,6 @@ __device__ __forceinline__ uint32_t pack_h2(float x0, float x1) {
   const half2v r = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
   return as_u32(r);
 }
-// Sum with the lane 8 places away inside each row of 16 (row_ror:8): lanes h
-// and h + 8 both receive x_h + x_{h+8}.
-__device__ __forceinline__ float add_ror8(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
-}
-
 // ---- LDS staging of the code stream ----------------------------------------
 // Chunks are copied global -> LDS with gfx950's direct loads (no VGPRs held
 // while in flight), several chunks ahead of the one being processed.  The
@@ -255,27 +249,74 @@ struct PageShape {
 // below 65504 for any scale of fp16 data.
 constexpr float kMaxSlack = 0.5f;
 
-template <int D, int KB, int VB, int G, bool CS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CS ? 3 : 2)))
+// Lane i of each row of 16 receives lane (i + N) mod 16 (DPP row_ror:16-N).
+template <int N>
+__device__ __forceinline__ uint32_t row_from(uint32_t x) {
+  static_assert(N > 0 && N < 16, "row rotation");
+  return __builtin_amdgcn_update_dpp(0u, x, 0x120 + (16 - N), 0xf, 0xf, true);
+}
+template <int N>
+__device__ __forceinline__ float row_from(float x) {
+  return __uint_as_float(row_from<N>(__float_as_uint(x)));
+}
+// Max / sum over the R replicas of a head slot (lanes h, h + 16/R, ... of a row).
+template <int R>
+__device__ __forceinline__ float replica_max(float x) {
+  if constexpr (R >= 2) x = fmax2(x, row_from<8>(x));
+  if constexpr (R >= 4) x = fmax2(x, row_from<4>(x));
+  return x;
+}
+template <int R>
+__device__ __forceinline__ float replica_sum(float x) {
+  if constexpr (R >= 2) x += row_from<8>(x);
+  if constexpr (R >= 4) x += row_from<4>(x);
+  return x;
+}
+
+// Column layout.  Lane l holds MFMA column l16 = l % 16 and lane group
+// j = l / 16.  The gqa query heads of the slice take head slots 0..GQC-1
+// (GQC = 4 for gqa <= 4, 8 for gqa = 8, 16 for gqa = 16); the 16 columns hold
+// R = 16 / GQC replicas of them (column l16 = head slot l16 % GQC, replica
+// rp = l16 / GQC).  The query side of QK^T carries two fp16 parts: with
+// GQC < 16, odd replicas hold the second part in their columns, so one MFMA
+// produces both and a DPP add with the column GQC places away gives every
+// lane the full score; with GQC = 16 the parts take two MFMAs.  Each replica
+// then keeps only NV = 8 / R of the 8 scores a lane holds (tokens tau(j, e),
+// e in [NV rp, NV rp + NV)), so the softmax, the PV weights and the
+// zero-point sums cost NV values per lane instead of 8.  Replica 0 gathers
+// the PV weights of the other replicas by DPP row rotation and owns the
+// output; the other replicas' PV columns are never read.
+template <int D, int KB, int VB, int G, int GQC>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
 void decode_kernel(DecodeArgs a) {
   using PS = PageShape<D, KB, VB, G>;
   constexpr int NKB = D / 32, NMT = D / 16, NCG = PS::NCG, CPG = PS::CPG;
-  constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4, VPW = 8 * NCG;
-  // B operands carry each value as two fp16 parts (hi + lo) so the folded
-  // products keep ~22 bits: in CS mode (at most 8 heads) hi sits in columns
-  // 0-7 and lo in columns 8-15 of one MFMA; otherwise two MFMAs.
-  constexpr int NP = CS ? 1 : 2;
+  constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4;
+  constexpr int R = 16 / GQC, NV = 8 / R, NPR = NV / 2;  // replicas, values and value pairs per lane
+  constexpr int VPL = NV * NCG;                           // value-parameter dwords a lane reads per chunk
+  static_assert(GQC == 4 || GQC == 8 || GQC == 16, "head slots per replica");
+  // B operands of QK^T carry each value as two fp16 parts (hi + lo) so the
+  // folded products keep ~22 bits: in the columns of odd replicas (NP = 1
+  // MFMA) when GQC < 16, else as two MFMAs.
+  constexpr int NP = GQC < 16 ? 1 : 2;
   const Layout& L = a.L;
   const int l = threadIdx.x, l16 = l & 15, j = l >> 4;
   const int S = a.splits;
   const int64_t slice = blockIdx.x / S;
   const int s = static_cast<int>(blockIdx.x % S);
   const int b = static_cast<int>(slice / a.Hkv), hkv = static_cast<int>(slice % a.Hkv);
-  const int h = CS ? (l16 & 7) : l16;
-  const bool lo_lane = CS && l16 >= 8;
+  const int h = l16 % GQC, rp = l16 / GQC;
   const bool hv = h < a.gqa;
   const int hq = hkv * a.gqa + (hv ? h : 0);
-  const uint32_t part_mask = lo_lane ? 0xFFFFFFFFu : 0u;  // this lane's part (CS mode)
+  const bool lo_cols = NP == 1 && (rp & 1);               // this lane's columns hold the second part
+  // full QK^T sum from the two parts' columns
+  auto combine = [&](float x) __attribute__((always_inline)) {
+    if constexpr (NP == 1) {
+      return x + row_from<GQC>(x);
+    } else {
+      return x;
+    }
+  };
 
   // ---- query: lane owns channels 32 kb + 8 j + e of head h, times log2(e)/sqrt(D)
   float qm[NKB][8];
@@ -312,8 +353,10 @@ void decode_kernel(DecodeArgs a) {
   //   qz: q itself, the B operand of the key zero-point bias and of the window;
   //   qh / ql: q / mult (the code multipliers of the key operand), from which
   //   the per-group B operand q * scale / mult is formed by exact-residual fp16
-  //   products.  In CS mode ql holds part 0 on hi lanes (so the same
-  //   instructions produce each lane's own part).
+  //   products.  With NP = 1, qz and ql hold this lane's own part (ql = part 0
+  //   in first-part columns) and qh is zero in first-part columns, so the same
+  //   three instructions produce either part: x = qh s, y = qh s - x (exact),
+  //   part = fp16(ql s + y).
   uint32_t qz[NP][NKB][4], qh[NKB][4], ql[NKB][4];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -325,37 +368,47 @@ void decode_kernel(DecodeArgs a) {
       const float d0 = x0 * (1.0f / code_mult<KB>(2 * i)), d1 = x1 * (1.0f / code_mult<KB>(2 * i + 1));
       const float e0 = static_cast<float>(static_cast<_Float16>(d0)), e1 = static_cast<float>(static_cast<_Float16>(d1));
       const uint32_t d_hi = pack_h2(d0, d1), d_lo = pack_h2(d0 - e0, d1 - e1);
-      if (CS) {
-        qz[0][kb][i] = lo_lane ? z_lo : z_hi;
-        ql[kb][i] = lo_lane ? d_lo : d_hi;
+      if constexpr (NP == 1) {
+        qz[0][kb][i] = lo_cols ? z_lo : z_hi;
+        ql[kb][i] = lo_cols ? d_lo : d_hi;
+        qh[kb][i] = lo_cols ? d_hi : 0u;
       } else {
         qz[0][kb][i] = z_hi;
         qz[NP - 1][kb][i] = z_lo;
         ql[kb][i] = d_lo;
+        qh[kb][i] = d_hi;
       }
-      qh[kb][i] = d_hi;
     }
 
   const CodeMasks<KB> uk;
   const CodeMasks<VB> uv;
 
-  // Online-softmax state (per column, uniform over j).  m is the running max
-  // in log2 units; acc holds the PV sums in units of 2^-24 while quantized
-  // chunks are processed (subnormal code operands), real units afterwards.
+  // Value-code multiplier of this lane's value pair pp (tokens e = NV rp + 2 pp
+  // and + 1 share it) and its log2.
+  float vmult[NPR], vmlog[NPR];
+#pragma unroll
+  for (int pp = 0; pp < NPR; ++pp) {
+    const int e = NV * rp + 2 * pp;
+    vmult[pp] = code_mult<VB>(e);
+    vmlog[pp] = VB == 4 ? 4.0f * ((e >> 1) & 1) : 2.0f * (e >> 1);
+  }
+
+  // Online-softmax state (per head, uniform over replicas and j).  m is the
+  // running max in log2 units; acc holds the PV sums in units of 2^-24 while
+  // quantized chunks are processed (subnormal code operands), real units
+  // afterwards.  lsum and zacc are this lane's share (its value slots).
   float m = -INFINITY, mslack = -INFINITY, lsum = 0.0f;
   f32x4 acc[NMT];
 #pragma unroll
   for (int i = 0; i < NMT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // zero-point sums per value group and per code-multiplier class i = e >> 1
-  // (the weights below are p / mult; the classes are rescaled at the end)
-  constexpr int NI = VB == 4 ? 2 : 4;
-  float zacc[NCG][NI];
+  // zero-point sums per value group and value pair, weighted by p / mult
+  float zacc[NCG][NPR];
 #pragma unroll
   for (int i = 0; i < NCG; ++i)
 #pragma unroll
-    for (int c = 0; c < NI; ++c) zacc[i][c] = 0.0f;
+    for (int pp = 0; pp < NPR; ++pp) zacc[i][pp] = 0.0f;
 
-  // (called wave-uniformly; mnew = max(m, chunk max) per column)
+  // (called wave-uniformly; mnew = max(m, chunk max) per head)
   auto rescale = [&](float mnew) __attribute__((always_inline)) {
     const float al = __builtin_amdgcn_exp2f(m - mnew);
 #pragma unroll
@@ -363,10 +416,31 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NCG; ++i)
 #pragma unroll
-      for (int c = 0; c < NI; ++c) zacc[i][c] *= al;
+      for (int pp = 0; pp < NPR; ++pp) zacc[i][pp] *= al;
     lsum *= al;
     m = mnew;
     mslack = mnew + kMaxSlack;
+  };
+  // this lane's NV scores out of the 8 it holds (tokens tau(j, e), e = NV rp + k)
+  auto own_values = [&](const float (&t)[8], float (&u)[NV]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) u[k] = t[k];
+#pragma unroll
+    for (int r = 1; r < R; ++r)
+#pragma unroll
+      for (int k = 0; k < NV; ++k) u[k] = rp == r ? t[NV * r + k] : u[k];
+  };
+  // PV B operand of replica 0 from the replicas' value pairs: pair i sits in
+  // replica i / NPR, slot i % NPR
+  auto gather_pairs = [&](const uint32_t (&c)[NPR], uint32_t (&o)[4]) __attribute__((always_inline)) {
+    static_for<0, 4>([&](auto ic) {
+      constexpr int i = decltype(ic)::value, r = i / NPR;
+      if constexpr (r == 0) {
+        o[i] = c[i % NPR];
+      } else {
+        o[i] = row_from<GQC * r>(c[i % NPR]);
+      }
+    });
   };
 
   const int g0 = s * static_cast<int>(a.groups_per_split);
@@ -382,6 +456,9 @@ void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF * SLOT];
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((KVQ_AS3 uint8_t*)ring));
   const uint32_t lane16 = static_cast<uint32_t>(l) * 16, lane4 = static_cast<uint32_t>(l) * 4;
+  // byte offset of this lane's value parameters inside a chunk's block
+  // (layout [j][pair][group][scale, zero] dwords, see kvq_layout.h)
+  const int vp_off = KC + VC + (j * 4 + NPR * rp) * NCG * 8;
 
   if (g1 > g0) {
     const uint8_t* slice_pages = a.cache + page_offset(L, slice, 0);
@@ -400,12 +477,12 @@ void decode_kernel(DecodeArgs a) {
 
     uint32_t bq[NP][NKB][4];  // B operand of QK^T (fp16 pairs), per part
     float cb = 0.0f;          // this group's zero-point score bias (log2 units)
-    // exponent offsets per value-code multiplier class: exp2(score - m - log2(mult))
-    // is p / mult, the weight the PV operand needs
-    float bmc[NI];
+    // exponent offsets per value pair: exp2(score - m - log2(mult)) is p / mult,
+    // the weight the PV operand needs
+    float bmc[NPR];
     auto set_bmc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int c = 0; c < NI; ++c) bmc[c] = (cb - m) - (VB == 4 ? 4.0f * (c & 1) : 2.0f * c);
+      for (int pp = 0; pp < NPR; ++pp) bmc[pp] = (cb - m) - vmlog[pp];
     };
 
     auto process = [&](const uint8_t* sl, bool group_start, auto&& refill) __attribute__((always_inline)) {
@@ -423,11 +500,11 @@ void decode_kernel(DecodeArgs a) {
             const half2v sv = as_h2(sw[i]), hh = as_h2(qh[kb][i]);
             const half2v x = pk_mul(hh, sv);
             const half2v y = pk_fma(hh, sv, -x);  // exact: hh * sv - x
-            if (CS) {
-              bq[0][kb][i] = as_u32(pk_fma(as_h2(ql[kb][i]), sv, as_h2(as_u32(y) & part_mask)));
+            if constexpr (NP == 1) {
+              bq[0][kb][i] = as_u32(pk_fma(as_h2(ql[kb][i]), sv, y));
             } else {
               bq[0][kb][i] = as_u32(x);
-              bq[NP - 1][kb][i] = as_u32(pk_fma(as_h2(ql[kb][i]), sv, y));
+              bq[1][kb][i] = as_u32(pk_fma(as_h2(ql[kb][i]), sv, y));
             }
           }
         }
@@ -441,10 +518,10 @@ void decode_kernel(DecodeArgs a) {
             cbt = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bz, cbt, 0, 0, 0);
           }
         }
-        cb = CS ? add_ror8(cbt[0]) : cbt[0];
+        cb = combine(cbt[0]);
         set_bmc();
       }
-      uint32_t kw[KW], vw[VW], vp[VPW];
+      uint32_t kw[KW], vw[VW], vp[VPL];
       if constexpr (KW >= 4) {
 #pragma unroll
         for (int v = 0; v < KW / 4; ++v) {
@@ -465,13 +542,15 @@ void decode_kernel(DecodeArgs a) {
         const u32x2 x = *reinterpret_cast<const u32x2*>(sl + KC + l * 8);
         vw[0] = x[0]; vw[1] = x[1];
       }
-      {
-        const u32x4* vpp = reinterpret_cast<const u32x4*>(sl + KC + VC) + j * (VPW / 4);
+      if constexpr (VPL % 4 == 0) {
 #pragma unroll
-        for (int v = 0; v < VPW / 4; ++v) {
-          const u32x4 x = vpp[v];
+        for (int v = 0; v < VPL / 4; ++v) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(sl + vp_off + 16 * v);
           vp[4 * v] = x[0]; vp[4 * v + 1] = x[1]; vp[4 * v + 2] = x[2]; vp[4 * v + 3] = x[3];
         }
+      } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(sl + vp_off);
+        vp[0] = x[0]; vp[1] = x[1];
       }
       // QK^T: two 16-token tiles; C = 2^-24 * (score - bias)
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
@@ -489,41 +568,47 @@ void decode_kernel(DecodeArgs a) {
       float t[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        t[r] = CS ? add_ror8(c0[r]) : c0[r];
-        t[4 + r] = CS ? add_ror8(c1[r]) : c1[r];
+        t[r] = combine(c0[r]);
+        t[4 + r] = combine(c1[r]);
       }
-      // online softmax over the chunk's 8 scores per lane (tokens tau(j, e))
-      const float tmax = fmax2(fmax2(fmax2(t[0], t[1]), fmax2(t[2], t[3])), fmax2(fmax2(t[4], t[5]), fmax2(t[6], t[7])));
-      const float cmax = wave_max_j(__builtin_fmaf(tmax, kTwo24, cb));
+      float u[NV];
+      own_values(t, u);
+      // online softmax over the head's 32 chunk scores (NV per lane)
+      float tmax = u[0];
+#pragma unroll
+      for (int k = 1; k < NV; ++k) tmax = fmax2(tmax, u[k]);
+      const float cmax = wave_max_j(__builtin_fmaf(replica_max<R>(tmax), kTwo24, cb));
       if (__builtin_amdgcn_ballot_w64(cmax > mslack)) {
         rescale(fmax2(m, cmax));
         set_bmc();
       }
-      // pm = p / mult (the exponent offset per class), lsum += pm * mult
-      float pm[8];
+      // pm = p / mult (the exponent offset per pair), lsum += pm * mult
+      float pm[NV];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pm[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[e], kTwo24, bmc[VB == 4 ? ((e >> 1) & 1) : (e >> 1)]));
-        lsum = __builtin_fmaf(pm[e], code_mult<VB>(e), lsum);
+      for (int k = 0; k < NV; ++k) {
+        pm[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(u[k], kTwo24, bmc[k >> 1]));
+        lsum = __builtin_fmaf(pm[k], vmult[k >> 1], lsum);
       }
-      // PV B operand p * value scale / mult (one fp16 part: its rounding is far
-      // below the matrix cores' own error on these sums) and the zero-point sums.
-      // In CS mode lanes 8-15 produce duplicate columns, cleared before the window.
-      uint32_t bp[NCG][4];
+      // PV weights p * value scale / mult (one fp16 part: its rounding is far
+      // below the matrix cores' own error on these sums) and the zero-point sums
+      uint32_t bpc[NCG][NPR];
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t sp = vp[cg * 8 + i], zp = vp[cg * 8 + 4 + i];
-          bp[cg][i] = mix_mul2(pm[2 * i], pm[2 * i + 1], sp);
-          float& z = zacc[cg][VB == 4 ? (i & 1) : i];
-          z = __builtin_fmaf(pm[2 * i], h2f_lo(zp), z);
-          z = __builtin_fmaf(pm[2 * i + 1], h2f_hi(zp), z);
+        for (int pp = 0; pp < NPR; ++pp) {
+          const uint32_t sp = vp[(pp * NCG + cg) * 2], zp = vp[(pp * NCG + cg) * 2 + 1];
+          bpc[cg][pp] = mix_mul2(pm[2 * pp], pm[2 * pp + 1], sp);
+          float& z = zacc[cg][pp];
+          z = __builtin_fmaf(pm[2 * pp], h2f_lo(zp), z);
+          z = __builtin_fmaf(pm[2 * pp + 1], h2f_hi(zp), z);
         }
       }
       // the slot's data has long been read into registers: refill it with a
       // later chunk before the PV products
       refill();
+      uint32_t bp[NCG][4];
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) gather_pairs(bpc[cg], bp[cg]);
       // PV on the subnormal code operands
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
@@ -563,10 +648,9 @@ void decode_kernel(DecodeArgs a) {
     }
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
   }
-  // quantized-chunk sums to real units; in CS mode lanes 8-15 held duplicate
-  // columns and now start the window's second parts from zero
+  // quantized-chunk sums to real units
 #pragma unroll
-  for (int i = 0; i < NMT; ++i) acc[i] = lo_lane ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i] * kTwo24;
+  for (int i = 0; i < NMT; ++i) acc[i] *= kTwo24;
 
   // ---- fp16 window chunks: the last split
   if (s == S - 1 && a.rc1 > a.rc0) {
@@ -589,8 +673,8 @@ void decode_kernel(DecodeArgs a) {
       float sc[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sc[r] = CS ? add_ror8(c0[r]) : c0[r];
-        sc[4 + r] = CS ? add_ror8(c1[r]) : c1[r];
+        sc[r] = combine(c0[r]);
+        sc[4 + r] = combine(c1[r]);
       }
       uint32_t vmask[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
       if (partial) {
@@ -602,33 +686,36 @@ void decode_kernel(DecodeArgs a) {
           }
         }
       }
-      float cmax = fmax2(fmax2(fmax2(sc[0], sc[1]), fmax2(sc[2], sc[3])), fmax2(fmax2(sc[4], sc[5]), fmax2(sc[6], sc[7])));
-      cmax = wave_max_j(cmax);
+      float u[NV];
+      own_values(sc, u);
+      float cmax = u[0];
+#pragma unroll
+      for (int k = 1; k < NV; ++k) cmax = fmax2(cmax, u[k]);
+      cmax = wave_max_j(replica_max<R>(cmax));
       if (__builtin_amdgcn_ballot_w64(cmax > mslack)) rescale(fmax2(m, cmax));
-      float p[8];
+      float p[NV];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(sc[e] - m);
-        lsum += p[e];
+      for (int k = 0; k < NV; ++k) {
+        p[k] = __builtin_amdgcn_exp2f(u[k] - m);
+        lsum += p[k];
       }
-      uint32_t bpr[NP][4];
+      // two-part fp16 weights (the window's values are fp16 data, no scales)
+      uint32_t ph[NPR], pl[NPR];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int pp = 0; pp < NPR; ++pp) {
         const uint32_t one = 0x3C003C00u;  // fp16 1.0 pair
-        if (CS) {
-          bpr[0][i] = split_part(p[2 * i], p[2 * i + 1], one, part_mask);
-        } else {
-          const uint32_t hi = mix_mul2(p[2 * i], p[2 * i + 1], one);
-          bpr[0][i] = hi;
-          bpr[NP - 1][i] = mix_fms2(p[2 * i], p[2 * i + 1], one, hi);
-        }
+        ph[pp] = mix_mul2(p[2 * pp], p[2 * pp + 1], one);
+        pl[pp] = mix_fms2(p[2 * pp], p[2 * pp + 1], one, ph[pp]);
       }
+      uint32_t bpr[2][4];
+      gather_pairs(ph, bpr[0]);
+      gather_pairs(pl, bpr[1]);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         u32x4 vwd = *reinterpret_cast<const u32x4*>(rch + kChunk * D * 2 + (mt * kLanes + l) * 16);
         vwd[0] &= vmask[0]; vwd[1] &= vmask[1]; vwd[2] &= vmask[2]; vwd[3] &= vmask[3];
 #pragma unroll
-        for (int pp = 0; pp < NP; ++pp) {
+        for (int pp = 0; pp < 2; ++pp) {
           const half8 bb = __builtin_bit_cast(half8, u32x4{bpr[pp][0], bpr[pp][1], bpr[pp][2], bpr[pp][3]});
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, vwd), bb, acc[mt], 0, 0, 0);
         }
@@ -636,23 +723,17 @@ void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- finalize: combine the two parts (CS), reduce over lane groups, write
-  if (CS) {
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mt][r] = add_ror8(acc[mt][r]);
-  }
-  lsum = wave_sum_j(lsum);
+  // ---- finalize: reduce the lane shares over replicas and lane groups, write
+  lsum = wave_sum_j(replica_sum<R>(lsum));
   float zsum[NCG];
 #pragma unroll
   for (int i = 0; i < NCG; ++i) {
     float z = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NI; ++c) z = __builtin_fmaf(zacc[i][c], VB == 4 ? ((c & 1) ? 16.0f : 1.0f) : static_cast<float>(1 << (2 * c)), z);
-    zsum[i] = wave_sum_j(z);
+    for (int pp = 0; pp < NPR; ++pp) z = __builtin_fmaf(zacc[i][pp], vmult[pp], z);
+    zsum[i] = wave_sum_j(replica_sum<R>(z));
   }
-  if (hv && !lo_lane) {
+  if (hv && rp == 0) {
     const int64_t row = static_cast<int64_t>(b) * a.Hq + hq;
     if (a.write_final) {
       const float inv = 1.0f / lsum;
@@ -753,10 +834,12 @@ template <int D, int KB, int VB, int G>
 hipError_t decode_t(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(a.L.slices * a.splits));
   const size_t lds = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
-  if (a.gqa <= 8)
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, true>), grid, dim3(kLanes), lds, s, a);
+  if (a.gqa <= 4)
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 4>), grid, dim3(kLanes), lds, s, a);
+  else if (a.gqa <= 8)
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 8>), grid, dim3(kLanes), lds, s, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, false>), grid, dim3(kLanes), lds, s, a);
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 16>), grid, dim3(kLanes), lds, s, a);
   return hipGetLastError();
 }
 template <int D, int KB, int VB>

@@ -152,16 +152,17 @@ KVQ_HD int kparam_index(const Layout& L, int c) {
 }
 
 // fp16 element index, inside a chunk's value-parameter block, of the scale of
-// (token t, value group cg); the zero is 8 elements (4 dwords) later.  Lane
-// group j reads its run of 8 * ncg dwords: per group cg four dwords of scale
-// pairs (tokens tau(j, 2i), tau(j, 2i + 1)) then four dwords of zero pairs,
-// so each dword is one fp16 pair of a PV B operand as it is.
+// (token t, value group cg); the zero is 2 elements (one dword) later.  The
+// block is [j][pair i][group cg][scale pair, zero pair] dwords, where pair i
+// holds tokens tau(j, 2i) and tau(j, 2i + 1): a lane that owns consecutive
+// token pairs of lane group j reads all their scales and zeros as one run,
+// and each scale dword is one fp16 pair of a PV B operand as it is.
 KVQ_HD int vparam_scale_elem(const Layout& L, int t, int cg) {
   int j, e;
   tau_inv(t, &j, &e);
-  return ((j * L.ncg + cg) * 8 + (e >> 1)) * 2 + (e & 1);
+  return (((j * 4 + (e >> 1)) * L.ncg + cg) * 2) * 2 + (e & 1);
 }
-KVQ_HD int vparam_zero_elem(const Layout& L, int t, int cg) { return vparam_scale_elem(L, t, cg) + 8; }
+KVQ_HD int vparam_zero_elem(const Layout& L, int t, int cg) { return vparam_scale_elem(L, t, cg) + 2; }
 
 // Byte offsets inside a ring chunk of the fp16 window copy of token t, channel c.
 // Keys are stored as the QK A operand, values as the PV A operand.

@@ -59,6 +59,8 @@ SMALL = [
     WORKLOADS[4].replace(name="mha-fwht-ragged", B=2, Hq=8, Hkv=8, N=2048 + 13),
     WORKLOADS[1].replace(name="d64-k4v4-g64-gqa2-f16", B=3, Hq=4, Hkv=2, D=64, N=1000, kbits=4, vbits=4, G=64, R=64, dtype="f16"),
     WORKLOADS[1].replace(name="k2v4-g32-gqa16-r0", B=1, Hq=32, Hkv=2, N=700, kbits=2, vbits=4, G=32, R=0),
+    WORKLOADS[1].replace(name="d64-k2v4-g32-gqa8", B=2, Hq=16, Hkv=2, D=64, N=1500 + 3, kbits=2, vbits=4, G=32, R=32),
+    WORKLOADS[1].replace(name="d64-k4v2-g64-gqa1", B=2, Hq=3, Hkv=3, D=64, N=900 + 9, kbits=4, vbits=2, G=64, R=64),
     WORKLOADS[0].replace(name="d64-rot-k4v2-g32", B=2, Hq=4, Hkv=4, N=333, kbits=4, vbits=2, rotate=True),
     WORKLOADS[1].replace(name="window-only", B=2, N=100, R=128),
     WORKLOADS[1].replace(name="single-token", B=2, N=1, R=32),
@@ -261,10 +263,10 @@ def test_capacity_and_empty_errors():
     assert torch.isfinite(out).all()
 
 
-@pytest.mark.parametrize("kb,vb,G,hq", [(kb, vb, G, hq) for kb in (2, 4) for vb in (2, 4) for G in (32, 64) for hq in (4, 16)],
+@pytest.mark.parametrize("kb,vb,G,hq", [(kb, vb, G, hq) for kb in (2, 4) for vb in (2, 4) for G in (32, 64) for hq in (4, 8, 16)],
                          ids=lambda v: str(v))
 def test_bits_group_gqa_matrix(kb, vb, G, hq):
     """Every decode kernel instantiation at D=128 (bit widths x group size x
-    column-split / two-MFMA operand modes), one kv head, ragged length."""
+    head-slot replica modes: gqa 4, 8, 16), one kv head, ragged length."""
     w = WORKLOADS[1].replace(name=f"k{kb}v{vb}g{G}h{hq}", B=1, Hq=hq, Hkv=1, N=1000 + 7, kbits=kb, vbits=vb, G=G, R=64)
     _check_full(w, splits=1)
