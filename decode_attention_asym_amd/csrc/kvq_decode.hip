@@ -573,13 +573,15 @@ void decode_kernel(DecodeArgs a) {
       }
       float u[NV];
       own_values(t, u);
-      // online softmax over the head's 32 chunk scores (NV per lane)
+      // online softmax over the head's 32 chunk scores (NV per lane): a lane
+      // whose own maximum passes the head's slack bound calls for a rescale;
+      // only then is the per-head maximum reduced over replicas and lane groups
       float tmax = u[0];
 #pragma unroll
       for (int k = 1; k < NV; ++k) tmax = fmax2(tmax, u[k]);
-      const float cmax = wave_max_j(__builtin_fmaf(replica_max<R>(tmax), kTwo24, cb));
-      if (__builtin_amdgcn_ballot_w64(cmax > mslack)) {
-        rescale(fmax2(m, cmax));
+      const float lmax = __builtin_fmaf(tmax, kTwo24, cb);
+      if (__builtin_amdgcn_ballot_w64(lmax > mslack)) {
+        rescale(fmax2(m, wave_max_j(replica_max<R>(lmax))));
         set_bmc();
       }
       // pm = p / mult (the exponent offset per pair), lsum += pm * mult
@@ -652,9 +654,11 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < NMT; ++i) acc[i] *= kTwo24;
 
-  // ---- fp16 window chunks: the last split
-  if (s == S - 1 && a.rc1 > a.rc0) {
-    for (int64_t rc = a.rc0; rc < a.rc1; ++rc) {
+  // ---- fp16 window chunks, spread over the splits (split s takes window chunks
+  // S - 1 - s, 2S - 1 - s, ...) so that no wave adds more than its share of
+  // these latency-bound reads to the end of the kernel
+  {
+    for (int64_t rc = a.rc0 + (S - 1 - s); rc < a.rc1; rc += S) {
       const uint8_t* rch = a.cache + ring_chunk_offset(L, slice, rc * kChunk);
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -688,11 +692,10 @@ void decode_kernel(DecodeArgs a) {
       }
       float u[NV];
       own_values(sc, u);
-      float cmax = u[0];
+      float lmax = u[0];
 #pragma unroll
-      for (int k = 1; k < NV; ++k) cmax = fmax2(cmax, u[k]);
-      cmax = wave_max_j(replica_max<R>(cmax));
-      if (__builtin_amdgcn_ballot_w64(cmax > mslack)) rescale(fmax2(m, cmax));
+      for (int k = 1; k < NV; ++k) lmax = fmax2(lmax, u[k]);
+      if (__builtin_amdgcn_ballot_w64(lmax > mslack)) rescale(fmax2(m, wave_max_j(replica_max<R>(lmax))));
       float p[NV];
 #pragma unroll
       for (int k = 0; k < NV; ++k) {

@@ -138,8 +138,8 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, v
  *   D + 1   l = sum_t 2^(x_t - m)
  * with x_t = log2(e) * q . k_t / sqrt(D) (scores in the base-2 domain).
  * Split s covers the contiguous token groups [s * c, min(ng, (s + 1) * c))
- * with c = ceil(ng / S) (ng quantized groups); the last split also covers
- * the fp16 window.
+ * with c = ceil(ng / S) (ng quantized groups), plus the fp16 window's 32-token
+ * chunks w (counted from the first window token) with w mod S = S - 1 - s.
  * bytes must be >= H_q * B * S * (D + 4) * 4.  Requires a non-empty cache. */
 kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials, size_t bytes, int32_t num_splits,
                                int32_t* splits_used, void* stream);

@@ -86,14 +86,21 @@ def test_split_counts_agree(splits):
 
 
 def _split_ranges(n, ng, G, S_req):
-    """Token ranges of the splits: contiguous, group-aligned runs of
-    ceil(ng / S) groups; the last split also takes the fp16 window."""
+    """Token ranges of each split: a contiguous, group-aligned run of
+    ceil(ng / S) groups, plus the fp16 window's 32-token chunks w with
+    w mod S = S - 1 - s."""
     S = min(S_req, max(1, ng))
     gps = -(-ng // S) if ng else 0
     if gps:
         S = -(-ng // gps)
-    cuts = [min(ng, s * gps) * G for s in range(S)] + [n]
-    return S, list(zip(cuts[:-1], cuts[1:]))
+    nq = ng * G
+    ranges = []
+    for s in range(S):
+        r = [(min(ng, s * gps) * G, min(ng, (s + 1) * gps) * G)]
+        for w in range(S - 1 - s, -(-(n - nq) // 32), S):
+            r.append((nq + 32 * w, min(n, nq + 32 * (w + 1))))
+        ranges.append([x for x in r if x[1] > x[0]])
+    return S, ranges
 
 
 def test_decode_partials_per_split_match_oracle():
@@ -125,8 +132,12 @@ def test_decode_partials_per_split_match_oracle():
         for h in range(w.Hkv):
             sl = canonical_slice(exp, b, h, w.D, w.kbits, w.vbits)
             hq = slice(h * w.gqa, (h + 1) * w.gqa)
-            for s, (t0, t1) in enumerate(ranges):
-                m, l, o = oracle.attend_partial(qb[hq], sl, w.D, w.G, w.R, t0, t1)
+            for s, rs in enumerate(ranges):
+                # the oracle's partial over the split's token ranges, merged (O9)
+                parts = [oracle.attend_partial(qb[hq], sl, w.D, w.G, w.R, t0, t1) for t0, t1 in rs]
+                m = np.max([pp[0] for pp in parts], axis=0)
+                l = sum(pp[1] * np.exp(pp[0] - m) for pp in parts)
+                o = sum(pp[2] * np.exp(pp[0] - m)[:, None] for pp in parts)
                 got = P[b, hq, s]
                 # m is the kernel's lazily moved reference point: at most 0.5 below the max
                 mx = m * log2e
