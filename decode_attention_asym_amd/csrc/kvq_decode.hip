@@ -226,6 +226,19 @@ constexpr int kp_after(int ch) {
   for (int k = 1; k < NBUF; ++k) n += ((ch + k) % CPG) == 0;
   return n;
 }
+// Parameter buffers for n chunks in flight: while chunk c is processed the
+// refill brings chunk c + n, so the groups of chunks c .. c + n are live,
+// except that a group's last chunk has read its parameters before the refill.
+template <int CPG>
+constexpr int param_buffers(int n) { return CPG == 1 ? n : n / CPG + 1; }
+// Chunks in flight per wave: as many as fit, with their parameter buffers, in
+// 13 KiB of LDS (three waves per SIMD, twelve per CU, within 160 KiB).
+template <int SLOT, int PB, int CPG>
+constexpr int ring_depth() {
+  int n = 2;
+  while ((n + 1) * SLOT + param_buffers<CPG>(n + 1) * PB <= 13 * 1024) ++n;
+  return n;
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
@@ -239,8 +252,9 @@ struct PageShape {
   static constexpr int NCG = D / G, CPG = G / kChunk;
   static constexpr int KC = kChunk * D * KB / 8, VC = kChunk * D * VB / 8;
   static constexpr int VPB = (kChunk * NCG * 4 + 255) / 256 * 256, KPB = 4 * D;
-  static constexpr int OFF_KC = 0, OFF_KP = CPG * KC, OFF_VC = OFF_KP + KPB, OFF_VP = OFF_VC + CPG * VC;
+  static constexpr int OFF_KC = 0, OFF_VC = CPG * KC, OFF_KP = OFF_VC + CPG * VC, OFF_VP = OFF_KP + KPB;
   static constexpr int BYTES = OFF_VP + CPG * VPB;
+  static constexpr int PB = KPB + CPG * VPB;  // the group's parameter block [KP][VP per chunk]
 };
 
 // Running-max slack of the online softmax (base-2 units): the accumulators
@@ -446,33 +460,38 @@ void decode_kernel(DecodeArgs a) {
   const int g0 = s * static_cast<int>(a.groups_per_split);
   const int g1 = min(g0 + static_cast<int>(a.groups_per_split), static_cast<int>(a.ngroups));
 
-  // ---- LDS ring of NBUF chunk slots: [key codes][value codes][value params][key params]
-  constexpr int KC = PS::KC, VC = PS::VC, VPB = PS::VPB, KPB = PS::KPB;
-  constexpr int SLOT = KC + VC + VPB + KPB;
-  // Slots per wave: three chunks in flight when the ring stays small enough
-  // for three waves per SIMD (12 per CU within 160 KiB of LDS), else two.
-  constexpr int NBUF = 4 * SLOT <= 13 * 1024 ? 4 : 3;
-  constexpr int NBASE = dma_count<KC>() + dma_count<VC>() + dma_count<VPB>(), NKP = dma_count<KPB>();
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF * SLOT];
+  // ---- LDS: a ring of NBUF chunk slots [key codes][value codes], and NPB
+  // parameter buffers, each one group's block [key scale/zero rows][value
+  // params per chunk], copied with the group's first chunk
+  constexpr int KC = PS::KC, VC = PS::VC, VPB = PS::VPB, KPB = PS::KPB, PB = PS::PB;
+  constexpr int SLOT = KC + VC;
+  // NBUF chunks are in flight; a group's parameters stay until its last chunk
+  // has read them, and the refill that reuses a buffer comes after that read.
+  constexpr int NBUF = ring_depth<SLOT, PB, CPG>(), NPB = param_buffers<CPG>(NBUF);
+  constexpr int NBASE = dma_count<KC>() + dma_count<VC>(), NKP = dma_count<PB>();
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF * SLOT + NPB * PB];
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((KVQ_AS3 uint8_t*)ring));
+  const uint32_t pbuf_lds = ring_lds + NBUF * SLOT;
   const uint32_t lane16 = static_cast<uint32_t>(l) * 16, lane4 = static_cast<uint32_t>(l) * 4;
-  // byte offset of this lane's value parameters inside a chunk's block
-  // (layout [j][pair][group][scale, zero] dwords, see kvq_layout.h)
-  const int vp_off = KC + VC + (j * 4 + NPR * rp) * NCG * 8;
+  // byte offset of this lane's value parameters inside a chunk's part of the
+  // parameter block (layout [j][pair][group][scale, zero] dwords, see kvq_layout.h)
+  const int vp_off = KPB + (j * 4 + NPR * rp) * NCG * 8;
 
   if (g1 > g0) {
     const uint8_t* slice_pages = a.cache + page_offset(L, slice, 0);
 
     // copy position chi of group gi into the slot at LDS address sl; a group's
-    // first chunk also carries the group's key scale/zero rows
+    // first chunk also brings the group's parameter block into buffer gi % NPB
+    auto pbuf_of = [&](int gi) __attribute__((always_inline)) {
+      return pbuf_lds + static_cast<uint32_t>((gi - g0) % NPB) * PB;
+    };
     auto issue = [&](int gi, auto chi_c, uint32_t sl) __attribute__((always_inline)) {
       constexpr int chi = decltype(chi_c)::value;
       const uint8_t* page = slice_pages + static_cast<int64_t>(gi) * PS::BYTES;
       lds_reads_done();
       dma_block<KC>(page + PS::OFF_KC + chi * KC, lane16, lane4, sl);
       dma_block<VC>(page + PS::OFF_VC + chi * VC, lane16, lane4, sl + KC);
-      dma_block<VPB>(page + PS::OFF_VP + chi * VPB, lane16, lane4, sl + KC + VC);
-      if constexpr (chi == 0) dma_block<KPB>(page + PS::OFF_KP, lane16, lane4, sl + KC + VC + VPB);
+      if constexpr (chi == 0) dma_block<PB>(page + PS::OFF_KP, lane16, lane4, pbuf_of(gi));
     };
 
     uint32_t bq[NP][NKB][4];  // B operand of QK^T (fp16 pairs), per part
@@ -485,13 +504,13 @@ void decode_kernel(DecodeArgs a) {
       for (int pp = 0; pp < NPR; ++pp) bmc[pp] = (cb - m) - vmlog[pp];
     };
 
-    auto process = [&](const uint8_t* sl, bool group_start, auto&& refill) __attribute__((always_inline)) {
-      if (group_start) {
+    auto process = [&](const uint8_t* sl, const uint8_t* pbk, int ch, auto&& refill) __attribute__((always_inline)) {
+      if (ch == 0) {
         // B operand from this group's key scales: q * s / mult in two parts
         // (exact-residual fp16 products), and the bias sum_c q_c z_c by MFMA
         // (every row of the bias tile is the same sum)
-        const u32x4* ps = reinterpret_cast<const u32x4*>(sl + KC + VC + VPB) + j * NKB;
-        const u32x4* pz = reinterpret_cast<const u32x4*>(sl + KC + VC + VPB + 2 * D) + j * NKB;
+        const u32x4* ps = reinterpret_cast<const u32x4*>(pbk) + j * NKB;
+        const u32x4* pz = reinterpret_cast<const u32x4*>(pbk + 2 * D) + j * NKB;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const u32x4 sw = ps[kb];
@@ -545,11 +564,11 @@ void decode_kernel(DecodeArgs a) {
       if constexpr (VPL % 4 == 0) {
 #pragma unroll
         for (int v = 0; v < VPL / 4; ++v) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(sl + vp_off + 16 * v);
+          const u32x4 x = *reinterpret_cast<const u32x4*>(pbk + ch * VPB + vp_off + 16 * v);
           vp[4 * v] = x[0]; vp[4 * v + 1] = x[1]; vp[4 * v + 2] = x[2]; vp[4 * v + 3] = x[3];
         }
       } else {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(sl + vp_off);
+        const u32x2 x = *reinterpret_cast<const u32x2*>(pbk + ch * VPB + vp_off);
         vp[0] = x[0]; vp[1] = x[1];
       }
       // QK^T: two 16-token tiles; C = 2^-24 * (score - bias)
@@ -642,7 +661,7 @@ void decode_kernel(DecodeArgs a) {
         // plus NKP for each of them that starts a group
         wait_vmcnt<(NBUF - 1) * NBASE + kp_after<NBUF, CPG>(ch) * NKP>();
         const uint32_t sl = sl_proc;
-        process(ring + (sl - ring_lds), ch == 0, [&]() __attribute__((always_inline)) {
+        process(ring + (sl - ring_lds), ring + (pbuf_of(g) - ring_lds), ch, [&]() __attribute__((always_inline)) {
           issue(min(g + ahead / CPG, g1 - 1), std::integral_constant<int, ahead % CPG>{}, sl);
         });
         sl_proc = next_slot(sl_proc);

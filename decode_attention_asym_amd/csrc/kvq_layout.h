@@ -82,10 +82,12 @@ inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int 
   L.vc_chunk_bytes = (int64_t)kLanes * L.vw * 4;
   L.vp_chunk_bytes = align_up((int64_t)kChunk * L.ncg * 4, 256);  // whole 256-byte DMA blocks
   L.kp_bytes = (int64_t)D * 4;
+  // page: [key codes per chunk][value codes per chunk][key scale, zero rows]
+  // [value params per chunk]; the parameters are one contiguous block
   L.off_kcodes = 0;
-  L.off_kparams = L.off_kcodes + L.chunks_per_group * L.kc_chunk_bytes;
-  L.off_vcodes = L.off_kparams + L.kp_bytes;
-  L.off_vparams = L.off_vcodes + L.chunks_per_group * L.vc_chunk_bytes;
+  L.off_vcodes = L.off_kcodes + L.chunks_per_group * L.kc_chunk_bytes;
+  L.off_kparams = L.off_vcodes + L.chunks_per_group * L.vc_chunk_bytes;
+  L.off_vparams = L.off_kparams + L.kp_bytes;
   L.page_bytes = L.off_vparams + L.chunks_per_group * L.vp_chunk_bytes;
   int64_t over = (int64_t)max_tokens - R;
   L.pages = over > 0 ? over / G : 0;
