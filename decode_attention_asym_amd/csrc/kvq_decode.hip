@@ -218,6 +218,13 @@ __device__ __forceinline__ void dma_block(const uint8_t* g, uint32_t lane16, uin
 }
 template <int BYTES>
 constexpr int dma_count() { return BYTES / 1024 + (BYTES % 1024) / 256; }
+// N copy instructions of 256 bytes each (global [g + 256 k, +256) to LDS
+// [lds + 256 k, +256)): stands in for N copies whose data is not needed.
+template <int N>
+__device__ __forceinline__ void dma_filler(const uint8_t* g, uint32_t lane4, uint32_t lds) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) dma_256(g + 256 * k, lane4, lds + 256 * k);
+}
 // Number of chunks among the NBUF - 1 issued after chunk position ch (mod
 // CPG) that start a group, i.e. that also carry key parameters.
 template <int NBUF, int CPG>
@@ -485,13 +492,24 @@ void decode_kernel(DecodeArgs a) {
     auto pbuf_of = [&](int gi) __attribute__((always_inline)) {
       return pbuf_lds + static_cast<uint32_t>((gi - g0) % NPB) * PB;
     };
+    // Copies for positions past the split's end keep the per-chunk copy count
+    // fixed (the waits count copies): their code part is the same number of
+    // copy instructions, each only 256 bytes of the split's last page, into a
+    // slot nobody reads; their parameter part repeats the split's last group
+    // into that group's own buffer (identical bytes).
     auto issue = [&](int gi, auto chi_c, uint32_t sl) __attribute__((always_inline)) {
       constexpr int chi = decltype(chi_c)::value;
-      const uint8_t* page = slice_pages + static_cast<int64_t>(gi) * PS::BYTES;
+      const bool real = gi < g1;
+      const int gp = real ? gi : g1 - 1;
+      const uint8_t* page = slice_pages + static_cast<int64_t>(gp) * PS::BYTES;
       lds_reads_done();
-      dma_block<KC>(page + PS::OFF_KC + chi * KC, lane16, lane4, sl);
-      dma_block<VC>(page + PS::OFF_VC + chi * VC, lane16, lane4, sl + KC);
-      if constexpr (chi == 0) dma_block<PB>(page + PS::OFF_KP, lane16, lane4, pbuf_of(gi));
+      if (real) {
+        dma_block<KC>(page + PS::OFF_KC + chi * KC, lane16, lane4, sl);
+        dma_block<VC>(page + PS::OFF_VC + chi * VC, lane16, lane4, sl + KC);
+      } else {
+        dma_filler<dma_count<KC>() + dma_count<VC>()>(page, lane4, sl);
+      }
+      if constexpr (chi == 0) dma_block<PB>(page + PS::OFF_KP, lane16, lane4, pbuf_of(gp));
     };
 
     uint32_t bq[NP][NKB][4];  // B operand of QK^T (fp16 pairs), per part
@@ -646,12 +664,10 @@ void decode_kernel(DecodeArgs a) {
     // one is being computed.
     uint32_t sl_proc = ring_lds;
     auto next_slot = [&](uint32_t x) { return x + SLOT == ring_lds + NBUF * SLOT ? ring_lds : x + SLOT; };
-    // prologue: NBUF chunks in flight (split boundaries are group-aligned;
-    // copies past the split's end repeat its last group, so the number of
-    // copies per issue never changes)
+    // prologue: NBUF chunks in flight (split boundaries are group-aligned)
     static_for<0, NBUF>([&](auto k) {
       constexpr int K = decltype(k)::value;
-      issue(min(g0 + K / CPG, g1 - 1), std::integral_constant<int, K % CPG>{}, ring_lds + K * SLOT);
+      issue(g0 + K / CPG, std::integral_constant<int, K % CPG>{}, ring_lds + K * SLOT);
     });
     for (int g = g0; g < g1; ++g) {
       static_for<0, CPG>([&](auto chc) {
@@ -662,7 +678,7 @@ void decode_kernel(DecodeArgs a) {
         wait_vmcnt<(NBUF - 1) * NBASE + kp_after<NBUF, CPG>(ch) * NKP>();
         const uint32_t sl = sl_proc;
         process(ring + (sl - ring_lds), ring + (pbuf_of(g) - ring_lds), ch, [&]() __attribute__((always_inline)) {
-          issue(min(g + ahead / CPG, g1 - 1), std::integral_constant<int, ahead % CPG>{}, sl);
+          issue(g + ahead / CPG, std::integral_constant<int, ahead % CPG>{}, sl);
         });
         sl_proc = next_slot(sl_proc);
       });
