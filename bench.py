@@ -155,7 +155,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 32k K4/V2 layer)")
     ap.add_argument("--splits", type=int, default=0, help="split count (0: the library's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-batches", type=int, default=8)
+    ap.add_argument("--cpu-sample-batches", type=int, default=16)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="instead of the benchmark, copy GIB GiB device-to-device 3 times (a plain copy of known "
                          "size, used to scale HBM byte counters)")
