@@ -53,22 +53,34 @@ def _declare(L):
     L.orc_rotate_f64.argtypes = [P, P, i32]
     L.orc_quantize_group.restype = None
     L.orc_quantize_group.argtypes = [P, i32, i32, P, P, P, P, P]
+    L.orc_quantize_group_sym.restype = None
+    L.orc_quantize_group_sym.argtypes = [P, i32, i32, P, P, P, P]
+    L.orc_group_max_error.restype = ctypes.c_float
+    L.orc_group_max_error.argtypes = [P, P, i32, ctypes.c_uint16, ctypes.c_uint16]
+    L.orc_quantize_group_hybrid.restype = i32
+    L.orc_quantize_group_hybrid.argtypes = [P, i32, i32, P, P, P]
     L.orc_num_quantized.restype = i64
     L.orc_num_quantized.argtypes = [i64, i32, i32]
+    L.orc_num_quantized_sink.restype = i64
+    L.orc_num_quantized_sink.argtypes = [i64, i32, i32, i32]
     L.orc_encode_slice.restype = i64
     L.orc_encode_slice.argtypes = [P, P, i32, i64, i32, i32, i32, i32, i32, i32] + [P] * 8
+    L.orc_encode_slice_ext.restype = i64
+    L.orc_encode_slice_ext.argtypes = [P, P, i32, i64, i32, i32, i32, i32, i32, i32, i32, i32] + [P] * 10
     L.orc_pack_codes.restype = None
     L.orc_pack_codes.argtypes = [P, i64, i32, i32, P]
     L.orc_unpack_codes.restype = None
     L.orc_unpack_codes.argtypes = [P, i64, i32, i32, P]
     L.orc_attend_partial.restype = None
-    L.orc_attend_partial.argtypes = [P, i32, i64, i32, i32, i32] + [P] * 8 + [i64, i64, P, P, P]
+    L.orc_attend_partial.argtypes = [P, i32, i64, i64, i32, i32] + [P] * 8 + [i64, i64, P, P, P]
     L.orc_attend_slice.restype = None
-    L.orc_attend_slice.argtypes = [P, i32, i64, i32, i32, i32] + [P] * 8 + [P]
+    L.orc_attend_slice.argtypes = [P, i32, i64, i64, i32, i32] + [P] * 8 + [P]
     L.orc_merge_partials.restype = None
     L.orc_merge_partials.argtypes = [i32, i32, i32, P, P, P, P]
     L.orc_bits_per_element.restype = f64
     L.orc_bits_per_element.argtypes = [i64, i32, i32, i32, i32, f64]
+    L.orc_bits_per_element_sink.restype = f64
+    L.orc_bits_per_element_sink.argtypes = [i64, i32, i32, i32, i32, i32, f64]
     return L
 
 
@@ -144,20 +156,50 @@ def quantize_group(x, bits: int):
     return codes, np.float32(s[0]), np.float32(mn[0]), int(sc[0]), int(zr[0])
 
 
-def num_quantized(n: int, G: int, R: int) -> int:
-    return int(lib().orc_num_quantized(n, G, R))
+def quantize_group_sym(x, bits: int):
+    """Symmetric quantizer of one group: (codes, s_f32, scale16_bits, zero16_bits)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(x.size, np.uint16)
+    s = np.zeros(1, np.float32)
+    sc = np.zeros(1, np.uint16)
+    zr = np.zeros(1, np.uint16)
+    lib().orc_quantize_group_sym(_p(x), x.size, bits, _p(codes), _p(s), _p(sc), _p(zr))
+    return codes, np.float32(s[0]), int(sc[0]), int(zr[0])
 
 
-def encode_slice(k, v, dtype: str, D: int, kbits: int, vbits: int, G: int, R: int, rotate: bool):
+def group_max_error(x, codes, scale16: int, zero16: int) -> float:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.ascontiguousarray(codes, dtype=np.uint16)
+    return float(lib().orc_group_max_error(_p(x), _p(codes), x.size, scale16, zero16))
+
+
+def quantize_group_hybrid(x, bits: int):
+    """Hybrid quantizer of one group: (codes, scale16_bits, zero16_bits, symmetric_kept)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(x.size, np.uint16)
+    sc = np.zeros(1, np.uint16)
+    zr = np.zeros(1, np.uint16)
+    sym = lib().orc_quantize_group_hybrid(_p(x), x.size, bits, _p(codes), _p(sc), _p(zr))
+    return codes, int(sc[0]), int(zr[0]), bool(sym)
+
+
+def num_quantized(n: int, G: int, R: int, sink: int = 0) -> int:
+    return int(lib().orc_num_quantized_sink(n, G, R, sink))
+
+
+def encode_slice(k, v, dtype: str, D: int, kbits: int, vbits: int, G: int, R: int, rotate: bool,
+                 sink: int = 0, hybrid: bool = False):
     """Encode one (batch, kv-head) slice.  k, v: [n][D] in the input dtype
     (float32 values for "f32", uint16 bit patterns for "f16"/"bf16").
 
-    Returns a dict of canonical arrays (codes unpacked, one per uint16)."""
+    Returns a dict of canonical arrays (codes unpacked, one per uint16); the
+    fp16 tokens (an attention-sink window of `sink` tokens, then the recent
+    window) are k_resid / v_resid; k_sym / v_sym mark symmetric groups."""
     np_dt = np.float32 if dtype == "f32" else np.uint16
     k = np.ascontiguousarray(k, dtype=np_dt).reshape(-1, D)
     v = np.ascontiguousarray(v, dtype=np_dt).reshape(-1, D)
     n = k.shape[0]
-    nq = num_quantized(n, G, R)
+    nq = num_quantized(n, G, R, sink)
     nr = n - nq
     out = {
         "k_codes": np.zeros((nq, D), np.uint16),
@@ -168,10 +210,13 @@ def encode_slice(k, v, dtype: str, D: int, kbits: int, vbits: int, G: int, R: in
         "v_zero": np.zeros((nq, D // G), np.uint16),
         "k_resid": np.zeros((nr, D), np.uint16),
         "v_resid": np.zeros((nr, D), np.uint16),
+        "k_sym": np.zeros((nq // G, D), np.uint8),
+        "v_sym": np.zeros((nq, D // G), np.uint8),
     }
-    r = lib().orc_encode_slice(
-        _p(k), _p(v), DTYPE_CODE[dtype], n, D, kbits, vbits, G, R, int(bool(rotate)),
-        *(_p(out[key]) for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")),
+    r = lib().orc_encode_slice_ext(
+        _p(k), _p(v), DTYPE_CODE[dtype], n, D, kbits, vbits, G, R, int(bool(rotate)), int(sink), int(bool(hybrid)),
+        *(_p(out[key]) for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid",
+                                   "k_sym", "v_sym")),
     )
     if r < 0:
         raise ValueError("orc_encode_slice rejected its arguments")
@@ -205,25 +250,28 @@ def _cache_ptrs(cache):
     return arrs, [_p(a) for a in arrs]
 
 
-def attend_slice(q, cache, D: int, G: int, R: int) -> np.ndarray:
-    """fp64 attention of q[nh][D] (fp64, rotated already if keys were) over a canonical slice."""
+def attend_slice(q, cache, D: int, G: int, R: int | None = None) -> np.ndarray:
+    """fp64 attention of q[nh][D] (fp64, rotated already if keys were) over a
+    canonical slice (its quantized token count is cache["nq"]; R is implied)."""
     q = np.ascontiguousarray(q, dtype=np.float64).reshape(-1, D)
     nh = q.shape[0]
     out = np.zeros((nh, D), np.float64)
     keep, ptrs = _cache_ptrs(cache)
-    lib().orc_attend_slice(_p(q), nh, int(cache["n"]), D, G, R, *ptrs, _p(out))
+    lib().orc_attend_slice(_p(q), nh, int(cache["n"]), int(cache["nq"]), D, G, *ptrs, _p(out))
     del keep
     return out
 
 
-def attend_partial(q, cache, D: int, G: int, R: int, t0: int, t1: int):
+def attend_partial(q, cache, D: int, G: int, R: int | None, t0: int, t1: int):
+    """Partial statistics over canonical token indices [t0, t1): the quantized
+    tokens first (cache["nq"] of them), then the fp16 tokens."""
     q = np.ascontiguousarray(q, dtype=np.float64).reshape(-1, D)
     nh = q.shape[0]
     m = np.zeros(nh, np.float64)
     l = np.zeros(nh, np.float64)
     o = np.zeros((nh, D), np.float64)
     keep, ptrs = _cache_ptrs(cache)
-    lib().orc_attend_partial(_p(q), nh, int(cache["n"]), D, G, R, *ptrs, t0, t1, _p(m), _p(l), _p(o))
+    lib().orc_attend_partial(_p(q), nh, int(cache["n"]), int(cache["nq"]), D, G, *ptrs, t0, t1, _p(m), _p(l), _p(o))
     del keep
     return m, l, o
 
@@ -246,8 +294,9 @@ def attend_slices_parallel(jobs, threads: int):
 
 
 # ---------------------------------------------------------------- accounting
-def bits_per_element(n: int, kbits: int, vbits: int, G: int, R: int, overhead_bits: float = 32.0) -> float:
-    return float(lib().orc_bits_per_element(n, kbits, vbits, G, R, overhead_bits))
+def bits_per_element(n: int, kbits: int, vbits: int, G: int, R: int, overhead_bits: float = 32.0,
+                     sink: int = 0) -> float:
+    return float(lib().orc_bits_per_element_sink(n, kbits, vbits, G, R, sink, overhead_bits))
 
 
 def kv_cache_bytes(layers: int, hidden: int, tokens: int, bits_per_elem: float) -> float:

@@ -25,6 +25,17 @@
  *    (stage 1, canalized rotation Y = X H).
  *  - Attention is softmax(q K^T / sqrt(d)) V: "Asymmetric Key-Value
  *    Quantization ...", section 1, evaluated in fp64 on the decoded cache.
+ *  - Attention-sink window: the first S0 tokens stay in fp16 next to the
+ *    window of recent tokens ("[Framework] ...", section IV, on the initial
+ *    attention-sink tokens; the high-precision windows for recent and sink
+ *    tokens of the InnerQ abstract on the page "WUSH-KV: KV Cache
+ *    Quantization with Data-Adaptive Transforms").  Quantized groups start
+ *    at token S0.
+ *  - Hybrid quantization: per group, a symmetric or the asymmetric quantizer,
+ *    chosen from the group's own values (InnerQ abstract, same page).  The
+ *    page names no symmetric formula and no selection rule; here symmetric is
+ *    x = s (code - c0), c0 = 2^(b-1) - 1, s = max|x| / c0, and the quantizer
+ *    with the smaller largest reconstruction error on the group is kept.
  *  - Bits-per-element accounting: "Asymmetric Key-Value Quantization ...",
  *    section 3.1 (average of key and value bit widths) and section 3.4
  *    (combined compression table); here the per-group fp16 scale and zero
@@ -41,6 +52,14 @@
 #define ORC_F32 0
 #define ORC_F16 1
 #define ORC_BF16 2
+
+int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n, int D,
+                             int kbits, int vbits, int G, int R, int rotate, int S0, int hybrid,
+                             uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
+                             uint16_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
+                             uint16_t* k_resid, uint16_t* v_resid, uint8_t* k_sym, uint8_t* v_sym);
+double orc_bits_per_element_sink(int64_t n, int kbits, int vbits, int G, int R, int S0,
+                                 double overhead_bits);
 
 /* ------------------------------------------------------------------------ */
 /* IEEE 754 binary16 and bfloat16 conversions, written from the formats.     */
@@ -177,6 +196,73 @@ void orc_quantize_group(const float* x, int count, int bits, uint16_t* codes,
   *zero16 = orc_f32_to_f16(mn);
 }
 
+/* Symmetric uniform quantizer for one group (same inputs as above), levels
+ * c0 = 2^(bits-1) - 1 on either side of zero:
+ *   M  = max |x| (+ 0.0f), s = M / c0, IEEE binary32 division
+ *   code = clamp(rne(x / s), -c0, c0) + c0, or c0 for every x if s == 0
+ *   scale16 = fp16_rne(s), zero16 = fp16_rne(-(scale16 * c0))
+ * so that zero16 + code * scale16 reconstructs s16 * (code - c0) up to the
+ * rounding of zero16. */
+void orc_quantize_group_sym(const float* x, int count, int bits, uint16_t* codes, float* s_out,
+                            uint16_t* scale16, uint16_t* zero16) {
+  float M = 0.0f;
+  for (int i = 0; i < count; ++i) {
+    float a = fabsf(x[i]);
+    if (a > M) M = a;
+  }
+  M = M + 0.0f;
+  float c0 = (float)((1u << (bits - 1)) - 1u);
+  float s = M / c0;
+  for (int i = 0; i < count; ++i) {
+    if (s == 0.0f) { codes[i] = (uint16_t)c0; continue; }
+    float q = rintf(x[i] / s);
+    if (q < -c0) q = -c0;
+    if (q > c0) q = c0;
+    codes[i] = (uint16_t)(q + c0);
+  }
+  if (s_out) *s_out = s;
+  *scale16 = orc_f32_to_f16(s);
+  *zero16 = orc_f32_to_f16(-(orc_f16_to_f32(*scale16) * c0));
+}
+
+/* Largest reconstruction error of a group in binary32: for each x,
+ * xhat = fp32(code * scale16) + zero16 (the product is exact, the sum is
+ * rounded), e = |x - xhat| (rounded); the maximum is exact. */
+float orc_group_max_error(const float* x, const uint16_t* codes, int count, uint16_t scale16,
+                          uint16_t zero16) {
+  float s = orc_f16_to_f32(scale16), z = orc_f16_to_f32(zero16), E = 0.0f;
+  for (int i = 0; i < count; ++i) {
+    float xh = (float)codes[i] * s;
+    xh = xh + z;
+    float e = fabsf(x[i] - xh);
+    if (e > E) E = e;
+  }
+  return E;
+}
+
+/* Hybrid: both quantizers, keep the symmetric one only if its largest error
+ * is strictly smaller.  Returns 1 if the symmetric quantizer was kept. */
+int orc_quantize_group_hybrid(const float* x, int count, int bits, uint16_t* codes,
+                              uint16_t* scale16, uint16_t* zero16) {
+  uint16_t* cs = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)count);
+  uint16_t sa, za, ss, zs;
+  orc_quantize_group(x, count, bits, codes, NULL, NULL, &sa, &za);
+  orc_quantize_group_sym(x, count, bits, cs, NULL, &ss, &zs);
+  float ea = orc_group_max_error(x, codes, count, sa, za);
+  float es = orc_group_max_error(x, cs, count, ss, zs);
+  int sym = es < ea;
+  if (sym) {
+    memcpy(codes, cs, sizeof(uint16_t) * (size_t)count);
+    *scale16 = ss;
+    *zero16 = zs;
+  } else {
+    *scale16 = sa;
+    *zero16 = za;
+  }
+  free(cs);
+  return sym;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Window bookkeeping.                                                       */
 /* ------------------------------------------------------------------------ */
@@ -187,6 +273,13 @@ int64_t orc_num_quantized(int64_t n, int G, int R) {
   int64_t over = n - R;
   if (over <= 0) return 0;
   return (over / G) * G;
+}
+
+/* With an attention-sink window of S0 tokens: tokens [0, min(n, S0)) stay in
+ * fp16, groups of G are aligned to token S0, and at least R of the most
+ * recent tokens after the sink stay in fp16. */
+int64_t orc_num_quantized_sink(int64_t n, int G, int R, int S0) {
+  return n > S0 ? orc_num_quantized(n - S0, G, R) : 0;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -206,10 +299,28 @@ int64_t orc_encode_slice(const void* k, const void* v, int dtype, int64_t n, int
                          uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
                          uint16_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
                          uint16_t* k_resid, uint16_t* v_resid) {
-  if (n < 0 || D <= 0 || G <= 0 || R < 0 || D % G != 0) return -1;
+  return orc_encode_slice_ext(k, v, dtype, n, D, kbits, vbits, G, R, rotate, 0, 0, k_codes, k_scale,
+                              k_zero, v_codes, v_scale, v_zero, k_resid, v_resid, NULL, NULL);
+}
+
+/* As orc_encode_slice, with an attention-sink window of S0 tokens (0: none)
+ * and, if `hybrid`, the per-group symmetric/asymmetric choice.  The
+ * quantized tokens are [s, s + nq) with s = min(n, S0) and
+ * nq = orc_num_quantized_sink(n, G, R, S0); k_resid / v_resid hold the other
+ * n - nq tokens in position order (the sink, then the recent window).
+ * k_sym [nq/G][D] and v_sym [nq][D/G] (may be NULL) receive 1 where a group
+ * took the symmetric quantizer. */
+int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n, int D,
+                             int kbits, int vbits, int G, int R, int rotate, int S0, int hybrid,
+                             uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
+                             uint16_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
+                             uint16_t* k_resid, uint16_t* v_resid, uint8_t* k_sym, uint8_t* v_sym) {
+  if (n < 0 || D <= 0 || G <= 0 || R < 0 || D % G != 0 || S0 < 0) return -1;
   if (kbits < 1 || kbits > 16 || vbits < 1 || vbits > 16) return -1;
+  if (hybrid && (kbits < 2 || vbits < 2)) return -1;
   if (rotate && (D & (D - 1)) != 0) return -1;
-  int64_t nq = orc_num_quantized(n, G, R);
+  int64_t nq = orc_num_quantized_sink(n, G, R, S0);
+  int64_t s0 = n < S0 ? n : S0;
   float* kt = (float*)malloc(sizeof(float) * (size_t)n * (size_t)D + 1);
   float* vt = (float*)malloc(sizeof(float) * (size_t)n * (size_t)D + 1);
   float* row = (float*)malloc(sizeof(float) * (size_t)D);
@@ -226,11 +337,17 @@ int64_t orc_encode_slice(const void* k, const void* v, int dtype, int64_t n, int
       vt[t * D + c] = orc_f16_to_f32(orc_f32_to_f16(load_in(v, dtype, (size_t)t * D + c)));
   }
 
-  /* keys: per channel, groups of G consecutive tokens */
+  /* keys: per channel, groups of G consecutive tokens (token s0 + q for
+   * quantized index q) */
   for (int64_t g = 0; g < nq / G; ++g)
     for (int c = 0; c < D; ++c) {
-      for (int i = 0; i < G; ++i) grp[i] = kt[(g * G + i) * D + c];
-      orc_quantize_group(grp, G, kbits, cod, NULL, NULL, &k_scale[g * D + c], &k_zero[g * D + c]);
+      for (int i = 0; i < G; ++i) grp[i] = kt[(s0 + g * G + i) * D + c];
+      int sym = 0;
+      if (hybrid)
+        sym = orc_quantize_group_hybrid(grp, G, kbits, cod, &k_scale[g * D + c], &k_zero[g * D + c]);
+      else
+        orc_quantize_group(grp, G, kbits, cod, NULL, NULL, &k_scale[g * D + c], &k_zero[g * D + c]);
+      if (k_sym) k_sym[g * D + c] = (uint8_t)sym;
       for (int i = 0; i < G; ++i) k_codes[(g * G + i) * D + c] = cod[i];
     }
 
@@ -238,17 +355,26 @@ int64_t orc_encode_slice(const void* k, const void* v, int dtype, int64_t n, int
   int ng = D / G;
   for (int64_t t = 0; t < nq; ++t)
     for (int j = 0; j < ng; ++j) {
-      for (int i = 0; i < G; ++i) grp[i] = vt[t * D + j * G + i];
-      orc_quantize_group(grp, G, vbits, cod, NULL, NULL, &v_scale[t * ng + j], &v_zero[t * ng + j]);
+      for (int i = 0; i < G; ++i) grp[i] = vt[(s0 + t) * D + j * G + i];
+      int sym = 0;
+      if (hybrid)
+        sym = orc_quantize_group_hybrid(grp, G, vbits, cod, &v_scale[t * ng + j], &v_zero[t * ng + j]);
+      else
+        orc_quantize_group(grp, G, vbits, cod, NULL, NULL, &v_scale[t * ng + j], &v_zero[t * ng + j]);
+      if (v_sym) v_sym[t * ng + j] = (uint8_t)sym;
       for (int i = 0; i < G; ++i) v_codes[t * D + j * G + i] = cod[i];
     }
 
-  /* fp16 window */
-  for (int64_t t = nq; t < n; ++t)
+  /* fp16 tokens in position order: the sink [0, s0), then the window */
+  int64_t r = 0;
+  for (int64_t t = 0; t < n; ++t) {
+    if (t >= s0 && t < s0 + nq) continue;
     for (int c = 0; c < D; ++c) {
-      k_resid[(t - nq) * D + c] = orc_f32_to_f16(kt[t * D + c]);
-      v_resid[(t - nq) * D + c] = orc_f32_to_f16(vt[t * D + c]);
+      k_resid[r * D + c] = orc_f32_to_f16(kt[t * D + c]);
+      v_resid[r * D + c] = orc_f32_to_f16(vt[t * D + c]);
     }
+    ++r;
+  }
 
   free(kt); free(vt); free(row); free(grp); free(cod);
   return nq;
@@ -317,18 +443,19 @@ static double value_at(int64_t t, int c, int64_t nq, int D, int G,
   return (double)orc_f16_to_f32(v_resid[(t - nq) * D + c]);
 }
 
-/* Unnormalized attention statistics over tokens [t0, t1) for nh query heads
- * q[nh][D] (fp64, already rotated if the keys were):
+/* Unnormalized attention statistics over tokens [t0, t1) of the canonical
+ * order (the nq quantized tokens, then the n - nq fp16 tokens) for nh query
+ * heads q[nh][D] (fp64, already rotated if the keys were):
  *   sigma_t = (sum_c q_c khat_tc) / sqrt(D)
  *   m = max sigma_t (-inf on an empty range), w_t = exp(sigma_t - m)
  *   l = sum w_t, o_c = sum w_t vhat_tc            (sums in token order)
  * m[nh], l[nh], o[nh][D]. */
-void orc_attend_partial(const double* q, int nh, int64_t n, int D, int G, int R,
+void orc_attend_partial(const double* q, int nh, int64_t n, int64_t nq, int D, int G,
                         const uint16_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
                         const uint16_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
                         const uint16_t* k_resid, const uint16_t* v_resid,
                         int64_t t0, int64_t t1, double* m, double* l, double* o) {
-  int64_t nq = orc_num_quantized(n, G, R);
+  (void)n;
   double inv_sqrt_d = 1.0 / sqrt((double)D);
   int64_t cnt = t1 > t0 ? t1 - t0 : 0;
   double* sig = (double*)malloc(sizeof(double) * (size_t)(cnt + 1));
@@ -359,13 +486,13 @@ void orc_attend_partial(const double* q, int nh, int64_t n, int D, int G, int R,
 }
 
 /* Full attention over all n tokens: out[nh][D] = o / l. */
-void orc_attend_slice(const double* q, int nh, int64_t n, int D, int G, int R,
+void orc_attend_slice(const double* q, int nh, int64_t n, int64_t nq, int D, int G,
                       const uint16_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
                       const uint16_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
                       const uint16_t* k_resid, const uint16_t* v_resid, double* out) {
   double* m = (double*)malloc(sizeof(double) * (size_t)nh);
   double* l = (double*)malloc(sizeof(double) * (size_t)nh);
-  orc_attend_partial(q, nh, n, D, G, R, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero,
+  orc_attend_partial(q, nh, n, nq, D, G, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero,
                      k_resid, v_resid, 0, n, m, l, out);
   for (int h = 0; h < nh; ++h)
     for (int c = 0; c < D; ++c) out[(size_t)h * D + c] /= l[h];
@@ -402,8 +529,14 @@ void orc_merge_partials(int S, int nh, int D, const double* m, const double* l, 
 /*   bpe = [nq (bk + ovh/G) + nq (bv + ovh/G) + 2*16*nr] / (2n)              */
 /* ------------------------------------------------------------------------ */
 double orc_bits_per_element(int64_t n, int kbits, int vbits, int G, int R, double overhead_bits) {
+  return orc_bits_per_element_sink(n, kbits, vbits, G, R, 0, overhead_bits);
+}
+
+/* The same with an fp16 attention-sink window of S0 tokens. */
+double orc_bits_per_element_sink(int64_t n, int kbits, int vbits, int G, int R, int S0,
+                                 double overhead_bits) {
   if (n <= 0) return 0.0;
-  int64_t nq = orc_num_quantized(n, G, R);
+  int64_t nq = orc_num_quantized_sink(n, G, R, S0);
   int64_t nr = n - nq;
   double q = (double)nq * (kbits + overhead_bits / G) + (double)nq * (vbits + overhead_bits / G);
   return (q + 2.0 * 16.0 * (double)nr) / (2.0 * (double)n);

@@ -427,3 +427,144 @@ def test_window_default_from_pages():
     from synth import WORKLOADS
 
     assert WORKLOADS[0].R == g["window_tokens"] and WORKLOADS[0].kbits == g["bits"] == WORKLOADS[0].vbits
+
+
+# ------------------------------------------------- hybrid quantizer, sink window
+def _fp16_vals(x):
+    return np.asarray(x, np.float32).astype(np.float16).astype(np.float32)
+
+
+def _max_err_f64(orc, x, codes, sc, zr):
+    s = float(orc.f16_bits_to_f32(np.array([sc], np.uint16))[0])
+    z = float(orc.f16_bits_to_f32(np.array([zr], np.uint16))[0])
+    return float(np.max(np.abs(np.asarray(x, np.float64) - (z + codes.astype(np.float64) * s))))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_symmetric_quantizer_reproduces_its_grid(orc, bits):
+    """Values on the grid s * k, |k| <= c0 (with 0 and both ends present), come
+    back exactly from the symmetric quantizer, codes k + c0; the asymmetric
+    quantizer cannot (2^b levels over 2 c0 + 1 grid points), so the hybrid
+    keeps the symmetric one."""
+    c0 = 2 ** (bits - 1) - 1
+    rng = np.random.default_rng(bits)
+    ks = np.concatenate([[-c0, 0, c0], rng.integers(-c0, c0 + 1, 29)])
+    x = _fp16_vals(0.5 * ks)
+    codes, s, sc, zr = orc.quantize_group_sym(x, bits)
+    assert s == np.float32(0.5 * c0 / c0)
+    assert np.array_equal(codes, (ks + c0).astype(np.uint16))
+    assert orc.f16_bits_to_f32(np.array([zr], np.uint16))[0] == np.float32(-0.5 * c0)
+    assert orc.group_max_error(x, codes, sc, zr) == 0.0
+    ca, _, _, sa, za = orc.quantize_group(x, bits)
+    assert orc.group_max_error(x, ca, sa, za) > 0.0
+    hc, hs, hz, sym = orc.quantize_group_hybrid(x, bits)
+    assert sym and np.array_equal(hc, codes) and (hs, hz) == (sc, zr)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_hybrid_keeps_asymmetric_for_one_sided_data(orc, bits):
+    """Data in [10, 11]: the asymmetric error is at most half a step of 1/(2^b-1)
+    (plus fp16 rounding of the scale), the symmetric one about 10 / c0 or more."""
+    rng = np.random.default_rng(7 + bits)
+    x = _fp16_vals(10.0 + rng.random(64))
+    ca, _, _, sa, za = orc.quantize_group(x, bits)
+    hc, hs, hz, sym = orc.quantize_group_hybrid(x, bits)
+    assert not sym
+    assert np.array_equal(hc, ca) and (hs, hz) == (sa, za)
+    assert _max_err_f64(orc, x, hc, hs, hz) <= 0.5 / (2 ** bits - 1) + 0.01
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_hybrid_never_worse_and_well_formed(orc, bits):
+    """On groups drawn from several shapes (centred, skewed, sparse, constant,
+    with signed zeros) the kept quantizer's largest error, evaluated
+    independently in fp64 from the stored fp16 parameters, is never above the
+    asymmetric one's (up to fp32 rounding of the error itself), and a kept
+    symmetric group has zero = fp16(-c0 * scale) and codes in [0, 2 c0]."""
+    c0 = 2 ** (bits - 1) - 1
+    rng = np.random.default_rng(100 + bits)
+    shapes = [
+        lambda: rng.standard_normal(32),
+        lambda: rng.standard_normal(32) + 3.0,
+        lambda: np.where(rng.random(32) < 0.8, 0.0, rng.standard_normal(32) * 5),
+        lambda: np.full(32, rng.standard_normal()),
+        lambda: np.concatenate([[-0.0, 0.0], rng.laplace(size=30)]),
+        lambda: rng.uniform(-1, 1, 32) ** 3,
+    ]
+    n_sym = 0
+    for it in range(600):
+        x = _fp16_vals(shapes[it % len(shapes)]())
+        ca, _, _, sa, za = orc.quantize_group(x, bits)
+        hc, hs, hz, sym = orc.quantize_group_hybrid(x, bits)
+        ea = _max_err_f64(orc, x, ca, sa, za)
+        eh = _max_err_f64(orc, x, hc, hs, hz)
+        assert eh <= ea + 1e-6 * max(1.0, float(np.max(np.abs(x))))
+        if sym:
+            n_sym += 1
+            s = orc.f16_bits_to_f32(np.array([hs], np.uint16))[0]
+            assert hz == int(orc.f32_to_f16_bits(np.array([-(s * np.float32(c0))], np.float32))[0])
+            assert hc.max() <= 2 * c0
+        else:
+            assert np.array_equal(hc, ca) and (hs, hz) == (sa, za)
+    assert 0 < n_sym < 600  # both quantizers occur
+
+
+def test_hybrid_constant_and_zero_groups_stay_asymmetric(orc):
+    for x in (np.zeros(32, np.float32), np.full(32, 1.5, np.float32), np.full(32, -3.25, np.float32)):
+        ca, s, mn, sa, za = orc.quantize_group(x, 2)
+        assert s == 0.0 and not ca.any()
+        hc, hs, hz, sym = orc.quantize_group_hybrid(x, 2)
+        assert not sym and (hs, hz) == (sa, za) and not hc.any()
+
+
+@pytest.mark.parametrize("G,R,S0", [(32, 64, 64), (64, 128, 64), (32, 0, 32), (32, 32, 128)])
+def test_sink_window_bookkeeping(orc, G, R, S0):
+    """Tokens [0, min(n, S0)) stay fp16, then whole groups aligned to S0 with
+    at least R recent tokens left in fp16."""
+    for n in range(0, S0 + R + 3 * G + 5):
+        expect = 0 if n <= S0 else max(0, (n - S0 - R) // G) * G
+        assert orc.num_quantized(n, G, R, S0) == expect
+
+
+def test_sink_encoding_is_the_tail_encoding_plus_fp16_prefix(orc):
+    """With a sink of S0 tokens the quantized groups are exactly those of the
+    sequence without its first S0 tokens, and the fp16 tokens are the first
+    S0 tokens (fp16 of the input) followed by that sequence's window."""
+    rng = np.random.default_rng(31)
+    D, G, R, S0, n = 64, 32, 32, 64, 64 + 5 * 32 + 17
+    k = rng.standard_normal((n, D)).astype(np.float32) * 3
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    for hybrid in (False, True):
+        a = orc.encode_slice(k, v, "f32", D, 4, 2, G, R, False, sink=S0, hybrid=hybrid)
+        b = orc.encode_slice(k[S0:], v[S0:], "f32", D, 4, 2, G, R, False, hybrid=hybrid)
+        assert a["nq"] == b["nq"] == 4 * 32
+        for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_sym", "v_sym"):
+            assert np.array_equal(a[key], b[key]), key
+        assert np.array_equal(a["k_resid"][:S0], orc.f32_to_f16_bits(k[:S0]))
+        assert np.array_equal(a["v_resid"][:S0], orc.f32_to_f16_bits(v[:S0]))
+        assert np.array_equal(a["k_resid"][S0:], b["k_resid"]) and np.array_equal(a["v_resid"][S0:], b["v_resid"])
+
+
+def test_sink_attention_without_quantized_tokens_is_exact_softmax(orc):
+    """n <= S0 + R + G - 1: nothing is quantized, so attention is exact softmax
+    attention over the fp16-rounded inputs (computed here with numpy)."""
+    rng = np.random.default_rng(5)
+    D, G, R, S0, n = 64, 32, 32, 64, 64 + 32 + 31
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    c = orc.encode_slice(k, v, "f32", D, 2, 2, G, R, False, sink=S0)
+    assert c["nq"] == 0
+    q = rng.standard_normal((2, D))
+    kh = k.astype(np.float16).astype(np.float64)
+    vh = v.astype(np.float16).astype(np.float64)
+    sc = q @ kh.T / np.sqrt(D)
+    w = np.exp(sc - sc.max(1, keepdims=True))
+    ref = w @ vh / w.sum(1, keepdims=True)
+    assert np.max(np.abs(orc.attend_slice(q, c, D, G, R) - ref)) < 1e-12
+
+
+def test_bits_per_element_with_sink_closed_form(orc):
+    # n = 8192, G = 32, R = 128, S0 = 64, K2/V2: nq = 32 * floor(8000 / 32) = 8000
+    # fp16 tokens 192; bpe = (8000 * (2 + 1) * 2 + 32 * 192) / (2 * 8192)
+    assert orc.num_quantized(8192, 32, 128, 64) == 8000
+    assert orc.bits_per_element(8192, 2, 2, 32, 128, sink=64) == pytest.approx((48000 + 6144) / 16384, abs=1e-12)
