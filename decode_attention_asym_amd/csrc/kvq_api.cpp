@@ -66,6 +66,9 @@ kvq_status validate(const kvq_config* c) {
   if (c->residual < 0 || c->residual > 1024 || c->residual % 32 != 0)
     return fail(KVQ_E_UNSUPPORTED, "residual %d must be a multiple of 32 in [0, 1024]", c->residual);
   if (c->rotate != 0 && c->rotate != 1) return fail(KVQ_E_ARG, "rotate must be 0 or 1");
+  if (c->sink_tokens < 0 || c->sink_tokens > 1024 || c->sink_tokens % c->group_size != 0)
+    return fail(KVQ_E_UNSUPPORTED, "sink_tokens %d must be a multiple of group_size in [0, 1024]", c->sink_tokens);
+  if (c->hybrid != 0 && c->hybrid != 1) return fail(KVQ_E_ARG, "hybrid must be 0 or 1");
   if (c->in_dtype < KVQ_F32 || c->in_dtype > KVQ_BF16) return fail(KVQ_E_ARG, "in_dtype %d unknown", c->in_dtype);
   if (!kvq::decode_supported(c->head_dim, c->k_bits, c->v_bits, c->group_size))
     return fail(KVQ_E_UNSUPPORTED, "no kernel for this (head_dim, bits, group) combination");
@@ -74,7 +77,7 @@ kvq_status validate(const kvq_config* c) {
 
 Layout layout_of(const kvq_config* c) {
   return kvq::make_layout(c->batch, c->num_kv_heads, c->head_dim, c->max_tokens, c->k_bits, c->v_bits, c->group_size,
-                          c->residual);
+                          c->residual, c->sink_tokens);
 }
 
 int max_splits(const kvq_config* c) {
@@ -96,7 +99,10 @@ kvq_status device_error(kvq_cache* h, hipError_t e, const char* what) {
   return fail(KVQ_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-int64_t ngroups_of(const kvq_cache* h) { return kvq::num_quantized(h->n, h->cfg.group_size, h->cfg.residual) / h->cfg.group_size; }
+int64_t nquant_of(const kvq_cache* h, int64_t n) {
+  return kvq::num_quantized(n, h->cfg.group_size, h->cfg.residual, h->cfg.sink_tokens);
+}
+int64_t ngroups_of(const kvq_cache* h) { return nquant_of(h, h->n) / h->cfg.group_size; }
 
 int choose_splits(kvq_cache* h) {
   if (h->cu_count <= 0) {
@@ -166,7 +172,7 @@ kvq_status kvq_reset(kvq_cache* h) {
 int64_t kvq_num_tokens(const kvq_cache* h) { return h ? h->n : -1; }
 
 int64_t kvq_num_quantized(const kvq_cache* h) {
-  return h ? kvq::num_quantized(h->n, h->cfg.group_size, h->cfg.residual) : -1;
+  return h ? nquant_of(h, h->n) : -1;
 }
 
 kvq_status kvq_append(kvq_cache* h, const void* k, const void* v, int32_t n_tokens, void* stream) {
@@ -179,8 +185,8 @@ kvq_status kvq_append(kvq_cache* h, const void* k, const void* v, int32_t n_toke
   if (n_new > h->cfg.max_tokens)
     return fail(KVQ_E_CAPACITY, "append of %d tokens to %lld exceeds max_tokens %d", n_tokens, (long long)h->n,
                 h->cfg.max_tokens);
-  const int G = h->cfg.group_size, R = h->cfg.residual;
-  const int64_t nq_old = kvq::num_quantized(h->n, G, R), nq_new = kvq::num_quantized(n_new, G, R);
+  const int G = h->cfg.group_size, S0 = h->cfg.sink_tokens;
+  const int64_t nq_old = nquant_of(h, h->n), nq_new = nquant_of(h, n_new);
   kvq::AppendArgs a{};
   a.cache = h->buf;
   a.L = h->L;
@@ -188,13 +194,18 @@ kvq_status kvq_append(kvq_cache* h, const void* k, const void* v, int32_t n_toke
   a.v = v;
   a.in_dtype = h->cfg.in_dtype;
   a.rotate = h->cfg.rotate;
+  a.hybrid = h->cfg.hybrid;
   a.Hkv = h->cfg.num_kv_heads;
   a.T = n_tokens;
   a.n_old = h->n;
   a.g_first = nq_old / G;
   a.n_flush = (nq_new - nq_old) / G;
-  a.w_first = std::max(h->n, nq_new);
-  a.n_write = n_new - a.w_first;
+  // new tokens that stay fp16: the part of the sink [0, S0) they reach, and
+  // the window [S0 + nq_new, n_new)
+  a.s_first = h->n;
+  a.n_sink_write = std::max<int64_t>(0, std::min<int64_t>(n_new, S0) - h->n);
+  a.w_first = std::max<int64_t>(h->n, S0 + nq_new);
+  a.n_write = std::max<int64_t>(0, n_new - a.w_first);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // flush before the window write: the write may reuse ring slots the flush reads
   hipError_t e = kvq::launch_flush(a, s);
@@ -249,8 +260,9 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
   a.ngroups = ng;
   a.splits = static_cast<int>(S);
   a.groups_per_split = gps;
-  a.rc0 = kvq::num_quantized(h->n, c.group_size, c.residual) / kvq::kChunk;
-  a.rc1 = (h->n + kvq::kChunk - 1) / kvq::kChunk;
+  a.rc0 = (c.sink_tokens + nquant_of(h, h->n)) / kvq::kChunk;
+  a.rc1 = std::max(a.rc0, (h->n + kvq::kChunk - 1) / kvq::kChunk);
+  a.nsc = (std::min<int64_t>(h->n, c.sink_tokens) + kvq::kChunk - 1) / kvq::kChunk;
   a.partial = partials;
   a.out = out;
   a.write_final = final ? 1 : 0;
@@ -310,10 +322,12 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
   if (e != hipSuccess) return device_error(h, e, "stream synchronize");
   const Layout& L = h->L;
   const int D = c.head_dim, G = c.group_size, kb = c.k_bits, vb = c.v_bits, ncg = D / G;
-  const int64_t nq = kvq::num_quantized(h->n, G, c.residual), nr = h->n - nq, ng = nq / G;
+  const int64_t nq = nquant_of(h, h->n), nr = h->n - nq, ng = nq / G;
+  const int64_t ns = std::min<int64_t>(h->n, c.sink_tokens);  // fp16 index r < ns: sink token r
   const int64_t krow = D * kb / 8, vrow = D * vb / 8;
   std::vector<uint8_t> pages(static_cast<size_t>(ng * L.page_bytes));
   std::vector<uint8_t> ring(static_cast<size_t>(L.ring_chunks * L.ring_chunk_bytes));
+  std::vector<uint8_t> sink(static_cast<size_t>(L.sink_chunks * L.ring_chunk_bytes));
   for (int64_t bi = 0; bi < bc; ++bi)
     for (int64_t hk = 0; hk < c.num_kv_heads; ++hk) {
       const int64_t slice = (b0 + bi) * c.num_kv_heads + hk;
@@ -325,6 +339,11 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
       e = hipMemcpy(ring.data(), h->buf + L.ring_offset + slice * L.ring_chunks * L.ring_chunk_bytes, ring.size(),
                     hipMemcpyDeviceToHost);
       if (e != hipSuccess) return device_error(h, e, "export copy");
+      if (!sink.empty()) {
+        e = hipMemcpy(sink.data(), h->buf + L.sink_offset + slice * L.sink_chunks * L.ring_chunk_bytes, sink.size(),
+                      hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return device_error(h, e, "export copy");
+      }
       for (int64_t t = 0; t < nq; ++t) {
         const uint8_t* page = pages.data() + (t / G) * L.page_bytes;
         const int ch = static_cast<int>((t % G) / kvq::kChunk), tt = static_cast<int>(t % kvq::kChunk);
@@ -367,8 +386,10 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
         }
       }
       for (int64_t t = 0; t < nr; ++t) {
-        const int64_t pos = nq + t;
-        const uint8_t* rc = ring.data() + ((pos / kvq::kChunk) % L.ring_chunks) * L.ring_chunk_bytes;
+        const int64_t pos = t < ns ? t : c.sink_tokens + nq + (t - ns);
+        const uint8_t* rc = pos < c.sink_tokens
+                                ? sink.data() + (pos / kvq::kChunk) * L.ring_chunk_bytes
+                                : ring.data() + ((pos / kvq::kChunk) % L.ring_chunks) * L.ring_chunk_bytes;
         const int tt = static_cast<int>(pos % kvq::kChunk);
         for (int cc = 0; cc < D; ++cc) {
           uint16_t kvb, vvb;
@@ -397,16 +418,19 @@ kvq_status kvq_import(kvq_cache* h, int64_t n_tokens, int32_t b0, int32_t bc, co
   if (e != hipSuccess) return device_error(h, e, "stream synchronize");
   const Layout& L = h->L;
   const int D = c.head_dim, G = c.group_size, kb = c.k_bits, vb = c.v_bits, ncg = D / G;
-  const int64_t nq = kvq::num_quantized(n_tokens, G, c.residual), nr = n_tokens - nq, ng = nq / G;
+  const int64_t nq = nquant_of(h, n_tokens), nr = n_tokens - nq, ng = nq / G;
+  const int64_t ns = std::min<int64_t>(n_tokens, c.sink_tokens);
   const int64_t krow = D * kb / 8, vrow = D * vb / 8;
   std::vector<uint8_t> pages(static_cast<size_t>(ng * L.page_bytes));
   std::vector<uint8_t> ring(static_cast<size_t>(L.ring_chunks * L.ring_chunk_bytes));
+  std::vector<uint8_t> sink(static_cast<size_t>(L.sink_chunks * L.ring_chunk_bytes));
   for (int64_t bi = 0; bi < bc; ++bi)
     for (int64_t hk = 0; hk < c.num_kv_heads; ++hk) {
       const int64_t slice = (b0 + bi) * c.num_kv_heads + hk;
       const int64_t oi = bi * c.num_kv_heads + hk;
       std::fill(pages.begin(), pages.end(), 0);
       std::fill(ring.begin(), ring.end(), 0);
+      std::fill(sink.begin(), sink.end(), 0);
       for (int64_t t = 0; t < nq; ++t) {
         uint8_t* page = pages.data() + (t / G) * L.page_bytes;
         const int ch = static_cast<int>((t % G) / kvq::kChunk), tt = static_cast<int>(t % kvq::kChunk);
@@ -438,8 +462,9 @@ kvq_status kvq_import(kvq_cache* h, int64_t n_tokens, int32_t b0, int32_t bc, co
         }
       }
       for (int64_t t = 0; t < nr; ++t) {
-        const int64_t pos = nq + t;
-        uint8_t* rc = ring.data() + ((pos / kvq::kChunk) % L.ring_chunks) * L.ring_chunk_bytes;
+        const int64_t pos = t < ns ? t : c.sink_tokens + nq + (t - ns);
+        uint8_t* rc = pos < c.sink_tokens ? sink.data() + (pos / kvq::kChunk) * L.ring_chunk_bytes
+                                          : ring.data() + ((pos / kvq::kChunk) % L.ring_chunks) * L.ring_chunk_bytes;
         const int tt = static_cast<int>(pos % kvq::kChunk);
         for (int cc = 0; cc < D; ++cc) {
           std::memcpy(rc + kvq::ring_k_offset(L, tt, cc), static_cast<const uint16_t*>(k_resid) + (oi * nr + t) * D + cc, 2);
@@ -453,6 +478,11 @@ kvq_status kvq_import(kvq_cache* h, int64_t n_tokens, int32_t b0, int32_t bc, co
       e = hipMemcpy(h->buf + L.ring_offset + slice * L.ring_chunks * L.ring_chunk_bytes, ring.data(), ring.size(),
                     hipMemcpyHostToDevice);
       if (e != hipSuccess) return device_error(h, e, "import copy");
+      if (!sink.empty()) {
+        e = hipMemcpy(h->buf + L.sink_offset + slice * L.sink_chunks * L.ring_chunk_bytes, sink.data(), sink.size(),
+                      hipMemcpyHostToDevice);
+        if (e != hipSuccess) return device_error(h, e, "import copy");
+      }
     }
   h->n = n_tokens;
   return ok();

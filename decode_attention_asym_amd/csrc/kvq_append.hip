@@ -36,6 +36,74 @@ __device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float
   return static_cast<uint32_t>(q);
 }
 
+// Symmetric code: clamp(rne(x / s), -c0, c0) + c0; c0 when s == 0.
+__device__ __forceinline__ uint32_t quant_code_sym(float x, float s, float c0) {
+  if (s == 0.0f) return static_cast<uint32_t>(c0);
+  float q = rintf(x / s);
+  q = fminf(fmaxf(q, -c0), c0);
+  return static_cast<uint32_t>(q + c0);
+}
+
+// Group parameters.  Asymmetric: s = (max - min) / (2^b - 1), zero = min.
+// With `hybrid`, also the symmetric quantizer (s = max|x| / c0, c0 = 2^(b-1) - 1,
+// zero = fp16(-c0 * fp16(s))), kept only if its largest reconstruction error
+// |x - (code * scale16 + zero16)| (product exact, sum and difference rounded
+// in binary32) is strictly smaller.  x(i) yields the group's i-th value.
+struct GroupQ {
+  float s, mn;          // binary32 scale and minimum the codes use
+  uint16_t scale16, zero16;
+  bool sym;
+};
+template <int COUNT, int BITS, typename F>
+__device__ GroupQ group_params(F&& x, bool hybrid) {
+  float mn = x(0), mx = mn, M = fabsf(mn);
+  for (int i = 1; i < COUNT; ++i) {
+    const float v = x(i);
+    mn = v < mn ? v : mn;
+    mx = v > mx ? v : mx;
+    M = fabsf(v) > M ? fabsf(v) : M;
+  }
+  mn = mn + 0.0f;
+  mx = mx + 0.0f;
+  M = M + 0.0f;
+  constexpr float levels = static_cast<float>((1 << BITS) - 1), c0 = static_cast<float>((1 << (BITS - 1)) - 1);
+  GroupQ r;
+  r.s = (mx - mn) / levels;
+  r.mn = mn;
+  r.scale16 = fp16_bits(r.s);
+  r.zero16 = fp16_bits(mn);
+  r.sym = false;
+  if (hybrid) {
+    const float ss = M / c0;
+    const uint16_t sc16 = fp16_bits(ss);
+    const float s16 = __half2float(__ushort_as_half(sc16));
+    const uint16_t z16 = fp16_bits(-(s16 * c0));
+    const float zs = __half2float(__ushort_as_half(z16));
+    const float sa = __half2float(__ushort_as_half(r.scale16)), za = __half2float(__ushort_as_half(r.zero16));
+    float ea = 0.0f, es = 0.0f;
+    for (int i = 0; i < COUNT; ++i) {
+      const float v = x(i);
+      const float xa = __fadd_rn(__fmul_rn(static_cast<float>(quant_code(v, mn, r.s, levels)), sa), za);
+      const float xs = __fadd_rn(__fmul_rn(static_cast<float>(quant_code_sym(v, ss, c0)), s16), zs);
+      ea = fmaxf(ea, fabsf(__fsub_rn(v, xa)));
+      es = fmaxf(es, fabsf(__fsub_rn(v, xs)));
+    }
+    if (es < ea) {
+      r.s = ss;
+      r.scale16 = sc16;
+      r.zero16 = z16;
+      r.sym = true;
+    }
+  }
+  return r;
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t code_of(float x, float mn, float s, bool sym) {
+  constexpr float levels = static_cast<float>((1 << BITS) - 1), c0 = static_cast<float>((1 << (BITS - 1)) - 1);
+  return sym ? quant_code_sym(x, s, c0) : quant_code(x, mn, s, levels);
+}
+
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // nearest binary32 to 1/sqrt(128)
 constexpr float kInvSqrt64 = 0.125f;
 
@@ -72,10 +140,12 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   __shared__ __half vx[G * D];  // values are fp16 after entry conversion
   __shared__ float ks[D], kmn[D];
   __shared__ float vs[G * NCG], vmn[G * NCG];
+  __shared__ bool ksym[D], vsym[G * NCG];
 
   const Layout& L = a.L;
   const int tid = threadIdx.x;
   const int64_t g = a.g_first + blockIdx.x;
+  const int64_t pos0 = L.S0 + g * G;  // token position of the group's first token
   const int64_t slice = blockIdx.y;
   const int64_t in_base = slice * a.T * D;  // [B][H_kv] flattened == slice
   uint8_t* ring = a.cache;
@@ -84,7 +154,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   bool any_new = false;
   for (int idx = tid; idx < G * D; idx += blockDim.x) {
     int i = idx / D, c = idx % D;
-    int64_t p = g * G + i;
+    int64_t p = pos0 + i;
     if (p >= a.n_old) {
       int64_t src = in_base + (p - a.n_old) * D + c;
       kx[idx] = load_in(a.k, a.in_dtype, src);
@@ -96,11 +166,11 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
       vx[idx] = *reinterpret_cast<const __half*>(rc + ring_v_offset(L, t, c));
     }
   }
-  any_new = (g * G + G) > a.n_old;
+  any_new = (pos0 + G) > a.n_old;
   __syncthreads();
   if (any_new) {
     // rows [first_new, G) come from the input: rotate (keys) then round to fp16
-    int first_new = a.n_old > g * G ? static_cast<int>(a.n_old - g * G) : 0;
+    int first_new = a.n_old > pos0 ? static_cast<int>(a.n_old - pos0) : 0;
     if (a.rotate) fwht_rows<D>(kx + first_new * D, G - first_new, tid, blockDim.x);
     for (int idx = first_new * D + tid; idx < G * D; idx += blockDim.x) kx[idx] = round_fp16(kx[idx]);
     __syncthreads();
@@ -109,47 +179,33 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   uint8_t* page = a.cache + page_offset(L, slice, g);
 
   // 2. parameters: keys per channel over G tokens, values per token over G channels
+  const bool hybrid = a.hybrid != 0;
   for (int c = tid; c < D; c += blockDim.x) {
-    float mn = kx[c], mx = kx[c];
-    for (int i = 1; i < G; ++i) {
-      float x = kx[i * D + c];
-      mn = x < mn ? x : mn;
-      mx = x > mx ? x : mx;
-    }
-    mn = mn + 0.0f;
-    mx = mx + 0.0f;
-    float s = (mx - mn) / static_cast<float>((1 << KB) - 1);
-    ks[c] = s;
-    kmn[c] = mn;
+    const GroupQ q = group_params<G, KB>([&](int i) { return kx[i * D + c]; }, hybrid);
+    ks[c] = q.s;
+    kmn[c] = q.mn;
+    ksym[c] = q.sym;
     uint16_t* kp = reinterpret_cast<uint16_t*>(page + L.off_kparams);
     int pi = kparam_index(L, c);
-    kp[pi] = fp16_bits(s);
-    kp[D + pi] = fp16_bits(mn);
+    kp[pi] = q.scale16;
+    kp[D + pi] = q.zero16;
   }
   for (int task = tid; task < G * NCG; task += blockDim.x) {
     int i = task / NCG, cg = task % NCG;
     const __half* row = vx + i * D + cg * G;
-    float mn = __half2float(row[0]), mx = mn;
-    for (int c = 1; c < G; ++c) {
-      float x = __half2float(row[c]);
-      mn = x < mn ? x : mn;
-      mx = x > mx ? x : mx;
-    }
-    mn = mn + 0.0f;
-    mx = mx + 0.0f;
-    float s = (mx - mn) / static_cast<float>((1 << VB) - 1);
-    vs[task] = s;
-    vmn[task] = mn;
+    const GroupQ q = group_params<G, VB>([&](int c) { return __half2float(row[c]); }, hybrid);
+    vs[task] = q.s;
+    vmn[task] = q.mn;
+    vsym[task] = q.sym;
     uint16_t* vp = reinterpret_cast<uint16_t*>(page + L.off_vparams + (i / kChunk) * L.vp_chunk_bytes);
-    vp[vparam_scale_elem(L, i % kChunk, cg)] = fp16_bits(s);
-    vp[vparam_zero_elem(L, i % kChunk, cg)] = fp16_bits(mn);
+    vp[vparam_scale_elem(L, i % kChunk, cg)] = q.scale16;
+    vp[vparam_zero_elem(L, i % kChunk, cg)] = q.zero16;
   }
   __syncthreads();
 
   // 3. key codes: each task assembles one dword of one lane of one chunk
   {
     constexpr int KW = 2 * NKB * KB / 4;
-    constexpr float KL = static_cast<float>((1 << KB) - 1);
     for (int task = tid; task < CPG * kLanes * KW; task += blockDim.x) {
       int ch = task / (kLanes * KW);
       int l = (task / KW) % kLanes;
@@ -163,7 +219,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         int i = ch * kChunk + 16 * mt + l16;  // token within the group
         for (int e = 0; e < 8; ++e) {
           int c = 32 * kb + 8 * j + e;
-          uint32_t code = quant_code(kx[i * D + c], kmn[c], ks[c], KL);
+          uint32_t code = code_of<KB>(kx[i * D + c], kmn[c], ks[c], ksym[c]);
           int bit = KB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
           word |= code << bit;
         }
@@ -175,7 +231,6 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   {
     constexpr int NMT = D / 16;
     constexpr int VW = NMT * VB / 4;
-    constexpr float VL = static_cast<float>((1 << VB) - 1);
     for (int task = tid; task < CPG * kLanes * VW; task += blockDim.x) {
       int ch = task / (kLanes * VW);
       int l = (task / VW) % kLanes;
@@ -189,7 +244,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         int cg = c / G;
         for (int e = 0; e < 8; ++e) {
           int i = ch * kChunk + tau(j, e);
-          uint32_t code = quant_code(__half2float(vx[i * D + c]), vmn[i * NCG + cg], vs[i * NCG + cg], VL);
+          uint32_t code = code_of<VB>(__half2float(vx[i * D + c]), vmn[i * NCG + cg], vs[i * NCG + cg], vsym[i * NCG + cg]);
           int bit = VB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
           word |= code << bit;
         }
@@ -199,20 +254,21 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   }
 }
 
-// One block of D threads per (window position written, slice).
+// One block of D threads per (fp16 position written, slice): the sink
+// positions of this call first, then its window positions.
 template <int D>
 __global__ __launch_bounds__(128) void window_write_kernel(AppendArgs a) {
   __shared__ float kx[D];
   const Layout& L = a.L;
   const int c = threadIdx.x;
-  const int64_t p = a.w_first + blockIdx.x;
+  const int64_t p = blockIdx.x < a.n_sink_write ? a.s_first + blockIdx.x : a.w_first + (blockIdx.x - a.n_sink_write);
   const int64_t slice = blockIdx.y;
   const int64_t src = (slice * a.T + (p - a.n_old)) * D + c;
   kx[c] = load_in(a.k, a.in_dtype, src);
   float v = round_fp16(load_in(a.v, a.in_dtype, src));
   __syncthreads();
   if (a.rotate) fwht_rows<D>(kx, 1, c, D);
-  uint8_t* rc = a.cache + ring_chunk_offset(L, slice, p);
+  uint8_t* rc = a.cache + fp16_chunk_offset(L, slice, p);
   int t = static_cast<int>(p % kChunk);
   *reinterpret_cast<__half*>(rc + ring_k_offset(L, t, c)) = __float2half_rn(kx[c]);
   *reinterpret_cast<__half*>(rc + ring_v_offset(L, t, c)) = __float2half_rn(v);
@@ -248,8 +304,8 @@ hipError_t launch_flush(const AppendArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_window_write(const AppendArgs& a, hipStream_t s) {
-  if (a.n_write <= 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>(a.n_write), static_cast<unsigned>(a.L.slices));
+  if (a.n_write + a.n_sink_write <= 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(a.n_sink_write + a.n_write), static_cast<unsigned>(a.L.slices));
   if (a.L.D == 64)
     hipLaunchKernelGGL((window_write_kernel<64>), grid, dim3(64), 0, s, a);
   else

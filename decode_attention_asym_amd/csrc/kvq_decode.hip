@@ -689,12 +689,15 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < NMT; ++i) acc[i] *= kTwo24;
 
-  // ---- fp16 window chunks, spread over the splits (split s takes window chunks
-  // S - 1 - s, 2S - 1 - s, ...) so that no wave adds more than its share of
-  // these latency-bound reads to the end of the kernel
+  // ---- fp16 chunks (the attention-sink chunks, then the recent window's),
+  // spread over the splits (split s takes chunks S - 1 - s, 2S - 1 - s, ...)
+  // so that no wave adds more than its share of these latency-bound reads to
+  // the end of the kernel
   {
-    for (int64_t rc = a.rc0 + (S - 1 - s); rc < a.rc1; rc += S) {
-      const uint8_t* rch = a.cache + ring_chunk_offset(L, slice, rc * kChunk);
+    const int64_t nfc = a.nsc + (a.rc1 - a.rc0);
+    for (int64_t fc = S - 1 - s; fc < nfc; fc += S) {
+      const int64_t rc = fc < a.nsc ? fc : a.rc0 + (fc - a.nsc);  // absolute chunk index
+      const uint8_t* rch = a.cache + fp16_chunk_offset(L, slice, rc * kChunk);
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {

@@ -15,6 +15,7 @@ struct AppendArgs {
   const void* v;
   int in_dtype;         // 0 f32, 1 f16, 2 bf16
   int rotate;
+  int hybrid;           // per-group symmetric/asymmetric choice
   int Hkv;
   int64_t T;            // tokens in this call
   int64_t n_old;        // tokens per sequence before the call
@@ -22,6 +23,8 @@ struct AppendArgs {
   int64_t n_flush;      // groups flushed by this call
   int64_t w_first;      // first window position written by this call
   int64_t n_write;      // window positions written by this call
+  int64_t s_first;      // first sink position written by this call
+  int64_t n_sink_write; // sink positions written by this call
 };
 
 struct DecodeArgs {
@@ -37,6 +40,7 @@ struct DecodeArgs {
   int splits;
   int64_t groups_per_split;
   int64_t rc0, rc1;     // window chunks [rc0, rc1) (absolute 32-token chunk indices)
+  int64_t nsc;          // sink chunks holding tokens (ceil(min(n, S0) / 32))
   float* partial;       // [B*H_q][splits][D + 4] when !write_final
   float* out;           // [B][H_q][D] when write_final (splits == 1)
   int write_final;

@@ -53,6 +53,8 @@ constexpr int kLanes = 64;
 
 struct Layout {
   int D, kbits, vbits, G, R;
+  int S0;                       // attention-sink tokens kept in fp16 (a multiple of G and of 32)
+  int sink_chunks;              // S0 / 32
   int nkb, nmt, ncg;            // D/32 key k-blocks, D/16 value M-tiles, D/G value groups
   int chunks_per_group;         // G / 32
   int kw, vw;                   // dwords per lane per chunk of key / value codes
@@ -67,13 +69,15 @@ struct Layout {
   int64_t ring_chunk_bytes;     // K part then V part, fp16, 32 * D * 2 each
   int64_t slices;               // B * H_kv
   int64_t pages_offset, ring_offset, total_bytes;
+  int64_t sink_offset;          // fp16 sink chunks, per slice, in the window ring's chunk format
 };
 
 KVQ_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int vbits, int G, int R) {
+inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int vbits, int G, int R, int S0 = 0) {
   Layout L{};
   L.D = D; L.kbits = kbits; L.vbits = vbits; L.G = G; L.R = R;
+  L.S0 = S0; L.sink_chunks = S0 / kChunk;
   L.nkb = D / 32; L.nmt = D / 16; L.ncg = D / G;
   L.chunks_per_group = G / kChunk;
   L.kw = 2 * L.nkb * kbits / 4;            // 4-bit: one dword per (mt, kb); 2-bit: half of that
@@ -89,7 +93,7 @@ inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int 
   L.off_kparams = L.off_vcodes + L.chunks_per_group * L.vc_chunk_bytes;
   L.off_vparams = L.off_kparams + L.kp_bytes;
   L.page_bytes = L.off_vparams + L.chunks_per_group * L.vp_chunk_bytes;
-  int64_t over = (int64_t)max_tokens - R;
+  int64_t over = (int64_t)max_tokens - S0 - R;
   L.pages = over > 0 ? over / G : 0;
   L.cap = R + G;
   L.ring_chunks = L.cap / kChunk;
@@ -97,7 +101,8 @@ inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int 
   L.slices = (int64_t)B * Hkv;
   L.pages_offset = 0;
   L.ring_offset = align_up(L.slices * L.pages * L.page_bytes, 256);
-  L.total_bytes = align_up(L.ring_offset + L.slices * L.ring_chunks * L.ring_chunk_bytes, 256);
+  L.sink_offset = align_up(L.ring_offset + L.slices * L.ring_chunks * L.ring_chunk_bytes, 256);
+  L.total_bytes = align_up(L.sink_offset + L.slices * L.sink_chunks * L.ring_chunk_bytes, 256);
   return L;
 }
 
@@ -189,9 +194,17 @@ KVQ_HD int64_t page_offset(const Layout& L, int64_t slice, int64_t g) {
 KVQ_HD int64_t ring_chunk_offset(const Layout& L, int64_t slice, int64_t pos) {
   return L.ring_offset + (slice * L.ring_chunks + (pos / kChunk) % L.ring_chunks) * L.ring_chunk_bytes;
 }
+// The fp16 chunk holding token position pos: a sink chunk for pos < S0, else
+// the window ring's.
+KVQ_HD int64_t fp16_chunk_offset(const Layout& L, int64_t slice, int64_t pos) {
+  return pos < L.S0 ? L.sink_offset + (slice * L.sink_chunks + pos / kChunk) * L.ring_chunk_bytes
+                    : ring_chunk_offset(L, slice, pos);
+}
 
-KVQ_HD int64_t num_quantized(int64_t n, int G, int R) {
-  int64_t over = n - R;
+// Quantized tokens among n: whole groups of G aligned to token S0 (after the
+// fp16 sink), leaving at least R recent tokens in fp16.
+KVQ_HD int64_t num_quantized(int64_t n, int G, int R, int S0 = 0) {
+  int64_t over = n - S0 - R;
   return over > 0 ? over / G * G : 0;
 }
 

@@ -35,6 +35,8 @@ class kvq_config(ctypes.Structure):
         ("residual", ctypes.c_int32),
         ("rotate", ctypes.c_int32),
         ("in_dtype", ctypes.c_int32),
+        ("sink_tokens", ctypes.c_int32),
+        ("hybrid", ctypes.c_int32),
     ]
 
 
@@ -101,12 +103,14 @@ class Config:
     residual: int
     rotate: bool = False
     in_dtype: str = "bf16"
+    sink_tokens: int = 0
+    hybrid: bool = False
 
     def c(self) -> kvq_config:
         return kvq_config(
             ctypes.sizeof(kvq_config), self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
             self.max_tokens, self.k_bits, self.v_bits, self.group_size, self.residual, int(bool(self.rotate)),
-            DTYPES[self.in_dtype],
+            DTYPES[self.in_dtype], self.sink_tokens, int(bool(self.hybrid)),
         )
 
 

@@ -73,6 +73,11 @@ typedef struct {
   int32_t residual;     /* R: recent tokens kept in fp16; a multiple of 32, 0 <= R <= 1024 */
   int32_t rotate;       /* 0 or 1: Walsh-Hadamard rotation of keys (append) and queries (decode) */
   int32_t in_dtype;     /* kvq_dtype of the k, v and q buffers passed in */
+  int32_t sink_tokens;  /* S0: the first S0 tokens stay in fp16 (attention sinks); a multiple of G
+                           in [0, 1024]; quantized groups then start at token S0 (0: no sink) */
+  int32_t hybrid;       /* 0 or 1: per group, keep a symmetric quantizer (scale max|x| / c0,
+                           c0 = 2^(b-1) - 1, zero = -c0 * scale) instead of the asymmetric one
+                           when its largest reconstruction error on the group is smaller */
 } kvq_config;
 
 /* Device bytes the cache buffer must hold for `cfg`, or 0 if `cfg` is

@@ -48,6 +48,8 @@ class Workload:
     dist: str        # "tiny" | "lognormal" | "drift"
     append_per_step: bool = False
     idx: int = 0
+    sink: int = 0            # attention-sink tokens kept in fp16
+    hybrid: bool = False     # per-group symmetric/asymmetric quantizer choice
 
     @property
     def gqa(self) -> int:

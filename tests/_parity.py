@@ -25,7 +25,8 @@ def oracle_encode_slices(w, K, V, pairs):
         b, h = bh
         k = to_oracle_input(K[b, h], w.dtype)
         v = to_oracle_input(V[b, h], w.dtype)
-        return oracle.encode_slice(k, v, w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate)
+        return oracle.encode_slice(k, v, w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate, sink=w.sink,
+                                   hybrid=w.hybrid)
 
     with ThreadPoolExecutor(THREADS) as ex:
         return dict(zip(pairs, ex.map(enc, pairs)))

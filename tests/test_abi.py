@@ -44,6 +44,7 @@ def _cfg(**kw):
     dict(head_dim=96), dict(k_bits=3), dict(v_bits=8), dict(group_size=16), dict(residual=48),
     dict(num_q_heads=6, num_kv_heads=2), dict(num_q_heads=64, num_kv_heads=2),
     dict(batch=0), dict(max_tokens=0), dict(head_dim=64, group_size=128),
+    dict(sink_tokens=32), dict(sink_tokens=-64), dict(sink_tokens=1088),
 ])
 def test_invalid_configs_rejected(bad):
     import decode_attention_asym_amd as kvq
@@ -54,21 +55,24 @@ def test_invalid_configs_rejected(bad):
 
 def test_cache_bytes_matches_bit_accounting():
     """Quantized pages hold exactly codes + fp16 scale/zero (the oracle's bits
-    per element), plus a fp16 window ring of R + G tokens per slice."""
+    per element), plus a fp16 window ring of R + G tokens and the fp16
+    attention-sink tokens per slice."""
     import decode_attention_asym_amd as kvq
     import oracle
 
-    for kb, vb, G, R, D in ((4, 2, 64, 128, 128), (2, 2, 32, 32, 128), (2, 4, 32, 64, 64)):
+    for kb, vb, G, R, D, S0 in ((4, 2, 64, 128, 128, 0), (2, 2, 32, 32, 128, 0), (2, 4, 32, 64, 64, 0),
+                                (4, 2, 64, 128, 128, 64), (2, 2, 32, 32, 64, 96)):
         n = 10000
         c = _cfg(k_bits=kb, v_bits=vb, group_size=G, residual=R, head_dim=D, max_tokens=n,
-                 num_q_heads=2, num_kv_heads=2)
-        nq = oracle.num_quantized(n, G, R)
-        quant_bits = oracle.bits_per_element(n, kb, vb, G, R) * 2 * n * D - 2 * 16 * (n - nq) * D
+                 num_q_heads=2, num_kv_heads=2, sink_tokens=S0)
+        nq = oracle.num_quantized(n, G, R, S0)
+        quant_bits = oracle.bits_per_element(n, kb, vb, G, R, sink=S0) * 2 * n * D - 2 * 16 * (n - nq) * D
         ring = (R + G) * D * 2 * 2
+        sink = S0 * D * 2 * 2
         total = kvq.cache_bytes(c)
         slices = c.batch * c.num_kv_heads
-        assert total >= slices * (quant_bits / 8 + ring)
-        assert total <= slices * (quant_bits / 8 + ring) + 512
+        assert total >= slices * (quant_bits / 8 + ring + sink)
+        assert total <= slices * (quant_bits / 8 + ring + sink) + 768
 
 
 def test_host_validation_without_device_work():

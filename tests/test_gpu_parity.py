@@ -66,6 +66,16 @@ SMALL = [
     WORKLOADS[1].replace(name="single-token", B=2, N=1, R=32),
     WORKLOADS[1].replace(name="window-full", B=2, N=128 + 31, R=128),
     WORKLOADS[1].replace(name="first-flush", B=2, N=128 + 32, R=128),
+    # attention-sink fp16 window and the per-group symmetric/asymmetric choice
+    WORKLOADS[2].replace(name="sink64-hybrid-k4v2-g64", B=2, N=4096 + 77, sink=64, hybrid=True),
+    WORKLOADS[3].replace(name="sink32-gqa8-r32", B=1, N=2000 + 5, sink=32),
+    WORKLOADS[1].replace(name="hybrid-k2v4-g32", B=2, N=1500 + 9, vbits=4, hybrid=True),
+    WORKLOADS[0].replace(name="d64-rot-sink-hybrid", B=2, Hq=4, Hkv=2, N=600 + 3, kbits=4, vbits=2, rotate=True,
+                         sink=64, hybrid=True),
+    WORKLOADS[1].replace(name="sink-only", B=2, N=100, R=32, G=64, sink=128),
+    WORKLOADS[1].replace(name="sink-no-flush-yet", B=2, N=64 + 128 + 31, R=128, sink=64),
+    WORKLOADS[1].replace(name="sink-first-flush", B=2, N=64 + 128 + 32, R=128, sink=64),
+    WORKLOADS[4].replace(name="mha-fwht-sink-hybrid", B=1, Hq=8, Hkv=8, N=1024 + 13, sink=32, hybrid=True),
 ]
 
 
@@ -85,33 +95,39 @@ def test_split_counts_agree(splits):
     _check_full(w, splits=splits, check_codes=(splits == 1))
 
 
-def _split_ranges(n, ng, G, S_req):
-    """Token ranges of each split: a contiguous, group-aligned run of
-    ceil(ng / S) groups, plus the fp16 window's 32-token chunks w with
-    w mod S = S - 1 - s."""
+def _split_ranges(n, ng, G, S_req, sink=0):
+    """Canonical token ranges (quantized tokens first, then the fp16 tokens:
+    sink, then window) of each split: a contiguous, group-aligned run of
+    ceil(ng / S) groups, plus the fp16 chunks f (the sink's 32-token chunks,
+    then the window's) with f mod S = S - 1 - s."""
     S = min(S_req, max(1, ng))
     gps = -(-ng // S) if ng else 0
     if gps:
         S = -(-ng // gps)
     nq = ng * G
+    ns = min(n, sink)
+    nsc = -(-ns // 32)
+    nwin = n - sink - nq if n > sink else 0
+    chunks = [(nq + 32 * c, nq + min(ns, 32 * c + 32)) for c in range(nsc)]
+    chunks += [(nq + ns + 32 * w, nq + ns + min(nwin, 32 * w + 32)) for w in range(-(-nwin // 32))]
     ranges = []
     for s in range(S):
         r = [(min(ng, s * gps) * G, min(ng, (s + 1) * gps) * G)]
-        for w in range(S - 1 - s, -(-(n - nq) // 32), S):
-            r.append((nq + 32 * w, min(n, nq + 32 * (w + 1))))
+        r += [chunks[f] for f in range(S - 1 - s, len(chunks), S)]
         ranges.append([x for x in r if x[1] > x[0]])
     return S, ranges
 
 
-def test_decode_partials_per_split_match_oracle():
+@pytest.mark.parametrize("sink", [0, 64])
+def test_decode_partials_per_split_match_oracle(sink):
     """kvq_decode_partials: every split's (m, l, o) against the oracle's partial
-    attention over the same token range; kvq_merge_partials of them equals
-    kvq_decode_attn_splits with the same split count, bit for bit."""
+    attention over the same tokens; kvq_merge_partials of them equals
+    kvq_decode_attn_splits with the same split count."""
     kvq = _lib()
     import oracle
     from _parity import canonical_slice, oracle_queries
 
-    w = WORKLOADS[2].replace(name="partials", B=2, Hq=8, Hkv=2, N=64 * 9 + 128 + 21)
+    w = WORKLOADS[2].replace(name=f"partials-sink{sink}", B=2, Hq=8, Hkv=2, N=sink + 64 * 9 + 128 + 21, sink=sink)
     syn, K, V, q, cache = _run_prefill(w)
     S_req = 4
     partials, S = cache.decode_partials(q, splits=S_req)
@@ -123,7 +139,7 @@ def test_decode_partials_per_split_match_oracle():
     assert err <= 1e-6, err
     exp = cache.export()
     ng = exp["nq"] // w.G
-    S_exp, ranges = _split_ranges(w.N, ng, w.G, S_req)
+    S_exp, ranges = _split_ranges(w.N, ng, w.G, S_req, sink)
     assert S == S_exp
     P = partials.reshape(-1)[:w.B * w.Hq * S * (w.D + 4)].double().cpu().numpy().reshape(w.B, w.Hq, S, w.D + 4)
     q_host = to_oracle_input(q, w.dtype)
@@ -203,9 +219,10 @@ def test_repeated_decodes_with_changing_split_counts():
         assert err <= TOL_REL_L2, (S, err)
 
 
-def test_stepwise_append_equals_prefill():
+@pytest.mark.parametrize("sink,hybrid", [(0, False), (64, True)])
+def test_stepwise_append_equals_prefill(sink, hybrid):
     kvq = _lib()
-    w = WORKLOADS[2].replace(name="stepwise", B=2, Hkv=2, Hq=8, N=700)
+    w = WORKLOADS[2].replace(name="stepwise", B=2, Hkv=2, Hq=8, N=700, sink=sink, hybrid=hybrid)
     syn = Synth(w, "cuda")
     K, V = syn.kv_all()
     a = kvq.KVQCache(kvq.config_for(w))
