@@ -66,15 +66,17 @@ def _declare(L):
     L.orc_encode_slice.restype = i64
     L.orc_encode_slice.argtypes = [P, P, i32, i64, i32, i32, i32, i32, i32, i32] + [P] * 8
     L.orc_encode_slice_ext.restype = i64
-    L.orc_encode_slice_ext.argtypes = [P, P, i32, i64, i32, i32, i32, i32, i32, i32, i32, i32] + [P] * 10
+    L.orc_encode_slice_ext.argtypes = [P, P, i32, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32] + [P] * 11
+    L.orc_row_norm_f32.restype = ctypes.c_float
+    L.orc_row_norm_f32.argtypes = [P, i32]
     L.orc_pack_codes.restype = None
     L.orc_pack_codes.argtypes = [P, i64, i32, i32, P]
     L.orc_unpack_codes.restype = None
     L.orc_unpack_codes.argtypes = [P, i64, i32, i32, P]
     L.orc_attend_partial.restype = None
-    L.orc_attend_partial.argtypes = [P, i32, i64, i64, i32, i32] + [P] * 8 + [i64, i64, P, P, P]
+    L.orc_attend_partial.argtypes = [P, i32, i64, i64, i32, i32] + [P] * 9 + [i64, i64, P, P, P]
     L.orc_attend_slice.restype = None
-    L.orc_attend_slice.argtypes = [P, i32, i64, i64, i32, i32] + [P] * 8 + [P]
+    L.orc_attend_slice.argtypes = [P, i32, i64, i64, i32, i32] + [P] * 9 + [P]
     L.orc_merge_partials.restype = None
     L.orc_merge_partials.argtypes = [i32, i32, i32, P, P, P, P]
     L.orc_bits_per_element.restype = f64
@@ -187,14 +189,20 @@ def num_quantized(n: int, G: int, R: int, sink: int = 0) -> int:
     return int(lib().orc_num_quantized_sink(n, G, R, sink))
 
 
+def row_norm_f32(x) -> float:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return float(lib().orc_row_norm_f32(_p(x), x.size))
+
+
 def encode_slice(k, v, dtype: str, D: int, kbits: int, vbits: int, G: int, R: int, rotate: bool,
-                 sink: int = 0, hybrid: bool = False):
+                 sink: int = 0, hybrid: bool = False, token_norm: bool = False):
     """Encode one (batch, kv-head) slice.  k, v: [n][D] in the input dtype
     (float32 values for "f32", uint16 bit patterns for "f16"/"bf16").
 
     Returns a dict of canonical arrays (codes unpacked, one per uint16); the
     fp16 tokens (an attention-sink window of `sink` tokens, then the recent
-    window) are k_resid / v_resid; k_sym / v_sym mark symmetric groups."""
+    window) are k_resid / v_resid; k_sym / v_sym mark symmetric groups;
+    k_norm (fp16 bits, one per quantized token) is present with token_norm."""
     np_dt = np.float32 if dtype == "f32" else np.uint16
     k = np.ascontiguousarray(k, dtype=np_dt).reshape(-1, D)
     v = np.ascontiguousarray(v, dtype=np_dt).reshape(-1, D)
@@ -213,11 +221,16 @@ def encode_slice(k, v, dtype: str, D: int, kbits: int, vbits: int, G: int, R: in
         "k_sym": np.zeros((nq // G, D), np.uint8),
         "v_sym": np.zeros((nq, D // G), np.uint8),
     }
+    k_norm = np.zeros(max(nq, 1), np.uint16)
     r = lib().orc_encode_slice_ext(
         _p(k), _p(v), DTYPE_CODE[dtype], n, D, kbits, vbits, G, R, int(bool(rotate)), int(sink), int(bool(hybrid)),
+        int(bool(token_norm)),
         *(_p(out[key]) for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid",
                                    "k_sym", "v_sym")),
+        _p(k_norm),
     )
+    if token_norm:
+        out["k_norm"] = k_norm[:nq].copy()
     if r < 0:
         raise ValueError("orc_encode_slice rejected its arguments")
     out["nq"] = nq
@@ -246,8 +259,16 @@ _CACHE_KEYS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "
 
 
 def _cache_ptrs(cache):
+    """Pointers to the canonical arrays, then to k_norm (NULL without token norms)."""
     arrs = [np.ascontiguousarray(cache[k], dtype=np.uint16) for k in _CACHE_KEYS]
-    return arrs, [_p(a) for a in arrs]
+    ptrs = [_p(a) for a in arrs]
+    if cache.get("k_norm") is not None:
+        kn = np.ascontiguousarray(cache["k_norm"], dtype=np.uint16)
+        arrs.append(kn)
+        ptrs.append(_p(kn))
+    else:
+        ptrs.append(None)
+    return arrs, ptrs
 
 
 def attend_slice(q, cache, D: int, G: int, R: int | None = None) -> np.ndarray:

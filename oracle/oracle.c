@@ -36,6 +36,13 @@
  *    page names no symmetric formula and no selection rule; here symmetric is
  *    x = s (code - c0), c0 = 2^(b-1) - 1, s = max|x| / c0, and the quantizer
  *    with the smaller largest reconstruction error on the group is kept.
+ *  - Token-norm scaling of the rotated keys (OScaR stage 2: "[Framework]
+ *    ...", section IV, omni-token scaling): each quantized key token is
+ *    divided by its L2 norm before the per-channel quantizer, and the norm is
+ *    kept (fp16) and multiplied back at decode.  The page gives no arithmetic;
+ *    here the norm is that of the fp16 (rotated) token row, summed as a fixed
+ *    pairwise tree in binary32 with a correctly rounded square root, the
+ *    normalized values are rounded to fp16, and a zero row keeps norm 0.
  *  - Bits-per-element accounting: "Asymmetric Key-Value Quantization ...",
  *    section 3.1 (average of key and value bit widths) and section 3.4
  *    (combined compression table); here the per-group fp16 scale and zero
@@ -55,9 +62,10 @@
 
 int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n, int D,
                              int kbits, int vbits, int G, int R, int rotate, int S0, int hybrid,
-                             uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
+                             int token_norm, uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
                              uint16_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
-                             uint16_t* k_resid, uint16_t* v_resid, uint8_t* k_sym, uint8_t* v_sym);
+                             uint16_t* k_resid, uint16_t* v_resid, uint8_t* k_sym, uint8_t* v_sym,
+                             uint16_t* k_norm);
 double orc_bits_per_element_sink(int64_t n, int kbits, int vbits, int G, int R, int S0,
                                  double overhead_bits);
 
@@ -263,6 +271,19 @@ int orc_quantize_group_hybrid(const float* x, int count, int bits, uint16_t* cod
   return sym;
 }
 
+/* L2 norm of a row of D values (D a power of two) in binary32: squares,
+ * then pairwise sums (element 2i + element 2i + 1, level by level), then a
+ * correctly rounded square root. */
+float orc_row_norm_f32(const float* x, int D) {
+  float* t = (float*)malloc(sizeof(float) * (size_t)D);
+  for (int c = 0; c < D; ++c) t[c] = x[c] * x[c];
+  for (int w = D; w > 1; w /= 2)
+    for (int i = 0; i < w / 2; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+  float r = sqrtf(t[0]);
+  free(t);
+  return r;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Window bookkeeping.                                                       */
 /* ------------------------------------------------------------------------ */
@@ -299,8 +320,8 @@ int64_t orc_encode_slice(const void* k, const void* v, int dtype, int64_t n, int
                          uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
                          uint16_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
                          uint16_t* k_resid, uint16_t* v_resid) {
-  return orc_encode_slice_ext(k, v, dtype, n, D, kbits, vbits, G, R, rotate, 0, 0, k_codes, k_scale,
-                              k_zero, v_codes, v_scale, v_zero, k_resid, v_resid, NULL, NULL);
+  return orc_encode_slice_ext(k, v, dtype, n, D, kbits, vbits, G, R, rotate, 0, 0, 0, k_codes, k_scale,
+                              k_zero, v_codes, v_scale, v_zero, k_resid, v_resid, NULL, NULL, NULL);
 }
 
 /* As orc_encode_slice, with an attention-sink window of S0 tokens (0: none)
@@ -309,16 +330,21 @@ int64_t orc_encode_slice(const void* k, const void* v, int dtype, int64_t n, int
  * nq = orc_num_quantized_sink(n, G, R, S0); k_resid / v_resid hold the other
  * n - nq tokens in position order (the sink, then the recent window).
  * k_sym [nq/G][D] and v_sym [nq][D/G] (may be NULL) receive 1 where a group
- * took the symmetric quantizer. */
+ * took the symmetric quantizer.  With `token_norm`, each quantized key token
+ * is divided by its norm (orc_row_norm_f32 of its fp16 row) and rounded to
+ * fp16 before the key quantizer, and k_norm [nq] receives the norms as fp16
+ * bits (0 for a zero row, whose normalized values are 0). */
 int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n, int D,
                              int kbits, int vbits, int G, int R, int rotate, int S0, int hybrid,
-                             uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
+                             int token_norm, uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
                              uint16_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
-                             uint16_t* k_resid, uint16_t* v_resid, uint8_t* k_sym, uint8_t* v_sym) {
+                             uint16_t* k_resid, uint16_t* v_resid, uint8_t* k_sym, uint8_t* v_sym,
+                             uint16_t* k_norm) {
   if (n < 0 || D <= 0 || G <= 0 || R < 0 || D % G != 0 || S0 < 0) return -1;
   if (kbits < 1 || kbits > 16 || vbits < 1 || vbits > 16) return -1;
   if (hybrid && (kbits < 2 || vbits < 2)) return -1;
-  if (rotate && (D & (D - 1)) != 0) return -1;
+  if ((rotate || token_norm) && (D & (D - 1)) != 0) return -1;
+  if (token_norm && !k_norm) return -1;
   int64_t nq = orc_num_quantized_sink(n, G, R, S0);
   int64_t s0 = n < S0 ? n : S0;
   float* kt = (float*)malloc(sizeof(float) * (size_t)n * (size_t)D + 1);
@@ -337,11 +363,26 @@ int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n,
       vt[t * D + c] = orc_f16_to_f32(orc_f32_to_f16(load_in(v, dtype, (size_t)t * D + c)));
   }
 
+  /* token-norm scaling of the quantized keys (the fp16 window keeps them as
+   * they are) */
+  float* kq = (float*)malloc(sizeof(float) * (size_t)(nq > 0 ? nq : 1) * (size_t)D);
+  for (int64_t t = 0; t < nq; ++t) {
+    const float* x = kt + (s0 + t) * D;
+    float* y = kq + t * D;
+    if (!token_norm) {
+      for (int c = 0; c < D; ++c) y[c] = x[c];
+      continue;
+    }
+    float nrm = orc_row_norm_f32(x, D);
+    k_norm[t] = orc_f32_to_f16(nrm);
+    for (int c = 0; c < D; ++c) y[c] = nrm == 0.0f ? 0.0f : orc_f16_to_f32(orc_f32_to_f16(x[c] / nrm));
+  }
+
   /* keys: per channel, groups of G consecutive tokens (token s0 + q for
    * quantized index q) */
   for (int64_t g = 0; g < nq / G; ++g)
     for (int c = 0; c < D; ++c) {
-      for (int i = 0; i < G; ++i) grp[i] = kt[(s0 + g * G + i) * D + c];
+      for (int i = 0; i < G; ++i) grp[i] = kq[(g * G + i) * D + c];
       int sym = 0;
       if (hybrid)
         sym = orc_quantize_group_hybrid(grp, G, kbits, cod, &k_scale[g * D + c], &k_zero[g * D + c]);
@@ -376,6 +417,7 @@ int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n,
     ++r;
   }
 
+  free(kq);
   free(kt); free(vt); free(row); free(grp); free(cod);
   return nq;
 }
@@ -422,11 +464,12 @@ void orc_unpack_codes(const uint8_t* in, int64_t rows, int D, int bits, uint16_t
 /* Dequantized key / value element of token t, channel c (fp64). */
 static double key_at(int64_t t, int c, int64_t nq, int D, int G,
                      const uint16_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
-                     const uint16_t* k_resid) {
+                     const uint16_t* k_resid, const uint16_t* k_norm) {
   if (t < nq) {
     int64_t g = t / G;
-    return (double)orc_f16_to_f32(k_zero[g * D + c]) +
-           (double)k_codes[t * D + c] * (double)orc_f16_to_f32(k_scale[g * D + c]);
+    double k = (double)orc_f16_to_f32(k_zero[g * D + c]) +
+               (double)k_codes[t * D + c] * (double)orc_f16_to_f32(k_scale[g * D + c]);
+    return k_norm ? k * (double)orc_f16_to_f32(k_norm[t]) : k;
   }
   return (double)orc_f16_to_f32(k_resid[(t - nq) * D + c]);
 }
@@ -453,7 +496,7 @@ static double value_at(int64_t t, int c, int64_t nq, int D, int G,
 void orc_attend_partial(const double* q, int nh, int64_t n, int64_t nq, int D, int G,
                         const uint16_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
                         const uint16_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
-                        const uint16_t* k_resid, const uint16_t* v_resid,
+                        const uint16_t* k_resid, const uint16_t* v_resid, const uint16_t* k_norm,
                         int64_t t0, int64_t t1, double* m, double* l, double* o) {
   (void)n;
   double inv_sqrt_d = 1.0 / sqrt((double)D);
@@ -465,7 +508,7 @@ void orc_attend_partial(const double* q, int nh, int64_t n, int64_t nq, int D, i
     for (int64_t t = t0; t < t1; ++t) {
       double s = 0.0;
       for (int c = 0; c < D; ++c)
-        s += qh[c] * key_at(t, c, nq, D, G, k_codes, k_scale, k_zero, k_resid);
+        s += qh[c] * key_at(t, c, nq, D, G, k_codes, k_scale, k_zero, k_resid, k_norm);
       s *= inv_sqrt_d;
       sig[t - t0] = s;
       if (s > mx) mx = s;
@@ -489,11 +532,12 @@ void orc_attend_partial(const double* q, int nh, int64_t n, int64_t nq, int D, i
 void orc_attend_slice(const double* q, int nh, int64_t n, int64_t nq, int D, int G,
                       const uint16_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
                       const uint16_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
-                      const uint16_t* k_resid, const uint16_t* v_resid, double* out) {
+                      const uint16_t* k_resid, const uint16_t* v_resid, const uint16_t* k_norm,
+                      double* out) {
   double* m = (double*)malloc(sizeof(double) * (size_t)nh);
   double* l = (double*)malloc(sizeof(double) * (size_t)nh);
   orc_attend_partial(q, nh, n, nq, D, G, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero,
-                     k_resid, v_resid, 0, n, m, l, out);
+                     k_resid, v_resid, k_norm, 0, n, m, l, out);
   for (int h = 0; h < nh; ++h)
     for (int c = 0; c < D; ++c) out[(size_t)h * D + c] /= l[h];
   free(m);

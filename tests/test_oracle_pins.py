@@ -568,3 +568,82 @@ def test_bits_per_element_with_sink_closed_form(orc):
     # fp16 tokens 192; bpe = (8000 * (2 + 1) * 2 + 32 * 192) / (2 * 8192)
     assert orc.num_quantized(8192, 32, 128, 64) == 8000
     assert orc.bits_per_element(8192, 2, 2, 32, 128, sink=64) == pytest.approx((48000 + 6144) / 16384, abs=1e-12)
+
+
+# --------------------------------------------------------- token-norm scaling
+def test_row_norm_closed_forms_and_summation_tree(orc):
+    x = np.zeros(128, np.float32)
+    x[0], x[1] = 3.0, 4.0
+    assert orc.row_norm_f32(x) == 5.0
+    assert orc.row_norm_f32(np.ones(128, np.float32)) == np.float32(np.sqrt(128.0))
+    assert orc.row_norm_f32(np.zeros(64, np.float32)) == 0.0
+    # squares [2^24, 1, 1, 1]: the pairwise tree gives (2^24 + 1) + (1 + 1) =
+    # 2^24 + 2 (the first sum rounds to 2^24), a left-to-right sum 2^24
+    assert orc.row_norm_f32(np.array([4096.0, 1.0, 1.0, 1.0], np.float32)) == np.float32(np.sqrt(2.0 ** 24 + 2))
+
+
+def test_token_norm_power_of_two_scaling(orc):
+    """Scaling a key token by 2^k (exact in fp16) leaves every code, scale and
+    zero unchanged and multiplies that token's stored norm by 2^k."""
+    rng = np.random.default_rng(11)
+    D, G, R, n = 64, 32, 32, 32 * 4 + 40
+    k = orc.f16_bits_to_f32(orc.f32_to_f16_bits(rng.standard_normal((n, D)).astype(np.float32)))
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    a = orc.encode_slice(k, v, "f32", D, 4, 2, G, R, False, token_norm=True)
+    k2 = k.copy()
+    scale = np.ones(n, np.float32)
+    scale[[3, 40, 77, 100]] = [4.0, 0.5, 2.0, 0.25]
+    k2 *= scale[:, None]
+    b = orc.encode_slice(k2, v, "f32", D, 4, 2, G, R, False, token_norm=True)
+    for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
+        assert np.array_equal(a[key], b[key]), key
+    na = orc.f16_bits_to_f32(a["k_norm"])
+    nb = orc.f16_bits_to_f32(b["k_norm"])
+    assert np.array_equal(nb, na * scale[:a["nq"]])
+
+
+def test_token_norm_attention_on_one_direction(orc):
+    """Keys 2^e_t * u along one direction u: every normalized row is the same,
+    so each channel group is constant (codes 0, zero = the normalized value)
+    and the decoded key is the stored norm times it; attention then equals
+    softmax over sigma_t = |2^e_t u|_norm * (q . u_hat) / sqrt(D) (numpy)."""
+    rng = np.random.default_rng(12)
+    D, G, R, n = 64, 32, 32, 32 * 3 + 32
+    u = orc.f16_bits_to_f32(orc.f32_to_f16_bits(rng.standard_normal(D).astype(np.float32)))
+    e = rng.integers(-3, 4, n)
+    k = (u[None, :] * (2.0 ** e)[:, None]).astype(np.float32)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    c = orc.encode_slice(k, v, "f32", D, 2, 2, G, R, False, token_norm=True)
+    nq = c["nq"]
+    assert nq == 96 and not c["k_codes"].any()
+    nrm = orc.row_norm_f32(u)
+    uh = orc.f16_bits_to_f32(orc.f32_to_f16_bits(u / np.float32(nrm))).astype(np.float64)
+    assert np.array_equal(orc.f16_bits_to_f32(c["k_zero"][0]).astype(np.float64), uh)
+    norms = orc.f16_bits_to_f32(c["k_norm"]).astype(np.float64)
+    kd = np.concatenate([norms[:, None] * uh[None, :], k[nq:].astype(np.float16).astype(np.float64)])
+    vd = np.concatenate([orc.f16_bits_to_f32(c["v_zero"]).repeat(G, 1) + c["v_codes"] *
+                         orc.f16_bits_to_f32(c["v_scale"]).repeat(G, 1), v[nq:].astype(np.float16)]).astype(np.float64)
+    q = rng.standard_normal((3, D))
+    sc = q @ kd.T / np.sqrt(D)
+    w = np.exp(sc - sc.max(1, keepdims=True))
+    ref = w @ vd / w.sum(1, keepdims=True)
+    assert np.max(np.abs(orc.attend_slice(q, c, D, G) - ref)) < 1e-12
+
+
+def test_token_norm_zero_rows_and_reconstruction(orc):
+    rng = np.random.default_rng(13)
+    D, G, R, n = 64, 32, 0, 64
+    k = rng.standard_normal((n, D)).astype(np.float32) * rng.uniform(0.1, 10, (n, 1)).astype(np.float32)
+    k[5] = 0.0
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    c = orc.encode_slice(k, v, "f32", D, 4, 2, G, R, False, token_norm=True)
+    nrm = orc.f16_bits_to_f32(c["k_norm"]).astype(np.float64)
+    assert nrm[5] == 0.0
+    s = orc.f16_bits_to_f32(c["k_scale"]).astype(np.float64).repeat(G, 0)
+    z = orc.f16_bits_to_f32(c["k_zero"]).astype(np.float64).repeat(G, 0)
+    kd = nrm[:, None] * (z + c["k_codes"] * s)
+    assert not kd[5].any()
+    # per element: |k - khat| <= norm * (s / 2 + fp16 rounding of the normalized value) + fp16 rounding of the norm
+    kh = k.astype(np.float16).astype(np.float64)
+    bound = nrm[:, None] * (s / 2 + 2.0 ** -11) + np.abs(kh) * 2.0 ** -10 + 1e-6
+    assert np.all(np.abs(kd - kh) <= bound)
