@@ -39,7 +39,7 @@ def decode_bytes(w, n: int) -> int:
     """Algorithmic bytes of one decode over n cached tokens per sequence."""
     nq = (max(0, n - w.sink - w.R) // w.G) * w.G
     nr = n - nq  # fp16 tokens: the attention sink and the recent window
-    per_quant_token = w.D * (w.kbits + w.vbits) // 8 + 4 * w.D // w.G + 4 * (w.D // w.G)
+    per_quant_token = w.D * (w.kbits + w.vbits) // 8 + 4 * w.D // w.G + 4 * (w.D // w.G) + 2 * int(w.token_norm)
     per_window_token = 4 * w.D  # fp16 K and V
     cache = w.B * w.Hkv * (nq * per_quant_token + nr * per_window_token)
     return cache + w.B * w.Hq * w.D * (in_bytes(w) + 4)
@@ -69,7 +69,8 @@ def cpu_baseline(w, K_host, V_host, q_host, batches, threads: int) -> dict:
     def enc(bh):
         b, h = bh
         return oracle.encode_slice(to_oracle_input(K_host[b][h], w.dtype), to_oracle_input(V_host[b][h], w.dtype),
-                                   w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate, sink=w.sink, hybrid=w.hybrid)
+                                   w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate, sink=w.sink, hybrid=w.hybrid,
+                                   token_norm=w.token_norm)
 
     with ThreadPoolExecutor(threads) as ex:
         encs = list(ex.map(enc, pairs))
@@ -156,6 +157,7 @@ def main() -> int:
     ap.add_argument("--splits", type=int, default=0, help="split count (0: the library's default)")
     ap.add_argument("--sink", type=int, default=0, help="attention-sink tokens kept in fp16 (a multiple of the group size)")
     ap.add_argument("--hybrid", action="store_true", help="per-group symmetric/asymmetric quantizer choice")
+    ap.add_argument("--token-norm", action="store_true", help="key tokens divided by their norm before quantization")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=16)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -181,9 +183,10 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     w = WORKLOADS[args.workload]
-    if args.sink or args.hybrid:
-        w = w.replace(name=w.name + (f"-sink{args.sink}" if args.sink else "") + ("-hybrid" if args.hybrid else ""),
-                      sink=args.sink, hybrid=args.hybrid)
+    if args.sink or args.hybrid or args.token_norm:
+        w = w.replace(name=w.name + (f"-sink{args.sink}" if args.sink else "") + ("-hybrid" if args.hybrid else "")
+                      + ("-tokennorm" if args.token_norm else ""),
+                      sink=args.sink, hybrid=args.hybrid, token_norm=args.token_norm)
     total = args.warmup + args.steps
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -277,7 +280,8 @@ def main() -> int:
         "config": {
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
             "context": w.N, "k_bits": w.kbits, "v_bits": w.vbits, "group": w.G, "residual": w.R,
-            "rotate": w.rotate, "sink": w.sink, "hybrid": w.hybrid, "splits": S, "parallelism": "single-gpu",
+            "rotate": w.rotate, "sink": w.sink, "hybrid": w.hybrid, "token_norm": w.token_norm, "splits": S,
+            "parallelism": "single-gpu",
         },
         "roofline": {
             "kernel": "decode_kernel (split dequant-attention)",

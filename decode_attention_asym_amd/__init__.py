@@ -27,5 +27,5 @@ def config_for(w, max_tokens: int | None = None) -> "Config":
         batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
         max_tokens=max_tokens or w.N, k_bits=w.kbits, v_bits=w.vbits, group_size=w.G,
         residual=w.R, rotate=w.rotate, in_dtype=w.dtype, sink_tokens=getattr(w, "sink", 0),
-        hybrid=getattr(w, "hybrid", False),
+        hybrid=getattr(w, "hybrid", False), token_norm=getattr(w, "token_norm", False),
     )

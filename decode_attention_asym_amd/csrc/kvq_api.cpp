@@ -69,6 +69,7 @@ kvq_status validate(const kvq_config* c) {
   if (c->sink_tokens < 0 || c->sink_tokens > 1024 || c->sink_tokens % c->group_size != 0)
     return fail(KVQ_E_UNSUPPORTED, "sink_tokens %d must be a multiple of group_size in [0, 1024]", c->sink_tokens);
   if (c->hybrid != 0 && c->hybrid != 1) return fail(KVQ_E_ARG, "hybrid must be 0 or 1");
+  if (c->token_norm != 0 && c->token_norm != 1) return fail(KVQ_E_ARG, "token_norm must be 0 or 1");
   if (c->in_dtype < KVQ_F32 || c->in_dtype > KVQ_BF16) return fail(KVQ_E_ARG, "in_dtype %d unknown", c->in_dtype);
   if (!kvq::decode_supported(c->head_dim, c->k_bits, c->v_bits, c->group_size))
     return fail(KVQ_E_UNSUPPORTED, "no kernel for this (head_dim, bits, group) combination");
@@ -77,7 +78,7 @@ kvq_status validate(const kvq_config* c) {
 
 Layout layout_of(const kvq_config* c) {
   return kvq::make_layout(c->batch, c->num_kv_heads, c->head_dim, c->max_tokens, c->k_bits, c->v_bits, c->group_size,
-                          c->residual, c->sink_tokens);
+                          c->residual, c->sink_tokens, c->token_norm);
 }
 
 int max_splits(const kvq_config* c) {
@@ -401,6 +402,52 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
       }
     }
   return ok();
+}
+
+// Key token norms live in each page's norm block, one 64-byte block per chunk.
+static kvq_status key_norms_copy(kvq_cache* h, int32_t b0, int32_t bc, void* out, const void* in, void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = h->cfg;
+  if (!c.token_norm) return fail(KVQ_E_STATE, "the cache has no key token norms (token_norm = 0)");
+  if (b0 < 0 || bc < 0 || b0 + bc > c.batch) return fail(KVQ_E_ARG, "batch range out of bounds");
+  if (!out && !in) return fail(KVQ_E_ARG, "norm array is NULL");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(h, e, "stream synchronize");
+  const Layout& L = h->L;
+  const int G = c.group_size;
+  const int64_t nq = nquant_of(h, h->n), ng = nq / G;
+  std::vector<uint8_t> pages(static_cast<size_t>(ng * L.page_bytes));
+  for (int64_t bi = 0; bi < bc; ++bi)
+    for (int64_t hk = 0; hk < c.num_kv_heads; ++hk) {
+      const int64_t slice = (b0 + bi) * c.num_kv_heads + hk;
+      const int64_t oi = bi * c.num_kv_heads + hk;
+      if (ng == 0) continue;
+      e = hipMemcpy(pages.data(), h->buf + kvq::page_offset(L, slice, 0), pages.size(), hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return device_error(h, e, "key norm copy");
+      for (int64_t t = 0; t < nq; ++t) {
+        uint16_t* kn = reinterpret_cast<uint16_t*>(pages.data() + (t / G) * L.page_bytes + L.off_knorm +
+                                                   ((t % G) / kvq::kChunk) * L.kn_chunk_bytes);
+        const int el = kvq::knorm_elem(static_cast<int>(t % kvq::kChunk));
+        if (out) static_cast<uint16_t*>(out)[oi * nq + t] = kn[el];
+        else kn[el] = static_cast<const uint16_t*>(in)[oi * nq + t];
+      }
+      if (in) {
+        e = hipMemcpy(h->buf + kvq::page_offset(L, slice, 0), pages.data(), pages.size(), hipMemcpyHostToDevice);
+        if (e != hipSuccess) return device_error(h, e, "key norm copy");
+      }
+    }
+  return ok();
+}
+
+kvq_status kvq_export_key_norms(kvq_cache* h, int32_t b0, int32_t bc, void* host_k_norm, void* stream) {
+  if (!host_k_norm) return fail(KVQ_E_ARG, "norm array is NULL");
+  return key_norms_copy(h, b0, bc, host_k_norm, nullptr, stream);
+}
+
+kvq_status kvq_import_key_norms(kvq_cache* h, int32_t b0, int32_t bc, const void* host_k_norm, void* stream) {
+  if (!host_k_norm) return fail(KVQ_E_ARG, "norm array is NULL");
+  return key_norms_copy(h, b0, bc, nullptr, host_k_norm, stream);
 }
 
 kvq_status kvq_import(kvq_cache* h, int64_t n_tokens, int32_t b0, int32_t bc, const void* k_codes,

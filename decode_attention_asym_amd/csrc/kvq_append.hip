@@ -104,6 +104,21 @@ __device__ __forceinline__ uint32_t code_of(float x, float mn, float s, bool sym
   return sym ? quant_code_sym(x, s, c0) : quant_code(x, mn, s, levels);
 }
 
+// L2 norm of a row of D values: squares, pairwise sums (element 2i + element
+// 2i + 1, level by level), correctly rounded square root -- a fixed order, so
+// the result does not depend on how the work is shared.
+template <int D>
+__device__ float row_norm(const float* x) {
+  float t[D / 2];
+#pragma unroll
+  for (int i = 0; i < D / 2; ++i) t[i] = __fadd_rn(__fmul_rn(x[2 * i], x[2 * i]), __fmul_rn(x[2 * i + 1], x[2 * i + 1]));
+#pragma unroll
+  for (int w = D / 2; w > 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) t[i] = __fadd_rn(t[2 * i], t[2 * i + 1]);
+  return sqrtf(t[0]);
+}
+
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // nearest binary32 to 1/sqrt(128)
 constexpr float kInvSqrt64 = 0.125f;
 
@@ -141,6 +156,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   __shared__ float ks[D], kmn[D];
   __shared__ float vs[G * NCG], vmn[G * NCG];
   __shared__ bool ksym[D], vsym[G * NCG];
+  __shared__ float knrm[G];
 
   const Layout& L = a.L;
   const int tid = threadIdx.x;
@@ -177,6 +193,24 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   }
 
   uint8_t* page = a.cache + page_offset(L, slice, g);
+
+  // key token norms: each key row is divided by its norm and rounded to fp16
+  // before the key quantizer; the norm is stored as fp16 (0 for a zero row,
+  // whose normalized values are 0)
+  if (L.token_norm) {
+    for (int i = tid; i < G; i += blockDim.x) {
+      const float nrm = row_norm<D>(kx + i * D);
+      knrm[i] = nrm;
+      uint16_t* kn = reinterpret_cast<uint16_t*>(page + L.off_knorm + (i / kChunk) * L.kn_chunk_bytes);
+      kn[knorm_elem(i % kChunk)] = fp16_bits(nrm);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += blockDim.x) {
+      const float nrm = knrm[idx / D];
+      kx[idx] = nrm == 0.0f ? 0.0f : round_fp16(kx[idx] / nrm);
+    }
+    __syncthreads();
+  }
 
   // 2. parameters: keys per channel over G tokens, values per token over G channels
   const bool hybrid = a.hybrid != 0;

@@ -208,16 +208,22 @@ __device__ __forceinline__ void dma_256(const uint8_t* gbase, uint32_t lane4, ui
 }
 // Outstanding LDS reads are drained before a slot is overwritten.
 __device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// A block of BYTES (a multiple of 4): 1 KiB copies, 256-byte copies, and for
+// a remainder one 4-byte-per-lane copy issued by only the lanes it needs.
 template <int BYTES>
 __device__ __forceinline__ void dma_block(const uint8_t* g, uint32_t lane16, uint32_t lane4, uint32_t lds) {
-  static_assert(BYTES % 256 == 0, "DMA blocks are whole 256-byte units");
+  static_assert(BYTES % 4 == 0, "DMA blocks are whole dwords");
 #pragma unroll
   for (int o = 0; o + 1024 <= BYTES; o += 1024) dma_1k(g + o, lane16, lds + o);
 #pragma unroll
-  for (int o = BYTES / 1024 * 1024; o < BYTES; o += 256) dma_256(g + o, lane4, lds + o);
+  for (int o = BYTES / 1024 * 1024; o + 256 <= BYTES; o += 256) dma_256(g + o, lane4, lds + o);
+  if constexpr (BYTES % 256 != 0) {
+    constexpr int o = BYTES / 256 * 256;
+    if (lane4 < static_cast<uint32_t>(BYTES % 256)) dma_256(g + o, lane4, lds + o);
+  }
 }
 template <int BYTES>
-constexpr int dma_count() { return BYTES / 1024 + (BYTES % 1024) / 256; }
+constexpr int dma_count() { return BYTES / 1024 + (BYTES % 1024) / 256 + (BYTES % 256 != 0 ? 1 : 0); }
 // N copy instructions of 256 bytes each (global [g + 256 k, +256) to LDS
 // [lds + 256 k, +256)): stands in for N copies whose data is not needed.
 template <int N>
@@ -254,14 +260,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Page geometry of one token group (the same numbers as make_layout's,
 // as compile-time constants of the kernel instance).
-template <int D, int KB, int VB, int G>
+template <int D, int KB, int VB, int G, bool TN>
 struct PageShape {
   static constexpr int NCG = D / G, CPG = G / kChunk;
   static constexpr int KC = kChunk * D * KB / 8, VC = kChunk * D * VB / 8;
-  static constexpr int VPB = (kChunk * NCG * 4 + 255) / 256 * 256, KPB = 4 * D;
+  static constexpr int VPB = (kChunk * NCG * 4 + 255) / 256 * 256, KPB = 4 * D, KNB = TN ? kChunk * 2 : 0;
   static constexpr int OFF_KC = 0, OFF_VC = CPG * KC, OFF_KP = OFF_VC + CPG * VC, OFF_VP = OFF_KP + KPB;
-  static constexpr int BYTES = OFF_VP + CPG * VPB;
-  static constexpr int PB = KPB + CPG * VPB;  // the group's parameter block [KP][VP per chunk]
+  static constexpr int OFF_KN = OFF_VP + CPG * VPB;
+  static constexpr int BYTES = OFF_KN + CPG * KNB;
+  // the group's parameter block [KP][VP per chunk][key norms per chunk]
+  static constexpr int PB = KPB + CPG * VPB + CPG * KNB;
 };
 
 // Running-max slack of the online softmax (base-2 units): the accumulators
@@ -307,10 +315,10 @@ __device__ __forceinline__ float replica_sum(float x) {
 // zero-point sums cost NV values per lane instead of 8.  Replica 0 gathers
 // the PV weights of the other replicas by DPP row rotation and owns the
 // output; the other replicas' PV columns are never read.
-template <int D, int KB, int VB, int G, int GQC>
+template <int D, int KB, int VB, int G, int GQC, bool TN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
 void decode_kernel(DecodeArgs a) {
-  using PS = PageShape<D, KB, VB, G>;
+  using PS = PageShape<D, KB, VB, G, TN>;
   constexpr int NKB = D / 32, NMT = D / 16, NCG = PS::NCG, CPG = PS::CPG;
   constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4;
   constexpr int R = 16 / GQC, NV = 8 / R, NPR = NV / 2;  // replicas, values and value pairs per lane
@@ -517,9 +525,10 @@ void decode_kernel(DecodeArgs a) {
     // exponent offsets per value pair: exp2(score - m - log2(mult)) is p / mult,
     // the weight the PV operand needs
     float bmc[NPR];
+    // (with key token norms the bias is inside each score, so it is left out)
     auto set_bmc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int pp = 0; pp < NPR; ++pp) bmc[pp] = (cb - m) - vmlog[pp];
+      for (int pp = 0; pp < NPR; ++pp) bmc[pp] = ((TN ? 0.0f : cb) - m) - vmlog[pp];
     };
 
     auto process = [&](const uint8_t* sl, const uint8_t* pbk, int ch, auto&& refill) __attribute__((always_inline)) {
@@ -558,7 +567,7 @@ void decode_kernel(DecodeArgs a) {
         cb = combine(cbt[0]);
         set_bmc();
       }
-      uint32_t kw[KW], vw[VW], vp[VPL];
+      uint32_t kw[KW], vw[VW], vp[VPL], kn[TN ? NPR : 1];
       if constexpr (KW >= 4) {
 #pragma unroll
         for (int v = 0; v < KW / 4; ++v) {
@@ -589,6 +598,19 @@ void decode_kernel(DecodeArgs a) {
         const u32x2 x = *reinterpret_cast<const u32x2*>(pbk + ch * VPB + vp_off);
         vp[0] = x[0]; vp[1] = x[1];
       }
+      if constexpr (TN) {
+        // this lane's token norms: fp16 pairs of its token pairs
+        const uint8_t* knp = pbk + KPB + CPG * VPB + ch * PS::KNB + (j * 4 + NPR * rp) * 4;
+        if constexpr (NPR == 4) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(knp);
+          kn[0] = x[0]; kn[1] = x[1]; kn[2] = x[2]; kn[3] = x[3];
+        } else if constexpr (NPR == 2) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(knp);
+          kn[0] = x[0]; kn[1] = x[1];
+        } else {
+          kn[0] = *reinterpret_cast<const uint32_t*>(knp);
+        }
+      }
       // QK^T: two 16-token tiles; C = 2^-24 * (score - bias)
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -613,10 +635,17 @@ void decode_kernel(DecodeArgs a) {
       // online softmax over the head's 32 chunk scores (NV per lane): a lane
       // whose own maximum passes the head's slack bound calls for a rescale;
       // only then is the per-head maximum reduced over replicas and lane groups
-      float tmax = u[0];
+      // with key token norms each score is norm * (q . khat_normalized)
+      float sc[NV];
+      if constexpr (TN) {
 #pragma unroll
-      for (int k = 1; k < NV; ++k) tmax = fmax2(tmax, u[k]);
-      const float lmax = __builtin_fmaf(tmax, kTwo24, cb);
+        for (int k = 0; k < NV; ++k)
+          sc[k] = __builtin_fmaf(u[k], kTwo24, cb) * ((k & 1) ? h2f_hi(kn[k >> 1]) : h2f_lo(kn[k >> 1]));
+      }
+      float tmax = TN ? sc[0] : u[0];
+#pragma unroll
+      for (int k = 1; k < NV; ++k) tmax = fmax2(tmax, TN ? sc[k] : u[k]);
+      const float lmax = TN ? tmax : __builtin_fmaf(tmax, kTwo24, cb);
       if (__builtin_amdgcn_ballot_w64(lmax > mslack)) {
         rescale(fmax2(m, wave_max_j(replica_max<R>(lmax))));
         set_bmc();
@@ -625,7 +654,7 @@ void decode_kernel(DecodeArgs a) {
       float pm[NV];
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        pm[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(u[k], kTwo24, bmc[k >> 1]));
+        pm[k] = __builtin_amdgcn_exp2f(TN ? sc[k] + bmc[k >> 1] : __builtin_fmaf(u[k], kTwo24, bmc[k >> 1]));
         lsum = __builtin_fmaf(pm[k], vmult[k >> 1], lsum);
       }
       // PV weights p * value scale / mult (one fp16 part: its rounding is far
@@ -871,17 +900,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   }
 }
 
-template <int D, int KB, int VB, int G>
-hipError_t decode_t(const DecodeArgs& a, hipStream_t s) {
+template <int D, int KB, int VB, int G, bool TN>
+hipError_t decode_tn(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(a.L.slices * a.splits));
   const size_t lds = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
   if (a.gqa <= 4)
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 4>), grid, dim3(kLanes), lds, s, a);
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 4, TN>), grid, dim3(kLanes), lds, s, a);
   else if (a.gqa <= 8)
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 8>), grid, dim3(kLanes), lds, s, a);
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 8, TN>), grid, dim3(kLanes), lds, s, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 16>), grid, dim3(kLanes), lds, s, a);
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 16, TN>), grid, dim3(kLanes), lds, s, a);
   return hipGetLastError();
+}
+template <int D, int KB, int VB, int G>
+hipError_t decode_t(const DecodeArgs& a, hipStream_t s) {
+  return a.L.token_norm ? decode_tn<D, KB, VB, G, true>(a, s) : decode_tn<D, KB, VB, G, false>(a, s);
 }
 template <int D, int KB, int VB>
 hipError_t decode_g(const DecodeArgs& a, hipStream_t s) {

@@ -54,6 +54,7 @@ constexpr int kLanes = 64;
 struct Layout {
   int D, kbits, vbits, G, R;
   int S0;                       // attention-sink tokens kept in fp16 (a multiple of G and of 32)
+  int token_norm;               // 1: quantized key tokens carry an fp16 norm
   int sink_chunks;              // S0 / 32
   int nkb, nmt, ncg;            // D/32 key k-blocks, D/16 value M-tiles, D/G value groups
   int chunks_per_group;         // G / 32
@@ -62,7 +63,8 @@ struct Layout {
   int64_t vc_chunk_bytes;
   int64_t vp_chunk_bytes;       // value scale/zero bytes of one chunk
   int64_t kp_bytes;             // key scale + zero bytes of one group
-  int64_t off_kcodes, off_kparams, off_vcodes, off_vparams, page_bytes;
+  int64_t kn_chunk_bytes;       // key token norms of one chunk (64, or 0 without token norms)
+  int64_t off_kcodes, off_kparams, off_vcodes, off_vparams, off_knorm, page_bytes;
   int64_t pages;                // pages (token groups) per slice
   int cap;                      // window ring slots per slice (R + G)
   int ring_chunks;              // cap / 32
@@ -74,10 +76,12 @@ struct Layout {
 
 KVQ_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int vbits, int G, int R, int S0 = 0) {
+inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int vbits, int G, int R, int S0 = 0,
+                          int token_norm = 0) {
   Layout L{};
   L.D = D; L.kbits = kbits; L.vbits = vbits; L.G = G; L.R = R;
   L.S0 = S0; L.sink_chunks = S0 / kChunk;
+  L.token_norm = token_norm;
   L.nkb = D / 32; L.nmt = D / 16; L.ncg = D / G;
   L.chunks_per_group = G / kChunk;
   L.kw = 2 * L.nkb * kbits / 4;            // 4-bit: one dword per (mt, kb); 2-bit: half of that
@@ -86,13 +90,16 @@ inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int 
   L.vc_chunk_bytes = (int64_t)kLanes * L.vw * 4;
   L.vp_chunk_bytes = align_up((int64_t)kChunk * L.ncg * 4, 256);  // whole 256-byte DMA blocks
   L.kp_bytes = (int64_t)D * 4;
+  L.kn_chunk_bytes = token_norm ? (int64_t)kChunk * 2 : 0;
   // page: [key codes per chunk][value codes per chunk][key scale, zero rows]
-  // [value params per chunk]; the parameters are one contiguous block
+  // [value params per chunk][key token norms per chunk]; the parameters are
+  // one contiguous block
   L.off_kcodes = 0;
   L.off_vcodes = L.off_kcodes + L.chunks_per_group * L.kc_chunk_bytes;
   L.off_kparams = L.off_vcodes + L.chunks_per_group * L.vc_chunk_bytes;
   L.off_vparams = L.off_kparams + L.kp_bytes;
-  L.page_bytes = L.off_vparams + L.chunks_per_group * L.vp_chunk_bytes;
+  L.off_knorm = L.off_vparams + L.chunks_per_group * L.vp_chunk_bytes;
+  L.page_bytes = L.off_knorm + L.chunks_per_group * L.kn_chunk_bytes;
   int64_t over = (int64_t)max_tokens - S0 - R;
   L.pages = over > 0 ? over / G : 0;
   L.cap = R + G;
@@ -170,6 +177,14 @@ KVQ_HD int vparam_scale_elem(const Layout& L, int t, int cg) {
   return (((j * 4 + (e >> 1)) * L.ncg + cg) * 2) * 2 + (e & 1);
 }
 KVQ_HD int vparam_zero_elem(const Layout& L, int t, int cg) { return vparam_scale_elem(L, t, cg) + 2; }
+
+// fp16 element index, inside a chunk's key-norm block, of token t's norm:
+// [j][pair i][e & 1] (the same token pairs as the value parameters).
+KVQ_HD int knorm_elem(int t) {
+  int j, e;
+  tau_inv(t, &j, &e);
+  return (j * 4 + (e >> 1)) * 2 + (e & 1);
+}
 
 // Byte offsets inside a ring chunk of the fp16 window copy of token t, channel c.
 // Keys are stored as the QK A operand, values as the PV A operand.

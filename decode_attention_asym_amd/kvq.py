@@ -37,6 +37,7 @@ class kvq_config(ctypes.Structure):
         ("in_dtype", ctypes.c_int32),
         ("sink_tokens", ctypes.c_int32),
         ("hybrid", ctypes.c_int32),
+        ("token_norm", ctypes.c_int32),
     ]
 
 
@@ -58,6 +59,8 @@ SIGNATURES = {
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_export": (ctypes.c_int, [_P, _I32, _I32] + [_P] * 8 + [_P]),
     "kvq_import": (ctypes.c_int, [_P, _I64, _I32, _I32] + [_P] * 8 + [_P]),
+    "kvq_export_key_norms": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
+    "kvq_import_key_norms": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
 }
 
 
@@ -105,12 +108,13 @@ class Config:
     in_dtype: str = "bf16"
     sink_tokens: int = 0
     hybrid: bool = False
+    token_norm: bool = False
 
     def c(self) -> kvq_config:
         return kvq_config(
             ctypes.sizeof(kvq_config), self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
             self.max_tokens, self.k_bits, self.v_bits, self.group_size, self.residual, int(bool(self.rotate)),
-            DTYPES[self.in_dtype], self.sink_tokens, int(bool(self.hybrid)),
+            DTYPES[self.in_dtype], self.sink_tokens, int(bool(self.hybrid)), int(bool(self.token_norm)),
         )
 
 
@@ -235,6 +239,10 @@ class KVQCache:
         keys = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")
         check(lib.kvq_export(self.h, batch_begin, bc, *(out[k].ctypes.data for k in keys), _stream(stream)),
               "kvq_export")
+        if c.token_norm:
+            out["k_norm"] = np.zeros((bc, H, nq), np.uint16)
+            check(lib.kvq_export_key_norms(self.h, batch_begin, bc, out["k_norm"].ctypes.data, _stream(stream)),
+                  "kvq_export_key_norms")
         out["nq"], out["n"] = nq, n
         return out
 
@@ -246,3 +254,7 @@ class KVQCache:
         bc = arrs[0].shape[0]
         check(lib.kvq_import(self.h, n_tokens, batch_begin, bc, *(a.ctypes.data for a in arrs), _stream(stream)),
               "kvq_import")
+        if self.cfg.token_norm:
+            kn = np.ascontiguousarray(arrays["k_norm"], dtype=np.uint16)
+            check(lib.kvq_import_key_norms(self.h, batch_begin, bc, kn.ctypes.data, _stream(stream)),
+                  "kvq_import_key_norms")

@@ -78,6 +78,10 @@ typedef struct {
   int32_t hybrid;       /* 0 or 1: per group, keep a symmetric quantizer (scale max|x| / c0,
                            c0 = 2^(b-1) - 1, zero = -c0 * scale) instead of the asymmetric one
                            when its largest reconstruction error on the group is smaller */
+  int32_t token_norm;   /* 0 or 1: divide each quantized key token by its L2 norm (binary32,
+                           pairwise summation tree, correctly rounded sqrt) before quantizing,
+                           keep the norm as fp16 and multiply it back into the score; with
+                           rotate = 1 this is the rotate-then-scale key pipeline */
 } kvq_config;
 
 /* Device bytes the cache buffer must hold for `cfg`, or 0 if `cfg` is
@@ -156,6 +160,13 @@ kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials,
  * (the most kvq_workspace_bytes ever provides for), else KVQ_E_ARG. */
 kvq_status kvq_merge_partials(const float* partials, float* out, int32_t rows, int32_t splits, int32_t head_dim,
                               void* stream);
+
+/* Key token norms (cfg.token_norm = 1 only, else KVQ_E_STATE), as fp16 bit
+ * patterns [bc][H_kv][n_q] for sequences [b0, b0 + bc): export copies them
+ * out (synchronizes `stream`), import writes them for the n_q quantized
+ * tokens of a cache filled by kvq_import (call it after kvq_import). */
+kvq_status kvq_export_key_norms(kvq_cache* cache, int32_t b0, int32_t bc, void* host_k_norm, void* stream);
+kvq_status kvq_import_key_norms(kvq_cache* cache, int32_t b0, int32_t bc, const void* host_k_norm, void* stream);
 
 /* Split count kvq_decode_attn would use for the current token count. */
 int32_t kvq_default_splits(const kvq_cache* cache);

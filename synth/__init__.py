@@ -50,6 +50,7 @@ class Workload:
     idx: int = 0
     sink: int = 0            # attention-sink tokens kept in fp16
     hybrid: bool = False     # per-group symmetric/asymmetric quantizer choice
+    token_norm: bool = False  # key tokens divided by their norm before quantization
 
     @property
     def gqa(self) -> int:

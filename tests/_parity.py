@@ -26,7 +26,7 @@ def oracle_encode_slices(w, K, V, pairs):
         k = to_oracle_input(K[b, h], w.dtype)
         v = to_oracle_input(V[b, h], w.dtype)
         return oracle.encode_slice(k, v, w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate, sink=w.sink,
-                                   hybrid=w.hybrid)
+                                   hybrid=w.hybrid, token_norm=w.token_norm)
 
     with ThreadPoolExecutor(THREADS) as ex:
         return dict(zip(pairs, ex.map(enc, pairs)))
@@ -43,7 +43,8 @@ def assert_export_matches(w, exp, b0, encs):
             if not np.array_equal(got, ref):
                 bad = np.argwhere(got != ref)
                 raise AssertionError(f"{key} mismatch at slice ({b},{h}): {len(bad)} bytes, first {bad[:5].tolist()}")
-        for key in ("k_scale", "k_zero", "v_scale", "v_zero", "k_resid", "v_resid"):
+        keys = ("k_scale", "k_zero", "v_scale", "v_zero", "k_resid", "v_resid") + (("k_norm",) if "k_norm" in enc else ())
+        for key in keys:
             got = exp[key][bi, h]
             if not np.array_equal(got, enc[key]):
                 bad = np.argwhere(got != enc[key])
@@ -59,6 +60,7 @@ def canonical_slice(exp, bi, h, D, kbits, vbits):
         "v_scale": exp["v_scale"][bi, h], "v_zero": exp["v_zero"][bi, h],
         "k_resid": exp["k_resid"][bi, h], "v_resid": exp["v_resid"][bi, h],
         "nq": exp["nq"], "n": exp["n"],
+        "k_norm": exp["k_norm"][bi, h] if "k_norm" in exp else None,
     }
 
 

@@ -101,6 +101,13 @@ def test_host_validation_without_device_work():
     finally:
         assert lib.kvq_destroy(h) == kvq.KVQ_OK
     assert lib.kvq_destroy(None) == kvq.KVQ_OK
+    # key norms exist only with token_norm
+    h2 = ctypes.c_void_p()
+    assert lib.kvq_create(ctypes.byref(cc), fake, need, ctypes.byref(h2)) == kvq.KVQ_OK
+    assert lib.kvq_export_key_norms(h2, 0, 1, fake, None) == kvq.KVQ_E_STATE
+    assert lib.kvq_import_key_norms(h2, 0, 1, fake, None) == kvq.KVQ_E_STATE
+    assert lib.kvq_export_key_norms(h2, 0, 1, None, None) == kvq.KVQ_E_ARG
+    assert lib.kvq_destroy(h2) == kvq.KVQ_OK
     # merge: argument checks before any launch
     assert lib.kvq_merge_partials(fake, fake, 4, 257, 128, None) == kvq.KVQ_E_ARG
     assert lib.kvq_merge_partials(fake, fake, 4, 0, 128, None) == kvq.KVQ_E_ARG
@@ -117,3 +124,14 @@ def test_workspace_bounds_split_request():
         c = _cfg(batch=1 if w == "tiny" else 64, num_kv_heads=8, num_q_heads=32)
         ws = kvq.workspace_bytes(c)
         assert ws > 0 and ws % 16 == 0
+
+
+def test_token_norm_adds_two_bytes_per_quantized_token():
+    import decode_attention_asym_amd as kvq
+
+    for G, R, D in ((64, 128, 128), (32, 32, 64)):
+        a = kvq.cache_bytes(_cfg(group_size=G, residual=R, head_dim=D, max_tokens=10000))
+        b = kvq.cache_bytes(_cfg(group_size=G, residual=R, head_dim=D, max_tokens=10000, token_norm=True))
+        slices = 2 * 2
+        pages = (10000 - R) // G
+        assert abs((b - a) - slices * pages * G * 2) <= 256

@@ -76,6 +76,11 @@ SMALL = [
     WORKLOADS[1].replace(name="sink-no-flush-yet", B=2, N=64 + 128 + 31, R=128, sink=64),
     WORKLOADS[1].replace(name="sink-first-flush", B=2, N=64 + 128 + 32, R=128, sink=64),
     WORKLOADS[4].replace(name="mha-fwht-sink-hybrid", B=1, Hq=8, Hkv=8, N=1024 + 13, sink=32, hybrid=True),
+    # key token norms after the rotation (rotate-then-scale keys), with and without rotation
+    WORKLOADS[4].replace(name="mha-fwht-tokennorm", B=2, Hq=8, Hkv=8, N=2048 + 13, token_norm=True),
+    WORKLOADS[2].replace(name="k4v2-g64-rot-tokennorm", B=2, N=3000 + 21, rotate=True, token_norm=True),
+    WORKLOADS[3].replace(name="gqa8-tokennorm-sink-hybrid", B=1, N=1500 + 7, token_norm=True, sink=64, hybrid=True),
+    WORKLOADS[0].replace(name="d64-tokennorm-k4v4", B=2, Hq=4, Hkv=2, N=700 + 1, kbits=4, vbits=4, token_norm=True),
 ]
 
 
@@ -118,8 +123,8 @@ def _split_ranges(n, ng, G, S_req, sink=0):
     return S, ranges
 
 
-@pytest.mark.parametrize("sink", [0, 64])
-def test_decode_partials_per_split_match_oracle(sink):
+@pytest.mark.parametrize("sink,tn", [(0, False), (64, False), (0, True)])
+def test_decode_partials_per_split_match_oracle(sink, tn):
     """kvq_decode_partials: every split's (m, l, o) against the oracle's partial
     attention over the same tokens; kvq_merge_partials of them equals
     kvq_decode_attn_splits with the same split count."""
@@ -127,7 +132,8 @@ def test_decode_partials_per_split_match_oracle(sink):
     import oracle
     from _parity import canonical_slice, oracle_queries
 
-    w = WORKLOADS[2].replace(name=f"partials-sink{sink}", B=2, Hq=8, Hkv=2, N=sink + 64 * 9 + 128 + 21, sink=sink)
+    w = WORKLOADS[2].replace(name=f"partials-sink{sink}-tn{int(tn)}", B=2, Hq=8, Hkv=2, N=sink + 64 * 9 + 128 + 21,
+                             sink=sink, token_norm=tn)
     syn, K, V, q, cache = _run_prefill(w)
     S_req = 4
     partials, S = cache.decode_partials(q, splits=S_req)
@@ -219,10 +225,10 @@ def test_repeated_decodes_with_changing_split_counts():
         assert err <= TOL_REL_L2, (S, err)
 
 
-@pytest.mark.parametrize("sink,hybrid", [(0, False), (64, True)])
-def test_stepwise_append_equals_prefill(sink, hybrid):
+@pytest.mark.parametrize("sink,hybrid,tn", [(0, False, False), (64, True, False), (64, True, True)])
+def test_stepwise_append_equals_prefill(sink, hybrid, tn):
     kvq = _lib()
-    w = WORKLOADS[2].replace(name="stepwise", B=2, Hkv=2, Hq=8, N=700, sink=sink, hybrid=hybrid)
+    w = WORKLOADS[2].replace(name="stepwise", B=2, Hkv=2, Hq=8, N=700, sink=sink, hybrid=hybrid, token_norm=tn)
     syn = Synth(w, "cuda")
     K, V = syn.kv_all()
     a = kvq.KVQCache(kvq.config_for(w))
@@ -236,16 +242,18 @@ def test_stepwise_append_equals_prefill(sink, hybrid):
         t += s
     assert a.num_tokens == b.num_tokens == w.N
     ea, eb = a.export(), b.export()
-    for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid"):
+    for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid") + (
+            ("k_norm",) if tn else ()):
         assert np.array_equal(ea[key], eb[key]), key
     encs = oracle_encode_slices(w, K, V, [(bb, h) for bb in range(w.B) for h in range(w.Hkv)])
     assert_export_matches(w, ea, 0, encs)
 
 
-def test_import_then_decode_matches_oracle():
+@pytest.mark.parametrize("tn", [False, True])
+def test_import_then_decode_matches_oracle(tn):
     """Decode on a cache the oracle encoded (imported), independent of the GPU quantizer."""
     kvq = _lib()
-    w = WORKLOADS[1].replace(name="import", B=2, N=2000 + 5)
+    w = WORKLOADS[1].replace(name=f"import-tn{int(tn)}", B=2, N=2000 + 5, token_norm=tn, rotate=tn)
     syn = Synth(w, "cpu")
     K, V = syn.kv_all()
     encs = oracle_encode_slices(w, K, V, [(b, h) for b in range(w.B) for h in range(w.Hkv)])
@@ -255,7 +263,7 @@ def test_import_then_decode_matches_oracle():
     for key, bits in (("k_codes", w.kbits), ("v_codes", w.vbits)):
         arrays[key] = np.stack([np.stack([oracle.pack_codes(encs[(b, h)][key], bits) for h in range(w.Hkv)])
                                 for b in range(w.B)])
-    for key in ("k_scale", "k_zero", "v_scale", "v_zero", "k_resid", "v_resid"):
+    for key in ("k_scale", "k_zero", "v_scale", "v_zero", "k_resid", "v_resid") + (("k_norm",) if tn else ()):
         arrays[key] = np.stack([np.stack([encs[(b, h)][key] for h in range(w.Hkv)]) for b in range(w.B)])
     cache = kvq.KVQCache(kvq.config_for(w))
     cache.import_(arrays, w.N)
