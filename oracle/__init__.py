@@ -66,7 +66,9 @@ def _declare(L):
     L.orc_encode_slice.restype = i64
     L.orc_encode_slice.argtypes = [P, P, i32, i64, i32, i32, i32, i32, i32, i32] + [P] * 8
     L.orc_encode_slice_ext.restype = i64
-    L.orc_encode_slice_ext.argtypes = [P, P, i32, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32] + [P] * 11
+    L.orc_encode_slice_ext.argtypes = [P, P, i32, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32] + [P] * 13
+    L.orc_adaptive_group_bits.restype = i64
+    L.orc_adaptive_group_bits.argtypes = [i32, i32, i32, i32, i32, P] + [i32] * 6 + [P, P]
     L.orc_row_norm_f32.restype = ctypes.c_float
     L.orc_row_norm_f32.argtypes = [P, i32]
     L.orc_pack_codes.restype = None
@@ -194,15 +196,31 @@ def row_norm_f32(x) -> float:
     return float(lib().orc_row_norm_f32(_p(x), x.size))
 
 
+def adaptive_group_bits(G: int, R: int, sink: int, delta: int, calls, low, mid, high):
+    """Per-group (key bits, value bits) of a position-adaptive slice built by
+    appends of `calls` tokens; low/mid/high are (key, value) bit pairs."""
+    calls = np.ascontiguousarray(calls, dtype=np.int64)
+    n = int(calls.sum())
+    cap = max(1, n // G + 1)
+    kb = np.zeros(cap, np.uint8)
+    vb = np.zeros(cap, np.uint8)
+    ng = lib().orc_adaptive_group_bits(G, R, sink, delta, calls.size, _p(calls), low[0], low[1], mid[0], mid[1],
+                                       high[0], high[1], _p(kb), _p(vb))
+    if ng < 0:
+        raise ValueError("orc_adaptive_group_bits rejected its arguments")
+    return kb[:ng].copy(), vb[:ng].copy()
+
+
 def encode_slice(k, v, dtype: str, D: int, kbits: int, vbits: int, G: int, R: int, rotate: bool,
-                 sink: int = 0, hybrid: bool = False, token_norm: bool = False):
+                 sink: int = 0, hybrid: bool = False, token_norm: bool = False, group_bits=None):
     """Encode one (batch, kv-head) slice.  k, v: [n][D] in the input dtype
     (float32 values for "f32", uint16 bit patterns for "f16"/"bf16").
 
     Returns a dict of canonical arrays (codes unpacked, one per uint16); the
     fp16 tokens (an attention-sink window of `sink` tokens, then the recent
     window) are k_resid / v_resid; k_sym / v_sym mark symmetric groups;
-    k_norm (fp16 bits, one per quantized token) is present with token_norm."""
+    k_norm (fp16 bits, one per quantized token) is present with token_norm.
+    group_bits = (key bits, value bits) arrays give per-group widths."""
     np_dt = np.float32 if dtype == "f32" else np.uint16
     k = np.ascontiguousarray(k, dtype=np_dt).reshape(-1, D)
     v = np.ascontiguousarray(v, dtype=np_dt).reshape(-1, D)
@@ -222,12 +240,17 @@ def encode_slice(k, v, dtype: str, D: int, kbits: int, vbits: int, G: int, R: in
         "v_sym": np.zeros((nq, D // G), np.uint8),
     }
     k_norm = np.zeros(max(nq, 1), np.uint16)
+    gkb = gvb = None
+    if group_bits is not None:
+        gkb = np.ascontiguousarray(group_bits[0], dtype=np.uint8)
+        gvb = np.ascontiguousarray(group_bits[1], dtype=np.uint8)
+        assert gkb.size >= nq // G and gvb.size >= nq // G
     r = lib().orc_encode_slice_ext(
         _p(k), _p(v), DTYPE_CODE[dtype], n, D, kbits, vbits, G, R, int(bool(rotate)), int(sink), int(bool(hybrid)),
         int(bool(token_norm)),
         *(_p(out[key]) for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid",
                                    "k_sym", "v_sym")),
-        _p(k_norm),
+        _p(k_norm), None if gkb is None else _p(gkb), None if gvb is None else _p(gvb),
     )
     if token_norm:
         out["k_norm"] = k_norm[:nq].copy()

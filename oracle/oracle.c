@@ -43,6 +43,14 @@
  *    here the norm is that of the fp16 (rotated) token row, summed as a fixed
  *    pairwise tree in binary32 with a correctly rounded square root, the
  *    normalized values are rounded to fp16, and a zero row keeps norm 0.
+ *  - Position-adaptive bit widths ("Asymmetric Key-Value Quantization ...",
+ *    section 3.2: high bits for the most recent Delta tokens, low bits for the
+ *    first Delta, middle bits between; section 7 notes that the method needs
+ *    token positions when it quantizes).  Here a group's bits are fixed when
+ *    it is quantized, from the sequence length n after the append that
+ *    quantizes it: recent if its last token is among the last Delta of n,
+ *    otherwise early if its last token is among the first Delta, otherwise
+ *    middle (the printed cases, recent taking precedence where they overlap).
  *  - Bits-per-element accounting: "Asymmetric Key-Value Quantization ...",
  *    section 3.1 (average of key and value bit widths) and section 3.4
  *    (combined compression table); here the per-group fp16 scale and zero
@@ -65,7 +73,7 @@ int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n,
                              int token_norm, uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
                              uint16_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
                              uint16_t* k_resid, uint16_t* v_resid, uint8_t* k_sym, uint8_t* v_sym,
-                             uint16_t* k_norm);
+                             uint16_t* k_norm, const uint8_t* group_kbits, const uint8_t* group_vbits);
 double orc_bits_per_element_sink(int64_t n, int kbits, int vbits, int G, int R, int S0,
                                  double overhead_bits);
 
@@ -303,6 +311,33 @@ int64_t orc_num_quantized_sink(int64_t n, int G, int R, int S0) {
   return n > S0 ? orc_num_quantized(n - S0, G, R) : 0;
 }
 
+/* Position-adaptive bit widths of the groups of a slice built by appends of
+ * calls[0], calls[1], ... tokens: group g (tokens S0 + gG .. S0 + gG + G - 1,
+ * 1-based positions p0 + 1 .. p1 with p1 = S0 + gG + G) is quantized by the
+ * first append after which it is quantized, with n = the length after that
+ * append; it is recent if p1 > n - delta, else early if p1 <= delta, else
+ * middle.  Writes the (key, value) bits of its region for each of the
+ * groups quantized after all calls; returns that count or -1. */
+int64_t orc_adaptive_group_bits(int G, int R, int S0, int delta, int ncalls, const int64_t* calls,
+                                int kb_low, int vb_low, int kb_mid, int vb_mid, int kb_high, int vb_high,
+                                uint8_t* group_kbits, uint8_t* group_vbits) {
+  if (G <= 0 || R < 0 || S0 < 0 || delta < 0 || ncalls < 0) return -1;
+  int64_t n = 0, done = 0;
+  for (int c = 0; c < ncalls; ++c) {
+    if (calls[c] < 0) return -1;
+    n += calls[c];
+    int64_t ng = orc_num_quantized_sink(n, G, R, S0) / G;
+    for (int64_t g = done; g < ng; ++g) {
+      int64_t p1 = (int64_t)S0 + g * G + G;
+      int region = p1 > n - delta ? 2 : (p1 <= delta ? 0 : 1);
+      group_kbits[g] = (uint8_t)(region == 2 ? kb_high : region == 0 ? kb_low : kb_mid);
+      group_vbits[g] = (uint8_t)(region == 2 ? vb_high : region == 0 ? vb_low : vb_mid);
+    }
+    done = ng;
+  }
+  return done;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Encode one (batch, kv-head) slice of n tokens into canonical arrays.      */
 /* ------------------------------------------------------------------------ */
@@ -321,7 +356,7 @@ int64_t orc_encode_slice(const void* k, const void* v, int dtype, int64_t n, int
                          uint16_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
                          uint16_t* k_resid, uint16_t* v_resid) {
   return orc_encode_slice_ext(k, v, dtype, n, D, kbits, vbits, G, R, rotate, 0, 0, 0, k_codes, k_scale,
-                              k_zero, v_codes, v_scale, v_zero, k_resid, v_resid, NULL, NULL, NULL);
+                              k_zero, v_codes, v_scale, v_zero, k_resid, v_resid, NULL, NULL, NULL, NULL, NULL);
 }
 
 /* As orc_encode_slice, with an attention-sink window of S0 tokens (0: none)
@@ -333,13 +368,15 @@ int64_t orc_encode_slice(const void* k, const void* v, int dtype, int64_t n, int
  * took the symmetric quantizer.  With `token_norm`, each quantized key token
  * is divided by its norm (orc_row_norm_f32 of its fp16 row) and rounded to
  * fp16 before the key quantizer, and k_norm [nq] receives the norms as fp16
- * bits (0 for a zero row, whose normalized values are 0). */
+ * bits (0 for a zero row, whose normalized values are 0).  group_kbits /
+ * group_vbits [nq/G] (may be NULL) give per-group bit widths in place of
+ * kbits / vbits (position-adaptive caches, see orc_adaptive_group_bits). */
 int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n, int D,
                              int kbits, int vbits, int G, int R, int rotate, int S0, int hybrid,
                              int token_norm, uint16_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
                              uint16_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
                              uint16_t* k_resid, uint16_t* v_resid, uint8_t* k_sym, uint8_t* v_sym,
-                             uint16_t* k_norm) {
+                             uint16_t* k_norm, const uint8_t* group_kbits, const uint8_t* group_vbits) {
   if (n < 0 || D <= 0 || G <= 0 || R < 0 || D % G != 0 || S0 < 0) return -1;
   if (kbits < 1 || kbits > 16 || vbits < 1 || vbits > 16) return -1;
   if (hybrid && (kbits < 2 || vbits < 2)) return -1;
@@ -382,12 +419,13 @@ int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n,
    * quantized index q) */
   for (int64_t g = 0; g < nq / G; ++g)
     for (int c = 0; c < D; ++c) {
+      const int kb = group_kbits ? group_kbits[g] : kbits;
       for (int i = 0; i < G; ++i) grp[i] = kq[(g * G + i) * D + c];
       int sym = 0;
       if (hybrid)
-        sym = orc_quantize_group_hybrid(grp, G, kbits, cod, &k_scale[g * D + c], &k_zero[g * D + c]);
+        sym = orc_quantize_group_hybrid(grp, G, kb, cod, &k_scale[g * D + c], &k_zero[g * D + c]);
       else
-        orc_quantize_group(grp, G, kbits, cod, NULL, NULL, &k_scale[g * D + c], &k_zero[g * D + c]);
+        orc_quantize_group(grp, G, kb, cod, NULL, NULL, &k_scale[g * D + c], &k_zero[g * D + c]);
       if (k_sym) k_sym[g * D + c] = (uint8_t)sym;
       for (int i = 0; i < G; ++i) k_codes[(g * G + i) * D + c] = cod[i];
     }
@@ -396,12 +434,13 @@ int64_t orc_encode_slice_ext(const void* k, const void* v, int dtype, int64_t n,
   int ng = D / G;
   for (int64_t t = 0; t < nq; ++t)
     for (int j = 0; j < ng; ++j) {
+      const int vb = group_vbits ? group_vbits[t / G] : vbits;
       for (int i = 0; i < G; ++i) grp[i] = vt[(s0 + t) * D + j * G + i];
       int sym = 0;
       if (hybrid)
-        sym = orc_quantize_group_hybrid(grp, G, vbits, cod, &v_scale[t * ng + j], &v_zero[t * ng + j]);
+        sym = orc_quantize_group_hybrid(grp, G, vb, cod, &v_scale[t * ng + j], &v_zero[t * ng + j]);
       else
-        orc_quantize_group(grp, G, vbits, cod, NULL, NULL, &v_scale[t * ng + j], &v_zero[t * ng + j]);
+        orc_quantize_group(grp, G, vb, cod, NULL, NULL, &v_scale[t * ng + j], &v_zero[t * ng + j]);
       if (v_sym) v_sym[t * ng + j] = (uint8_t)sym;
       for (int i = 0; i < G; ++i) v_codes[t * D + j * G + i] = cod[i];
     }

@@ -647,3 +647,67 @@ def test_token_norm_zero_rows_and_reconstruction(orc):
     kh = k.astype(np.float16).astype(np.float64)
     bound = nrm[:, None] * (s / 2 + 2.0 ** -11) + np.abs(kh) * 2.0 ** -10 + 1e-6
     assert np.all(np.abs(kd - kh) <= bound)
+
+
+# ------------------------------------------------- position-adaptive bit widths
+LOW, MID, HIGH = (2, 2), (4, 2), (4, 4)
+
+
+def test_adaptive_regions_of_a_prefill_closed_form(orc):
+    """Prefill of 8192 tokens, delta 1024, G 64, R 128: 126 groups; group g ends
+    at 1-based position 64 g + 64.  Early (<= 1024): g < 16; recent (> 8192 -
+    1024 = 7168): g >= 112; middle in between."""
+    kb, vb = orc.adaptive_group_bits(64, 128, 0, 1024, [8192], LOW, MID, HIGH)
+    assert kb.size == 126
+    g = np.arange(126)
+    expect = np.where(g >= 112, 2, np.where(g < 16, 0, 1))
+    bits = np.array([LOW, MID, HIGH])
+    assert np.array_equal(kb, bits[expect, 0]) and np.array_equal(vb, bits[expect, 1])
+
+
+def test_adaptive_regions_short_prefill_and_sink(orc):
+    # n = 1500 < 2 delta: a group both early and recent is recent (printed order);
+    # 21 groups, recent when 64 g + 64 > 476, i.e. g >= 7
+    kb, vb = orc.adaptive_group_bits(64, 128, 0, 1024, [1500], LOW, MID, HIGH)
+    assert kb.size == 21
+    assert np.array_equal(kb, np.where(np.arange(21) >= 7, 4, 2)) and np.array_equal(vb, kb)
+    # with a 64-token sink the groups shift by 64 positions: group g ends at 64 g + 128
+    kb, vb = orc.adaptive_group_bits(64, 128, 64, 1024, [8192], LOW, MID, HIGH)
+    g = np.arange(kb.size)
+    assert kb.size == 125
+    assert np.array_equal(kb, np.where(64 * g + 128 > 7168, 4, np.where(64 * g + 128 <= 1024, 2, 4)))
+    assert np.array_equal(vb, np.where(64 * g + 128 > 7168, 4, 2))
+
+
+def test_adaptive_groups_quantized_while_decoding_are_recent(orc):
+    """One token per append: each group is quantized when n = S0 + gG + G + R,
+    its last token is at n - R > n - delta, so every group is recent."""
+    kb, vb = orc.adaptive_group_bits(32, 64, 0, 1024, [1] * 3000, LOW, MID, HIGH)
+    assert kb.size == (3000 - 64) // 32 and (kb == 4).all() and (vb == 4).all()
+    # a prefill, then steps: the prefill's regions stay, later groups are recent
+    kb2, _ = orc.adaptive_group_bits(32, 64, 0, 1024, [5000] + [1] * 500, LOW, MID, HIGH)
+    kb1, _ = orc.adaptive_group_bits(32, 64, 0, 1024, [5000], LOW, MID, HIGH)
+    assert np.array_equal(kb2[:kb1.size], kb1) and (kb2[kb1.size:] == 4).all()
+    assert (kb1 == 2).any() and (kb1 == 4).any()
+
+
+def test_adaptive_encoding_is_per_group_fixed_bit_encoding(orc):
+    """Each group's codes and parameters are those of the fixed-width encoder
+    at that group's bits; equal bits everywhere is the plain encoder."""
+    rng = np.random.default_rng(21)
+    D, G, R, n = 64, 32, 32, 32 * 12 + 40
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    gk = np.array([2, 4, 4, 2, 2, 4, 2, 4, 4, 4, 2, 2], np.uint8)
+    gv = np.array([2, 2, 4, 4, 2, 4, 2, 2, 4, 4, 4, 2], np.uint8)
+    a = orc.encode_slice(k, v, "f32", D, 4, 2, G, R, False, group_bits=(gk, gv))
+    ref = {(kb, vb): orc.encode_slice(k, v, "f32", D, kb, vb, G, R, False) for kb in (2, 4) for vb in (2, 4)}
+    for g in range(12):
+        r = ref[(int(gk[g]), int(gv[g]))]
+        sl = slice(g * G, g * G + G)
+        assert np.array_equal(a["k_codes"][sl], r["k_codes"][sl])
+        assert np.array_equal(a["k_scale"][g], r["k_scale"][g]) and np.array_equal(a["k_zero"][g], r["k_zero"][g])
+        assert np.array_equal(a["v_codes"][sl], r["v_codes"][sl]) and np.array_equal(a["v_scale"][sl], r["v_scale"][sl])
+    same = orc.encode_slice(k, v, "f32", D, 4, 2, G, R, False, group_bits=(np.full(12, 4, np.uint8), np.full(12, 2, np.uint8)))
+    for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid"):
+        assert np.array_equal(same[key], ref[(4, 2)][key]), key
