@@ -35,24 +35,36 @@ def in_bytes(w) -> int:
     return 4 if w.dtype == "f32" else 2
 
 
-def decode_bytes(w, n: int) -> int:
-    """Algorithmic bytes of one decode over n cached tokens per sequence."""
+def quant_token_bytes(w, kb: int, vb: int) -> int:
+    """Bytes per quantized token: codes, key scale/zero per channel shared by G
+    tokens, value scale/zero per channel group, the key norm if any."""
+    return w.D * (kb + vb) // 8 + 4 * w.D // w.G + 4 * (w.D // w.G) + 2 * int(w.token_norm)
+
+
+def decode_bytes(w, n: int, gbits=None) -> int:
+    """Algorithmic bytes of one decode over n cached tokens per sequence;
+    gbits = (key bits, value bits) per group for position-adaptive caches."""
     nq = (max(0, n - w.sink - w.R) // w.G) * w.G
     nr = n - nq  # fp16 tokens: the attention sink and the recent window
-    per_quant_token = w.D * (w.kbits + w.vbits) // 8 + 4 * w.D // w.G + 4 * (w.D // w.G) + 2 * int(w.token_norm)
+    if gbits is None:
+        quant = nq * quant_token_bytes(w, w.kbits, w.vbits)
+    else:
+        ng = nq // w.G
+        quant = sum(w.G * quant_token_bytes(w, int(kb), int(vb)) for kb, vb in zip(gbits[0][:ng], gbits[1][:ng]))
     per_window_token = 4 * w.D  # fp16 K and V
-    cache = w.B * w.Hkv * (nq * per_quant_token + nr * per_window_token)
+    cache = w.B * w.Hkv * (quant + nr * per_window_token)
     return cache + w.B * w.Hq * w.D * (in_bytes(w) + 4)
 
 
-def append_bytes(w, n_before: int) -> int:
+def append_bytes(w, n_before: int, gbits=None) -> int:
     """Algorithmic bytes of appending one token to sequences holding n_before."""
     slices = w.B * w.Hkv
     b = slices * w.D * (2 * in_bytes(w) + 4)  # read k, v; write both as fp16
     nq0 = (max(0, n_before - w.sink - w.R) // w.G) * w.G
     nq1 = (max(0, n_before + 1 - w.sink - w.R) // w.G) * w.G
     if nq1 > nq0:  # one group flushed: read its fp16 tokens, write the page
-        page = w.G * w.D * (w.kbits + w.vbits) // 8 + 4 * w.D + w.G * 4 * (w.D // w.G)
+        kb, vb = (w.kbits, w.vbits) if gbits is None else (int(gbits[0][nq0 // w.G]), int(gbits[1][nq0 // w.G]))
+        page = w.G * quant_token_bytes(w, kb, vb)
         b += slices * (w.G * w.D * 4 + page)
     return b
 
@@ -66,11 +78,16 @@ def cpu_baseline(w, K_host, V_host, q_host, batches, threads: int) -> dict:
     pairs = [(b, h) for b in batches for h in range(w.Hkv)]
     from concurrent.futures import ThreadPoolExecutor
 
+    gb = None
+    if w.adapt_delta:  # the prefill's group bits
+        gb = oracle.adaptive_group_bits(w.G, w.R, w.sink, w.adapt_delta, [w.N], w.bits_low, (w.kbits, w.vbits),
+                                        w.bits_high)
+
     def enc(bh):
         b, h = bh
         return oracle.encode_slice(to_oracle_input(K_host[b][h], w.dtype), to_oracle_input(V_host[b][h], w.dtype),
                                    w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate, sink=w.sink, hybrid=w.hybrid,
-                                   token_norm=w.token_norm)
+                                   token_norm=w.token_norm, group_bits=gb)
 
     with ThreadPoolExecutor(threads) as ex:
         encs = list(ex.map(enc, pairs))
@@ -87,7 +104,7 @@ def cpu_baseline(w, K_host, V_host, q_host, batches, threads: int) -> dict:
     dt = time.perf_counter() - t0
     full = dt * (w.B * w.Hkv) / len(pairs)
     return {
-        "value": round(decode_bytes(w, w.N) / full / 1e9, 3),
+        "value": round(decode_bytes(w, w.N, gb) / full / 1e9, 3),
         "unit": "GB/s",
         "us_per_step": round(full * 1e6, 1),
         "cores": threads,
@@ -158,6 +175,10 @@ def main() -> int:
     ap.add_argument("--sink", type=int, default=0, help="attention-sink tokens kept in fp16 (a multiple of the group size)")
     ap.add_argument("--hybrid", action="store_true", help="per-group symmetric/asymmetric quantizer choice")
     ap.add_argument("--token-norm", action="store_true", help="key tokens divided by their norm before quantization")
+    ap.add_argument("--adapt-delta", type=int, default=0,
+                    help="position-adaptive bit widths: region size Delta in tokens (0: off)")
+    ap.add_argument("--bits-low", default="2,2", help="key,value bits of the first Delta tokens")
+    ap.add_argument("--bits-high", default="4,4", help="key,value bits of the last Delta tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=16)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -183,10 +204,14 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     w = WORKLOADS[args.workload]
-    if args.sink or args.hybrid or args.token_norm:
+    if args.sink or args.hybrid or args.token_norm or args.adapt_delta:
+        lo = tuple(int(x) for x in args.bits_low.split(","))
+        hi = tuple(int(x) for x in args.bits_high.split(","))
+        adapt = f"-adapt{args.adapt_delta}-lo{lo[0]}{lo[1]}-hi{hi[0]}{hi[1]}" if args.adapt_delta else ""
         w = w.replace(name=w.name + (f"-sink{args.sink}" if args.sink else "") + ("-hybrid" if args.hybrid else "")
-                      + ("-tokennorm" if args.token_norm else ""),
-                      sink=args.sink, hybrid=args.hybrid, token_norm=args.token_norm)
+                      + ("-tokennorm" if args.token_norm else "") + adapt,
+                      sink=args.sink, hybrid=args.hybrid, token_norm=args.token_norm, adapt_delta=args.adapt_delta,
+                      bits_low=lo if args.adapt_delta else (0, 0), bits_high=hi if args.adapt_delta else (0, 0))
     total = args.warmup + args.steps
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -213,7 +238,9 @@ def main() -> int:
     qs = [syn.q(i) for i in range(total)]
     rows = w.B * w.Hq
     S = args.splits or cache.default_splits()
-    partials = torch.empty((rows, S, w.D + 4), dtype=torch.float32, device=dev)
+    # a position-adaptive cache may use a few more splits than asked (at least one per run of equal bits)
+    cap = max(S, kvq.workspace_bytes(kvq.config_for(w, max_tokens=w.N + total)) // (rows * (w.D + 4) * 4))
+    partials = torch.empty((rows, cap, w.D + 4), dtype=torch.float32, device=dev)
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
 
     def step(i, evs=None):
@@ -247,8 +274,9 @@ def main() -> int:
     ms_step = ms_total / args.steps
     dec_ms = [a.elapsed_time(b) for a, b in evs]
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
-    step_bytes = [decode_bytes(w, n0 + i + 1) + append_bytes(w, n0 + i) for i in range(args.steps)]
-    dec_bytes = [decode_bytes(w, n0 + i + 1) for i in range(args.steps)]
+    gbits = cache.group_bits() if w.adapt_delta else None  # a group's bits never change once quantized
+    step_bytes = [decode_bytes(w, n0 + i + 1, gbits) + append_bytes(w, n0 + i, gbits) for i in range(args.steps)]
+    dec_bytes = [decode_bytes(w, n0 + i + 1, gbits) for i in range(args.steps)]
     value = sum(step_bytes) / (ms_total * 1e-3) / 1e9
     achieved = (sum(dec_bytes) / len(dec_bytes)) / (dec_avg_ms * 1e-3) / 1e9
     assert torch.isfinite(out).all()
@@ -281,6 +309,7 @@ def main() -> int:
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
             "context": w.N, "k_bits": w.kbits, "v_bits": w.vbits, "group": w.G, "residual": w.R,
             "rotate": w.rotate, "sink": w.sink, "hybrid": w.hybrid, "token_norm": w.token_norm, "splits": S,
+            "adapt_delta": w.adapt_delta, "bits_low": list(w.bits_low), "bits_high": list(w.bits_high),
             "parallelism": "single-gpu",
         },
         "roofline": {

@@ -28,4 +28,6 @@ def config_for(w, max_tokens: int | None = None) -> "Config":
         max_tokens=max_tokens or w.N, k_bits=w.kbits, v_bits=w.vbits, group_size=w.G,
         residual=w.R, rotate=w.rotate, in_dtype=w.dtype, sink_tokens=getattr(w, "sink", 0),
         hybrid=getattr(w, "hybrid", False), token_norm=getattr(w, "token_norm", False),
+        adapt_delta=getattr(w, "adapt_delta", 0), bits_low=tuple(getattr(w, "bits_low", (0, 0))),
+        bits_high=tuple(getattr(w, "bits_high", (0, 0))),
     )

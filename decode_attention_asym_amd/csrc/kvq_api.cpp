@@ -24,11 +24,12 @@ using kvq::Layout;
 
 struct kvq_cache {
   kvq_config cfg;
-  Layout L;
+  Layout L;                 // middle bits; page_bytes is the group slot size
   uint8_t* buf;
   int64_t n;
   bool poisoned;
   int cu_count;
+  std::vector<uint8_t> gk, gv;  // key / value bits of each quantized group
 };
 
 namespace {
@@ -70,15 +71,56 @@ kvq_status validate(const kvq_config* c) {
     return fail(KVQ_E_UNSUPPORTED, "sink_tokens %d must be a multiple of group_size in [0, 1024]", c->sink_tokens);
   if (c->hybrid != 0 && c->hybrid != 1) return fail(KVQ_E_ARG, "hybrid must be 0 or 1");
   if (c->token_norm != 0 && c->token_norm != 1) return fail(KVQ_E_ARG, "token_norm must be 0 or 1");
+  if (c->adapt_delta < 0 || c->adapt_delta % c->group_size != 0)
+    return fail(KVQ_E_UNSUPPORTED, "adapt_delta %d must be a non-negative multiple of group_size", c->adapt_delta);
+  if (c->adapt_delta > 0) {
+    for (int b : {c->k_bits_low, c->v_bits_low, c->k_bits_high, c->v_bits_high})
+      if (b != 2 && b != 4) return fail(KVQ_E_UNSUPPORTED, "adaptive bit widths must be 2 or 4");
+    if (!kvq::decode_supported(c->head_dim, c->k_bits_low, c->v_bits_low, c->group_size) ||
+        !kvq::decode_supported(c->head_dim, c->k_bits_high, c->v_bits_high, c->group_size))
+      return fail(KVQ_E_UNSUPPORTED, "no kernel for an adaptive (head_dim, bits, group) combination");
+  }
   if (c->in_dtype < KVQ_F32 || c->in_dtype > KVQ_BF16) return fail(KVQ_E_ARG, "in_dtype %d unknown", c->in_dtype);
   if (!kvq::decode_supported(c->head_dim, c->k_bits, c->v_bits, c->group_size))
     return fail(KVQ_E_UNSUPPORTED, "no kernel for this (head_dim, bits, group) combination");
   return KVQ_OK;
 }
 
+Layout layout_bits(const kvq_config* c, int kb, int vb, int64_t stride) {
+  return kvq::make_layout(c->batch, c->num_kv_heads, c->head_dim, c->max_tokens, kb, vb, c->group_size, c->residual,
+                          c->sink_tokens, c->token_norm, stride);
+}
+
+// The cache layout: middle bits, with group slots as large as the widest page.
 Layout layout_of(const kvq_config* c) {
-  return kvq::make_layout(c->batch, c->num_kv_heads, c->head_dim, c->max_tokens, c->k_bits, c->v_bits, c->group_size,
-                          c->residual, c->sink_tokens, c->token_norm);
+  int64_t stride = layout_bits(c, c->k_bits, c->v_bits, 0).page_bytes;
+  if (c->adapt_delta > 0) {
+    stride = std::max(stride, layout_bits(c, c->k_bits_low, c->v_bits_low, 0).page_bytes);
+    stride = std::max(stride, layout_bits(c, c->k_bits_high, c->v_bits_high, 0).page_bytes);
+  }
+  return layout_bits(c, c->k_bits, c->v_bits, stride);
+}
+
+// Layout of the pages of one bit width inside this cache's group slots.
+Layout layout_for(const kvq_cache* h, int kb, int vb) { return layout_bits(&h->cfg, kb, vb, h->L.page_bytes); }
+
+// Layout of each of the first ng groups' pages.
+std::vector<Layout> group_layouts(const kvq_cache* h, int64_t ng) {
+  std::vector<Layout> gl(static_cast<size_t>(ng), h->L);
+  if (h->cfg.adapt_delta > 0)
+    for (int64_t g = 0; g < ng; ++g) gl[g] = layout_for(h, h->gk[g], h->gv[g]);
+  return gl;
+}
+
+// Runs of consecutive groups with equal bit widths among groups [g0, g1).
+struct Run { int64_t g0, g1; int kb, vb; };
+std::vector<Run> runs_of(const kvq_cache* h, int64_t g0, int64_t g1) {
+  std::vector<Run> r;
+  for (int64_t g = g0; g < g1; ++g) {
+    if (r.empty() || r.back().kb != h->gk[g] || r.back().vb != h->gv[g]) r.push_back({g, g, h->gk[g], h->gv[g]});
+    r.back().g1 = g + 1;
+  }
+  return r;
 }
 
 int max_splits(const kvq_config* c) {
@@ -123,6 +165,33 @@ int choose_splits(kvq_cache* h) {
   return static_cast<int>(std::max<int64_t>(1, s));
 }
 
+// Split counts of the runs of equal-bit groups: about S times the run's share
+// of the page bytes each, at least one, at most max(S, runs) in total (more
+// splits than S, to give short runs their own, measured slower: the grid then
+// holds more than the workgroups one pass of the CUs runs).
+std::vector<int64_t> run_splits(const kvq_cache* h, const std::vector<Run>& runs, int64_t S) {
+  std::vector<double> wgt(runs.size());
+  double tot_w = 0;
+  for (size_t i = 0; i < runs.size(); ++i) {
+    wgt[i] = double(runs[i].g1 - runs[i].g0) * double(layout_bits(&h->cfg, runs[i].kb, runs[i].vb, 0).page_bytes);
+    tot_w += wgt[i];
+  }
+  std::vector<int64_t> sp(runs.size());
+  int64_t tot = 0;
+  for (size_t i = 0; i < runs.size(); ++i) {
+    sp[i] = std::max<int64_t>(1, static_cast<int64_t>(double(S) * wgt[i] / tot_w + 0.5));
+    sp[i] = std::min<int64_t>(sp[i], runs[i].g1 - runs[i].g0);
+    tot += sp[i];
+  }
+  const int64_t cap = std::max<int64_t>(S, static_cast<int64_t>(runs.size()));
+  while (tot > cap) {
+    size_t k = static_cast<size_t>(std::max_element(sp.begin(), sp.end()) - sp.begin());
+    --sp[k];
+    --tot;
+  }
+  return sp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,6 +224,13 @@ kvq_status kvq_create(const kvq_config* cfg, void* cache_buf, size_t cache_bytes
   h->n = 0;
   h->poisoned = false;
   h->cu_count = 0;
+  try {
+    h->gk.assign(static_cast<size_t>(L.pages), static_cast<uint8_t>(cfg->k_bits));
+    h->gv.assign(static_cast<size_t>(L.pages), static_cast<uint8_t>(cfg->v_bits));
+  } catch (...) {
+    delete h;
+    return fail(KVQ_E_ARG, "out of host memory");
+  }
   *out = h;
   return ok();
 }
@@ -208,9 +284,28 @@ kvq_status kvq_append(kvq_cache* h, const void* k, const void* v, int32_t n_toke
   a.w_first = std::max<int64_t>(h->n, S0 + nq_new);
   a.n_write = std::max<int64_t>(0, n_new - a.w_first);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // flush before the window write: the write may reuse ring slots the flush reads
-  hipError_t e = kvq::launch_flush(a, s);
-  if (e != hipSuccess) return device_error(h, e, "flush kernel launch");
+  const kvq_config& c = h->cfg;
+  const int64_t gf = a.g_first, gl = a.g_first + a.n_flush;
+  if (c.adapt_delta > 0) {
+    // bits of the groups quantized now, from their place in the n_new tokens
+    for (int64_t g = gf; g < gl; ++g) {
+      const int64_t p1 = S0 + g * G + G;  // one past the group's last token
+      const int region = p1 > n_new - c.adapt_delta ? 2 : (p1 <= c.adapt_delta ? 0 : 1);
+      h->gk[g] = static_cast<uint8_t>(region == 2 ? c.k_bits_high : region == 0 ? c.k_bits_low : c.k_bits);
+      h->gv[g] = static_cast<uint8_t>(region == 2 ? c.v_bits_high : region == 0 ? c.v_bits_low : c.v_bits);
+    }
+  }
+  // flush before the window write: the write may reuse ring slots the flush
+  // reads; one launch per run of groups with equal bits
+  hipError_t e = hipSuccess;
+  for (const Run& r : runs_of(h, gf, gl)) {
+    kvq::AppendArgs ar = a;
+    ar.L = layout_for(h, r.kb, r.vb);
+    ar.g_first = r.g0;
+    ar.n_flush = r.g1 - r.g0;
+    e = kvq::launch_flush(ar, s);
+    if (e != hipSuccess) return device_error(h, e, "flush kernel launch");
+  }
   e = kvq::launch_window_write(a, s);
   if (e != hipSuccess) return device_error(h, e, "window write kernel launch");
   h->n = n_new;
@@ -224,7 +319,9 @@ int32_t kvq_default_splits(const kvq_cache* h) {
 
 namespace {
 
-// Validate and launch the split kernel; write_final selects direct output (S == 1).
+// Validate and launch the split kernels (one per run of groups with equal
+// bits); allow_final selects direct output
+// when the whole decode is one split.
 kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partials, size_t bytes, int32_t num_splits,
                          bool allow_final, int32_t* splits_used, hipStream_t s) {
   kvq_status st = check_handle(h);
@@ -236,9 +333,22 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
     return fail(KVQ_E_ARG, "num_splits %d above the workspace maximum %d", num_splits, max_splits(&h->cfg));
   const kvq_config& c = h->cfg;
   const int64_t ng = ngroups_of(h);
-  int64_t S = std::min<int64_t>(num_splits, std::max<int64_t>(1, ng));
-  int64_t gps = ng > 0 ? (ng + S - 1) / S : 0;
-  if (gps > 0) S = (ng + gps - 1) / gps;  // no empty split
+  std::vector<Run> runs = runs_of(h, 0, ng);
+  if (runs.empty()) runs.push_back({0, 0, c.k_bits, c.v_bits});
+  if (static_cast<int64_t>(runs.size()) > max_splits(&c))
+    return fail(KVQ_E_UNSUPPORTED, "%zu runs of equal bit widths exceed the split maximum %d", runs.size(),
+                max_splits(&c));
+  std::vector<int64_t> sp(runs.size(), 1), gps(runs.size(), 0);
+  if (ng > 0) sp = run_splits(h, runs, std::min<int64_t>(num_splits, ng));
+  int64_t S = 0;
+  for (size_t i = 0; i < runs.size(); ++i) {
+    const int64_t len = runs[i].g1 - runs[i].g0;
+    if (len > 0) {
+      gps[i] = (len + sp[i] - 1) / sp[i];
+      sp[i] = (len + gps[i] - 1) / gps[i];  // no empty split
+    }
+    S += sp[i];
+  }
   const int64_t rows = static_cast<int64_t>(c.batch) * c.num_q_heads;
   const bool final = allow_final && S == 1;
   if (final) {
@@ -250,7 +360,6 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
   }
   kvq::DecodeArgs a{};
   a.cache = h->buf;
-  a.L = h->L;
   a.q = q;
   a.in_dtype = c.in_dtype;
   a.rotate = c.rotate;
@@ -258,17 +367,49 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
   a.Hq = c.num_q_heads;
   a.Hkv = c.num_kv_heads;
   a.n = h->n;
-  a.ngroups = ng;
-  a.splits = static_cast<int>(S);
-  a.groups_per_split = gps;
   a.rc0 = (c.sink_tokens + nquant_of(h, h->n)) / kvq::kChunk;
   a.rc1 = std::max(a.rc0, (h->n + kvq::kChunk - 1) / kvq::kChunk);
   a.nsc = (std::min<int64_t>(h->n, c.sink_tokens) + kvq::kChunk - 1) / kvq::kChunk;
   a.partial = partials;
   a.out = out;
   a.write_final = final ? 1 : 0;
-  hipError_t e = kvq::launch_decode(a, s);
-  if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
+  a.splits_total = S;
+  // the fp16 chunks go with the run that has the most splits
+  const size_t fp16_run = static_cast<size_t>(std::max_element(sp.begin(), sp.end()) - sp.begin());
+  if (runs.size() > 1 && runs.size() <= static_cast<size_t>(kvq::kMaxRuns)) {
+    // one launch for all runs
+    kvq::MixedRuns mr{};
+    mr.n = static_cast<int>(runs.size());
+    mr.fp16_run = static_cast<int>(fp16_run);
+    int64_t off = 0;
+    for (size_t i = 0; i < runs.size(); ++i) {
+      mr.bits[i] = 16 * runs[i].kb + runs[i].vb;
+      mr.splits[i] = static_cast<int>(sp[i]);
+      mr.split_off[i] = static_cast<int>(off);
+      mr.g_base[i] = runs[i].g0;
+      mr.ngroups[i] = runs[i].g1 - runs[i].g0;
+      mr.gps[i] = gps[i];
+      off += sp[i];
+    }
+    a.L = h->L;
+    hipError_t e = kvq::launch_decode_mixed(a, mr, s);
+    if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
+    if (splits_used) *splits_used = static_cast<int32_t>(S);
+    return ok();
+  }
+  int64_t off = 0;
+  for (size_t i = 0; i < runs.size(); ++i) {
+    a.L = layout_for(h, runs[i].kb, runs[i].vb);
+    a.g_base = runs[i].g0;
+    a.ngroups = runs[i].g1 - runs[i].g0;
+    a.splits = static_cast<int>(sp[i]);
+    a.groups_per_split = gps[i];
+    a.split_off = off;
+    a.do_fp16 = i == fp16_run ? 1 : 0;
+    hipError_t e = kvq::launch_decode(a, s);
+    if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
+    off += sp[i];
+  }
   if (splits_used) *splits_used = static_cast<int32_t>(S);
   return ok();
 }
@@ -321,11 +462,14 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
   if (b0 < 0 || bc < 0 || b0 + bc > c.batch) return fail(KVQ_E_ARG, "batch range [%d, %d) out of [0, %d)", b0, b0 + bc, c.batch);
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(h, e, "stream synchronize");
+  if (c.adapt_delta > 0 && (k_codes || v_codes))
+    return fail(KVQ_E_UNSUPPORTED, "packed code export needs one bit width; use kvq_export_codes_u8");
   const Layout& L = h->L;
   const int D = c.head_dim, G = c.group_size, kb = c.k_bits, vb = c.v_bits, ncg = D / G;
   const int64_t nq = nquant_of(h, h->n), nr = h->n - nq, ng = nq / G;
   const int64_t ns = std::min<int64_t>(h->n, c.sink_tokens);  // fp16 index r < ns: sink token r
   const int64_t krow = D * kb / 8, vrow = D * vb / 8;
+  const std::vector<Layout> GL = group_layouts(h, ng);
   std::vector<uint8_t> pages(static_cast<size_t>(ng * L.page_bytes));
   std::vector<uint8_t> ring(static_cast<size_t>(L.ring_chunks * L.ring_chunk_bytes));
   std::vector<uint8_t> sink(static_cast<size_t>(L.sink_chunks * L.ring_chunk_bytes));
@@ -347,6 +491,7 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
       }
       for (int64_t t = 0; t < nq; ++t) {
         const uint8_t* page = pages.data() + (t / G) * L.page_bytes;
+        const Layout& PL = GL[t / G];
         const int ch = static_cast<int>((t % G) / kvq::kChunk), tt = static_cast<int>(t % kvq::kChunk);
         if (k_codes) {
           uint8_t* row = static_cast<uint8_t*>(k_codes) + (oi * nq + t) * krow;
@@ -373,15 +518,15 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
           }
         }
         for (int cg = 0; cg < ncg; ++cg) {
-          const uint16_t* vpp = reinterpret_cast<const uint16_t*>(page + L.off_vparams + ch * L.vp_chunk_bytes);
-          if (v_scale) static_cast<uint16_t*>(v_scale)[(oi * nq + t) * ncg + cg] = vpp[kvq::vparam_scale_elem(L, tt, cg)];
-          if (v_zero) static_cast<uint16_t*>(v_zero)[(oi * nq + t) * ncg + cg] = vpp[kvq::vparam_zero_elem(L, tt, cg)];
+          const uint16_t* vpp = reinterpret_cast<const uint16_t*>(page + PL.off_vparams + ch * PL.vp_chunk_bytes);
+          if (v_scale) static_cast<uint16_t*>(v_scale)[(oi * nq + t) * ncg + cg] = vpp[kvq::vparam_scale_elem(PL, tt, cg)];
+          if (v_zero) static_cast<uint16_t*>(v_zero)[(oi * nq + t) * ncg + cg] = vpp[kvq::vparam_zero_elem(PL, tt, cg)];
         }
       }
       for (int64_t g = 0; g < ng; ++g) {
-        const uint16_t* kp = reinterpret_cast<const uint16_t*>(pages.data() + g * L.page_bytes + L.off_kparams);
+        const uint16_t* kp = reinterpret_cast<const uint16_t*>(pages.data() + g * L.page_bytes + GL[g].off_kparams);
         for (int cc = 0; cc < D; ++cc) {
-          int pi = kvq::kparam_index(L, cc);
+          int pi = kvq::kparam_index(GL[g], cc);
           if (k_scale) static_cast<uint16_t*>(k_scale)[(oi * ng + g) * D + cc] = kp[pi];
           if (k_zero) static_cast<uint16_t*>(k_zero)[(oi * ng + g) * D + cc] = kp[D + pi];
         }
@@ -404,6 +549,58 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
   return ok();
 }
 
+kvq_status kvq_export_codes_u8(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void* v_codes, void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = h->cfg;
+  if (b0 < 0 || bc < 0 || b0 + bc > c.batch) return fail(KVQ_E_ARG, "batch range out of bounds");
+  if (!k_codes && !v_codes) return fail(KVQ_E_ARG, "code arrays are NULL");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(h, e, "stream synchronize");
+  const Layout& L = h->L;
+  const int D = c.head_dim, G = c.group_size;
+  const int64_t nq = nquant_of(h, h->n), ng = nq / G;
+  const std::vector<Layout> GL = group_layouts(h, ng);
+  std::vector<uint8_t> pages(static_cast<size_t>(ng * L.page_bytes));
+  for (int64_t bi = 0; bi < bc; ++bi)
+    for (int64_t hk = 0; hk < c.num_kv_heads; ++hk) {
+      if (ng == 0) continue;
+      const int64_t slice = (b0 + bi) * c.num_kv_heads + hk;
+      const int64_t oi = bi * c.num_kv_heads + hk;
+      e = hipMemcpy(pages.data(), h->buf + kvq::page_offset(L, slice, 0), pages.size(), hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return device_error(h, e, "export copy");
+      for (int64_t t = 0; t < nq; ++t) {
+        const uint8_t* page = pages.data() + (t / G) * L.page_bytes;
+        const Layout& PL = GL[t / G];
+        const int ch = static_cast<int>((t % G) / kvq::kChunk), tt = static_cast<int>(t % kvq::kChunk);
+        for (int cc = 0; cc < D; ++cc) {
+          int64_t byte; int bit; uint32_t w;
+          if (k_codes) {
+            kvq::kcode_loc(PL, tt, cc, &byte, &bit);
+            std::memcpy(&w, page + PL.off_kcodes + ch * PL.kc_chunk_bytes + byte, 4);
+            static_cast<uint8_t*>(k_codes)[(oi * nq + t) * D + cc] = static_cast<uint8_t>((w >> bit) & ((1u << PL.kbits) - 1u));
+          }
+          if (v_codes) {
+            kvq::vcode_loc(PL, tt, cc, &byte, &bit);
+            std::memcpy(&w, page + PL.off_vcodes + ch * PL.vc_chunk_bytes + byte, 4);
+            static_cast<uint8_t*>(v_codes)[(oi * nq + t) * D + cc] = static_cast<uint8_t>((w >> bit) & ((1u << PL.vbits) - 1u));
+          }
+        }
+      }
+    }
+  return ok();
+}
+
+int64_t kvq_group_bits(const kvq_cache* h, uint8_t* k_bits, uint8_t* v_bits, int64_t cap) {
+  if (!h) return -1;
+  const int64_t ng = ngroups_of(h);
+  for (int64_t g = 0; g < std::min(ng, cap); ++g) {
+    if (k_bits) k_bits[g] = h->gk[g];
+    if (v_bits) v_bits[g] = h->gv[g];
+  }
+  return ng;
+}
+
 // Key token norms live in each page's norm block, one 64-byte block per chunk.
 static kvq_status key_norms_copy(kvq_cache* h, int32_t b0, int32_t bc, void* out, const void* in, void* stream) {
   kvq_status st = check_handle(h);
@@ -417,6 +614,7 @@ static kvq_status key_norms_copy(kvq_cache* h, int32_t b0, int32_t bc, void* out
   const Layout& L = h->L;
   const int G = c.group_size;
   const int64_t nq = nquant_of(h, h->n), ng = nq / G;
+  const std::vector<Layout> GL = group_layouts(h, ng);
   std::vector<uint8_t> pages(static_cast<size_t>(ng * L.page_bytes));
   for (int64_t bi = 0; bi < bc; ++bi)
     for (int64_t hk = 0; hk < c.num_kv_heads; ++hk) {
@@ -426,8 +624,9 @@ static kvq_status key_norms_copy(kvq_cache* h, int32_t b0, int32_t bc, void* out
       e = hipMemcpy(pages.data(), h->buf + kvq::page_offset(L, slice, 0), pages.size(), hipMemcpyDeviceToHost);
       if (e != hipSuccess) return device_error(h, e, "key norm copy");
       for (int64_t t = 0; t < nq; ++t) {
-        uint16_t* kn = reinterpret_cast<uint16_t*>(pages.data() + (t / G) * L.page_bytes + L.off_knorm +
-                                                   ((t % G) / kvq::kChunk) * L.kn_chunk_bytes);
+        const Layout& PL = GL[t / G];
+        uint16_t* kn = reinterpret_cast<uint16_t*>(pages.data() + (t / G) * L.page_bytes + PL.off_knorm +
+                                                   ((t % G) / kvq::kChunk) * PL.kn_chunk_bytes);
         const int el = kvq::knorm_elem(static_cast<int>(t % kvq::kChunk));
         if (out) static_cast<uint16_t*>(out)[oi * nq + t] = kn[el];
         else kn[el] = static_cast<const uint16_t*>(in)[oi * nq + t];
@@ -461,6 +660,7 @@ kvq_status kvq_import(kvq_cache* h, int64_t n_tokens, int32_t b0, int32_t bc, co
   if (b0 < 0 || bc < 0 || b0 + bc > c.batch) return fail(KVQ_E_ARG, "batch range out of bounds");
   if (!k_codes || !k_scale || !k_zero || !v_codes || !v_scale || !v_zero || !k_resid || !v_resid)
     return fail(KVQ_E_ARG, "import arrays must not be NULL");
+  if (c.adapt_delta > 0) return fail(KVQ_E_UNSUPPORTED, "import into a position-adaptive cache");
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(h, e, "stream synchronize");
   const Layout& L = h->L;

@@ -245,11 +245,13 @@ constexpr int kp_after(int ch) {
 template <int CPG>
 constexpr int param_buffers(int n) { return CPG == 1 ? n : n / CPG + 1; }
 // Chunks in flight per wave: as many as fit, with their parameter buffers, in
-// 13 KiB of LDS (three waves per SIMD, twelve per CU, within 160 KiB).
+// 12800 bytes of LDS, so that twelve waves (three per SIMD) fit in a CU's
+// 160 KiB: measured on gfx950, 13312 bytes per workgroup already cost a
+// workgroup slot per CU (allocation is rounded up beyond the byte count).
 template <int SLOT, int PB, int CPG>
 constexpr int ring_depth() {
   int n = 2;
-  while ((n + 1) * SLOT + param_buffers<CPG>(n + 1) * PB <= 13 * 1024) ++n;
+  while ((n + 1) * SLOT + param_buffers<CPG>(n + 1) * PB <= 12800) ++n;
   return n;
 }
 template <int N>
@@ -271,6 +273,15 @@ struct PageShape {
   // the group's parameter block [KP][VP per chunk][key norms per chunk]
   static constexpr int PB = KPB + CPG * VPB + CPG * KNB;
 };
+
+// LDS bytes of the chunk ring and parameter buffers of one page shape.
+template <int D, int KB, int VB, int G, bool TN>
+constexpr int ring_bytes() {
+  using PS = PageShape<D, KB, VB, G, TN>;
+  constexpr int SLOT = PS::KC + PS::VC;
+  constexpr int n = ring_depth<SLOT, PS::PB, PS::CPG>();
+  return n * SLOT + param_buffers<PS::CPG>(n) * PS::PB;
+}
 
 // Running-max slack of the online softmax (base-2 units): the accumulators
 // are rescaled only when a chunk's maximum exceeds the running maximum by more
@@ -315,9 +326,11 @@ __device__ __forceinline__ float replica_sum(float x) {
 // zero-point sums cost NV values per lane instead of 8.  Replica 0 gathers
 // the PV weights of the other replicas by DPP row rotation and owns the
 // output; the other replicas' PV columns are never read.
+//
+// decode_split is one workgroup's work: split s of slice `slice`, with the
+// LDS ring at `ring` (ring_bytes<...>() bytes).
 template <int D, int KB, int VB, int G, int GQC, bool TN>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
-void decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t slice, const int s, uint8_t* ring) {
   using PS = PageShape<D, KB, VB, G, TN>;
   constexpr int NKB = D / 32, NMT = D / 16, NCG = PS::NCG, CPG = PS::CPG;
   constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4;
@@ -331,8 +344,6 @@ void decode_kernel(DecodeArgs a) {
   const Layout& L = a.L;
   const int l = threadIdx.x, l16 = l & 15, j = l >> 4;
   const int S = a.splits;
-  const int64_t slice = blockIdx.x / S;
-  const int s = static_cast<int>(blockIdx.x % S);
   const int b = static_cast<int>(slice / a.Hkv), hkv = static_cast<int>(slice % a.Hkv);
   const int h = l16 % GQC, rp = l16 / GQC;
   const bool hv = h < a.gqa;
@@ -472,8 +483,8 @@ void decode_kernel(DecodeArgs a) {
     });
   };
 
-  const int g0 = s * static_cast<int>(a.groups_per_split);
-  const int g1 = min(g0 + static_cast<int>(a.groups_per_split), static_cast<int>(a.ngroups));
+  const int g0 = static_cast<int>(a.g_base) + s * static_cast<int>(a.groups_per_split);
+  const int g1 = min(g0 + static_cast<int>(a.groups_per_split), static_cast<int>(a.g_base + a.ngroups));
 
   // ---- LDS: a ring of NBUF chunk slots [key codes][value codes], and NPB
   // parameter buffers, each one group's block [key scale/zero rows][value
@@ -484,7 +495,7 @@ void decode_kernel(DecodeArgs a) {
   // has read them, and the refill that reuses a buffer comes after that read.
   constexpr int NBUF = ring_depth<SLOT, PB, CPG>(), NPB = param_buffers<CPG>(NBUF);
   constexpr int NBASE = dma_count<KC>() + dma_count<VC>(), NKP = dma_count<PB>();
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF * SLOT + NPB * PB];
+  static_assert(NBUF * SLOT + NPB * PB == ring_bytes<D, KB, VB, G, TN>(), "ring size");
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((KVQ_AS3 uint8_t*)ring));
   const uint32_t pbuf_lds = ring_lds + NBUF * SLOT;
   const uint32_t lane16 = static_cast<uint32_t>(l) * 16, lane4 = static_cast<uint32_t>(l) * 4;
@@ -509,7 +520,7 @@ void decode_kernel(DecodeArgs a) {
       constexpr int chi = decltype(chi_c)::value;
       const bool real = gi < g1;
       const int gp = real ? gi : g1 - 1;
-      const uint8_t* page = slice_pages + static_cast<int64_t>(gp) * PS::BYTES;
+      const uint8_t* page = slice_pages + static_cast<int64_t>(gp) * L.page_bytes;  // page slots (>= PS::BYTES)
       lds_reads_done();
       if (real) {
         dma_block<KC>(page + PS::OFF_KC + chi * KC, lane16, lane4, sl);
@@ -723,7 +734,7 @@ void decode_kernel(DecodeArgs a) {
   // so that no wave adds more than its share of these latency-bound reads to
   // the end of the kernel
   {
-    const int64_t nfc = a.nsc + (a.rc1 - a.rc0);
+    const int64_t nfc = a.do_fp16 ? a.nsc + (a.rc1 - a.rc0) : 0;
     for (int64_t fc = S - 1 - s; fc < nfc; fc += S) {
       const int64_t rc = fc < a.nsc ? fc : a.rc0 + (fc - a.nsc);  // absolute chunk index
       const uint8_t* rch = a.cache + fp16_chunk_offset(L, slice, rc * kChunk);
@@ -814,7 +825,7 @@ void decode_kernel(DecodeArgs a) {
         *reinterpret_cast<f32x4*>(a.out + row * D + c0) = o;
       }
     } else {
-      float* pr = a.partial + (row * S + s) * (D + 4);
+      float* pr = a.partial + (row * a.splits_total + a.split_off + s) * (D + 4);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int c0 = 16 * mt + 4 * j;
@@ -826,6 +837,60 @@ void decode_kernel(DecodeArgs a) {
         pr[D + 1] = lsum;
       }
     }
+  }
+}
+
+template <int D, int KB, int VB, int G, int GQC, bool TN>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
+void decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[ring_bytes<D, KB, VB, G, TN>()];
+  decode_split<D, KB, VB, G, GQC, TN>(a, blockIdx.x / a.splits, static_cast<int>(blockIdx.x % a.splits), ring);
+}
+
+// Groups of several bit widths in one launch: workgroup (slice, split) finds
+// the run of equal-width groups that its split belongs to and runs that
+// width's body, so the runs share one grid instead of one launch each.
+template <int D, int G>
+constexpr int mixed_ring_bytes() {
+  constexpr int a = ring_bytes<D, 2, 2, G, false>(), b = ring_bytes<D, 2, 4, G, false>();
+  constexpr int c = ring_bytes<D, 4, 2, G, false>(), d = ring_bytes<D, 4, 4, G, false>();
+  constexpr int e = ring_bytes<D, 2, 2, G, true>(), f = ring_bytes<D, 2, 4, G, true>();
+  constexpr int g = ring_bytes<D, 4, 2, G, true>(), h = ring_bytes<D, 4, 4, G, true>();
+  constexpr int m1 = a > b ? a : b, m2 = c > d ? c : d, m3 = e > f ? e : f, m4 = g > h ? g : h;
+  constexpr int m5 = m1 > m2 ? m1 : m2, m6 = m3 > m4 ? m3 : m4;
+  return m5 > m6 ? m5 : m6;
+}
+
+template <int D, int G, int GQC, bool TN>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
+void decode_mixed_kernel(DecodeArgs a, MixedRuns mr) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[mixed_ring_bytes<D, G>()];
+  const int64_t slice = blockIdx.x / a.splits_total;
+  const int sg = static_cast<int>(blockIdx.x % a.splits_total);
+  int bits = mr.bits[0], sp = mr.splits[0], off = 0;
+  int64_t gb = mr.g_base[0], ng = mr.ngroups[0], gps = mr.gps[0];
+  bool f16 = mr.fp16_run == 0;
+#pragma unroll
+  for (int i = 1; i < kMaxRuns; ++i) {
+    if (i < mr.n && sg >= mr.split_off[i]) {
+      bits = mr.bits[i]; sp = mr.splits[i]; off = mr.split_off[i];
+      gb = mr.g_base[i]; ng = mr.ngroups[i]; gps = mr.gps[i];
+      f16 = mr.fp16_run == i;
+    }
+  }
+  DecodeArgs r = a;
+  r.splits = sp;
+  r.split_off = off;
+  r.g_base = gb;
+  r.ngroups = ng;
+  r.groups_per_split = gps;
+  r.do_fp16 = f16 ? 1 : 0;
+  const int s = sg - off;
+  switch (bits) {
+    case 0x22: decode_split<D, 2, 2, G, GQC, TN>(r, slice, s, ring); break;
+    case 0x24: decode_split<D, 2, 4, G, GQC, TN>(r, slice, s, ring); break;
+    case 0x42: decode_split<D, 4, 2, G, GQC, TN>(r, slice, s, ring); break;
+    default: decode_split<D, 4, 4, G, GQC, TN>(r, slice, s, ring); break;
   }
 }
 
@@ -938,6 +1003,34 @@ bool decode_supported(int D, int kbits, int vbits, int G) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   return a.L.D == 64 ? decode_k<64>(a, s) : decode_k<128>(a, s);
+}
+
+namespace {
+template <int D, int G, bool TN>
+hipError_t mixed_t(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(a.L.slices * a.splits_total));
+  const size_t lds = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
+  if (a.gqa <= 4)
+    hipLaunchKernelGGL((decode_mixed_kernel<D, G, 4, TN>), grid, dim3(kLanes), lds, s, a, mr);
+  else if (a.gqa <= 8)
+    hipLaunchKernelGGL((decode_mixed_kernel<D, G, 8, TN>), grid, dim3(kLanes), lds, s, a, mr);
+  else
+    hipLaunchKernelGGL((decode_mixed_kernel<D, G, 16, TN>), grid, dim3(kLanes), lds, s, a, mr);
+  return hipGetLastError();
+}
+template <int D, int G>
+hipError_t mixed_g(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s) {
+  return a.L.token_norm ? mixed_t<D, G, true>(a, mr, s) : mixed_t<D, G, false>(a, mr, s);
+}
+template <int D>
+hipError_t mixed_d(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s) {
+  return a.L.G == 32 ? mixed_g<D, 32>(a, mr, s) : mixed_g<D, 64>(a, mr, s);
+}
+}  // namespace
+
+hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s) {
+  if (mr.n < 1 || mr.n > kMaxRuns) return hipErrorInvalidValue;
+  return a.L.D == 64 ? mixed_d<64>(a, mr, s) : mixed_d<128>(a, mr, s);
 }
 
 hipError_t launch_merge(const float* partial, float* out, int rows, int splits, int D, hipStream_t s) {

@@ -36,9 +36,13 @@ struct DecodeArgs {
   int gqa;
   int Hq, Hkv;
   int64_t n;            // tokens per sequence
-  int64_t ngroups;      // quantized groups per sequence
-  int splits;
+  int64_t ngroups;      // quantized groups of this launch
+  int splits;           // splits of this launch
   int64_t groups_per_split;
+  int64_t g_base;       // first group of this launch (groups [g_base, g_base + ngroups))
+  int split_off;        // this launch's first split slot in the partials
+  int splits_total;     // split slots per row in the partials
+  int do_fp16;          // this launch also covers the sink and window chunks
   int64_t rc0, rc1;     // window chunks [rc0, rc1) (absolute 32-token chunk indices)
   int64_t nsc;          // sink chunks holding tokens (ceil(min(n, S0) / 32))
   float* partial;       // [B*H_q][splits][D + 4] when !write_final
@@ -46,10 +50,28 @@ struct DecodeArgs {
   int write_final;
 };
 
+// Runs of groups with equal bit widths decoded by one launch: run i covers
+// groups [g_base[i], g_base[i] + ngroups[i]) with splits[i] splits of gps[i]
+// groups, in split slots [split_off[i], split_off[i] + splits[i]); bits[i] is
+// 16 * key bits + value bits; run fp16_run also covers the fp16 chunks.
+constexpr int kMaxRuns = 8;
+struct MixedRuns {
+  int n;
+  int fp16_run;
+  int bits[kMaxRuns];
+  int splits[kMaxRuns];
+  int split_off[kMaxRuns];
+  int64_t g_base[kMaxRuns];
+  int64_t ngroups[kMaxRuns];
+  int64_t gps[kMaxRuns];
+};
+
 // Both return hipSuccess or the launch error.
 hipError_t launch_flush(const AppendArgs& a, hipStream_t s);
 hipError_t launch_window_write(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// a: splits_total, L (any of the runs' layouts) and the common fields
+hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s);
 hipError_t launch_merge(const float* partial, float* out, int rows, int splits, int D, hipStream_t s);
 
 bool decode_supported(int D, int kbits, int vbits, int G);

@@ -76,8 +76,11 @@ struct Layout {
 
 KVQ_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// page_stride > 0 spaces the group pages that far apart (>= this layout's own
+// page size): caches whose groups have different bit widths give every
+// group a slot of the widest page.
 inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int vbits, int G, int R, int S0 = 0,
-                          int token_norm = 0) {
+                          int token_norm = 0, int64_t page_stride = 0) {
   Layout L{};
   L.D = D; L.kbits = kbits; L.vbits = vbits; L.G = G; L.R = R;
   L.S0 = S0; L.sink_chunks = S0 / kChunk;
@@ -100,6 +103,7 @@ inline Layout make_layout(int B, int Hkv, int D, int max_tokens, int kbits, int 
   L.off_vparams = L.off_kparams + L.kp_bytes;
   L.off_knorm = L.off_vparams + L.chunks_per_group * L.vp_chunk_bytes;
   L.page_bytes = L.off_knorm + L.chunks_per_group * L.kn_chunk_bytes;
+  if (page_stride > L.page_bytes) L.page_bytes = page_stride;
   int64_t over = (int64_t)max_tokens - S0 - R;
   L.pages = over > 0 ? over / G : 0;
   L.cap = R + G;

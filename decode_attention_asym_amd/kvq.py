@@ -38,6 +38,11 @@ class kvq_config(ctypes.Structure):
         ("sink_tokens", ctypes.c_int32),
         ("hybrid", ctypes.c_int32),
         ("token_norm", ctypes.c_int32),
+        ("adapt_delta", ctypes.c_int32),
+        ("k_bits_low", ctypes.c_int32),
+        ("v_bits_low", ctypes.c_int32),
+        ("k_bits_high", ctypes.c_int32),
+        ("v_bits_high", ctypes.c_int32),
     ]
 
 
@@ -61,6 +66,8 @@ SIGNATURES = {
     "kvq_import": (ctypes.c_int, [_P, _I64, _I32, _I32] + [_P] * 8 + [_P]),
     "kvq_export_key_norms": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "kvq_import_key_norms": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
+    "kvq_export_codes_u8": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P]),
+    "kvq_group_bits": (_I64, [_P, _P, _P, _I64]),
 }
 
 
@@ -109,12 +116,16 @@ class Config:
     sink_tokens: int = 0
     hybrid: bool = False
     token_norm: bool = False
+    adapt_delta: int = 0
+    bits_low: tuple = (0, 0)   # (key, value) bits of early groups when adapt_delta > 0
+    bits_high: tuple = (0, 0)  # (key, value) bits of recent groups when adapt_delta > 0
 
     def c(self) -> kvq_config:
         return kvq_config(
             ctypes.sizeof(kvq_config), self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
             self.max_tokens, self.k_bits, self.v_bits, self.group_size, self.residual, int(bool(self.rotate)),
             DTYPES[self.in_dtype], self.sink_tokens, int(bool(self.hybrid)), int(bool(self.token_norm)),
+            self.adapt_delta, self.bits_low[0], self.bits_low[1], self.bits_high[0], self.bits_high[1],
         )
 
 
@@ -207,13 +218,28 @@ class KVQCache:
         import torch
 
         S_req = self.default_splits() if splits is None else splits
-        rows = self.cfg.batch * self.cfg.num_q_heads
+        rows, W = self.cfg.batch * self.cfg.num_q_heads, self.cfg.head_dim + 4
         if partials is None:
-            partials = torch.empty((rows, S_req, self.cfg.head_dim + 4), dtype=torch.float32, device=q.device)
+            # a position-adaptive cache may use a few more splits than asked
+            # (one per run of equal bit widths at least)
+            cap = max(S_req, self.ws.numel() // (rows * W * 4))
+            partials = torch.empty((rows, cap, W), dtype=torch.float32, device=q.device)
         used = ctypes.c_int32(0)
         check(lib.kvq_decode_partials(self.h, _ptr(q), _ptr(partials), partials.numel() * 4, S_req,
                                       ctypes.byref(used), _stream(stream)), "kvq_decode_partials")
-        return partials, int(used.value)
+        S = int(used.value)
+        if partials.dim() == 3 and partials.shape[1] != S:
+            partials = partials.reshape(-1)[: rows * S * W].view(rows, S, W)
+        return partials, S
+
+    def group_bits(self):
+        """(key bits, value bits) uint8 arrays, one entry per quantized group."""
+        import numpy as np
+
+        ng = int(lib.kvq_group_bits(self.h, None, None, 0))
+        kb, vb = np.zeros(max(ng, 1), np.uint8), np.zeros(max(ng, 1), np.uint8)
+        lib.kvq_group_bits(self.h, kb.ctypes.data, vb.ctypes.data, ng)
+        return kb[:ng], vb[:ng]
 
     def reset(self) -> None:
         check(lib.kvq_reset(self.h), "kvq_reset")
@@ -226,19 +252,27 @@ class KVQCache:
         bc = c.batch - batch_begin if batch_count is None else batch_count
         nq, n = self.num_quantized, self.num_tokens
         nr, D, G, H = n - nq, c.head_dim, c.group_size, c.num_kv_heads
+        adaptive = c.adapt_delta > 0
         out = {
-            "k_codes": np.zeros((bc, H, nq, D * c.k_bits // 8), np.uint8),
+            "k_codes": None if adaptive else np.zeros((bc, H, nq, D * c.k_bits // 8), np.uint8),
             "k_scale": np.zeros((bc, H, nq // G, D), np.uint16),
             "k_zero": np.zeros((bc, H, nq // G, D), np.uint16),
-            "v_codes": np.zeros((bc, H, nq, D * c.v_bits // 8), np.uint8),
+            "v_codes": None if adaptive else np.zeros((bc, H, nq, D * c.v_bits // 8), np.uint8),
             "v_scale": np.zeros((bc, H, nq, D // G), np.uint16),
             "v_zero": np.zeros((bc, H, nq, D // G), np.uint16),
             "k_resid": np.zeros((bc, H, nr, D), np.uint16),
             "v_resid": np.zeros((bc, H, nr, D), np.uint16),
         }
         keys = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")
-        check(lib.kvq_export(self.h, batch_begin, bc, *(out[k].ctypes.data for k in keys), _stream(stream)),
-              "kvq_export")
+        check(lib.kvq_export(self.h, batch_begin, bc, *(None if out[k] is None else out[k].ctypes.data for k in keys),
+                             _stream(stream)), "kvq_export")
+        if adaptive:
+            # codes of mixed widths: one per byte, with the groups' bit widths
+            out["k_codes_u8"] = np.zeros((bc, H, nq, D), np.uint8)
+            out["v_codes_u8"] = np.zeros((bc, H, nq, D), np.uint8)
+            check(lib.kvq_export_codes_u8(self.h, batch_begin, bc, out["k_codes_u8"].ctypes.data,
+                                          out["v_codes_u8"].ctypes.data, _stream(stream)), "kvq_export_codes_u8")
+            out["k_gbits"], out["v_gbits"] = self.group_bits()
         if c.token_norm:
             out["k_norm"] = np.zeros((bc, H, nq), np.uint16)
             check(lib.kvq_export_key_norms(self.h, batch_begin, bc, out["k_norm"].ctypes.data, _stream(stream)),

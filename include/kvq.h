@@ -82,6 +82,15 @@ typedef struct {
                            pairwise summation tree, correctly rounded sqrt) before quantizing,
                            keep the norm as fp16 and multiply it back into the score; with
                            rotate = 1 this is the rotate-then-scale key pipeline */
+  int32_t adapt_delta;  /* Delta >= 0, a multiple of G (0: off): position-adaptive bit widths.
+                           A group's bits are fixed when it is quantized, from the length n
+                           after that append: (k_bits_high, v_bits_high) if its last token is
+                           among the last Delta of n, else (k_bits_low, v_bits_low) if it is
+                           among the first Delta tokens, else (k_bits, v_bits).  The cache then
+                           depends on how tokens were appended (a long prefill gets all three
+                           regions, groups quantized while decoding are recent), and every group
+                           slot is sized for the widest of the three. */
+  int32_t k_bits_low, v_bits_low, k_bits_high, v_bits_high; /* in {2, 4}; used when adapt_delta > 0 */
 } kvq_config;
 
 /* Device bytes the cache buffer must hold for `cfg`, or 0 if `cfg` is
@@ -149,6 +158,12 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, v
  * Split s covers the contiguous token groups [s * c, min(ng, (s + 1) * c))
  * with c = ceil(ng / S) (ng quantized groups), plus the fp16 window's 32-token
  * chunks w (counted from the first window token) with w mod S = S - 1 - s.
+ * (A position-adaptive cache first cuts its groups into runs of equal bit
+ * widths and splits each run that way into consecutive split slots, in
+ * proportion to its page bytes, at least one per run; the fp16 chunks go with
+ * the run that has the most splits.  S is then the total, at most
+ * max(num_splits, runs); KVQ_E_UNSUPPORTED when there are more runs than the
+ * workspace maximum of splits.)
  * bytes must be >= H_q * B * S * (D + 4) * 4.  Requires a non-empty cache. */
 kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials, size_t bytes, int32_t num_splits,
                                int32_t* splits_used, void* stream);
@@ -199,11 +214,25 @@ kvq_status kvq_export(kvq_cache* cache, int32_t batch_begin, int32_t batch_count
                       void* k_zero, void* v_codes, void* v_scale, void* v_zero, void* k_resid, void* v_resid,
                       void* stream);
 
+/* Codes one per byte, uint8 [bc][H_kv][nq][D] (keys, values; either may be
+ * NULL), whatever the groups' bit widths: the export for position-adaptive
+ * caches, where kvq_export's packed code arrays are KVQ_E_UNSUPPORTED (its
+ * parameter and fp16 arrays keep their shapes).  Synchronizes `stream`. */
+kvq_status kvq_export_codes_u8(kvq_cache* cache, int32_t batch_begin, int32_t batch_count, void* k_codes,
+                               void* v_codes, void* stream);
+
+/* Key and value bit widths of the quantized groups, oldest first: writes
+ * min(ng, cap) entries to each non-NULL array and returns ng (the number of
+ * quantized groups per sequence), or -1 for a NULL handle.  Without
+ * adapt_delta every entry is (k_bits, v_bits). */
+int64_t kvq_group_bits(const kvq_cache* cache, uint8_t* k_bits, uint8_t* v_bits, int64_t cap);
+
 /* Inverse of kvq_export: write canonical arrays (same shapes, none NULL) for
  * sequences [batch_begin, batch_begin + batch_count) holding n_tokens tokens
  * each into the device cache, and set the cache's token count to n_tokens
  * (every sequence shares one count, so import every sequence before decoding).
- * Synchronizes `stream`.  KVQ_E_CAPACITY if n_tokens > max_tokens. */
+ * Synchronizes `stream`.  KVQ_E_CAPACITY if n_tokens > max_tokens;
+ * KVQ_E_UNSUPPORTED for a position-adaptive cache (adapt_delta > 0). */
 kvq_status kvq_import(kvq_cache* cache, int64_t n_tokens, int32_t batch_begin, int32_t batch_count,
                       const void* k_codes, const void* k_scale, const void* k_zero, const void* v_codes,
                       const void* v_scale, const void* v_zero, const void* k_resid, const void* v_resid,

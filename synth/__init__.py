@@ -51,6 +51,9 @@ class Workload:
     sink: int = 0            # attention-sink tokens kept in fp16
     hybrid: bool = False     # per-group symmetric/asymmetric quantizer choice
     token_norm: bool = False  # key tokens divided by their norm before quantization
+    adapt_delta: int = 0      # position-adaptive bit widths: region size Delta (0: off)
+    bits_low: tuple = (0, 0)  # (key, value) bits of early groups
+    bits_high: tuple = (0, 0)  # (key, value) bits of recent groups
 
     @property
     def gqa(self) -> int:

@@ -18,15 +18,29 @@ def log(*a):
     print(*a, flush=True, file=sys.stderr)
 
 
-def oracle_encode_slices(w, K, V, pairs):
-    """Oracle encoding of (b, hkv) slices.  K, V: torch [B, Hkv, n, D] (any device)."""
+def oracle_group_bits(w, calls):
+    """Per-group (key, value) bits of a position-adaptive workload appended in
+    `calls` (token counts per append), or None without adaptive bits."""
+    if not w.adapt_delta:
+        return None
+    return oracle.adaptive_group_bits(w.G, w.R, w.sink, w.adapt_delta, calls, w.bits_low, (w.kbits, w.vbits),
+                                      w.bits_high)
+
+
+def oracle_encode_slices(w, K, V, pairs, calls=None):
+    """Oracle encoding of (b, hkv) slices.  K, V: torch [B, Hkv, n, D] (any
+    device); calls: the append sizes that built the cache (adaptive bits)."""
+    gb = oracle_group_bits(w, [K.shape[2]] if calls is None else calls)
 
     def enc(bh):
         b, h = bh
         k = to_oracle_input(K[b, h], w.dtype)
         v = to_oracle_input(V[b, h], w.dtype)
-        return oracle.encode_slice(k, v, w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate, sink=w.sink,
-                                   hybrid=w.hybrid, token_norm=w.token_norm)
+        e = oracle.encode_slice(k, v, w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate, sink=w.sink,
+                                hybrid=w.hybrid, token_norm=w.token_norm, group_bits=gb)
+        if gb is not None:
+            e["gbits"] = gb
+        return e
 
     with ThreadPoolExecutor(THREADS) as ex:
         return dict(zip(pairs, ex.map(enc, pairs)))
@@ -37,7 +51,19 @@ def assert_export_matches(w, exp, b0, encs):
     for (b, h), enc in encs.items():
         bi = b - b0
         assert exp["nq"] == enc["nq"], (exp["nq"], enc["nq"])
-        for key, bits in (("k_codes", w.kbits), ("v_codes", w.vbits)):
+        if "gbits" in enc:
+            ng = enc["nq"] // w.G
+            assert np.array_equal(exp["k_gbits"], enc["gbits"][0][:ng]), "key group bits"
+            assert np.array_equal(exp["v_gbits"], enc["gbits"][1][:ng]), "value group bits"
+        code_keys = (("k_codes", w.kbits), ("v_codes", w.vbits))
+        if "k_codes_u8" in exp:  # mixed widths: one code per byte
+            code_keys = ()
+            for key in ("k_codes", "v_codes"):
+                got = exp[key + "_u8"][bi, h]
+                if not np.array_equal(got, enc[key]):
+                    bad = np.argwhere(got != enc[key])
+                    raise AssertionError(f"{key} mismatch at slice ({b},{h}): {len(bad)} codes, first {bad[:5].tolist()}")
+        for key, bits in code_keys:
             ref = oracle.pack_codes(enc[key], bits) if enc["nq"] else np.zeros((0, w.D * bits // 8), np.uint8)
             got = exp[key][bi, h]
             if not np.array_equal(got, ref):
@@ -53,9 +79,15 @@ def assert_export_matches(w, exp, b0, encs):
 
 def canonical_slice(exp, bi, h, D, kbits, vbits):
     """One slice of an export as an oracle cache dict (codes unpacked)."""
+    if "k_codes_u8" in exp:
+        kc = exp["k_codes_u8"][bi, h].astype(np.uint16)
+        vc = exp["v_codes_u8"][bi, h].astype(np.uint16)
+    else:
+        kc = oracle.unpack_codes(exp["k_codes"][bi, h], D, kbits)
+        vc = oracle.unpack_codes(exp["v_codes"][bi, h], D, vbits)
     return {
-        "k_codes": oracle.unpack_codes(exp["k_codes"][bi, h], D, kbits),
-        "v_codes": oracle.unpack_codes(exp["v_codes"][bi, h], D, vbits),
+        "k_codes": kc,
+        "v_codes": vc,
         "k_scale": exp["k_scale"][bi, h], "k_zero": exp["k_zero"][bi, h],
         "v_scale": exp["v_scale"][bi, h], "v_zero": exp["v_zero"][bi, h],
         "k_resid": exp["k_resid"][bi, h], "v_resid": exp["v_resid"][bi, h],

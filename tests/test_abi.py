@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     text = open(os.path.join(ROOT, "include", "kvq.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_three_calls():
@@ -135,3 +135,52 @@ def test_token_norm_adds_two_bytes_per_quantized_token():
         slices = 2 * 2
         pages = (10000 - R) // G
         assert abs((b - a) - slices * pages * G * 2) <= 256
+
+
+@pytest.mark.parametrize("bad", [
+    dict(adapt_delta=32),  # not a multiple of G = 64
+    dict(adapt_delta=-64),
+    dict(adapt_delta=128, bits_low=(3, 2), bits_high=(4, 4)),
+    dict(adapt_delta=128, bits_low=(2, 2), bits_high=(4, 8)),
+    dict(adapt_delta=128),  # widths left at 0
+])
+def test_invalid_adaptive_configs_rejected(bad):
+    import decode_attention_asym_amd as kvq
+
+    assert kvq.cache_bytes(_cfg(**bad)) == 0
+    assert kvq.lib.kvq_last_error()
+
+
+def test_adaptive_group_slots_hold_the_widest_page():
+    """Every group slot of a position-adaptive cache is as large as the widest
+    of the three (key, value) bit pairs' pages; the fp16 parts do not change."""
+    import decode_attention_asym_amd as kvq
+
+    n, G, R = 10000, 64, 128
+    base = dict(max_tokens=n, group_size=G, residual=R, k_bits=2, v_bits=2)
+    pages = (n - R) // G
+    slices = 2 * 2
+    plain = {(kb, vb): kvq.cache_bytes(_cfg(**{**base, "k_bits": kb, "v_bits": vb})) for kb in (2, 4) for vb in (2, 4)}
+    a = kvq.cache_bytes(_cfg(**base, adapt_delta=512, bits_low=(2, 2), bits_high=(4, 4)))
+    assert a == plain[(4, 4)]
+    b = kvq.cache_bytes(_cfg(**base, adapt_delta=512, bits_low=(2, 4), bits_high=(2, 2)))
+    assert b == plain[(2, 4)]
+    # the widest page per slot: K4V4 pages are (4 + 4) * D / 8 * G bytes of codes larger than K2V2 by 2x
+    assert (plain[(4, 4)] - plain[(2, 2)]) == pytest.approx(slices * pages * G * 128 * 4 / 8, abs=512)
+
+
+def test_group_bits_on_a_fresh_handle():
+    import decode_attention_asym_amd as kvq
+    from decode_attention_asym_amd.kvq import lib
+
+    c = _cfg(adapt_delta=128, bits_low=(2, 2), bits_high=(4, 4))
+    cc = c.c()
+    h = ctypes.c_void_p()
+    assert lib.kvq_create(ctypes.byref(cc), 1 << 40, kvq.cache_bytes(c), ctypes.byref(h)) == kvq.KVQ_OK
+    try:
+        assert lib.kvq_group_bits(h, None, None, 0) == 0
+        assert lib.kvq_export_codes_u8(h, 0, 1, None, None, None) == kvq.KVQ_E_ARG
+        assert lib.kvq_export_codes_u8(h, 0, 3, 1 << 40, None, None) == kvq.KVQ_E_ARG  # batch range
+    finally:
+        lib.kvq_destroy(h)
+    assert lib.kvq_group_bits(None, None, None, 0) == -1

@@ -81,6 +81,17 @@ SMALL = [
     WORKLOADS[2].replace(name="k4v2-g64-rot-tokennorm", B=2, N=3000 + 21, rotate=True, token_norm=True),
     WORKLOADS[3].replace(name="gqa8-tokennorm-sink-hybrid", B=1, N=1500 + 7, token_norm=True, sink=64, hybrid=True),
     WORKLOADS[0].replace(name="d64-tokennorm-k4v4", B=2, Hq=4, Hkv=2, N=700 + 1, kbits=4, vbits=4, token_norm=True),
+    # position-adaptive bit widths (early / middle / recent groups), one prefill
+    WORKLOADS[2].replace(name="adapt-k4v2-lo22-hi44", B=2, N=3000 + 21, adapt_delta=512, bits_low=(2, 2),
+                         bits_high=(4, 4)),
+    WORKLOADS[1].replace(name="adapt-k2v2-lo24-hi42-sink", B=2, N=2000 + 3, sink=64, adapt_delta=256,
+                         bits_low=(2, 4), bits_high=(4, 2)),
+    WORKLOADS[0].replace(name="d64-adapt-tokennorm-gqa2", B=2, Hq=4, Hkv=2, N=900 + 5, token_norm=True,
+                         adapt_delta=128, bits_low=(4, 4), bits_high=(4, 4)),
+    WORKLOADS[3].replace(name="gqa8-adapt-hybrid", B=1, N=2500 + 9, hybrid=True, adapt_delta=640,
+                         bits_low=(4, 2), bits_high=(4, 4)),
+    WORKLOADS[1].replace(name="adapt-delta-covers-all", B=2, N=700 + 3, adapt_delta=4096, bits_low=(2, 2),
+                         bits_high=(4, 4)),
 ]
 
 
@@ -247,6 +258,97 @@ def test_stepwise_append_equals_prefill(sink, hybrid, tn):
         assert np.array_equal(ea[key], eb[key]), key
     encs = oracle_encode_slices(w, K, V, [(bb, h) for bb in range(w.B) for h in range(w.Hkv)])
     assert_export_matches(w, ea, 0, encs)
+
+
+@pytest.mark.parametrize("sink,tn", [(0, False), (64, True)])
+def test_adaptive_stepwise_matches_oracle(sink, tn):
+    """Position-adaptive bits built by a prefill and then appends: the groups'
+    bits follow the lengths after each append, codes and parameters are
+    bit-exact, and decode over the mixed-width runs (several split counts, so
+    runs get one or more splits) matches the oracle."""
+    kvq = _lib()
+    w = WORKLOADS[2].replace(name="adaptive-stepwise", B=2, Hkv=2, Hq=8, N=2600, sink=sink, token_norm=tn,
+                             adapt_delta=384, bits_low=(2, 2), bits_high=(4, 4))
+    syn = Synth(w, "cuda")
+    K, V = syn.kv_all()
+    c = kvq.KVQCache(kvq.config_for(w))
+    sizes = [1500, 1, 64, 1, 200, 3, 130, 1]
+    sizes.append(w.N - sum(sizes))
+    t = 0
+    q = syn.q()
+    q_host = to_oracle_input(q, w.dtype)
+    for i, sz in enumerate(sizes):
+        c.append(K[:, :, t:t + sz].contiguous(), V[:, :, t:t + sz].contiguous())
+        t += sz
+        if i in (0, 4, len(sizes) - 1):
+            exp = c.export()
+            encs = oracle_encode_slices(w, K[:, :, :t], V[:, :, :t], [(b, h) for b in range(w.B) for h in range(w.Hkv)],
+                                        calls=sizes[:i + 1])
+            assert_export_matches(w, exp, 0, encs)
+            kb, _ = c.group_bits()
+            log(f"[adaptive] n={t}: group bits runs {np.flatnonzero(np.diff(kb.astype(int))).tolist()}")
+            ref = oracle_rows(w, exp, 0, q_host, list(range(w.B)))
+            refs = np.stack([ref[b] for b in range(w.B)])
+            for splits in (1, 2, 7, None):
+                out = c.decode(q, splits=splits)
+                torch.cuda.synchronize()
+                err, _ = rel_l2(out.double().cpu().numpy(), refs)
+                log(f"[adaptive] n={t} splits={splits}: rel L2 {err:.3e}")
+                assert err <= TOL_REL_L2, (t, splits, err)
+
+
+def test_adaptive_many_runs_matches_oracle():
+    """Appends of 512 tokens with Delta = 256 > R leave, per append, middle
+    groups then two groups quantized while recent: more runs of equal widths
+    than one mixed launch takes (8), so the decode falls back to one launch
+    per run; before that, with fewer runs, it uses the mixed launch."""
+    kvq = _lib()
+    w = WORKLOADS[2].replace(name="adaptive-many-runs", B=1, Hkv=2, Hq=8, N=600 + 5 * 512, adapt_delta=256,
+                             bits_low=(2, 2), bits_high=(4, 4))
+    syn = Synth(w, "cuda")
+    K, V = syn.kv_all()
+    c = kvq.KVQCache(kvq.config_for(w))
+    sizes = [600] + [512] * 5
+    q = syn.q()
+    q_host = to_oracle_input(q, w.dtype)
+    t = 0
+    for i, sz in enumerate(sizes):
+        c.append(K[:, :, t:t + sz].contiguous(), V[:, :, t:t + sz].contiguous())
+        t += sz
+        if i not in (2, len(sizes) - 1):
+            continue
+        kb, vb = c.group_bits()
+        pair = kb.astype(int) * 16 + vb
+        runs = 1 + int(np.count_nonzero(np.diff(pair)))
+        log(f"[adaptive] n={t}: {runs} runs of equal widths")
+        assert (runs <= 8) if i == 2 else (runs > 8)
+        exp = c.export()
+        encs = oracle_encode_slices(w, K[:, :, :t], V[:, :, :t], [(0, h) for h in range(w.Hkv)], calls=sizes[:i + 1])
+        assert_export_matches(w, exp, 0, encs)
+        ref = oracle_rows(w, exp, 0, q_host, [0])[0]
+        for splits in (1, 5, None):
+            out = c.decode(q, splits=splits)
+            torch.cuda.synchronize()
+            err, _ = rel_l2(out[0].double().cpu().numpy(), ref)
+            log(f"[adaptive] n={t} splits={splits}: rel L2 {err:.3e}")
+            assert err <= TOL_REL_L2, (t, splits, err)
+
+
+def test_adaptive_rejects_import_and_packed_export():
+    kvq = _lib()
+    w = WORKLOADS[1].replace(name="adaptive-api", B=1, N=600, adapt_delta=128, bits_low=(2, 2), bits_high=(4, 4))
+    syn = Synth(w, "cuda")
+    K, V = syn.kv_all()
+    c = kvq.KVQCache(kvq.config_for(w))
+    c.append(K, V)
+    exp = c.export()
+    assert exp["k_codes"] is None and exp["k_codes_u8"].shape == (1, w.Hkv, c.num_quantized, w.D)
+    z = np.zeros(16, np.uint8)
+    st = kvq.lib.kvq_export(c.h, 0, 1, z.ctypes.data, *([None] * 7), 0)
+    assert st == kvq.KVQ_E_UNSUPPORTED
+    arrs = [np.zeros(1 << 20, np.uint8) for _ in range(8)]
+    st = kvq.lib.kvq_import(c.h, 600, 0, 1, *(a.ctypes.data for a in arrs), 0)
+    assert st == kvq.KVQ_E_UNSUPPORTED
 
 
 @pytest.mark.parametrize("tn", [False, True])
