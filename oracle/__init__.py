@@ -85,6 +85,12 @@ def _declare(L):
     L.orc_bits_per_element.argtypes = [i64, i32, i32, i32, i32, f64]
     L.orc_bits_per_element_sink.restype = f64
     L.orc_bits_per_element_sink.argtypes = [i64, i32, i32, i32, i32, i32, f64]
+    L.orc_code_histogram.restype = i32
+    L.orc_code_histogram.argtypes = [P, i64, i32, P]
+    L.orc_kl_divergence.restype = f64
+    L.orc_kl_divergence.argtypes = [P, P, i32]
+    L.orc_drift_check.restype = i32
+    L.orc_drift_check.argtypes = [P, P, i64, i32, i32, i32, i32, P, P, f64, P, P, P]
     return L
 
 
@@ -209,6 +215,39 @@ def adaptive_group_bits(G: int, R: int, sink: int, delta: int, calls, low, mid, 
     if ng < 0:
         raise ValueError("orc_adaptive_group_bits rejected its arguments")
     return kb[:ng].copy(), vb[:ng].copy()
+
+
+def code_histogram(codes, bits: int) -> np.ndarray:
+    """Counts of each code value in [0, 2^bits) (int64)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint16).reshape(-1)
+    hist = np.zeros(1 << bits, np.int64)
+    if lib().orc_code_histogram(_p(codes), codes.size, bits, _p(hist)) < 0:
+        raise ValueError("code out of range")
+    return hist
+
+
+def kl_divergence(p, q) -> float:
+    """D_KL(p || q), natural log, 0 log 0 = 0, +inf where q has no mass."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    assert p.shape == q.shape
+    return float(lib().orc_kl_divergence(_p(p), _p(q), p.size))
+
+
+def drift_check(k_codes, v_codes, G: int, D: int, kbits: int, vbits: int, cal_k, cal_v, thr: float = 0.1):
+    """Per-group KL of the key and value code histograms of one slice's
+    canonical codes against calibration counts; returns (kl_k, kl_v, flags)."""
+    k_codes = np.ascontiguousarray(k_codes, dtype=np.uint16)
+    v_codes = np.ascontiguousarray(v_codes, dtype=np.uint16)
+    ng = k_codes.size // (G * D)
+    cal_k = np.ascontiguousarray(cal_k, dtype=np.int64)
+    cal_v = np.ascontiguousarray(cal_v, dtype=np.int64)
+    kl_k, kl_v = np.zeros(max(ng, 1)), np.zeros(max(ng, 1))
+    flags = np.zeros(max(ng, 1), np.uint8)
+    if lib().orc_drift_check(_p(k_codes), _p(v_codes), ng, G, D, kbits, vbits, _p(cal_k), _p(cal_v), thr,
+                             _p(kl_k), _p(kl_v), _p(flags)) < 0:
+        raise ValueError("orc_drift_check rejected its arguments")
+    return kl_k[:ng], kl_v[:ng], flags[:ng]
 
 
 def encode_slice(k, v, dtype: str, D: int, kbits: int, vbits: int, G: int, R: int, rotate: bool,

@@ -51,6 +51,17 @@
  *    quantizes it: recent if its last token is among the last Delta of n,
  *    otherwise early if its last token is among the first Delta, otherwise
  *    middle (the printed cases, recent taking precedence where they overlap).
+ *  - Drift detection ("Asymmetric Key-Value Quantization ...", section 3.3:
+ *    the KL divergence of the current distribution of quantized values from
+ *    the calibration distribution, a threshold of 0.1 triggering a
+ *    requantization of the affected tokens).  Here the distributions are code
+ *    histograms: a group's key codes (all G x D of them) and value codes,
+ *    against the pooled code histogram of a calibration range of groups of
+ *    the same kv head; KL in natural log with 0 log 0 = 0 and +inf where the
+ *    calibration has no mass; a group is flagged when its KL exceeds the
+ *    threshold.  The requantization itself is the uniform quantizer applied
+ *    again to the affected groups' tokens (the page's Lloyd-Max step is not
+ *    reproduced), i.e. the ordinary encoding of those tokens.
  *  - Bits-per-element accounting: "Asymmetric Key-Value Quantization ...",
  *    section 3.1 (average of key and value bit widths) and section 3.4
  *    (combined compression table); here the per-group fp16 scale and zero
@@ -336,6 +347,67 @@ int64_t orc_adaptive_group_bits(int G, int R, int S0, int delta, int ncalls, con
     done = ng;
   }
   return done;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Drift detection: code histograms and their KL divergence from a          */
+/* calibration histogram ("Asymmetric Key-Value Quantization ...", 3.3).     */
+/* ------------------------------------------------------------------------ */
+
+/* Adds the histogram of `count` codes (each in [0, 2^bits)) to hist[2^bits].
+ * Returns -1 if a code is out of range. */
+int orc_code_histogram(const uint16_t* codes, int64_t count, int bits, int64_t* hist) {
+  const int nb = 1 << bits;
+  for (int64_t i = 0; i < count; ++i) {
+    if (codes[i] >= nb) return -1;
+    hist[codes[i]] += 1;
+  }
+  return 0;
+}
+
+/* D_KL(p || q) = sum_i p_i ln(p_i / q_i) over nb bins, summed in bin order;
+ * bins with p_i = 0 contribute 0, a bin with p_i > 0 and q_i = 0 makes it
+ * +inf. */
+double orc_kl_divergence(const double* p, const double* q, int nb) {
+  double kl = 0.0;
+  for (int i = 0; i < nb; ++i) {
+    if (p[i] == 0.0) continue;
+    if (q[i] == 0.0) return INFINITY;
+    kl += p[i] * log(p[i] / q[i]);
+  }
+  return kl;
+}
+
+/* Drift check of ng quantized groups of one slice, canonical codes
+ * k_codes / v_codes [ng * G][D].  The calibration histograms are counts
+ * (cal_k[2^kbits], cal_v[2^vbits]), turned into probabilities by dividing by
+ * their totals; a group's probabilities are its counts divided by G * D.
+ * Writes kl_k[g], kl_v[g] and flags[g] = (kl_k > thr) | (kl_v > thr) << 1.
+ * Returns 0, or -1 on bad arguments. */
+int orc_drift_check(const uint16_t* k_codes, const uint16_t* v_codes, int64_t ng, int G, int D, int kbits,
+                    int vbits, const int64_t* cal_k, const int64_t* cal_v, double thr, double* kl_k,
+                    double* kl_v, uint8_t* flags) {
+  if (ng < 0 || G <= 0 || D <= 0 || kbits < 1 || kbits > 8 || vbits < 1 || vbits > 8) return -1;
+  const int nbk = 1 << kbits, nbv = 1 << vbits;
+  double qk[256], qv[256], pk[256], pv[256];
+  int64_t tk = 0, tv = 0;
+  for (int i = 0; i < nbk; ++i) tk += cal_k[i];
+  for (int i = 0; i < nbv; ++i) tv += cal_v[i];
+  if (tk <= 0 || tv <= 0) return -1;
+  for (int i = 0; i < nbk; ++i) qk[i] = (double)cal_k[i] / (double)tk;
+  for (int i = 0; i < nbv; ++i) qv[i] = (double)cal_v[i] / (double)tv;
+  const int64_t per = (int64_t)G * D;
+  for (int64_t g = 0; g < ng; ++g) {
+    int64_t hk[256] = {0}, hv[256] = {0};
+    if (orc_code_histogram(k_codes + g * per, per, kbits, hk) < 0) return -1;
+    if (orc_code_histogram(v_codes + g * per, per, vbits, hv) < 0) return -1;
+    for (int i = 0; i < nbk; ++i) pk[i] = (double)hk[i] / (double)per;
+    for (int i = 0; i < nbv; ++i) pv[i] = (double)hv[i] / (double)per;
+    kl_k[g] = orc_kl_divergence(pk, qk, nbk);
+    kl_v[g] = orc_kl_divergence(pv, qv, nbv);
+    flags[g] = (uint8_t)((kl_k[g] > thr ? 1 : 0) | (kl_v[g] > thr ? 2 : 0));
+  }
+  return 0;
 }
 
 /* ------------------------------------------------------------------------ */

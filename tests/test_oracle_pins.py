@@ -711,3 +711,95 @@ def test_adaptive_encoding_is_per_group_fixed_bit_encoding(orc):
     same = orc.encode_slice(k, v, "f32", D, 4, 2, G, R, False, group_bits=(np.full(12, 4, np.uint8), np.full(12, 2, np.uint8)))
     for key in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid"):
         assert np.array_equal(same[key], ref[(4, 2)][key]), key
+
+
+# ------------------------------------------------- drift detection (KL of code histograms)
+def test_kl_closed_forms(orc):
+    ln = np.log
+    assert orc.kl_divergence([0.25, 0.25, 0.5], [0.25, 0.25, 0.5]) == 0.0
+    # one-hot p: D_KL = -ln q_i
+    assert orc.kl_divergence([0, 0, 1], [0.25, 0.25, 0.5]) == pytest.approx(ln(2), rel=1e-15)
+    assert orc.kl_divergence([1, 0, 0], [0.25, 0.25, 0.5]) == pytest.approx(ln(4), rel=1e-15)
+    assert orc.kl_divergence([1, 0], [0.5, 0.5]) == pytest.approx(ln(2), rel=1e-15)
+    # mass where the calibration has none: infinite; no mass where it has none: ignored
+    assert orc.kl_divergence([0.5, 0.5], [1.0, 0.0]) == float("inf")
+    assert orc.kl_divergence([1.0, 0.0], [1.0, 0.0]) == 0.0
+    # two bins, p = (1/4, 3/4), q = (1/2, 1/2): (1/4) ln(1/2) + (3/4) ln(3/2) = (3/4) ln 3 - ln 2
+    assert orc.kl_divergence([0.25, 0.75], [0.5, 0.5]) == pytest.approx(0.75 * ln(3) - ln(2), rel=1e-14)
+
+
+def test_kl_matches_library_relative_entropy(orc):
+    from scipy.stats import entropy
+
+    rng = np.random.default_rng(5)
+    for nb in (4, 16):
+        for _ in range(50):
+            p = rng.dirichlet(np.ones(nb) * 0.7)
+            q = rng.dirichlet(np.ones(nb) * 2.0)
+            got = orc.kl_divergence(p, q)
+            assert got == pytest.approx(entropy(p, q), rel=1e-12, abs=1e-15)
+            assert got > 0.0  # Gibbs: zero only at p = q
+
+
+def test_code_histogram_counts(orc):
+    ramp = np.arange(16 * 37) % 16
+    h = orc.code_histogram(ramp, 4)
+    assert np.array_equal(h, np.full(16, 37))
+    rng = np.random.default_rng(9)
+    c = rng.integers(0, 4, 5000)
+    h = orc.code_histogram(c, 2)
+    assert h.sum() == 5000 and np.array_equal(h, np.bincount(c, minlength=4))
+    assert np.array_equal(orc.code_histogram(rng.permutation(c), 2), h)
+    with pytest.raises(ValueError):
+        orc.code_histogram(np.array([4]), 2)
+
+
+def test_drift_check_flags_closed_forms(orc):
+    G, D = 32, 64
+    per = G * D
+    # calibration: key codes uniform over 16 values, value codes (1, 1, 1, 5) / 8
+    cal_k = np.full(16, 1000, np.int64)
+    cal_v = np.array([1, 1, 1, 5], np.int64) * 100
+    kc = np.zeros((3, per), np.uint16)
+    vc = np.zeros((3, per), np.uint16)
+    kc[0] = np.arange(per) % 16                       # matches the calibration exactly
+    vc[0] = np.repeat([0, 1, 2, 3, 3, 3, 3, 3], per // 8)
+    kc[1] = 7                                         # one value: KL = ln 16
+    vc[1] = 3                                         # one value: KL = ln (8 / 5)
+    kc[2] = np.arange(per) % 8                        # half the values, evenly: KL = ln 2
+    vc[2] = np.arange(per) % 4                        # uniform vs (1,1,1,5)/8: sum 1/4 ln(2) * 3 + 1/4 ln(2/5)
+    kl_k, kl_v, flags = orc.drift_check(kc.reshape(-1, D), vc.reshape(-1, D), G, D, 4, 2, cal_k, cal_v, 0.1)
+    ln = np.log
+    assert kl_k[0] == 0.0 and kl_v[0] == 0.0 and flags[0] == 0
+    assert kl_k[1] == pytest.approx(ln(16), rel=1e-14) and kl_v[1] == pytest.approx(ln(8 / 5), rel=1e-14)
+    assert flags[1] == 3
+    assert kl_k[2] == pytest.approx(ln(2), rel=1e-14)
+    assert kl_v[2] == pytest.approx(0.75 * ln(2) + 0.25 * ln(2 / 5), rel=1e-13)
+    assert flags[2] == (1 | (2 if kl_v[2] > 0.1 else 0))
+    # the threshold is strict
+    _, _, f = orc.drift_check(kc.reshape(-1, D), vc.reshape(-1, D), G, D, 4, 2, cal_k, cal_v, float(kl_k[2]))
+    assert (f[2] & 1) == 0
+
+
+def test_drift_check_on_encoded_caches(orc):
+    """Stationary Gaussian tokens stay far below the 0.1 threshold against a
+    calibration taken from the first groups; tokens whose values turn heavy
+    tailed (most near zero, a few large) concentrate their codes and cross it."""
+    rng = np.random.default_rng(13)
+    D, G, R, n = 64, 32, 32, 32 * 40 + 32
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    # groups 30..39: heavy tails (a scale of 0.05 with 5% of entries times 40)
+    sl = slice(30 * G, 40 * G)
+    for x in (k, v):
+        x[sl] *= 0.05
+        mask = rng.random(x[sl].shape) < 0.05
+        x[sl][mask] *= 40
+    enc = orc.encode_slice(k, v, "f32", D, 4, 2, G, R, False)
+    ng = enc["nq"] // G
+    assert ng == 40
+    cal_k = orc.code_histogram(enc["k_codes"][:10 * G], 4)
+    cal_v = orc.code_histogram(enc["v_codes"][:10 * G], 2)
+    kl_k, kl_v, flags = orc.drift_check(enc["k_codes"], enc["v_codes"], G, D, 4, 2, cal_k, cal_v, 0.1)
+    assert (kl_k[:30] < 0.05).all() and (kl_v[:30] < 0.05).all() and (flags[:30] == 0).all()
+    assert (kl_k[30:] > 0.1).all() and (kl_v[30:] > 0.1).all() and (flags[30:] == 3).all()
