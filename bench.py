@@ -179,6 +179,8 @@ def main() -> int:
                     help="position-adaptive bit widths: region size Delta in tokens (0: off)")
     ap.add_argument("--bits-low", default="2,2", help="key,value bits of the first Delta tokens")
     ap.add_argument("--bits-high", default="4,4", help="key,value bits of the last Delta tokens")
+    ap.add_argument("--drift", action="store_true",
+                    help="also time the drift check (code histograms + KL per group) over every quantized group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=16)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -281,6 +283,28 @@ def main() -> int:
     achieved = (sum(dec_bytes) / len(dec_bytes)) / (dec_avg_ms * 1e-3) / 1e9
     assert torch.isfinite(out).all()
 
+    drift = None
+    if args.drift and not w.adapt_delta:
+        ng = cache.num_groups()
+        kh, vh = cache.code_histograms(0, max(1, ng // 3))
+        for _ in range(2):
+            cache.drift_check(kh, vh)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        d0.record()
+        for _ in range(reps):
+            _, _, fl = cache.drift_check(kh, vh)
+        d1.record()
+        torch.cuda.synchronize()
+        us = d0.elapsed_time(d1) / reps * 1e3
+        slices = w.B * w.Hkv
+        nbytes = slices * ng * (w.G * w.D * (w.kbits + w.vbits) // 8 + 17)  # codes read, KL pair + flag written
+        drift = {"kernel": "drift_kernel (code histograms + KL per group)", "groups": slices * ng,
+                 "avg_us": round(us, 2), "bytes": nbytes, "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                 "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                 "flagged": int((fl != 0).sum().item())}
+
     cpu = None
     if not args.no_cpu_baseline:
         from synth import to_oracle_input  # noqa: F401
@@ -324,6 +348,7 @@ def main() -> int:
             "bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes)),
         },
         "prefill_ms": round(prefill_ms, 2),
+        **({"drift_check": drift} if drift else {}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

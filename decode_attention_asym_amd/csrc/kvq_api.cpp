@@ -452,6 +452,95 @@ kvq_status kvq_decode_attn(kvq_cache* h, const void* q, float* out, void* ws, si
   return kvq_decode_attn_splits(h, q, out, ws, ws_bytes, choose_splits(h), stream);
 }
 
+// ---------------------------------------------------------------- drift detection
+
+namespace {
+kvq_status drift_common(kvq_cache* h, int64_t g0, int64_t g1, kvq::DriftArgs* a) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  if (h->cfg.adapt_delta > 0) return fail(KVQ_E_UNSUPPORTED, "drift detection on a position-adaptive cache");
+  const int64_t ng = ngroups_of(h);
+  if (g0 < 0 || g1 < g0 || g1 > ng)
+    return fail(KVQ_E_ARG, "group range [%lld, %lld) outside the %lld quantized groups", (long long)g0, (long long)g1,
+                (long long)ng);
+  *a = kvq::DriftArgs{};
+  a->cache = h->buf;
+  a->L = h->L;
+  a->Hkv = h->cfg.num_kv_heads;
+  a->g0 = g0;
+  a->ng = g1 - g0;
+  return KVQ_OK;
+}
+}  // namespace
+
+kvq_status kvq_code_histograms(kvq_cache* h, int64_t g0, int64_t g1, uint64_t* k_hist, uint64_t* v_hist,
+                               void* stream) {
+  kvq::DriftArgs a;
+  kvq_status st = drift_common(h, g0, g1, &a);
+  if (st != KVQ_OK) return st;
+  if (!k_hist || !v_hist || !aligned(k_hist, 8) || !aligned(v_hist, 8))
+    return fail(KVQ_E_ARG, "histogram arrays NULL or not 8-byte aligned");
+  a.hist_k = k_hist;
+  a.hist_v = v_hist;
+  hipError_t e = kvq::launch_code_histograms(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(h, e, "histogram kernel launch");
+  return ok();
+}
+
+kvq_status kvq_drift_check(kvq_cache* h, int64_t g0, int64_t g1, const uint64_t* cal_k, const uint64_t* cal_v,
+                           double threshold, double* kl_k, double* kl_v, uint8_t* flags, void* stream) {
+  kvq::DriftArgs a;
+  kvq_status st = drift_common(h, g0, g1, &a);
+  if (st != KVQ_OK) return st;
+  if (!cal_k || !cal_v || !kl_k || !kl_v || !flags || !aligned(cal_k, 8) || !aligned(cal_v, 8) || !aligned(kl_k, 8) ||
+      !aligned(kl_v, 8))
+    return fail(KVQ_E_ARG, "drift arrays NULL or not 8-byte aligned");
+  if (!(threshold >= 0.0)) return fail(KVQ_E_ARG, "threshold must be >= 0");
+  a.cal_k = cal_k;
+  a.cal_v = cal_v;
+  a.threshold = threshold;
+  a.kl_k = kl_k;
+  a.kl_v = kl_v;
+  a.flags = flags;
+  hipError_t e = kvq::launch_drift_check(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(h, e, "drift kernel launch");
+  return ok();
+}
+
+kvq_status kvq_requantize(kvq_cache* h, int64_t g0, int64_t g1, const void* k, const void* v, const uint8_t* flags,
+                          void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  const int64_t ng = ngroups_of(h);
+  if (g0 < 0 || g1 < g0 || g1 > ng)
+    return fail(KVQ_E_ARG, "group range [%lld, %lld) outside the %lld quantized groups", (long long)g0, (long long)g1,
+                (long long)ng);
+  if (g1 == g0) return ok();
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_E_ARG, "k/v NULL or not 16-byte aligned");
+  const int G = h->cfg.group_size;
+  kvq::AppendArgs a{};
+  a.cache = h->buf;
+  a.k = k;
+  a.v = v;
+  a.in_dtype = h->cfg.in_dtype;
+  a.rotate = h->cfg.rotate;
+  a.hybrid = h->cfg.hybrid;
+  a.Hkv = h->cfg.num_kv_heads;
+  a.T = (g1 - g0) * G;
+  a.n_old = h->cfg.sink_tokens + g0 * G;  // every token of the range comes from k, v
+  a.flags = flags;
+  a.flag_g0 = g0;
+  a.flag_stride = g1 - g0;
+  for (const Run& r : runs_of(h, g0, g1)) {
+    a.L = layout_for(h, r.kb, r.vb);
+    a.g_first = r.g0;
+    a.n_flush = r.g1 - r.g0;
+    hipError_t e = kvq::launch_flush(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_error(h, e, "requantize kernel launch");
+  }
+  return ok();
+}
+
 // ---------------------------------------------------------------- export / import
 
 kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void* k_scale, void* k_zero,

@@ -163,6 +163,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   const int64_t g = a.g_first + blockIdx.x;
   const int64_t pos0 = L.S0 + g * G;  // token position of the group's first token
   const int64_t slice = blockIdx.y;
+  if (a.flags != nullptr && a.flags[slice * a.flag_stride + (g - a.flag_g0)] == 0) return;  // not requantized
   const int64_t in_base = slice * a.T * D;  // [B][H_kv] flattened == slice
   uint8_t* ring = a.cache;
 

@@ -25,6 +25,27 @@ struct AppendArgs {
   int64_t n_write;      // window positions written by this call
   int64_t s_first;      // first sink position written by this call
   int64_t n_sink_write; // sink positions written by this call
+  // requantization: only groups g with flags[slice * flag_stride + g - flag_g0]
+  // != 0 are rewritten (all when flags is null)
+  const uint8_t* flags;
+  int64_t flag_g0;
+  int64_t flag_stride;
+};
+
+// Drift detection over groups [g0, g0 + ng) of every slice.
+struct DriftArgs {
+  const uint8_t* cache;
+  Layout L;
+  int Hkv;
+  int64_t g0, ng;
+  const uint64_t* cal_k;  // [H_kv][2^k_bits] calibration code counts
+  const uint64_t* cal_v;  // [H_kv][2^v_bits]
+  double threshold;
+  double* kl_k;           // [slices][ng]
+  double* kl_v;
+  uint8_t* flags;         // bit 0: key KL > threshold, bit 1: value KL > threshold
+  uint64_t* hist_k;       // [H_kv][2^k_bits] (histogram mode)
+  uint64_t* hist_v;
 };
 
 struct DecodeArgs {
@@ -73,6 +94,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // a: splits_total, L (any of the runs' layouts) and the common fields
 hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s);
 hipError_t launch_merge(const float* partial, float* out, int rows, int splits, int D, hipStream_t s);
+hipError_t launch_code_histograms(const DriftArgs& a, hipStream_t s);
+hipError_t launch_drift_check(const DriftArgs& a, hipStream_t s);
 
 bool decode_supported(int D, int kbits, int vbits, int G);
 

@@ -68,6 +68,9 @@ SIGNATURES = {
     "kvq_import_key_norms": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "kvq_export_codes_u8": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P]),
     "kvq_group_bits": (_I64, [_P, _P, _P, _I64]),
+    "kvq_code_histograms": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "kvq_drift_check": (ctypes.c_int, [_P, _I64, _I64, _P, _P, ctypes.c_double, _P, _P, _P, _P]),
+    "kvq_requantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
 }
 
 
@@ -231,6 +234,43 @@ class KVQCache:
         if partials.dim() == 3 and partials.shape[1] != S:
             partials = partials.reshape(-1)[: rows * S * W].view(rows, S, W)
         return partials, S
+
+    def num_groups(self) -> int:
+        return self.num_quantized // self.cfg.group_size
+
+    def code_histograms(self, g0: int = 0, g1: int | None = None, stream=None):
+        """Calibration code counts over groups [g0, g1): (k_hist [H_kv, 2^k_bits],
+        v_hist [H_kv, 2^v_bits]) int64 device tensors."""
+        import torch
+
+        c = self.cfg
+        g1 = self.num_groups() if g1 is None else g1
+        dev = self.buf.device
+        kh = torch.empty((c.num_kv_heads, 1 << c.k_bits), dtype=torch.int64, device=dev)
+        vh = torch.empty((c.num_kv_heads, 1 << c.v_bits), dtype=torch.int64, device=dev)
+        check(lib.kvq_code_histograms(self.h, g0, g1, _ptr(kh), _ptr(vh), _stream(stream)), "kvq_code_histograms")
+        return kh, vh
+
+    def drift_check(self, cal_k, cal_v, g0: int = 0, g1: int | None = None, threshold: float = 0.1, stream=None):
+        """Per (slice, group) KL of the code histograms against calibration
+        counts: (kl_k, kl_v float64, flags uint8), each [B * H_kv, g1 - g0]."""
+        import torch
+
+        c = self.cfg
+        g1 = self.num_groups() if g1 is None else g1
+        dev = self.buf.device
+        shape = (c.batch * c.num_kv_heads, g1 - g0)
+        kl_k = torch.empty(shape, dtype=torch.float64, device=dev)
+        kl_v = torch.empty(shape, dtype=torch.float64, device=dev)
+        flags = torch.empty(shape, dtype=torch.uint8, device=dev)
+        check(lib.kvq_drift_check(self.h, g0, g1, _ptr(cal_k), _ptr(cal_v), threshold, _ptr(kl_k), _ptr(kl_v),
+                                  _ptr(flags), _stream(stream)), "kvq_drift_check")
+        return kl_k, kl_v, flags
+
+    def requantize(self, k, v, g0: int, g1: int, flags=None, stream=None) -> None:
+        """Quantize groups [g0, g1) again from k, v [B, H_kv, (g1 - g0) * G, D]
+        where flags (uint8 [B * H_kv, g1 - g0]) is nonzero (all if None)."""
+        check(lib.kvq_requantize(self.h, g0, g1, _ptr(k), _ptr(v), _ptr(flags), _stream(stream)), "kvq_requantize")
 
     def group_bits(self):
         """(key bits, value bits) uint8 arrays, one entry per quantized group."""

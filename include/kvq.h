@@ -183,6 +183,39 @@ kvq_status kvq_merge_partials(const float* partials, float* out, int32_t rows, i
 kvq_status kvq_export_key_norms(kvq_cache* cache, int32_t b0, int32_t bc, void* host_k_norm, void* stream);
 kvq_status kvq_import_key_norms(kvq_cache* cache, int32_t b0, int32_t bc, const void* host_k_norm, void* stream);
 
+/* Drift detection ("Asymmetric Key-Value Quantization: 2-Bit Values and
+ * 4-Bit Keys under Long-Context Drift", section 3.3: the KL divergence of the
+ * current distribution of quantized values from the calibration
+ * distribution, a threshold of 0.1 by default triggering requantization).
+ * Quantized groups are numbered 0 .. kvq_num_quantized / G - 1 in token
+ * order; a group's distribution is the histogram of its G x D key codes (of
+ * its value codes).  Not for position-adaptive caches (KVQ_E_UNSUPPORTED).
+ *
+ * kvq_code_histograms: code counts over groups [g0, g1) of every sequence,
+ *   per kv head, into device arrays k_hist [H_kv][2^k_bits] and
+ *   v_hist [H_kv][2^v_bits] (uint64, 8-byte aligned, overwritten); the
+ *   calibration histograms kvq_drift_check takes.
+ * kvq_drift_check: for every slice s = b * H_kv + h and group g in [g0, g1),
+ *   with p the group's counts / (G * D) and q the calibration counts of head h
+ *   divided by their total: kl = sum_i p_i ln(p_i / q_i) (bins with p_i = 0
+ *   add 0; p_i > 0 = q_i makes it +inf), fp64, for keys and values, into
+ *   device arrays kl_k, kl_v [B * H_kv][g1 - g0] (double), and
+ *   flags (uint8, same shape) = (kl_k > threshold) | (kl_v > threshold) << 1.
+ *   A calibration histogram with no counts gives +inf.
+ * kvq_requantize: quantize groups [g0, g1) again from the tokens k, v
+ *   (device, [B][H_kv][(g1 - g0) * G][D], in_dtype, entry conversion and
+ *   rotation as in kvq_append), for the groups whose flag is nonzero
+ *   (flags: device uint8 [B * H_kv][g1 - g0] as written by kvq_drift_check,
+ *   or NULL for all); each group keeps its bit widths.  The uniform quantizer
+ *   recomputes its scale and zero from the given tokens (no Lloyd-Max
+ *   levels).  KVQ_E_ARG for a range outside the quantized groups. */
+kvq_status kvq_code_histograms(kvq_cache* cache, int64_t g0, int64_t g1, uint64_t* k_hist, uint64_t* v_hist,
+                               void* stream);
+kvq_status kvq_drift_check(kvq_cache* cache, int64_t g0, int64_t g1, const uint64_t* cal_k, const uint64_t* cal_v,
+                           double threshold, double* kl_k, double* kl_v, uint8_t* flags, void* stream);
+kvq_status kvq_requantize(kvq_cache* cache, int64_t g0, int64_t g1, const void* k, const void* v,
+                          const uint8_t* flags, void* stream);
+
 /* Split count kvq_decode_attn would use for the current token count. */
 int32_t kvq_default_splits(const kvq_cache* cache);
 

@@ -184,3 +184,31 @@ def test_group_bits_on_a_fresh_handle():
     finally:
         lib.kvq_destroy(h)
     assert lib.kvq_group_bits(None, None, None, 0) == -1
+
+
+def test_drift_entry_points_validate_on_the_host():
+    import decode_attention_asym_amd as kvq
+    from decode_attention_asym_amd.kvq import lib
+
+    c = _cfg()
+    cc = c.c()
+    fake = 1 << 40
+    h = ctypes.c_void_p()
+    assert lib.kvq_create(ctypes.byref(cc), fake, kvq.cache_bytes(c), ctypes.byref(h)) == kvq.KVQ_OK
+    try:
+        # an empty cache has no quantized groups: any non-empty range is out of bounds
+        assert lib.kvq_code_histograms(h, 0, 1, fake, fake, None) == kvq.KVQ_E_ARG
+        assert lib.kvq_drift_check(h, 0, 1, fake, fake, 0.1, fake, fake, fake, None) == kvq.KVQ_E_ARG
+        assert lib.kvq_requantize(h, 0, 1, fake, fake, None, None) == kvq.KVQ_E_ARG
+        assert lib.kvq_requantize(h, 0, 0, None, None, None, None) == kvq.KVQ_OK  # empty range: no-op
+        assert lib.kvq_drift_check(h, 0, 0, None, fake, 0.1, fake, fake, fake, None) == kvq.KVQ_E_ARG
+        assert lib.kvq_drift_check(h, 0, 0, fake, fake, -1.0, fake, fake, fake, None) == kvq.KVQ_E_ARG
+    finally:
+        lib.kvq_destroy(h)
+    ca = _cfg(adapt_delta=128, bits_low=(2, 2), bits_high=(4, 4)).c()
+    assert lib.kvq_create(ctypes.byref(ca), fake, kvq.cache_bytes(_cfg(adapt_delta=128, bits_low=(2, 2),
+                                                                        bits_high=(4, 4))), ctypes.byref(h)) == 0
+    try:
+        assert lib.kvq_code_histograms(h, 0, 0, fake, fake, None) == kvq.KVQ_E_UNSUPPORTED
+    finally:
+        lib.kvq_destroy(h)
