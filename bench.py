@@ -169,7 +169,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64, help="timed steps (64 spans one group flush at G=64)")
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=96,
+                    help="untimed steps first: after the prefill the step time settles over the first ~64 steps "
+                         "(measured 1012, 400, 373, 341, 335 .. 322 us per 8-step block on the 32k layer)")
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 32k K4/V2 layer)")
     ap.add_argument("--splits", type=int, default=0, help="split count (0: the library's default)")
     ap.add_argument("--sink", type=int, default=0, help="attention-sink tokens kept in fp16 (a multiple of the group size)")
@@ -179,6 +181,8 @@ def main() -> int:
                     help="position-adaptive bit widths: region size Delta in tokens (0: off)")
     ap.add_argument("--bits-low", default="2,2", help="key,value bits of the first Delta tokens")
     ap.add_argument("--bits-high", default="4,4", help="key,value bits of the last Delta tokens")
+    ap.add_argument("--kernel-steps", type=int, default=32,
+                    help="steps after the timed ones that time the decode launch (with and without it)")
     ap.add_argument("--drift", action="store_true",
                     help="also time the drift check (code histograms + KL per group) over every quantized group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -214,7 +218,7 @@ def main() -> int:
                       + ("-tokennorm" if args.token_norm else "") + adapt,
                       sink=args.sink, hybrid=args.hybrid, token_norm=args.token_norm, adapt_delta=args.adapt_delta,
                       bits_low=lo if args.adapt_delta else (0, 0), bits_high=hi if args.adapt_delta else (0, 0))
-    total = args.warmup + args.steps
+    total = args.warmup + args.steps + 2 * args.kernel_steps
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     syn = Synth(w, dev, positions=w.N + total + 1)
@@ -242,46 +246,54 @@ def main() -> int:
     S = args.splits or cache.default_splits()
     # a position-adaptive cache may use a few more splits than asked (at least one per run of equal bits)
     cap = max(S, kvq.workspace_bytes(kvq.config_for(w, max_tokens=w.N + total)) // (rows * (w.D + 4) * 4))
-    partials = torch.empty((rows, cap, w.D + 4), dtype=torch.float32, device=dev)
+    partials = torch.empty(rows * cap * (w.D + 4), dtype=torch.float32, device=dev)
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
 
-    def step(i, evs=None):
+    def step(i):
         k, v = step_kv[i]
         cache.append(k, v)
-        if evs:
-            evs[0].record()
-        if S > 1:
-            _, used = cache.decode_partials(qs[i], partials, splits=S)
-            if evs:
-                evs[1].record()
-            merge_partials(partials, out, rows, used, w.D)
-        else:
-            cache.decode(qs[i], out, splits=1)
-            if evs:
-                evs[1].record()
+        _, used = cache.decode_partials(qs[i], partials, splits=S)
+        merge_partials(partials, out, rows, used, w.D)
+        return used
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: the K steps alone (no event inside it: an event recorded
+    # between two kernels slows the kernel after it, measured +35 us on the
+    # decode in a rocprofv3 trace, with or without the event's system fence)
+    nk = args.kernel_steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     n0 = cache.num_tokens
     torch.cuda.synchronize()
-    start.record()
+    ev[0].record()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    end.record()
+        step(args.warmup + i)
+    ev[1].record()
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
+    # the decode kernel's average launch duration, by difference, right after
+    # (an idle GPU restarts slower: the first ~60 steps after a pause of a few
+    # ms run up to 3x the settled step time): nk more steps, then nk steps
+    # without the decode (append and merge only), each span between two events
+    ev[2].record()
+    for i in range(nk):
+        used = step(args.warmup + args.steps + i)
+    ev[3].record()
+    for i in range(nk):
+        k, v = step_kv[args.warmup + args.steps + nk + i]
+        cache.append(k, v)
+        merge_partials(partials, out, rows, used, w.D)  # the last decode's partials
+    ev[4].record()
+    torch.cuda.synchronize()
+    ms_total = ev[0].elapsed_time(ev[1])
     ms_step = ms_total / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
     gbits = cache.group_bits() if w.adapt_delta else None  # a group's bits never change once quantized
     step_bytes = [decode_bytes(w, n0 + i + 1, gbits) + append_bytes(w, n0 + i, gbits) for i in range(args.steps)]
-    dec_bytes = [decode_bytes(w, n0 + i + 1, gbits) for i in range(args.steps)]
     value = sum(step_bytes) / (ms_total * 1e-3) / 1e9
-    achieved = (sum(dec_bytes) / len(dec_bytes)) / (dec_avg_ms * 1e-3) / 1e9
     assert torch.isfinite(out).all()
+    dec_avg_ms = (ev[2].elapsed_time(ev[3]) - ev[3].elapsed_time(ev[4])) / nk
+    n1 = n0 + args.steps
+    dec_bytes = [decode_bytes(w, n1 + i + 1, gbits) for i in range(nk)]
+    achieved = (sum(dec_bytes) / len(dec_bytes)) / (dec_avg_ms * 1e-3) / 1e9
 
     drift = None
     if args.drift and not w.adapt_delta:
@@ -345,6 +357,8 @@ def main() -> int:
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(w.name),
             "avg_us": round(dec_avg_ms * 1e3, 2),
+            "launches_timed": nk,
+            "timing": "per launch: (span of nk steps) - (span of nk steps without the decode), after the timed steps",
             "bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes)),
         },
         "prefill_ms": round(prefill_ms, 2),

@@ -147,7 +147,8 @@ int64_t nquant_of(const kvq_cache* h, int64_t n) {
 }
 int64_t ngroups_of(const kvq_cache* h) { return nquant_of(h, h->n) / h->cfg.group_size; }
 
-int choose_splits(kvq_cache* h) {
+// Split count for a decode over n tokens.
+int choose_splits(kvq_cache* h, int64_t n) {
   if (h->cu_count <= 0) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
@@ -159,7 +160,7 @@ int choose_splits(kvq_cache* h) {
   int64_t slices = h->L.slices;
   int64_t target = static_cast<int64_t>(h->cu_count) * 16;  // about four waves per SIMD
   int64_t s = (target + slices - 1) / slices;
-  int64_t ng = ngroups_of(h);
+  int64_t ng = nquant_of(h, n) / h->cfg.group_size;
   s = std::min<int64_t>(s, std::max<int64_t>(1, ng / 2));
   s = std::min<int64_t>(s, max_splits(&h->cfg));
   return static_cast<int>(std::max<int64_t>(1, s));
@@ -252,7 +253,11 @@ int64_t kvq_num_quantized(const kvq_cache* h) {
   return h ? nquant_of(h, h->n) : -1;
 }
 
-kvq_status kvq_append(kvq_cache* h, const void* k, const void* v, int32_t n_tokens, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kvq_status append_impl(kvq_cache* h, const void* k, const void* v, int32_t n_tokens, void* stream) {
   kvq_status st = check_handle(h);
   if (st != KVQ_OK) return st;
   if (n_tokens < 0) return fail(KVQ_E_ARG, "n_tokens %d < 0", n_tokens);
@@ -312,9 +317,17 @@ kvq_status kvq_append(kvq_cache* h, const void* k, const void* v, int32_t n_toke
   return ok();
 }
 
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_append(kvq_cache* h, const void* k, const void* v, int32_t n_tokens, void* stream) {
+  return append_impl(h, k, v, n_tokens, stream);
+}
+
 int32_t kvq_default_splits(const kvq_cache* h) {
   if (!h) return 0;
-  return choose_splits(const_cast<kvq_cache*>(h));
+  return choose_splits(const_cast<kvq_cache*>(h), h->n);
 }
 
 namespace {
@@ -434,6 +447,54 @@ kvq_status kvq_decode_partials(kvq_cache* h, const void* q, float* partials, siz
   return launch_splits(h, q, nullptr, partials, bytes, num_splits, false, splits_used, static_cast<hipStream_t>(stream));
 }
 
+namespace {
+// Append one token and decode.  Everything a launch could reject is checked
+// before the first launch.
+kvq_status append_decode(kvq_cache* h, const void* k, const void* v, const void* q, float* out, float* partials,
+                         size_t bytes, int32_t num_splits, bool allow_final, int32_t* splits_used, hipStream_t s) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = h->cfg;
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_E_ARG, "k/v NULL or not 16-byte aligned");
+  if (!q || !aligned(q, 16)) return fail(KVQ_E_ARG, "q NULL or not 16-byte aligned");
+  if (h->n + 1 > c.max_tokens) return fail(KVQ_E_CAPACITY, "append of 1 token to %lld exceeds max_tokens %d",
+                                           (long long)h->n, c.max_tokens);
+  if (num_splits < 1 || num_splits > max_splits(&c))
+    return fail(KVQ_E_ARG, "num_splits %d outside [1, %d]", num_splits, max_splits(&c));
+  const int64_t rows = static_cast<int64_t>(c.batch) * c.num_q_heads;
+  const size_t need = static_cast<size_t>(rows * max_splits(&c) * (c.head_dim + 4) * sizeof(float));
+  if (!partials || !aligned(partials, 16) || bytes < need)
+    return fail(KVQ_E_ARG, "workspace/partials NULL, misaligned or %zu < %zu bytes", bytes, need);
+  if (allow_final && (!out || !aligned(out, 16))) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
+  if (static_cast<int64_t>(runs_of(h, 0, ngroups_of(h)).size()) + 1 > max_splits(&c))
+    return fail(KVQ_E_UNSUPPORTED, "runs of equal bit widths exceed the split maximum %d", max_splits(&c));
+  st = append_impl(h, k, v, 1, s);
+  if (st != KVQ_OK) return st;
+  return launch_splits(h, q, out, partials, bytes, num_splits, allow_final, splits_used, s);
+}
+}  // namespace
+
+kvq_status kvq_append_decode_attn(kvq_cache* h, const void* k, const void* v, const void* q, float* out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t S_req = choose_splits(h, h->n + 1);  // as kvq_decode_attn after the append
+  int32_t S = 0;
+  st = append_decode(h, k, v, q, out, static_cast<float*>(ws), ws_bytes, S_req, true, &S, s);
+  if (st != KVQ_OK || S == 1) return st;
+  const int64_t rows = static_cast<int64_t>(h->cfg.batch) * h->cfg.num_q_heads;
+  hipError_t e = kvq::launch_merge(static_cast<float*>(ws), out, static_cast<int>(rows), S, h->cfg.head_dim, s);
+  if (e != hipSuccess) return device_error(h, e, "merge kernel launch");
+  return ok();
+}
+
+kvq_status kvq_append_decode_partials(kvq_cache* h, const void* k, const void* v, const void* q, float* partials,
+                                      size_t bytes, int32_t num_splits, int32_t* splits_used, void* stream) {
+  return append_decode(h, k, v, q, nullptr, partials, bytes, num_splits, false, splits_used,
+                       static_cast<hipStream_t>(stream));
+}
+
 kvq_status kvq_merge_partials(const float* partials, float* out, int32_t rows, int32_t splits, int32_t head_dim,
                               void* stream) {
   if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16))
@@ -449,7 +510,7 @@ kvq_status kvq_merge_partials(const float* partials, float* out, int32_t rows, i
 kvq_status kvq_decode_attn(kvq_cache* h, const void* q, float* out, void* ws, size_t ws_bytes, void* stream) {
   kvq_status st = check_handle(h);
   if (st != KVQ_OK) return st;
-  return kvq_decode_attn_splits(h, q, out, ws, ws_bytes, choose_splits(h), stream);
+  return kvq_decode_attn_splits(h, q, out, ws, ws_bytes, choose_splits(h, h->n), stream);
 }
 
 // ---------------------------------------------------------------- drift detection

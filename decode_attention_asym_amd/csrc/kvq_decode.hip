@@ -348,6 +348,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   const int h = l16 % GQC, rp = l16 / GQC;
   const bool hv = h < a.gqa;
   const int hq = hkv * a.gqa + (hv ? h : 0);
+
   const bool lo_cols = NP == 1 && (rp & 1);               // this lane's columns hold the second part
   // full QK^T sum from the two parts' columns
   auto combine = [&](float x) __attribute__((always_inline)) {

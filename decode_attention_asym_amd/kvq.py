@@ -68,6 +68,8 @@ SIGNATURES = {
     "kvq_import_key_norms": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "kvq_export_codes_u8": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P]),
     "kvq_group_bits": (_I64, [_P, _P, _P, _I64]),
+    "kvq_append_decode_attn": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "kvq_append_decode_partials": (ctypes.c_int, [_P, _P, _P, _P, _P, _SZ, _I32, ctypes.POINTER(_I32), _P]),
     "kvq_code_histograms": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "kvq_drift_check": (ctypes.c_int, [_P, _I64, _I64, _P, _P, ctypes.c_double, _P, _P, _P, _P]),
     "kvq_requantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
@@ -215,6 +217,32 @@ class KVQCache:
                                             _stream(stream))
         check(st, "kvq_decode_attn")
         return out
+
+    def append_decode(self, k, v, q, out=None, stream=None):
+        """One step: append one token (k, v [B, H_kv, 1, D]) and decode q,
+        every argument checked before anything is enqueued."""
+        import torch
+
+        if out is None:
+            out = torch.empty((self.cfg.batch, self.cfg.num_q_heads, self.cfg.head_dim), dtype=torch.float32,
+                              device=q.device)
+        check(lib.kvq_append_decode_attn(self.h, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(self.ws), self.ws.numel(),
+                                         _stream(stream)), "kvq_append_decode_attn")
+        return out
+
+    def append_decode_partials(self, k, v, q, partials=None, splits: int | None = None, stream=None):
+        """As append_decode, stopping at the split partials; returns (partials, S)."""
+        import torch
+
+        rows, W = self.cfg.batch * self.cfg.num_q_heads, self.cfg.head_dim + 4
+        if partials is None:
+            partials = torch.empty(self.ws.numel() // 4, dtype=torch.float32, device=q.device)
+        S_req = splits if splits is not None else int(lib.kvq_default_splits(self.h))
+        used = ctypes.c_int32(0)
+        check(lib.kvq_append_decode_partials(self.h, _ptr(k), _ptr(v), _ptr(q), _ptr(partials), partials.numel() * 4,
+                                             S_req, ctypes.byref(used), _stream(stream)), "kvq_append_decode_partials")
+        S = int(used.value)
+        return partials.reshape(-1)[: rows * S * W].view(rows, S, W), S
 
     def decode_partials(self, q, partials=None, splits: int | None = None, stream=None):
         """Split partials [B*H_q, S, D+4] (o unnormalized, m, l in base 2); returns (partials, S)."""

@@ -168,6 +168,19 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, v
 kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials, size_t bytes, int32_t num_splits,
                                int32_t* splits_used, void* stream);
 
+/* One decode step: kvq_append of one token (k, v: [B][H_kv][1][D]) followed
+ * by kvq_decode_attn (or kvq_decode_partials); results and cache contents
+ * are those of the two calls.  The workspace / partials must hold
+ * kvq_workspace_bytes (all splits the library may use).  Every argument is
+ * checked before any work is enqueued, so on an error nothing has been
+ * appended.  (Writing the new token inside the decode kernel instead of by
+ * the window-write kernel was measured slower by 6-16 us per step.) */
+kvq_status kvq_append_decode_attn(kvq_cache* cache, const void* k, const void* v, const void* q, float* out,
+                                  void* workspace, size_t ws_bytes, void* stream);
+kvq_status kvq_append_decode_partials(kvq_cache* cache, const void* k, const void* v, const void* q,
+                                      float* partials, size_t bytes, int32_t num_splits, int32_t* splits_used,
+                                      void* stream);
+
 /* Merge `splits` partials per row (layout above, `rows` rows) into
  * out[rows][head_dim] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
  * M = max_s m_s; splits with m_s = -inf contribute nothing, and a row whose

@@ -426,3 +426,89 @@ def test_bits_group_gqa_matrix(kb, vb, G, hq):
     head-slot replica modes: gqa 4, 8, 16), one kv head, ragged length."""
     w = WORKLOADS[1].replace(name=f"k{kb}v{vb}g{G}h{hq}", B=1, Hq=hq, Hkv=1, N=1000 + 7, kbits=kb, vbits=vb, G=G, R=64)
     _check_full(w, splits=1)
+
+
+STEP = [
+    WORKLOADS[2].replace(name="step-k4v2-g64", B=2, Hq=8, Hkv=2, N=1000 + 7),
+    WORKLOADS[4].replace(name="step-mha-fwht", B=1, Hq=4, Hkv=4, N=500 + 60),
+    WORKLOADS[0].replace(name="step-d64-gqa16-rot", B=2, Hq=32, Hkv=2, N=300 + 17, rotate=True),
+    WORKLOADS[1].replace(name="step-sink-start", B=2, Hq=8, Hkv=2, N=20, sink=64, R=32),
+    WORKLOADS[1].replace(name="step-r0", B=2, Hq=8, Hkv=2, N=640 + 30, R=0),
+    WORKLOADS[2].replace(name="step-adapt-tokennorm", B=1, Hq=8, Hkv=2, N=1500, adapt_delta=256, bits_low=(2, 2),
+                         bits_high=(4, 4), token_norm=True, rotate=True),
+]
+
+
+@pytest.mark.parametrize("w", STEP, ids=lambda w: w.name)
+def test_step_entry_equals_separate_calls(w):
+    """kvq_append_decode_attn gives bit-identical outputs and cache contents to
+    kvq_append + kvq_decode_attn, step by step across group flushes (sink,
+    R = 0, rotation, gqa 16, adaptive widths); the final state also matches
+    the oracle."""
+    kvq = _lib()
+    steps = 70
+    syn = Synth(w, "cuda", positions=w.N + steps + 1)
+    K, V = syn.kv_all()
+    a = kvq.KVQCache(kvq.config_for(w, w.N + steps))
+    b = kvq.KVQCache(kvq.config_for(w, w.N + steps))
+    a.append(K, V)
+    b.append(K, V)
+    ks, vs = [K], [V]
+    for i in range(steps):
+        k, v = syn.step_kv(i)
+        q = syn.q(i + 1)
+        a.append(k, v)
+        oa = a.decode(q)
+        ob = b.append_decode(k, v, q)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), f"step {i}: outputs differ"
+        ks.append(k)
+        vs.append(v)
+    ea, eb = a.export(), b.export()
+    for key in ("k_scale", "k_zero", "v_scale", "v_zero", "k_resid", "v_resid") + (
+            ("k_codes", "v_codes") if not w.adapt_delta else ("k_codes_u8", "v_codes_u8")):
+        assert np.array_equal(ea[key], eb[key]), key
+    # the stepped cache against the oracle
+    Kall, Vall = torch.cat(ks, dim=2), torch.cat(vs, dim=2)
+    calls = [w.N] + [1] * steps
+    encs = oracle_encode_slices(w, Kall, Vall, [(bb, h) for bb in range(w.B) for h in range(w.Hkv)], calls=calls)
+    assert_export_matches(w, eb, 0, encs)
+    q = syn.q(steps)
+    out = b.decode(q)
+    torch.cuda.synchronize()
+    ref = oracle_rows(w, eb, 0, to_oracle_input(q, w.dtype), list(range(w.B)))
+    err, _ = rel_l2(out.double().cpu().numpy(), np.stack([ref[bb] for bb in range(w.B)]))
+    log(f"[step] {w.name}: rel L2 {err:.3e} after {steps} steps")
+    assert err <= TOL_REL_L2
+
+
+def test_step_partials_and_argument_checks():
+    kvq = _lib()
+    w = WORKLOADS[2].replace(name="step-partials", B=2, Hq=8, Hkv=2, N=900)
+    syn = Synth(w, "cuda", positions=w.N + 4)
+    K, V = syn.kv_all()
+    a = kvq.KVQCache(kvq.config_for(w, w.N + 3))
+    b = kvq.KVQCache(kvq.config_for(w, w.N + 3))
+    a.append(K, V)
+    b.append(K, V)
+    k, v = syn.step_kv(0)
+    q = syn.q(1)
+    a.append(k, v)
+    pa, Sa = a.decode_partials(q, splits=3)
+    pb, Sb = b.append_decode_partials(k, v, q, splits=3)
+    torch.cuda.synchronize()
+    # o, m, l of every split (the last two floats of a record are padding)
+    assert Sa == Sb and torch.equal(pa[:, :, :w.D + 2], pb[:, :, :w.D + 2])
+    # checked before anything is enqueued: the token count does not move
+    n = b.num_tokens
+    small = torch.empty(16, dtype=torch.float32, device="cuda")
+    with pytest.raises(kvq.KVQError):
+        b.append_decode_partials(k, v, q, small, splits=3)
+    with pytest.raises(kvq.KVQError):
+        b.append_decode_partials(k, v, q, splits=10 ** 6)
+    assert b.num_tokens == n
+    b.append_decode(k, v, q)
+    b.append_decode(k, v, q)
+    with pytest.raises(kvq.KVQError):  # capacity
+        b.append_decode(k, v, q)
+    assert b.num_tokens == w.N + 3
