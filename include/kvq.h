@@ -162,8 +162,8 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, v
  * widths and splits each run that way into consecutive split slots, in
  * proportion to its page bytes, at least one per run; the fp16 chunks go with
  * the run that has the most splits.  S is then the total, at most
- * max(num_splits, runs); KVQ_E_UNSUPPORTED when there are more runs than the
- * workspace maximum of splits.)
+ * num_splits + runs - 1 and within the workspace maximum; KVQ_E_UNSUPPORTED
+ * when there are more runs than that maximum.)
  * bytes must be >= H_q * B * S * (D + 4) * 4.  Requires a non-empty cache. */
 kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials, size_t bytes, int32_t num_splits,
                                int32_t* splits_used, void* stream);
