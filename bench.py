@@ -196,7 +196,8 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (this path has no multi-GPU "
-              f"mode: every (batch, kv-head) slice is independent, see DESIGN.md for how it would shard).",
+              f"mode: every (batch, kv-head) slice is independent, so batches or kv heads would be split over "
+              f"GPUs with no exchange, and a long context over GPUs with one merge of the split partials).",
               file=sys.stderr)
         return 2
 
