@@ -26,6 +26,7 @@ SOURCES = {
     # MFMA accumulators in ArchVGPRs: the softmax rescale multiplies them with
     # VALU, which otherwise costs AGPR<->VGPR copies every chunk
     "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "kvq_merge.hip": [],
     # KL terms are products and sums rounded one by one, as in the oracle
     "kvq_drift.hip": ["-ffp-contract=off"],
     "kvq_api.cpp": ["-ffp-contract=off"],
