@@ -127,20 +127,20 @@ constexpr float kInvSqrt64 = 0.125f;
 // then one multiply by the binary32 constant nearest 1/sqrt(D).  Every output
 // depends only on the fixed butterfly sequence, so the result is independent
 // of how threads share the work.
-template <int D>
+template <int D, int STRIDE = D>
 __device__ void fwht_rows(float* x, int rows, int tid, int nthreads) {
   for (int h = 1; h < D; h <<= 1) {
     for (int k = tid; k < rows * (D / 2); k += nthreads) {
       int r = k / (D / 2), p = k % (D / 2);
       int i0 = (p / h) * 2 * h + (p % h);
-      float a = x[r * D + i0], b = x[r * D + i0 + h];
-      x[r * D + i0] = a + b;
-      x[r * D + i0 + h] = a - b;
+      float a = x[r * STRIDE + i0], b = x[r * STRIDE + i0 + h];
+      x[r * STRIDE + i0] = a + b;
+      x[r * STRIDE + i0 + h] = a - b;
     }
     __syncthreads();
   }
   const float c = D == 128 ? kInvSqrt128 : kInvSqrt64;
-  for (int k = tid; k < rows * D; k += nthreads) x[k] = x[k] * c;
+  for (int k = tid; k < rows * D; k += nthreads) x[(k / D) * STRIDE + k % D] = x[(k / D) * STRIDE + k % D] * c;
   __syncthreads();
 }
 
@@ -151,8 +151,11 @@ template <int D, int KB, int VB, int G>
 __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   constexpr int NKB = D / 32, NCG = D / G;
   constexpr int CPG = G / kChunk;
-  __shared__ float kx[G * D];
-  __shared__ __half vx[G * D];  // values are fp16 after entry conversion
+  // token rows padded by one bank (4 bytes) so that the lanes reading one
+  // channel of 16 or 32 consecutive tokens hit different LDS banks
+  constexpr int KS = D + 1, VS = D + 2;
+  __shared__ float kx[G * KS];
+  __shared__ __half vx[G * VS];  // values are fp16 after entry conversion
   __shared__ float ks[D], kmn[D];
   __shared__ float vs[G * NCG], vmn[G * NCG];
   __shared__ bool ksym[D], vsym[G * NCG];
@@ -169,27 +172,58 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
 
   // 1. gather (entry conversion of new tokens; window tokens are fp16 already)
   bool any_new = false;
+  if (pos0 >= a.n_old && a.in_dtype != 0) {
+    // the whole group comes from this call's 2-byte input: G * D contiguous
+    // elements per tensor, read as 16-byte vectors, every load of a thread
+    // issued before the first is used
+    constexpr int NVEC = G * D / 8, PER = NVEC / 256;
+    static_assert(NVEC % 256 == 0, "whole vectors per thread");
+    const uint4* kp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + in_base + (pos0 - a.n_old) * D);
+    const uint4* vp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + in_base + (pos0 - a.n_old) * D);
+    uint4 kv[PER], vv[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      kv[r] = kp[tid + 256 * r];
+      vv[r] = vp[tid + 256 * r];
+    }
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int e0 = (tid + 256 * r) * 8, i = e0 / D, c0 = e0 % D;
+      const uint32_t kw[4] = {kv[r].x, kv[r].y, kv[r].z, kv[r].w}, vw[4] = {vv[r].x, vv[r].y, vv[r].z, vv[r].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t ku = static_cast<uint16_t>(kw[e >> 1] >> (16 * (e & 1)));
+        const uint16_t vu = static_cast<uint16_t>(vw[e >> 1] >> (16 * (e & 1)));
+        const float kf = a.in_dtype == 1 ? __half2float(__ushort_as_half(ku)) : __uint_as_float(static_cast<uint32_t>(ku) << 16);
+        const float vf = a.in_dtype == 1 ? __half2float(__ushort_as_half(vu)) : __uint_as_float(static_cast<uint32_t>(vu) << 16);
+        kx[i * KS + c0 + e] = kf;
+        vx[i * VS + c0 + e] = __float2half_rn(vf);
+      }
+    }
+  } else {
   for (int idx = tid; idx < G * D; idx += blockDim.x) {
     int i = idx / D, c = idx % D;
     int64_t p = pos0 + i;
     if (p >= a.n_old) {
       int64_t src = in_base + (p - a.n_old) * D + c;
-      kx[idx] = load_in(a.k, a.in_dtype, src);
-      vx[idx] = __float2half_rn(load_in(a.v, a.in_dtype, src));
+      kx[i * KS + c] = load_in(a.k, a.in_dtype, src);
+      vx[i * VS + c] = __float2half_rn(load_in(a.v, a.in_dtype, src));
     } else {
       const uint8_t* rc = ring + ring_chunk_offset(L, slice, p);
       int t = static_cast<int>(p % kChunk);
-      kx[idx] = __half2float(*reinterpret_cast<const __half*>(rc + ring_k_offset(L, t, c)));
-      vx[idx] = *reinterpret_cast<const __half*>(rc + ring_v_offset(L, t, c));
+      kx[i * KS + c] = __half2float(*reinterpret_cast<const __half*>(rc + ring_k_offset(L, t, c)));
+      vx[i * VS + c] = *reinterpret_cast<const __half*>(rc + ring_v_offset(L, t, c));
     }
+  }
   }
   any_new = (pos0 + G) > a.n_old;
   __syncthreads();
   if (any_new) {
     // rows [first_new, G) come from the input: rotate (keys) then round to fp16
     int first_new = a.n_old > pos0 ? static_cast<int>(a.n_old - pos0) : 0;
-    if (a.rotate) fwht_rows<D>(kx + first_new * D, G - first_new, tid, blockDim.x);
-    for (int idx = first_new * D + tid; idx < G * D; idx += blockDim.x) kx[idx] = round_fp16(kx[idx]);
+    if (a.rotate) fwht_rows<D, KS>(kx + first_new * KS, G - first_new, tid, blockDim.x);
+    for (int idx = first_new * D + tid; idx < G * D; idx += blockDim.x)
+      kx[(idx / D) * KS + idx % D] = round_fp16(kx[(idx / D) * KS + idx % D]);
     __syncthreads();
   }
 
@@ -200,7 +234,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   // whose normalized values are 0)
   if (L.token_norm) {
     for (int i = tid; i < G; i += blockDim.x) {
-      const float nrm = row_norm<D>(kx + i * D);
+      const float nrm = row_norm<D>(kx + i * KS);
       knrm[i] = nrm;
       uint16_t* kn = reinterpret_cast<uint16_t*>(page + L.off_knorm + (i / kChunk) * L.kn_chunk_bytes);
       kn[knorm_elem(i % kChunk)] = fp16_bits(nrm);
@@ -208,7 +242,8 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += blockDim.x) {
       const float nrm = knrm[idx / D];
-      kx[idx] = nrm == 0.0f ? 0.0f : round_fp16(kx[idx] / nrm);
+      float& xk = kx[(idx / D) * KS + idx % D];
+      xk = nrm == 0.0f ? 0.0f : round_fp16(xk / nrm);
     }
     __syncthreads();
   }
@@ -216,7 +251,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   // 2. parameters: keys per channel over G tokens, values per token over G channels
   const bool hybrid = a.hybrid != 0;
   for (int c = tid; c < D; c += blockDim.x) {
-    const GroupQ q = group_params<G, KB>([&](int i) { return kx[i * D + c]; }, hybrid);
+    const GroupQ q = group_params<G, KB>([&](int i) { return kx[i * KS + c]; }, hybrid);
     ks[c] = q.s;
     kmn[c] = q.mn;
     ksym[c] = q.sym;
@@ -227,7 +262,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   }
   for (int task = tid; task < G * NCG; task += blockDim.x) {
     int i = task / NCG, cg = task % NCG;
-    const __half* row = vx + i * D + cg * G;
+    const __half* row = vx + i * VS + cg * G;
     const GroupQ q = group_params<G, VB>([&](int c) { return __half2float(row[c]); }, hybrid);
     vs[task] = q.s;
     vmn[task] = q.mn;
@@ -254,7 +289,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         int i = ch * kChunk + 16 * mt + l16;  // token within the group
         for (int e = 0; e < 8; ++e) {
           int c = 32 * kb + 8 * j + e;
-          uint32_t code = code_of<KB>(kx[i * D + c], kmn[c], ks[c], ksym[c]);
+          uint32_t code = code_of<KB>(kx[i * KS + c], kmn[c], ks[c], ksym[c]);
           int bit = KB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
           word |= code << bit;
         }
@@ -279,7 +314,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         int cg = c / G;
         for (int e = 0; e < 8; ++e) {
           int i = ch * kChunk + tau(j, e);
-          uint32_t code = code_of<VB>(__half2float(vx[i * D + c]), vmn[i * NCG + cg], vs[i * NCG + cg], vsym[i * NCG + cg]);
+          uint32_t code = code_of<VB>(__half2float(vx[i * VS + c]), vmn[i * NCG + cg], vs[i * NCG + cg], vsym[i * NCG + cg]);
           int bit = VB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
           word |= code << bit;
         }
