@@ -172,6 +172,68 @@ int choose_splits(kvq_cache* h, int64_t n) {
   return static_cast<int>(std::max<int64_t>(1, s));
 }
 
+// Pieces of a decode over runs of several widths, for one launch (see
+// kvq::MixedPlan).  With S splits' worth of page bytes per slice, T = bytes /
+// S: a run smaller than T ("short") is one piece; the long runs are cut, in
+// group order, into S pieces: first one partner piece of T minus each short
+// run's bytes, then pieces of T.  All long pieces come first in dispatch
+// order and fill the CUs; the partners finish first and their slots take
+// the short pieces, so every slot ends with about T bytes.  The fp16 chunks
+// go to the pieces of T.  Returns false (use one launch per run) when the
+// runs do not fit this scheme.
+bool plan_pieces(const kvq_cache* h, const std::vector<Run>& runs, int64_t S, kvq::MixedPlan* mp) {
+  const kvq_config& c = h->cfg;
+  std::vector<int64_t> pb(runs.size()), bytes(runs.size());
+  int64_t total = 0;
+  for (size_t i = 0; i < runs.size(); ++i) {
+    pb[i] = layout_bits(&c, runs[i].kb, runs[i].vb, 0).page_bytes;
+    bytes[i] = (runs[i].g1 - runs[i].g0) * pb[i];
+    total += bytes[i];
+  }
+  const double T = static_cast<double>(total) / static_cast<double>(S);
+  std::vector<size_t> shorts, longs;
+  for (size_t i = 0; i < runs.size(); ++i) (static_cast<double>(bytes[i]) < T ? shorts : longs).push_back(i);
+  const int64_t nshort = static_cast<int64_t>(shorts.size());
+  if (longs.empty() || nshort >= S) return false;
+  // byte targets of the long pieces, in dispatch order
+  std::vector<double> target;
+  for (size_t i : shorts) target.push_back(T - static_cast<double>(bytes[i]));
+  while (static_cast<int64_t>(target.size()) < S) target.push_back(T);
+  std::vector<kvq::MixedPiece> body, tail;
+  size_t ti = 0;
+  int nf16 = 0;
+  for (size_t li = 0; li < longs.size(); ++li) {
+    const Run& r = runs[longs[li]];
+    int64_t g = r.g0;
+    while (g < r.g1) {
+      const double want = ti < target.size() ? target[ti] : T;
+      // the boundary nearest to `want` bytes, at least one group, within the run
+      int64_t n = std::max<int64_t>(1, static_cast<int64_t>(want / pb[longs[li]] + 0.5));
+      if (li + 1 == longs.size() && ti + 1 >= target.size()) n = r.g1 - g;  // the last piece takes the rest
+      n = std::min<int64_t>(n, r.g1 - g);
+      const bool partner = ti < shorts.size();
+      body.push_back({16 * r.kb + r.vb, static_cast<int>(g), static_cast<int>(g + n), 0, partner ? -1 : nf16++});
+      g += n;
+      ++ti;
+    }
+  }
+  for (size_t i : shorts) tail.push_back({16 * runs[i].kb + runs[i].vb, static_cast<int>(runs[i].g0),
+                                          static_cast<int>(runs[i].g1), 0, -1});
+  if (nf16 == 0) {  // no piece of T: the first long piece takes the fp16 chunks
+    body[0].f16 = 0;
+    nf16 = 1;
+  }
+  const size_t np = body.size() + tail.size();
+  if (np > static_cast<size_t>(kvq::kMaxPieces) || static_cast<int64_t>(np) > max_splits(&c)) return false;
+  mp->npieces = static_cast<int>(np);
+  mp->nf16 = nf16;
+  size_t k = 0;
+  for (const auto& pc : body) mp->p[k++] = pc;
+  for (const auto& pc : tail) mp->p[k++] = pc;
+  for (size_t q = 0; q < np; ++q) mp->p[q].slot = static_cast<int>(q);
+  return true;
+}
+
 // Split counts of the runs of equal-bit groups: about S times the run's share
 // of the page bytes each, at least one, at most S + runs - 1 in total (short
 // runs get a split of their own without shortening the long runs': on the
@@ -359,16 +421,23 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
   if (static_cast<int64_t>(runs.size()) > max_splits(&c))
     return fail(KVQ_E_UNSUPPORTED, "%zu runs of equal bit widths exceed the split maximum %d", runs.size(),
                 max_splits(&c));
+  kvq::MixedPlan plan{};
+  const bool mixed = runs.size() > 1 && runs.size() <= static_cast<size_t>(kvq::kMaxRuns) &&
+                     plan_pieces(h, runs, std::min<int64_t>(num_splits, ng), &plan);
   std::vector<int64_t> sp(runs.size(), 1), gps(runs.size(), 0);
-  if (ng > 0) sp = run_splits(h, runs, std::min<int64_t>(num_splits, ng));
   int64_t S = 0;
-  for (size_t i = 0; i < runs.size(); ++i) {
-    const int64_t len = runs[i].g1 - runs[i].g0;
-    if (len > 0) {
-      gps[i] = (len + sp[i] - 1) / sp[i];
-      sp[i] = (len + gps[i] - 1) / gps[i];  // no empty split
+  if (mixed) {
+    S = plan.npieces;
+  } else {
+    if (ng > 0) sp = run_splits(h, runs, std::min<int64_t>(num_splits, ng));
+    for (size_t i = 0; i < runs.size(); ++i) {
+      const int64_t len = runs[i].g1 - runs[i].g0;
+      if (len > 0) {
+        gps[i] = (len + sp[i] - 1) / sp[i];
+        sp[i] = (len + gps[i] - 1) / gps[i];  // no empty split
+      }
+      S += sp[i];
     }
-    S += sp[i];
   }
   const int64_t rows = static_cast<int64_t>(c.batch) * c.num_q_heads;
   const bool final = allow_final && S == 1;
@@ -397,23 +466,9 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
   a.splits_total = S;
   // the fp16 chunks go with the run that has the most splits
   const size_t fp16_run = static_cast<size_t>(std::max_element(sp.begin(), sp.end()) - sp.begin());
-  if (runs.size() > 1 && runs.size() <= static_cast<size_t>(kvq::kMaxRuns)) {
-    // one launch for all runs
-    kvq::MixedRuns mr{};
-    mr.n = static_cast<int>(runs.size());
-    mr.fp16_run = static_cast<int>(fp16_run);
-    int64_t off = 0;
-    for (size_t i = 0; i < runs.size(); ++i) {
-      mr.bits[i] = 16 * runs[i].kb + runs[i].vb;
-      mr.splits[i] = static_cast<int>(sp[i]);
-      mr.split_off[i] = static_cast<int>(off);
-      mr.g_base[i] = runs[i].g0;
-      mr.ngroups[i] = runs[i].g1 - runs[i].g0;
-      mr.gps[i] = gps[i];
-      off += sp[i];
-    }
+  if (mixed) {
     a.L = h->L;
-    hipError_t e = kvq::launch_decode_mixed(a, mr, s);
+    hipError_t e = kvq::launch_decode_mixed(a, plan, s);
     if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
     if (splits_used) *splits_used = static_cast<int32_t>(S);
     return ok();

@@ -848,9 +848,9 @@ void decode_kernel(DecodeArgs a) {
   decode_split<D, KB, VB, G, GQC, TN>(a, blockIdx.x / a.splits, static_cast<int>(blockIdx.x % a.splits), ring);
 }
 
-// Groups of several bit widths in one launch: workgroup (slice, split) finds
-// the run of equal-width groups that its split belongs to and runs that
-// width's body, so the runs share one grid instead of one launch each.
+// Groups of several bit widths in one launch: each block looks up its piece
+// (a range of groups of one width, see MixedPlan) and runs that width's body
+// over it; the LDS ring is sized for the widest body.
 template <int D, int G>
 constexpr int mixed_ring_bytes() {
   constexpr int a = ring_bytes<D, 2, 2, G, false>(), b = ring_bytes<D, 2, 4, G, false>();
@@ -864,30 +864,23 @@ constexpr int mixed_ring_bytes() {
 
 template <int D, int G, int GQC, bool TN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
-void decode_mixed_kernel(DecodeArgs a, MixedRuns mr) {
+void decode_mixed_kernel(DecodeArgs a, MixedPlan mp) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[mixed_ring_bytes<D, G>()];
-  const int64_t slice = blockIdx.x / a.splits_total;
-  const int sg = static_cast<int>(blockIdx.x % a.splits_total);
-  int bits = mr.bits[0], sp = mr.splits[0], off = 0;
-  int64_t gb = mr.g_base[0], ng = mr.ngroups[0], gps = mr.gps[0];
-  bool f16 = mr.fp16_run == 0;
-#pragma unroll
-  for (int i = 1; i < kMaxRuns; ++i) {
-    if (i < mr.n && sg >= mr.split_off[i]) {
-      bits = mr.bits[i]; sp = mr.splits[i]; off = mr.split_off[i];
-      gb = mr.g_base[i]; ng = mr.ngroups[i]; gps = mr.gps[i];
-      f16 = mr.fp16_run == i;
-    }
-  }
+  const int64_t slice = blockIdx.x % a.L.slices;
+  const MixedPiece pc = mp.p[blockIdx.x / a.L.slices];
+  // the piece's range and slot through the split arithmetic of decode_split:
+  // split s (its fp16 index, or 0) of groups_per_split = g1 - g0 starting
+  // s pieces before g0
+  const int s = pc.f16 >= 0 ? pc.f16 : 0;
+  const int64_t gps = pc.g1 - pc.g0;
   DecodeArgs r = a;
-  r.splits = sp;
-  r.split_off = off;
-  r.g_base = gb;
-  r.ngroups = ng;
+  r.splits = mp.nf16 > 0 ? mp.nf16 : 1;
   r.groups_per_split = gps;
-  r.do_fp16 = f16 ? 1 : 0;
-  const int s = sg - off;
-  switch (bits) {
+  r.g_base = pc.g0 - s * gps;
+  r.ngroups = pc.g1 - r.g_base;
+  r.split_off = pc.slot - s;
+  r.do_fp16 = pc.f16 >= 0 ? 1 : 0;
+  switch (pc.bits) {
     case 0x22: decode_split<D, 2, 2, G, GQC, TN>(r, slice, s, ring); break;
     case 0x24: decode_split<D, 2, 4, G, GQC, TN>(r, slice, s, ring); break;
     case 0x42: decode_split<D, 4, 2, G, GQC, TN>(r, slice, s, ring); break;
@@ -937,8 +930,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
 
 namespace {
 template <int D, int G, bool TN>
-hipError_t mixed_t(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(a.L.slices * a.splits_total));
+hipError_t mixed_t(const DecodeArgs& a, const MixedPlan& mr, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(a.L.slices * mr.npieces));
   const size_t lds = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
   if (a.gqa <= 4)
     hipLaunchKernelGGL((decode_mixed_kernel<D, G, 4, TN>), grid, dim3(kLanes), lds, s, a, mr);
@@ -949,17 +942,17 @@ hipError_t mixed_t(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s) {
   return hipGetLastError();
 }
 template <int D, int G>
-hipError_t mixed_g(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s) {
+hipError_t mixed_g(const DecodeArgs& a, const MixedPlan& mr, hipStream_t s) {
   return a.L.token_norm ? mixed_t<D, G, true>(a, mr, s) : mixed_t<D, G, false>(a, mr, s);
 }
 template <int D>
-hipError_t mixed_d(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s) {
+hipError_t mixed_d(const DecodeArgs& a, const MixedPlan& mr, hipStream_t s) {
   return a.L.G == 32 ? mixed_g<D, 32>(a, mr, s) : mixed_g<D, 64>(a, mr, s);
 }
 }  // namespace
 
-hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s) {
-  if (mr.n < 1 || mr.n > kMaxRuns) return hipErrorInvalidValue;
+hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedPlan& mr, hipStream_t s) {
+  if (mr.npieces < 1 || mr.npieces > kMaxPieces) return hipErrorInvalidValue;
   return a.L.D == 64 ? mixed_d<64>(a, mr, s) : mixed_d<128>(a, mr, s);
 }
 

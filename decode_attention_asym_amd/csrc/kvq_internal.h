@@ -71,28 +71,28 @@ struct DecodeArgs {
   int write_final;
 };
 
-// Runs of groups with equal bit widths decoded by one launch: run i covers
-// groups [g_base[i], g_base[i] + ngroups[i]) with splits[i] splits of gps[i]
-// groups, in split slots [split_off[i], split_off[i] + splits[i]); bits[i] is
-// 16 * key bits + value bits; run fp16_run also covers the fp16 chunks.
+// Groups of several bit widths decoded by one launch, as a table of pieces
+// in dispatch order: piece k of every slice covers groups [g0, g1) of one
+// width (bits = 16 * key bits + value bits), writes partial slot `slot` and
+// takes the fp16 chunks of index f16 among nf16 sharers (none if f16 < 0).
+// Block b runs piece b / slices of slice b % slices, so all slices' piece 0
+// is dispatched first, then piece 1, ...
 constexpr int kMaxRuns = 8;
-struct MixedRuns {
-  int n;
-  int fp16_run;
-  int bits[kMaxRuns];
-  int splits[kMaxRuns];
-  int split_off[kMaxRuns];
-  int64_t g_base[kMaxRuns];
-  int64_t ngroups[kMaxRuns];
-  int64_t gps[kMaxRuns];
+constexpr int kMaxPieces = 48;
+struct MixedPiece {
+  int bits, g0, g1, slot, f16;
+};
+struct MixedPlan {
+  int npieces, nf16;
+  MixedPiece p[kMaxPieces];
 };
 
 // Both return hipSuccess or the launch error.
 hipError_t launch_flush(const AppendArgs& a, hipStream_t s);
 hipError_t launch_window_write(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
-// a: splits_total, L (any of the runs' layouts) and the common fields
-hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedRuns& mr, hipStream_t s);
+// a: splits_total (= npieces), L (any of the widths' layouts) and the common fields
+hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedPlan& mp, hipStream_t s);
 hipError_t launch_merge(const float* partial, float* out, int rows, int splits, int D, hipStream_t s);
 hipError_t launch_code_histograms(const DriftArgs& a, hipStream_t s);
 hipError_t launch_drift_check(const DriftArgs& a, hipStream_t s);

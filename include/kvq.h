@@ -158,12 +158,16 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, v
  * Split s covers the contiguous token groups [s * c, min(ng, (s + 1) * c))
  * with c = ceil(ng / S) (ng quantized groups), plus the fp16 window's 32-token
  * chunks w (counted from the first window token) with w mod S = S - 1 - s.
- * (A position-adaptive cache first cuts its groups into runs of equal bit
- * widths and splits each run that way into consecutive split slots, in
- * proportion to its page bytes, at least one per run; the fp16 chunks go with
- * the run that has the most splits.  S is then the total, at most
- * num_splits + runs - 1 and within the workspace maximum; KVQ_E_UNSUPPORTED
- * when there are more runs than that maximum.)
+ * (A position-adaptive cache decodes pieces of one width each instead: with
+ * T = the slice's page bytes / num_splits, every run smaller than T is one
+ * piece, and the other runs are cut in group order into a piece of T minus
+ * each small run's bytes, then pieces of T (the fp16 chunks are shared by the
+ * pieces of T); slots follow that order (the big runs' pieces, then the small
+ * runs), and S is the number of pieces.  When that does not apply (all runs
+ * small, more than 8 runs, more pieces than fit) each run is split on its
+ * own in proportion to its page bytes, at least once, the run with the most
+ * splits taking the fp16 chunks, and S is at most num_splits + runs - 1;
+ * KVQ_E_UNSUPPORTED when the runs outnumber the workspace maximum of splits.)
  * bytes must be >= H_q * B * S * (D + 4) * 4.  Requires a non-empty cache. */
 kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials, size_t bytes, int32_t num_splits,
                                int32_t* splits_used, void* stream);
