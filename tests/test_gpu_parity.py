@@ -512,3 +512,33 @@ def test_step_partials_and_argument_checks():
     with pytest.raises(kvq.KVQError):  # capacity
         b.append_decode(k, v, q)
     assert b.num_tokens == w.N + 3
+
+
+def test_adaptive_pieces_at_many_split_counts():
+    """The piece plan of a position-adaptive cache (big runs cut into partner
+    pieces and pieces of T bytes, small runs last; per-run splits when that
+    does not apply) gives the oracle's attention at every split count, and
+    the partials of every plan merge to the same output."""
+    kvq = _lib()
+    w = WORKLOADS[2].replace(name="adaptive-pieces", B=2, Hkv=2, Hq=8, N=6000 + 37, adapt_delta=640,
+                             bits_low=(2, 2), bits_high=(4, 4), sink=64)
+    syn = Synth(w, "cuda")
+    K, V = syn.kv_all()
+    c = kvq.KVQCache(kvq.config_for(w))
+    c.append(K, V)
+    q = syn.q()
+    exp = c.export()
+    encs = oracle_encode_slices(w, K, V, [(b, h) for b in range(w.B) for h in range(w.Hkv)])
+    assert_export_matches(w, exp, 0, encs)
+    ref = oracle_rows(w, exp, 0, to_oracle_input(q, w.dtype), list(range(w.B)))
+    refs = np.stack([ref[b] for b in range(w.B)])
+    for splits in (1, 2, 3, 4, 5, 6, 9, 16, 40, None):
+        out = c.decode(q, splits=splits)
+        parts, S = c.decode_partials(q, splits=splits if splits else c.default_splits())
+        merged = torch.empty_like(out)
+        kvq.merge_partials(parts, merged, w.B * w.Hq, S, w.D)
+        torch.cuda.synchronize()
+        err, _ = rel_l2(out.double().cpu().numpy(), refs)
+        log(f"[pieces] splits={splits}: {S} slots, rel L2 {err:.3e}")
+        assert err <= TOL_REL_L2, (splits, err)
+        assert torch.allclose(merged, out, rtol=1e-6, atol=1e-7), splits
