@@ -104,21 +104,6 @@ __device__ __forceinline__ uint32_t code_of(float x, float mn, float s, bool sym
   return sym ? quant_code_sym(x, s, c0) : quant_code(x, mn, s, levels);
 }
 
-// L2 norm of a row of D values: squares, pairwise sums (element 2i + element
-// 2i + 1, level by level), correctly rounded square root -- a fixed order, so
-// the result does not depend on how the work is shared.
-template <int D>
-__device__ float row_norm(const float* x) {
-  float t[D / 2];
-#pragma unroll
-  for (int i = 0; i < D / 2; ++i) t[i] = __fadd_rn(__fmul_rn(x[2 * i], x[2 * i]), __fmul_rn(x[2 * i + 1], x[2 * i + 1]));
-#pragma unroll
-  for (int w = D / 2; w > 1; w /= 2)
-#pragma unroll
-    for (int i = 0; i < w / 2; ++i) t[i] = __fadd_rn(t[2 * i], t[2 * i + 1]);
-  return sqrtf(t[0]);
-}
-
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // nearest binary32 to 1/sqrt(128)
 constexpr float kInvSqrt64 = 0.125f;
 
@@ -233,11 +218,25 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   // before the key quantizer; the norm is stored as fp16 (0 for a zero row,
   // whose normalized values are 0)
   if (L.token_norm) {
-    for (int i = tid; i < G; i += blockDim.x) {
-      const float nrm = row_norm<D>(kx + i * KS);
-      knrm[i] = nrm;
-      uint16_t* kn = reinterpret_cast<uint16_t*>(page + L.off_knorm + (i / kChunk) * L.kn_chunk_bytes);
-      kn[knorm_elem(i % kChunk)] = fp16_bits(nrm);
+    // one wave per row: lane t takes the square sum of elements 2t, 2t + 1
+    // (or, for D = 64, lanes 0..31), then each tree level adds pairs (2t,
+    // 2t + 1) of the level below: a fixed order, so the norm does not depend
+    // on how the work is shared; then a correctly rounded square root
+    const int lane = tid % kLanes, wave = tid / kLanes, nwaves = blockDim.x / kLanes;
+    for (int i = wave; i < G; i += nwaves) {
+      const float* row = kx + i * KS;
+      float t = 0.0f;
+      if (lane < D / 2) t = __fadd_rn(__fmul_rn(row[2 * lane], row[2 * lane]), __fmul_rn(row[2 * lane + 1], row[2 * lane + 1]));
+      for (int w = D / 2; w > 1; w /= 2) {
+        const float a0 = __shfl(t, (2 * lane) % kLanes), a1 = __shfl(t, (2 * lane + 1) % kLanes);
+        t = lane < w / 2 ? __fadd_rn(a0, a1) : 0.0f;
+      }
+      if (lane == 0) {
+        const float nrm = sqrtf(t);
+        knrm[i] = nrm;
+        uint16_t* kn = reinterpret_cast<uint16_t*>(page + L.off_knorm + (i / kChunk) * L.kn_chunk_bytes);
+        kn[knorm_elem(i % kChunk)] = fp16_bits(nrm);
+      }
     }
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += blockDim.x) {
