@@ -9,12 +9,13 @@
 // group's distribution is the histogram of its G x D key codes (and of its
 // value codes); the calibration is a histogram of code counts per kv head.
 //
-// One wave per (group, slice).  Codes are counted without unpacking them: b
-// code words (b = bit width) are folded into b bit planes of 32 codes each
-// (plane k holds bit k of every code), the count of value v is the popcount
-// of the AND of the planes or their complements, and the 2^b per-lane counts
-// are summed over the wave by a reduce-scatter (each exchange halves the
-// counters a lane keeps), so each lane ends with the total of one bin.
+// One wave per few consecutive groups of one slice.  Codes are counted
+// without unpacking them: b code words (b = bit width) are transposed into b
+// bit planes of 32 codes each (plane k holds bit k of every code), the count
+// of value v is the popcount of the AND of the planes or their complements,
+// and the 2^b per-lane counts are summed over the wave by a reduce-scatter
+// (each exchange halves the counters a lane keeps), so each lane ends with
+// the total of one bin.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,45 +26,79 @@ namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-template <int B>
-constexpr uint32_t plane_mask() { return B == 4 ? 0x11111111u : 0x55555555u; }
+// Groups one wave visits (consecutive groups of one slice), two at a time: the
+// per-wave set-up (calibration probabilities, page addressing) is paid once
+// for them, and the next pair's codes load while a pair is reduced.
+constexpr int kGroupsPerWave = 4;
 
-// Adds the counts of the 32 / B codes in each of B words w[0..B) to cnt[2^B].
-template <int B>
-__device__ __forceinline__ void count_words(const uint32_t (&w)[B], uint32_t (&cnt)[1 << B]) {
-  constexpr uint32_t M = plane_mask<B>();
-  uint32_t P[B];
-#pragma unroll
-  for (int k = 0; k < B; ++k) {
-    uint32_t x = 0;
-#pragma unroll
-    for (int j = 0; j < B; ++j) x |= ((w[j] >> k) & M) << j;
-    P[k] = x;  // bit (B * i + j) = bit k of code i of word j
-  }
-  if constexpr (B == 2) {
-    const uint32_t n0 = ~P[0], n1 = ~P[1];
-    cnt[0] += __builtin_popcount(n0 & n1);
-    cnt[1] += __builtin_popcount(P[0] & n1);
-    cnt[2] += __builtin_popcount(n0 & P[1]);
-    cnt[3] += __builtin_popcount(P[0] & P[1]);
-  } else {
-    const uint32_t n0 = ~P[0], n1 = ~P[1], n2 = ~P[2], n3 = ~P[3];
-    const uint32_t lo[4] = {n0 & n1, P[0] & n1, n0 & P[1], P[0] & P[1]};
-    const uint32_t hi[4] = {n2 & n3, P[2] & n3, n2 & P[3], P[2] & P[3]};
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-      for (int l = 0; l < 4; ++l) cnt[4 * h + l] += __builtin_popcount(lo[l] & hi[h]);
-  }
+// Bits of a where m is set, bits of b elsewhere.
+__device__ __forceinline__ uint32_t pick(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+// The value x, opaque to the optimizer (no instruction): keeps the compiler
+// from folding the plane transposes into the count products, which it
+// otherwise expands into more instructions than it saves.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
 }
 
-// Counts of the codes in BYTES contiguous bytes at p (a multiple of 1 KiB or
-// 512 B), spread over the wave's lanes.
-template <int B, int BYTES>
-__device__ __forceinline__ void count_block(const uint8_t* p, int l, uint32_t (&cnt)[1 << B]) {
-  constexpr int DW = BYTES / 4 / kLanes;  // dwords per lane
-  static_assert(BYTES % (4 * kLanes) == 0 && DW % B == 0, "whole bit-plane batches per lane");
-  uint32_t w[DW];
+// Counting works on bit planes: B words of B-bit codes are transposed so that
+// plane k holds bit k of every one of their 32 codes (the same bit position in
+// every plane belongs to the same code); the number of codes equal to v is then
+// the popcount of the AND of the planes (or their complements) selected by v.
+// Counts of the value whose low (and high) bits are all zero are not formed
+// per batch: they follow at the end from the number of codes a lane counted.
+//
+// Two 2-bit words: bit 2i + j of plane k is bit k of code i of word j.
+// Adds to c[1..3].
+__device__ __forceinline__ void count_batch2(uint32_t w0, uint32_t w1, uint32_t (&c)[4]) {
+  const uint32_t p0 = opaque(pick(0xAAAAAAAAu, w1 << 1, w0)), p1 = opaque(pick(0x55555555u, w0 >> 1, w1));
+  c[1] += __builtin_popcount(p0 & ~p1);
+  c[2] += __builtin_popcount(~p0 & p1);
+  c[3] += __builtin_popcount(p0 & p1);
+}
+// c[0] from the lane's code total.
+__device__ __forceinline__ void finish2(uint32_t total, uint32_t (&c)[4]) { c[0] = total - c[1] - c[2] - c[3]; }
+
+// Four 4-bit words: a 4 x 4 bit transpose inside every nibble position in two
+// stages (pairs of words swap single bits, then pairs of pairs swap bit pairs),
+// so bit 4i + j of plane k is bit k of code i of word j.  Code v = 4h + l:
+// low planes (p0, p1) select l, high planes (p2, p3) select h.  Adds to c[4h + l]
+// for h, l >= 1, and to lc[l] / hc[h] the codes whose low / high half is l / h.
+__device__ __forceinline__ void count_batch4(const uint32_t (&w)[4], uint32_t (&c)[16], uint32_t (&lc)[4],
+                                             uint32_t (&hc)[4]) {
+  const uint32_t a0 = opaque(pick(0xAAAAAAAAu, w[1] << 1, w[0])), a1 = opaque(pick(0x55555555u, w[0] >> 1, w[1]));
+  const uint32_t a2 = opaque(pick(0xAAAAAAAAu, w[3] << 1, w[2])), a3 = opaque(pick(0x55555555u, w[2] >> 1, w[3]));
+  const uint32_t p0 = opaque(pick(0xCCCCCCCCu, a2 << 2, a0)), p2 = opaque(pick(0x33333333u, a0 >> 2, a2));
+  const uint32_t p1 = opaque(pick(0xCCCCCCCCu, a3 << 2, a1)), p3 = opaque(pick(0x33333333u, a1 >> 2, a3));
+  const uint32_t lo[4] = {0u, p0 & ~p1, ~p0 & p1, p0 & p1};
+  const uint32_t hi[4] = {0u, p2 & ~p3, ~p2 & p3, p2 & p3};
+#pragma unroll
+  for (int h = 1; h < 4; ++h)
+#pragma unroll
+    for (int l = 1; l < 4; ++l) c[4 * h + l] += __builtin_popcount(lo[l] & hi[h]);
+#pragma unroll
+  for (int k = 1; k < 4; ++k) {
+    lc[k] += __builtin_popcount(lo[k]);
+    hc[k] += __builtin_popcount(hi[k]);
+  }
+}
+__device__ __forceinline__ void finish4(uint32_t total, const uint32_t (&lc)[4], const uint32_t (&hc)[4],
+                                        uint32_t (&c)[16]) {
+#pragma unroll
+  for (int l = 1; l < 4; ++l) c[l] = lc[l] - c[4 + l] - c[8 + l] - c[12 + l];
+#pragma unroll
+  for (int h = 1; h < 4; ++h) c[4 * h] = hc[h] - c[4 * h + 1] - c[4 * h + 2] - c[4 * h + 3];
+  uint32_t r = total;
+#pragma unroll
+  for (int v = 1; v < 16; ++v) r -= c[v];
+  c[0] = r;
+}
+
+// The DW dwords of a code block that lane l holds (16-byte non-temporal loads
+// when DW is a multiple of 4): dword i of lane l is dword (i / 4) * 256 + 4 l +
+// i % 4 of the block (or i * 64 + l), the same assignment for every block.
+template <int DW>
+__device__ __forceinline__ void load_block(const uint8_t* p, int l, uint32_t (&w)[DW]) {
   if constexpr (DW % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < DW / 4; ++i) {
@@ -74,12 +109,26 @@ __device__ __forceinline__ void count_block(const uint8_t* p, int l, uint32_t (&
 #pragma unroll
     for (int i = 0; i < DW; ++i) w[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + i * kLanes + l);
   }
+}
+
+// Per-lane counts of the codes in DW dwords of B-bit codes.
+template <int B, int DW>
+__device__ __forceinline__ void count_lane(const uint32_t (&w)[DW], uint32_t (&c)[1 << B]) {
+  static_assert(DW % B == 0, "whole bit-plane batches per lane");
 #pragma unroll
-  for (int i = 0; i < DW / B; ++i) {
-    uint32_t ww[B];
+  for (int i = 0; i < (1 << B); ++i) c[i] = 0;
+  if constexpr (B == 2) {
 #pragma unroll
-    for (int j = 0; j < B; ++j) ww[j] = w[B * i + j];
-    count_words<B>(ww, cnt);
+    for (int i = 0; i < DW / 2; ++i) count_batch2(w[2 * i], w[2 * i + 1], c);
+    finish2(DW * 16, c);
+  } else {
+    uint32_t lc[4] = {0u, 0u, 0u, 0u}, hc[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < DW / 4; ++i) {
+      const uint32_t ww[4] = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+      count_batch4(ww, c, lc, hc);
+    }
+    finish4(DW * 8, lc, hc, c);
   }
 }
 
@@ -116,46 +165,41 @@ __device__ __forceinline__ int bin_of_lane(int l) {
   return (l >> (6 - LOG)) & (NB - 1);
 }
 
-// KL term of one bin: p ln(p / q), 0 for p = 0, +inf for p > 0 = q (fp64;
-// p = c / per with per = G * D a power of two, so c * (1 / per) is exact).
-__device__ __forceinline__ double kl_term(uint32_t c, double inv_per, uint64_t cq, double tot) {
-  if (c == 0) return 0.0;
-  if (cq == 0) return __builtin_inf();
-  const double p = static_cast<double>(c) * inv_per;
-  const double q = static_cast<double>(cq) / tot;
-  return p * log(p / q);
-}
-
-__device__ __forceinline__ double wave_sum_f64(double t) {
+// Sum of t over the lanes l' with l' = l (mod STRIDE), in every such lane.
+template <int STRIDE>
+__device__ __forceinline__ double strided_sum_f64(double t) {
 #pragma unroll
-  for (int m = 32; m >= 1; m /= 2) t += __shfl_xor(t, m);
+  for (int m = STRIDE; m < kLanes; m *= 2) t += __shfl_xor(t, m);
   return t;
 }
 
+// One wave per kGroupsPerWave consecutive groups of one slice.
 template <int D, int KB, int VB, int G, bool HIST>
 __global__ __launch_bounds__(64) void drift_kernel(DriftArgs a) {
   constexpr int NBK = 1 << KB, NBV = 1 << VB;
-  constexpr int KBYTES = G * D * KB / 8, VBYTES = G * D * VB / 8;
+  constexpr int KDW = G * D * KB / 8 / 4 / kLanes, VDW = G * D * VB / 8 / 4 / kLanes;  // dwords per lane
+  static_assert(G * D * KB / 8 == KDW * 4 * kLanes && G * D * VB / 8 == VDW * 4 * kLanes, "whole dwords per lane");
   const Layout& L = a.L;
   const int l = threadIdx.x;
-  const int64_t g = a.g0 + blockIdx.x;
   const int64_t slice = blockIdx.y;
   const int hkv = static_cast<int>(slice % a.Hkv);
-  const uint8_t* page = a.cache + page_offset(L, slice, g);
-  uint32_t ck[NBK], cv[NBV];
-#pragma unroll
-  for (int i = 0; i < NBK; ++i) ck[i] = 0;
-#pragma unroll
-  for (int i = 0; i < NBV; ++i) cv[i] = 0;
-  count_block<KB, KBYTES>(page + L.off_kcodes, l, ck);
-  count_block<VB, VBYTES>(page + L.off_vcodes, l, cv);
-  const uint32_t tk = wave_bins<NBK>(ck, l), tv = wave_bins<NBV>(cv, l);
+  const int64_t gb = a.g0 + static_cast<int64_t>(blockIdx.x) * kGroupsPerWave;
+  const int64_t ge = min(gb + kGroupsPerWave, a.g0 + a.ng);
+  const uint8_t* page = a.cache + page_offset(L, slice, gb);
   const int bk = bin_of_lane<NBK>(l), bv = bin_of_lane<NBV>(l);
-  if constexpr (HIST) {
-    if ((l & (64 / NBK - 1)) == 0) atomicAdd(reinterpret_cast<unsigned long long*>(a.hist_k) + hkv * NBK + bk, tk);
-    if ((l & (64 / NBV - 1)) == 0) atomicAdd(reinterpret_cast<unsigned long long*>(a.hist_v) + hkv * NBV + bv, tv);
-  } else {
-    // calibration totals
+
+  // KL terms, one fp64 logarithm per lane for two groups at once: the first
+  // group's key bins in lanes 0 mod 4 (or 16), its value bins in lanes 2 mod 4
+  // (or 16), the second group's in lanes 1 and 3 mod 4 (or 16); within those,
+  // the first lane of each bin's lanes.  A bin's term is p ln(p / q), 0 for
+  // p = 0, +inf for p > 0 = q, with p = c / (G D) (exact: G D is a power of
+  // two) and the calibration probability q = count / total formed once per
+  // wave.
+  static_assert(((G * D) & (G * D - 1)) == 0, "G * D is a power of two");
+  const int r = l & (64 / NBK - 1), rv = l & (64 / NBV - 1);
+  const bool kl0 = r == 0, kl1 = r == 1, vl0 = rv == 2, vl1 = rv == 3;
+  double q = 0.0;
+  if constexpr (!HIST) {
     const uint64_t* qk = a.cal_k + hkv * NBK;
     const uint64_t* qv = a.cal_v + hkv * NBV;
     uint64_t sk = 0, sv = 0;
@@ -163,21 +207,75 @@ __global__ __launch_bounds__(64) void drift_kernel(DriftArgs a) {
     for (int i = 0; i < NBK; ++i) sk += qk[i];
 #pragma unroll
     for (int i = 0; i < NBV; ++i) sv += qv[i];
-    static_assert(((G * D) & (G * D - 1)) == 0, "G * D is a power of two");
-    // one term per lane: key bin bk in the first lane of each key bin's lanes,
-    // value bin bv in the second lane of each value bin's lanes, so one fp64
-    // logarithm serves both
-    const bool kl = (l & (64 / NBK - 1)) == 0, vl = (l & (64 / NBV - 1)) == 1;
-    const double term = kl_term(kl ? tk : (vl ? tv : 0u), 1.0 / static_cast<double>(G * D),
-                                kl ? qk[bk] : qv[bv], static_cast<double>(kl ? sk : sv));
-    const double klk = wave_sum_f64(kl ? term : 0.0);
-    const double klv = wave_sum_f64(vl ? term : 0.0);
-    if (l == 0) {
-      const int64_t o = slice * a.ng + (g - a.g0);
-      a.kl_k[o] = klk;
-      a.kl_v[o] = klv;
-      a.flags[o] = static_cast<uint8_t>((klk > a.threshold ? 1 : 0) | (klv > a.threshold ? 2 : 0));
+    const bool kk = kl0 || kl1;
+    q = static_cast<double>(kk ? qk[bk] : qv[bv]) / static_cast<double>(kk ? sk : sv);
+  }
+
+  uint32_t hk[NBK], hv[NBV];  // per-lane totals over the wave's groups (histogram mode)
+#pragma unroll
+  for (int i = 0; i < NBK; ++i) hk[i] = 0;
+#pragma unroll
+  for (int i = 0; i < NBV; ++i) hv[i] = 0;
+  // two register sets: groups g and g + 1 of a pair; the next pair's codes
+  // load while this pair's counts are reduced and turned into KL terms
+  uint32_t kw0[KDW], vw0[VDW], kw1[KDW], vw1[VDW];
+  load_block<KDW>(page + L.off_kcodes, l, kw0);
+  load_block<VDW>(page + L.off_vcodes, l, vw0);
+  if (gb + 1 < ge) {
+    load_block<KDW>(page + L.page_bytes + L.off_kcodes, l, kw1);
+    load_block<VDW>(page + L.page_bytes + L.off_vcodes, l, vw1);
+  }
+#pragma unroll 1
+  for (int64_t g = gb; g < ge; g += 2) {
+    const bool two = g + 1 < ge;
+    uint32_t ck0[NBK], cv0[NBV], ck1[NBK], cv1[NBV];
+    count_lane<KB, KDW>(kw0, ck0);
+    count_lane<VB, VDW>(vw0, cv0);
+    if (two) {
+      count_lane<KB, KDW>(kw1, ck1);
+      count_lane<VB, VDW>(vw1, cv1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NBK; ++i) ck1[i] = 0;
+#pragma unroll
+      for (int i = 0; i < NBV; ++i) cv1[i] = 0;
     }
+    const uint8_t* pn = page + (g + 2 - gb) * L.page_bytes;
+    if (g + 2 < ge) {
+      load_block<KDW>(pn + L.off_kcodes, l, kw0);
+      load_block<VDW>(pn + L.off_vcodes, l, vw0);
+    }
+    if (g + 3 < ge) {
+      load_block<KDW>(pn + L.page_bytes + L.off_kcodes, l, kw1);
+      load_block<VDW>(pn + L.page_bytes + L.off_vcodes, l, vw1);
+    }
+    if constexpr (HIST) {
+#pragma unroll
+      for (int i = 0; i < NBK; ++i) hk[i] += ck0[i] + ck1[i];
+#pragma unroll
+      for (int i = 0; i < NBV; ++i) hv[i] += cv0[i] + cv1[i];
+    } else {
+      const uint32_t tk0 = wave_bins<NBK>(ck0, l), tv0 = wave_bins<NBV>(cv0, l);
+      const uint32_t tk1 = wave_bins<NBK>(ck1, l), tv1 = wave_bins<NBV>(cv1, l);
+      const uint32_t c = kl0 ? tk0 : kl1 ? tk1 : vl0 ? tv0 : vl1 ? tv1 : 0u;
+      const double p = static_cast<double>(c) * (1.0 / static_cast<double>(G * D));
+      const double term = c == 0 ? 0.0 : (q == 0.0 ? __builtin_inf() : p * log(p / q));
+      // lane j < 4 ends with the sum of the terms in lanes j mod 4: the first
+      // group's key and value KL in lanes 0 and 2, the second's in 1 and 3
+      const double t = strided_sum_f64<4>(term);
+      const double tv = __shfl(t, (l + 2) & (kLanes - 1));
+      if (l < 2 && (l == 0 || two)) {
+        const int64_t o = slice * a.ng + (g + l - a.g0);
+        a.kl_k[o] = t;
+        a.kl_v[o] = tv;
+        a.flags[o] = static_cast<uint8_t>((t > a.threshold ? 1 : 0) | (tv > a.threshold ? 2 : 0));
+      }
+    }
+  }
+  if constexpr (HIST) {
+    const uint32_t tk = wave_bins<NBK>(hk, l), tv = wave_bins<NBV>(hv, l);
+    if ((l & (64 / NBK - 1)) == 0) atomicAdd(reinterpret_cast<unsigned long long*>(a.hist_k) + hkv * NBK + bk, tk);
+    if ((l & (64 / NBV - 1)) == 0) atomicAdd(reinterpret_cast<unsigned long long*>(a.hist_v) + hkv * NBV + bv, tv);
   }
 }
 
@@ -188,7 +286,7 @@ __global__ void fill_u64_kernel(uint64_t* p, int64_t n) {
 
 template <int D, int KB, int VB, int G>
 hipError_t drift_t(const DriftArgs& a, bool hist, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(a.ng), static_cast<unsigned>(a.L.slices));
+  dim3 grid(static_cast<unsigned>((a.ng + kGroupsPerWave - 1) / kGroupsPerWave), static_cast<unsigned>(a.L.slices));
   if (hist)
     hipLaunchKernelGGL((drift_kernel<D, KB, VB, G, true>), grid, dim3(kLanes), 0, s, a);
   else
