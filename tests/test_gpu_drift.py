@@ -153,3 +153,40 @@ def test_requantize_partial_range_and_adaptive_cache():
         c.requantize(Kn, Vn, g0, ng + 1)
     with pytest.raises(kvq.KVQError):
         c.code_histograms(0, 4)  # no drift detection on adaptive caches
+
+
+@pytest.mark.parametrize("g0,g1", [(5, 6), (3, 10), (7, 20), (1, 40)])
+def test_drift_subranges_equal_full_range(g0, g1):
+    """Histograms and KL over a middle group range (odd starts and lengths, so
+    the kernel's groups per wave and its pairs end mid-way) equal the oracle's
+    and the same groups' values from the full-range call."""
+    kvq = _lib()
+    import oracle
+
+    w = DRIFT[0].replace(name="drift-subrange", B=1, Hq=8, Hkv=2, N=3000)
+    syn = Synth(w, "cuda")
+    K, V = syn.kv_all()
+    _heavy_tail(K, 1500, 2400, 21)
+    c = kvq.KVQCache(kvq.config_for(w))
+    c.append(K, V)
+    ng = c.num_groups()
+    assert g1 <= ng
+    pairs = [(0, h) for h in range(w.Hkv)]
+    encs = oracle_encode_slices(w, K, V, pairs)
+    kh, vh = c.code_histograms(g0, g1)
+    ref_k = np.zeros((w.Hkv, 1 << w.kbits), np.int64)
+    ref_v = np.zeros((w.Hkv, 1 << w.vbits), np.int64)
+    for (b, h), e in encs.items():
+        ref_k[h] += oracle.code_histogram(e["k_codes"][g0 * w.G:g1 * w.G], w.kbits)
+        ref_v[h] += oracle.code_histogram(e["v_codes"][g0 * w.G:g1 * w.G], w.vbits)
+    assert np.array_equal(kh.cpu().numpy(), ref_k)
+    assert np.array_equal(vh.cpu().numpy(), ref_v)
+    full = [x.cpu().numpy() for x in c.drift_check(kh, vh, 0, ng, THR)]
+    part = [x.cpu().numpy() for x in c.drift_check(kh, vh, g0, g1, THR)]
+    for f, p in zip(full, part):
+        assert np.array_equal(f[:, g0:g1], p)
+    for (b, h), e in encs.items():
+        rk, rv, rf = oracle.drift_check(e["k_codes"][g0 * w.G:g1 * w.G], e["v_codes"][g0 * w.G:g1 * w.G], w.G, w.D,
+                                        w.kbits, w.vbits, ref_k[h], ref_v[h], THR)
+        np.testing.assert_allclose(part[0][h], rk, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(part[1][h], rv, rtol=1e-12, atol=1e-15)
