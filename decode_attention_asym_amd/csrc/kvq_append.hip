@@ -12,6 +12,8 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -28,68 +30,103 @@ __device__ __forceinline__ float round_fp16(float x) { return __half2float(__flo
 
 __device__ __forceinline__ uint16_t fp16_bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
 
+// rne(fl(n / s)) for |n / s| <= 16, given rs = fl(1 / s) (correctly
+// rounded).  fl(n * rs) is within 2^-19 of n / s (two roundings of relative
+// size 2^-24 on a quotient below 16) and fl(n / s) within 2^-20 of it, so the
+// two round to the same integer unless n * rs lies within 2^-18 of a
+// half-integer.  The test is wider (2^-12); a wave in which some lane falls
+// inside it (a few percent of waves per code) takes the correctly rounded
+// division for those lanes.
+constexpr float kTieGuard = 0.5f - 0x1.0p-12f;
+__device__ __forceinline__ float rne_quotient(float n, float s, float rs) {
+  const float f = n * rs;
+  float t = rintf(f);
+  const bool near = fabsf(f - t) > kTieGuard;
+  if (__builtin_amdgcn_ballot_w64(near) != 0) {
+    if (near) t = rintf(n / s);
+  }
+  return t;
+}
+
 // code = clamp(rne((x - mn) / s), 0, levels); 0 when the group is constant.
-__device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float levels) {
+__device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float rs, float levels) {
   if (s == 0.0f) return 0u;
-  float q = rintf((x - mn) / s);
+  float q = rne_quotient(x - mn, s, rs);
   q = fminf(fmaxf(q, 0.0f), levels);
   return static_cast<uint32_t>(q);
 }
 
 // Symmetric code: clamp(rne(x / s), -c0, c0) + c0; c0 when s == 0.
-__device__ __forceinline__ uint32_t quant_code_sym(float x, float s, float c0) {
+__device__ __forceinline__ uint32_t quant_code_sym(float x, float s, float rs, float c0) {
   if (s == 0.0f) return static_cast<uint32_t>(c0);
-  float q = rintf(x / s);
+  float q = rne_quotient(x, s, rs);
   q = fminf(fmaxf(q, -c0), c0);
   return static_cast<uint32_t>(q + c0);
 }
 
+__device__ __forceinline__ float recip(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
+
 // Group parameters.  Asymmetric: s = (max - min) / (2^b - 1), zero = min.
-// With `hybrid`, also the symmetric quantizer (s = max|x| / c0, c0 = 2^(b-1) - 1,
+// With HYB, also the symmetric quantizer (s = max|x| / c0, c0 = 2^(b-1) - 1,
 // zero = fp16(-c0 * fp16(s))), kept only if its largest reconstruction error
 // |x - (code * scale16 + zero16)| (product exact, sum and difference rounded
-// in binary32) is strictly smaller.  x(i) yields the group's i-th value.
+// in binary32) is strictly smaller.
+//
+// Two adjacent lanes share a group: x(i), i < COUNT / 2, yields this lane's
+// half of it, and minima, maxima and largest errors are combined with the
+// partner lane (lane ^ 1); both lanes return the same parameters.  Minimum,
+// maximum and largest error do not depend on the order of their operands
+// (inputs are finite; a zero's sign is normalized by the + 0).
 struct GroupQ {
   float s, mn;          // binary32 scale and minimum the codes use
+  float rs;             // fl(1 / s), 0 when s == 0
   uint16_t scale16, zero16;
   bool sym;
 };
-template <int COUNT, int BITS, typename F>
-__device__ GroupQ group_params(F&& x, bool hybrid) {
+template <int COUNT, int BITS, bool HYB, typename F>
+__device__ __forceinline__ GroupQ group_params_pair(F&& x) {
+  constexpr int H = COUNT / 2;
   float mn = x(0), mx = mn, M = fabsf(mn);
-  for (int i = 1; i < COUNT; ++i) {
+  for (int i = 1; i < H; ++i) {
     const float v = x(i);
-    mn = v < mn ? v : mn;
-    mx = v > mx ? v : mx;
-    M = fabsf(v) > M ? fabsf(v) : M;
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+    if constexpr (HYB) M = fmaxf(M, fabsf(v));
   }
+  mn = fminf(mn, __shfl_xor(mn, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  if constexpr (HYB) M = fmaxf(M, __shfl_xor(M, 1));
   mn = mn + 0.0f;
   mx = mx + 0.0f;
-  M = M + 0.0f;
   constexpr float levels = static_cast<float>((1 << BITS) - 1), c0 = static_cast<float>((1 << (BITS - 1)) - 1);
   GroupQ r;
   r.s = (mx - mn) / levels;
+  r.rs = recip(r.s);
   r.mn = mn;
   r.scale16 = fp16_bits(r.s);
   r.zero16 = fp16_bits(mn);
   r.sym = false;
-  if (hybrid) {
-    const float ss = M / c0;
+  if constexpr (HYB) {
+    M = M + 0.0f;
+    const float ss = M / c0, rss = recip(ss);
     const uint16_t sc16 = fp16_bits(ss);
     const float s16 = __half2float(__ushort_as_half(sc16));
     const uint16_t z16 = fp16_bits(-(s16 * c0));
     const float zs = __half2float(__ushort_as_half(z16));
     const float sa = __half2float(__ushort_as_half(r.scale16)), za = __half2float(__ushort_as_half(r.zero16));
     float ea = 0.0f, es = 0.0f;
-    for (int i = 0; i < COUNT; ++i) {
+    for (int i = 0; i < H; ++i) {
       const float v = x(i);
-      const float xa = __fadd_rn(__fmul_rn(static_cast<float>(quant_code(v, mn, r.s, levels)), sa), za);
-      const float xs = __fadd_rn(__fmul_rn(static_cast<float>(quant_code_sym(v, ss, c0)), s16), zs);
+      const float xa = __fadd_rn(__fmul_rn(static_cast<float>(quant_code(v, mn, r.s, r.rs, levels)), sa), za);
+      const float xs = __fadd_rn(__fmul_rn(static_cast<float>(quant_code_sym(v, ss, rss, c0)), s16), zs);
       ea = fmaxf(ea, fabsf(__fsub_rn(v, xa)));
       es = fmaxf(es, fabsf(__fsub_rn(v, xs)));
     }
+    ea = fmaxf(ea, __shfl_xor(ea, 1));
+    es = fmaxf(es, __shfl_xor(es, 1));
     if (es < ea) {
       r.s = ss;
+      r.rs = rss;
       r.scale16 = sc16;
       r.zero16 = z16;
       r.sym = true;
@@ -98,10 +135,13 @@ __device__ GroupQ group_params(F&& x, bool hybrid) {
   return r;
 }
 
-template <int BITS>
-__device__ __forceinline__ uint32_t code_of(float x, float mn, float s, bool sym) {
+template <int BITS, bool HYB>
+__device__ __forceinline__ uint32_t code_of(float x, float mn, float s, float rs, bool sym) {
   constexpr float levels = static_cast<float>((1 << BITS) - 1), c0 = static_cast<float>((1 << (BITS - 1)) - 1);
-  return sym ? quant_code_sym(x, s, c0) : quant_code(x, mn, s, levels);
+  if constexpr (HYB) {
+    if (sym) return quant_code_sym(x, s, rs, c0);
+  }
+  return quant_code(x, mn, s, rs, levels);
 }
 
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // nearest binary32 to 1/sqrt(128)
@@ -132,17 +172,30 @@ __device__ void fwht_rows(float* x, int rows, int tid, int nthreads) {
 // One block per (flushed group, slice): gathers the group's G tokens (from
 // the fp16 window ring, or from the input for tokens of this call), computes
 // per-channel key and per-token value parameters, and writes the page.
-template <int D, int KB, int VB, int G>
+// F32K: keys are staged in binary32 (needed by the rotation and the token
+// norms, which round to fp16 only after their arithmetic); without either,
+// keys are fp16 from entry conversion on and staged as fp16, which halves
+// their LDS and lets four blocks share a CU at G = 64 instead of three.
+template <int D, int KB, int VB, int G, bool F32K>
 __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   constexpr int NKB = D / 32, NCG = D / G;
   constexpr int CPG = G / kChunk;
   // token rows padded by one bank (4 bytes) so that the lanes reading one
   // channel of 16 or 32 consecutive tokens hit different LDS banks
-  constexpr int KS = D + 1, VS = D + 2;
-  __shared__ float kx[G * KS];
+  using KT = typename std::conditional<F32K, float, __half>::type;
+  constexpr int KS = F32K ? D + 1 : D + 2, VS = D + 2;
+  __shared__ KT kx[G * KS];
   __shared__ __half vx[G * VS];  // values are fp16 after entry conversion
-  __shared__ float ks[D], kmn[D];
-  __shared__ float vs[G * NCG], vmn[G * NCG];
+  // a staged key as binary32, and the store of an entry-converted key (fp16
+  // staging rounds it to fp16 here, as the entry conversion does anyway)
+  auto kget = [&](int i) __attribute__((always_inline)) -> float {
+    if constexpr (F32K) return kx[i]; else return __half2float(kx[i]);
+  };
+  auto kput = [&](int i, float x) __attribute__((always_inline)) {
+    if constexpr (F32K) kx[i] = x; else kx[i] = __float2half_rn(x);
+  };
+  __shared__ float ks[D], kmn[D], krs[D];
+  __shared__ float vs[G * NCG], vmn[G * NCG], vrs[G * NCG];
   __shared__ bool ksym[D], vsym[G * NCG];
   __shared__ float knrm[G];
 
@@ -181,7 +234,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         const uint16_t vu = static_cast<uint16_t>(vw[e >> 1] >> (16 * (e & 1)));
         const float kf = a.in_dtype == 1 ? __half2float(__ushort_as_half(ku)) : __uint_as_float(static_cast<uint32_t>(ku) << 16);
         const float vf = a.in_dtype == 1 ? __half2float(__ushort_as_half(vu)) : __uint_as_float(static_cast<uint32_t>(vu) << 16);
-        kx[i * KS + c0 + e] = kf;
+        kput(i * KS + c0 + e, kf);
         vx[i * VS + c0 + e] = __float2half_rn(vf);
       }
     }
@@ -191,24 +244,26 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
     int64_t p = pos0 + i;
     if (p >= a.n_old) {
       int64_t src = in_base + (p - a.n_old) * D + c;
-      kx[i * KS + c] = load_in(a.k, a.in_dtype, src);
+      kput(i * KS + c, load_in(a.k, a.in_dtype, src));
       vx[i * VS + c] = __float2half_rn(load_in(a.v, a.in_dtype, src));
     } else {
       const uint8_t* rc = ring + ring_chunk_offset(L, slice, p);
       int t = static_cast<int>(p % kChunk);
-      kx[i * KS + c] = __half2float(*reinterpret_cast<const __half*>(rc + ring_k_offset(L, t, c)));
+      kput(i * KS + c, __half2float(*reinterpret_cast<const __half*>(rc + ring_k_offset(L, t, c))));
       vx[i * VS + c] = *reinterpret_cast<const __half*>(rc + ring_v_offset(L, t, c));
     }
   }
   }
   any_new = (pos0 + G) > a.n_old;
   __syncthreads();
-  if (any_new) {
+  if (F32K && any_new) {
     // rows [first_new, G) come from the input: rotate (keys) then round to fp16
     int first_new = a.n_old > pos0 ? static_cast<int>(a.n_old - pos0) : 0;
-    if (a.rotate) fwht_rows<D, KS>(kx + first_new * KS, G - first_new, tid, blockDim.x);
-    for (int idx = first_new * D + tid; idx < G * D; idx += blockDim.x)
-      kx[(idx / D) * KS + idx % D] = round_fp16(kx[(idx / D) * KS + idx % D]);
+    if constexpr (F32K) {
+      if (a.rotate) fwht_rows<D, KS>(kx + first_new * KS, G - first_new, tid, blockDim.x);
+      for (int idx = first_new * D + tid; idx < G * D; idx += blockDim.x)
+        kx[(idx / D) * KS + idx % D] = round_fp16(kx[(idx / D) * KS + idx % D]);
+    }
     __syncthreads();
   }
 
@@ -217,109 +272,132 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   // key token norms: each key row is divided by its norm and rounded to fp16
   // before the key quantizer; the norm is stored as fp16 (0 for a zero row,
   // whose normalized values are 0)
-  if (L.token_norm) {
-    // one wave per row: lane t takes the square sum of elements 2t, 2t + 1
-    // (or, for D = 64, lanes 0..31), then each tree level adds pairs (2t,
-    // 2t + 1) of the level below: a fixed order, so the norm does not depend
-    // on how the work is shared; then a correctly rounded square root
-    const int lane = tid % kLanes, wave = tid / kLanes, nwaves = blockDim.x / kLanes;
-    for (int i = wave; i < G; i += nwaves) {
-      const float* row = kx + i * KS;
-      float t = 0.0f;
-      if (lane < D / 2) t = __fadd_rn(__fmul_rn(row[2 * lane], row[2 * lane]), __fmul_rn(row[2 * lane + 1], row[2 * lane + 1]));
-      for (int w = D / 2; w > 1; w /= 2) {
-        const float a0 = __shfl(t, (2 * lane) % kLanes), a1 = __shfl(t, (2 * lane + 1) % kLanes);
-        t = lane < w / 2 ? __fadd_rn(a0, a1) : 0.0f;
+  if constexpr (F32K) {
+    if (L.token_norm) {
+      // one wave per row: lane t takes the square sum of elements 2t, 2t + 1
+      // (or, for D = 64, lanes 0..31), then each tree level adds pairs (2t,
+      // 2t + 1) of the level below: a fixed order, so the norm does not depend
+      // on how the work is shared; then a correctly rounded square root
+      const int lane = tid % kLanes, wave = tid / kLanes, nwaves = blockDim.x / kLanes;
+      for (int i = wave; i < G; i += nwaves) {
+        const float* row = kx + i * KS;
+        float t = 0.0f;
+        if (lane < D / 2) t = __fadd_rn(__fmul_rn(row[2 * lane], row[2 * lane]), __fmul_rn(row[2 * lane + 1], row[2 * lane + 1]));
+        for (int w = D / 2; w > 1; w /= 2) {
+          const float a0 = __shfl(t, (2 * lane) % kLanes), a1 = __shfl(t, (2 * lane + 1) % kLanes);
+          t = lane < w / 2 ? __fadd_rn(a0, a1) : 0.0f;
+        }
+        if (lane == 0) {
+          const float nrm = sqrtf(t);
+          knrm[i] = nrm;
+          uint16_t* kn = reinterpret_cast<uint16_t*>(page + L.off_knorm + (i / kChunk) * L.kn_chunk_bytes);
+          kn[knorm_elem(i % kChunk)] = fp16_bits(nrm);
+        }
       }
-      if (lane == 0) {
-        const float nrm = sqrtf(t);
-        knrm[i] = nrm;
-        uint16_t* kn = reinterpret_cast<uint16_t*>(page + L.off_knorm + (i / kChunk) * L.kn_chunk_bytes);
-        kn[knorm_elem(i % kChunk)] = fp16_bits(nrm);
+      __syncthreads();
+      for (int idx = tid; idx < G * D; idx += blockDim.x) {
+        const float nrm = knrm[idx / D];
+        const int k = (idx / D) * KS + idx % D;
+        kput(k, nrm == 0.0f ? 0.0f : round_fp16(kget(k) / nrm));
+      }
+      __syncthreads();
+    }
+  }
+
+  // 2. parameters: keys per channel over G tokens, values per token over G
+  // channels; two adjacent lanes per group, each over half of it
+  auto params = [&](auto hyb_c) __attribute__((always_inline)) {
+    constexpr bool HYB = decltype(hyb_c)::value;
+    for (int t = tid; t < 2 * D; t += blockDim.x) {
+      const int c = t >> 1, h = t & 1;
+      const GroupQ q = group_params_pair<G, KB, HYB>([&](int i) { return kget((h * (G / 2) + i) * KS + c); });
+      if (h == 0) {
+        ks[c] = q.s;
+        krs[c] = q.rs;
+        kmn[c] = q.mn;
+        ksym[c] = q.sym;
+        uint16_t* kp = reinterpret_cast<uint16_t*>(page + L.off_kparams);
+        const int pi = kparam_index(L, c);
+        kp[pi] = q.scale16;
+        kp[D + pi] = q.zero16;
+      }
+    }
+    for (int t = tid; t < 2 * G * NCG; t += blockDim.x) {
+      const int task = t >> 1, h = t & 1;
+      const int i = task / NCG, cg = task % NCG;
+      const __half* row = vx + i * VS + cg * G + h * (G / 2);
+      const GroupQ q = group_params_pair<G, VB, HYB>([&](int c) { return __half2float(row[c]); });
+      if (h == 0) {
+        vs[task] = q.s;
+        vrs[task] = q.rs;
+        vmn[task] = q.mn;
+        vsym[task] = q.sym;
+        uint16_t* vp = reinterpret_cast<uint16_t*>(page + L.off_vparams + (i / kChunk) * L.vp_chunk_bytes);
+        vp[vparam_scale_elem(L, i % kChunk, cg)] = q.scale16;
+        vp[vparam_zero_elem(L, i % kChunk, cg)] = q.zero16;
       }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += blockDim.x) {
-      const float nrm = knrm[idx / D];
-      float& xk = kx[(idx / D) * KS + idx % D];
-      xk = nrm == 0.0f ? 0.0f : round_fp16(xk / nrm);
-    }
-    __syncthreads();
-  }
-
-  // 2. parameters: keys per channel over G tokens, values per token over G channels
-  const bool hybrid = a.hybrid != 0;
-  for (int c = tid; c < D; c += blockDim.x) {
-    const GroupQ q = group_params<G, KB>([&](int i) { return kx[i * KS + c]; }, hybrid);
-    ks[c] = q.s;
-    kmn[c] = q.mn;
-    ksym[c] = q.sym;
-    uint16_t* kp = reinterpret_cast<uint16_t*>(page + L.off_kparams);
-    int pi = kparam_index(L, c);
-    kp[pi] = q.scale16;
-    kp[D + pi] = q.zero16;
-  }
-  for (int task = tid; task < G * NCG; task += blockDim.x) {
-    int i = task / NCG, cg = task % NCG;
-    const __half* row = vx + i * VS + cg * G;
-    const GroupQ q = group_params<G, VB>([&](int c) { return __half2float(row[c]); }, hybrid);
-    vs[task] = q.s;
-    vmn[task] = q.mn;
-    vsym[task] = q.sym;
-    uint16_t* vp = reinterpret_cast<uint16_t*>(page + L.off_vparams + (i / kChunk) * L.vp_chunk_bytes);
-    vp[vparam_scale_elem(L, i % kChunk, cg)] = q.scale16;
-    vp[vparam_zero_elem(L, i % kChunk, cg)] = q.zero16;
-  }
-  __syncthreads();
-
+  };
   // 3. key codes: each task assembles one dword of one lane of one chunk
-  {
-    constexpr int KW = 2 * NKB * KB / 4;
-    for (int task = tid; task < CPG * kLanes * KW; task += blockDim.x) {
-      int ch = task / (kLanes * KW);
-      int l = (task / KW) % kLanes;
-      int d = task % KW;
-      int l16 = l & 15, j = l >> 4;
-      uint32_t word = 0;
-      constexpr int SUBS = KB == 4 ? 1 : 2;
-      for (int sub = 0; sub < SUBS; ++sub) {
-        int combo = KB == 4 ? d : 2 * d + sub;
-        int mt = combo / NKB, kb = combo % NKB;
-        int i = ch * kChunk + 16 * mt + l16;  // token within the group
-        for (int e = 0; e < 8; ++e) {
-          int c = 32 * kb + 8 * j + e;
-          uint32_t code = code_of<KB>(kx[i * KS + c], kmn[c], ks[c], ksym[c]);
-          int bit = KB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
-          word |= code << bit;
+  // 4. value codes, likewise
+  auto codes = [&](auto hyb_c) __attribute__((always_inline)) {
+    constexpr bool HYB = decltype(hyb_c)::value;
+    {
+      constexpr int KW = 2 * NKB * KB / 4;
+      for (int task = tid; task < CPG * kLanes * KW; task += blockDim.x) {
+        int ch = task / (kLanes * KW);
+        int l = (task / KW) % kLanes;
+        int d = task % KW;
+        int l16 = l & 15, j = l >> 4;
+        uint32_t word = 0;
+        constexpr int SUBS = KB == 4 ? 1 : 2;
+        for (int sub = 0; sub < SUBS; ++sub) {
+          int combo = KB == 4 ? d : 2 * d + sub;
+          int mt = combo / NKB, kb = combo % NKB;
+          int i = ch * kChunk + 16 * mt + l16;  // token within the group
+          for (int e = 0; e < 8; ++e) {
+            int c = 32 * kb + 8 * j + e;
+            uint32_t code = code_of<KB, HYB>(kget(i * KS + c), kmn[c], ks[c], krs[c], HYB && ksym[c]);
+            int bit = KB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
+            word |= code << bit;
+          }
         }
+        *reinterpret_cast<uint32_t*>(page + L.off_kcodes + ch * L.kc_chunk_bytes + lane_dword_offset(KW, l, d)) = word;
       }
-      *reinterpret_cast<uint32_t*>(page + L.off_kcodes + ch * L.kc_chunk_bytes + lane_dword_offset(KW, l, d)) = word;
     }
-  }
-  // 4. value codes
-  {
-    constexpr int NMT = D / 16;
-    constexpr int VW = NMT * VB / 4;
-    for (int task = tid; task < CPG * kLanes * VW; task += blockDim.x) {
-      int ch = task / (kLanes * VW);
-      int l = (task / VW) % kLanes;
-      int d = task % VW;
-      int l16 = l & 15, j = l >> 4;
-      uint32_t word = 0;
-      constexpr int SUBS = VB == 4 ? 1 : 2;
-      for (int sub = 0; sub < SUBS; ++sub) {
-        int mt = VB == 4 ? d : 2 * d + sub;
-        int c = 16 * mt + l16;
-        int cg = c / G;
-        for (int e = 0; e < 8; ++e) {
-          int i = ch * kChunk + tau(j, e);
-          uint32_t code = code_of<VB>(__half2float(vx[i * VS + c]), vmn[i * NCG + cg], vs[i * NCG + cg], vsym[i * NCG + cg]);
-          int bit = VB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
-          word |= code << bit;
+    {
+      constexpr int NMT = D / 16;
+      constexpr int VW = NMT * VB / 4;
+      for (int task = tid; task < CPG * kLanes * VW; task += blockDim.x) {
+        int ch = task / (kLanes * VW);
+        int l = (task / VW) % kLanes;
+        int d = task % VW;
+        int l16 = l & 15, j = l >> 4;
+        uint32_t word = 0;
+        constexpr int SUBS = VB == 4 ? 1 : 2;
+        for (int sub = 0; sub < SUBS; ++sub) {
+          int mt = VB == 4 ? d : 2 * d + sub;
+          int c = 16 * mt + l16;
+          int cg = c / G;
+          for (int e = 0; e < 8; ++e) {
+            int i = ch * kChunk + tau(j, e);
+            const int pv = i * NCG + cg;
+            uint32_t code = code_of<VB, HYB>(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB && vsym[pv]);
+            int bit = VB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
+            word |= code << bit;
+          }
         }
+        *reinterpret_cast<uint32_t*>(page + L.off_vcodes + ch * L.vc_chunk_bytes + lane_dword_offset(VW, l, d)) = word;
       }
-      *reinterpret_cast<uint32_t*>(page + L.off_vcodes + ch * L.vc_chunk_bytes + lane_dword_offset(VW, l, d)) = word;
     }
+  };
+  if (a.hybrid != 0) {
+    params(std::true_type{});
+    codes(std::true_type{});
+  } else {
+    params(std::false_type{});
+    codes(std::false_type{});
   }
 }
 
@@ -346,7 +424,10 @@ __global__ __launch_bounds__(128) void window_write_kernel(AppendArgs a) {
 template <int D, int KB, int VB, int G>
 hipError_t flush_t(const AppendArgs& a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(a.n_flush), static_cast<unsigned>(a.L.slices));
-  hipLaunchKernelGGL((flush_kernel<D, KB, VB, G>), grid, dim3(256), 0, s, a);
+  if (a.rotate || a.L.token_norm)
+    hipLaunchKernelGGL((flush_kernel<D, KB, VB, G, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((flush_kernel<D, KB, VB, G, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
