@@ -134,19 +134,20 @@ def _split_ranges(n, ng, G, S_req, sink=0):
     return S, ranges
 
 
-@pytest.mark.parametrize("sink,tn", [(0, False), (64, False), (0, True)])
-def test_decode_partials_per_split_match_oracle(sink, tn):
+@pytest.mark.parametrize("base,sink,tn,S_req", [(2, 0, False, 4), (2, 64, False, 4), (2, 0, True, 4),
+                                                (1, 0, False, 8), (1, 0, True, 8), (1, 64, False, 8)])
+def test_decode_partials_per_split_match_oracle(base, sink, tn, S_req):
     """kvq_decode_partials: every split's (m, l, o) against the oracle's partial
     attention over the same tokens; kvq_merge_partials of them equals
-    kvq_decode_attn_splits with the same split count."""
+    kvq_decode_attn_splits with the same split count (64- and 32-token groups,
+    with and without sink chunks and key token norms)."""
     kvq = _lib()
     import oracle
     from _parity import canonical_slice, oracle_queries
 
-    w = WORKLOADS[2].replace(name=f"partials-sink{sink}-tn{int(tn)}", B=2, Hq=8, Hkv=2, N=sink + 64 * 9 + 128 + 21,
-                             sink=sink, token_norm=tn)
+    w = WORKLOADS[base].replace(name=f"partials-g{WORKLOADS[base].G}-sink{sink}-tn{int(tn)}", B=2, Hq=8, Hkv=2,
+                                N=sink + 64 * 9 + 128 + 21, sink=sink, token_norm=tn)
     syn, K, V, q, cache = _run_prefill(w)
-    S_req = 4
     partials, S = cache.decode_partials(q, splits=S_req)
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
     kvq.merge_partials(partials, out, w.B * w.Hq, S, w.D)
