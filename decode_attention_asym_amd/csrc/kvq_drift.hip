@@ -26,10 +26,19 @@ namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// Groups one wave visits (consecutive groups of one slice), two at a time: the
-// per-wave set-up (calibration probabilities, page addressing) is paid once
-// for them, and the next pair's codes load while a pair is reduced.
-constexpr int kGroupsPerWave = 4;
+// Groups one KL pass covers: each bin's total sits in 64 / 2^b lanes after
+// the reduction, so a pass can give every group's key and value bins a lane
+// of their own while the lanes still cover a logarithm each: two groups when
+// a width is 4 bits (16 bins in lanes of 4), four with 2-bit keys and values.
+// A wave visits four consecutive groups of one slice (two passes, or one):
+// the per-wave set-up (calibration probabilities, page addressing) is paid
+// once for them, and with two passes the next pass's codes load while a pass
+// is reduced.  (Eight groups per wave with 2-bit codes measured slower on the
+// smaller caches: fewer waves.)
+template <int KB, int VB>
+constexpr int groups_per_pass() { return KB == 2 && VB == 2 ? 4 : 2; }
+template <int KB, int VB>
+constexpr int groups_per_wave() { return 4; }
 
 // Bits of a where m is set, bits of b elsewhere.
 __device__ __forceinline__ uint32_t pick(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
@@ -173,31 +182,33 @@ __device__ __forceinline__ double strided_sum_f64(double t) {
   return t;
 }
 
-// One wave per kGroupsPerWave consecutive groups of one slice.
+// One wave per groups_per_wave() consecutive groups of one slice.
 template <int D, int KB, int VB, int G, bool HIST>
 __global__ __launch_bounds__(64) void drift_kernel(DriftArgs a) {
   constexpr int NBK = 1 << KB, NBV = 1 << VB;
+  constexpr int NG = groups_per_pass<KB, VB>(), GPW = groups_per_wave<KB, VB>();
   constexpr int KDW = G * D * KB / 8 / 4 / kLanes, VDW = G * D * VB / 8 / 4 / kLanes;  // dwords per lane
   static_assert(G * D * KB / 8 == KDW * 4 * kLanes && G * D * VB / 8 == VDW * 4 * kLanes, "whole dwords per lane");
   const Layout& L = a.L;
   const int l = threadIdx.x;
   const int64_t slice = blockIdx.y;
   const int hkv = static_cast<int>(slice % a.Hkv);
-  const int64_t gb = a.g0 + static_cast<int64_t>(blockIdx.x) * kGroupsPerWave;
-  const int64_t ge = min(gb + kGroupsPerWave, a.g0 + a.ng);
+  const int64_t gb = a.g0 + static_cast<int64_t>(blockIdx.x) * GPW;
+  const int64_t ge = min(gb + GPW, a.g0 + a.ng);
   const uint8_t* page = a.cache + page_offset(L, slice, gb);
   const int bk = bin_of_lane<NBK>(l), bv = bin_of_lane<NBV>(l);
 
-  // KL terms, one fp64 logarithm per lane for two groups at once: the first
-  // group's key bins in lanes 0 mod 4 (or 16), its value bins in lanes 2 mod 4
-  // (or 16), the second group's in lanes 1 and 3 mod 4 (or 16); within those,
-  // the first lane of each bin's lanes.  A bin's term is p ln(p / q), 0 for
-  // p = 0, +inf for p > 0 = q, with p = c / (G D) (exact: G D is a power of
-  // two) and the calibration probability q = count / total formed once per
-  // wave.
+  // KL terms, one fp64 logarithm per lane for the NG groups of a pass: with
+  // RS = min(64 / 2^b_K, 64 / 2^b_V) lanes per bin, group i's key bins sit in
+  // the lanes i mod RS and its value bins in the lanes NG + i mod RS (within
+  // each bin's lanes, one lane).  A bin's term is p ln(p / q), 0 for p = 0,
+  // +inf for p > 0 = q, with p = c / (G D) (exact: G D is a power of two) and
+  // the calibration probability q = count / total formed once per wave.
   static_assert(((G * D) & (G * D - 1)) == 0, "G * D is a power of two");
-  const int r = l & (64 / NBK - 1), rv = l & (64 / NBV - 1);
-  const bool kl0 = r == 0, kl1 = r == 1, vl0 = rv == 2, vl1 = rv == 3;
+  constexpr int RS = (64 / NBK) < (64 / NBV) ? 64 / NBK : 64 / NBV;
+  static_assert(2 * NG <= RS, "a lane per group and bin");
+  const int rk = l & (64 / NBK - 1), rv = l & (64 / NBV - 1);
+  const int kslot = rk < NG ? rk : -1, vslot = rv >= NG && rv < 2 * NG ? rv - NG : -1;
   double q = 0.0;
   if constexpr (!HIST) {
     const uint64_t* qk = a.cal_k + hkv * NBK;
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(64) void drift_kernel(DriftArgs a) {
     for (int i = 0; i < NBK; ++i) sk += qk[i];
 #pragma unroll
     for (int i = 0; i < NBV; ++i) sv += qv[i];
-    const bool kk = kl0 || kl1;
+    const bool kk = kslot >= 0;
     q = static_cast<double>(kk ? qk[bk] : qv[bv]) / static_cast<double>(kk ? sk : sv);
   }
 
@@ -216,55 +227,61 @@ __global__ __launch_bounds__(64) void drift_kernel(DriftArgs a) {
   for (int i = 0; i < NBK; ++i) hk[i] = 0;
 #pragma unroll
   for (int i = 0; i < NBV; ++i) hv[i] = 0;
-  // two register sets: groups g and g + 1 of a pair; the next pair's codes
-  // load while this pair's counts are reduced and turned into KL terms
-  uint32_t kw0[KDW], vw0[VDW], kw1[KDW], vw1[VDW];
-  load_block<KDW>(page + L.off_kcodes, l, kw0);
-  load_block<VDW>(page + L.off_vcodes, l, vw0);
-  if (gb + 1 < ge) {
-    load_block<KDW>(page + L.page_bytes + L.off_kcodes, l, kw1);
-    load_block<VDW>(page + L.page_bytes + L.off_vcodes, l, vw1);
+  // one register set per group of a pass; the next pass's codes load while
+  // this pass's counts are reduced and turned into KL terms
+  uint32_t kw[NG][KDW], vw[NG][VDW];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    if (gb + i < ge) {
+      load_block<KDW>(page + i * L.page_bytes + L.off_kcodes, l, kw[i]);
+      load_block<VDW>(page + i * L.page_bytes + L.off_vcodes, l, vw[i]);
+    }
   }
 #pragma unroll 1
-  for (int64_t g = gb; g < ge; g += 2) {
-    const bool two = g + 1 < ge;
-    uint32_t ck0[NBK], cv0[NBV], ck1[NBK], cv1[NBV];
-    count_lane<KB, KDW>(kw0, ck0);
-    count_lane<VB, VDW>(vw0, cv0);
-    if (two) {
-      count_lane<KB, KDW>(kw1, ck1);
-      count_lane<VB, VDW>(vw1, cv1);
-    } else {
+  for (int64_t g = gb; g < ge; g += NG) {
+    uint32_t ck[NG][NBK], cv[NG][NBV];
 #pragma unroll
-      for (int i = 0; i < NBK; ++i) ck1[i] = 0;
+    for (int i = 0; i < NG; ++i) {
+      if (g + i < ge) {
+        count_lane<KB, KDW>(kw[i], ck[i]);
+        count_lane<VB, VDW>(vw[i], cv[i]);
+      } else {
 #pragma unroll
-      for (int i = 0; i < NBV; ++i) cv1[i] = 0;
+        for (int k = 0; k < NBK; ++k) ck[i][k] = 0;
+#pragma unroll
+        for (int k = 0; k < NBV; ++k) cv[i][k] = 0;
+      }
     }
-    const uint8_t* pn = page + (g + 2 - gb) * L.page_bytes;
-    if (g + 2 < ge) {
-      load_block<KDW>(pn + L.off_kcodes, l, kw0);
-      load_block<VDW>(pn + L.off_vcodes, l, vw0);
-    }
-    if (g + 3 < ge) {
-      load_block<KDW>(pn + L.page_bytes + L.off_kcodes, l, kw1);
-      load_block<VDW>(pn + L.page_bytes + L.off_vcodes, l, vw1);
+    const uint8_t* pn = page + (g + NG - gb) * L.page_bytes;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      if (g + NG + i < ge) {
+        load_block<KDW>(pn + i * L.page_bytes + L.off_kcodes, l, kw[i]);
+        load_block<VDW>(pn + i * L.page_bytes + L.off_vcodes, l, vw[i]);
+      }
     }
     if constexpr (HIST) {
 #pragma unroll
-      for (int i = 0; i < NBK; ++i) hk[i] += ck0[i] + ck1[i];
+      for (int i = 0; i < NG; ++i) {
 #pragma unroll
-      for (int i = 0; i < NBV; ++i) hv[i] += cv0[i] + cv1[i];
+        for (int k = 0; k < NBK; ++k) hk[k] += ck[i][k];
+#pragma unroll
+        for (int k = 0; k < NBV; ++k) hv[k] += cv[i][k];
+      }
     } else {
-      const uint32_t tk0 = wave_bins<NBK>(ck0, l), tv0 = wave_bins<NBV>(cv0, l);
-      const uint32_t tk1 = wave_bins<NBK>(ck1, l), tv1 = wave_bins<NBV>(cv1, l);
-      const uint32_t c = kl0 ? tk0 : kl1 ? tk1 : vl0 ? tv0 : vl1 ? tv1 : 0u;
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const uint32_t tk = wave_bins<NBK>(ck[i], l), tv = wave_bins<NBV>(cv[i], l);
+        c = kslot == i ? tk : vslot == i ? tv : c;
+      }
       const double p = static_cast<double>(c) * (1.0 / static_cast<double>(G * D));
       const double term = c == 0 ? 0.0 : (q == 0.0 ? __builtin_inf() : p * log(p / q));
-      // lane j < 4 ends with the sum of the terms in lanes j mod 4: the first
-      // group's key and value KL in lanes 0 and 2, the second's in 1 and 3
-      const double t = strided_sum_f64<4>(term);
-      const double tv = __shfl(t, (l + 2) & (kLanes - 1));
-      if (l < 2 && (l == 0 || two)) {
+      // lane j < 2 NG ends with the sum of the terms in lanes j mod RS: group
+      // j's key KL for j < NG, group j - NG's value KL after that
+      const double t = strided_sum_f64<RS>(term);
+      const double tv = __shfl(t, (l + NG) & (kLanes - 1));
+      if (l < NG && g + l < ge) {
         const int64_t o = slice * a.ng + (g + l - a.g0);
         a.kl_k[o] = t;
         a.kl_v[o] = tv;
@@ -286,7 +303,8 @@ __global__ void fill_u64_kernel(uint64_t* p, int64_t n) {
 
 template <int D, int KB, int VB, int G>
 hipError_t drift_t(const DriftArgs& a, bool hist, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>((a.ng + kGroupsPerWave - 1) / kGroupsPerWave), static_cast<unsigned>(a.L.slices));
+  constexpr int GPW = groups_per_wave<KB, VB>();
+  dim3 grid(static_cast<unsigned>((a.ng + GPW - 1) / GPW), static_cast<unsigned>(a.L.slices));
   if (hist)
     hipLaunchKernelGGL((drift_kernel<D, KB, VB, G, true>), grid, dim3(kLanes), 0, s, a);
   else
