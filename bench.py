@@ -89,8 +89,10 @@ def cpu_baseline(w, K_host, V_host, q_host, batches, threads: int) -> dict:
                                    w.dtype, w.D, w.kbits, w.vbits, w.G, w.R, w.rotate, sink=w.sink, hybrid=w.hybrid,
                                    token_norm=w.token_norm, group_bits=gb)
 
+    t_enc = time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
         encs = list(ex.map(enc, pairs))
+    t_enc = time.perf_counter() - t_enc
     jobs = []
     for (b, h), e in zip(pairs, encs):
         q = oracle.input_to_f64(to_oracle_input(q_host[b], w.dtype), w.dtype).reshape(w.Hq, w.D)
@@ -103,14 +105,26 @@ def cpu_baseline(w, K_host, V_host, q_host, batches, threads: int) -> dict:
     oracle.attend_slices_parallel(jobs, threads)
     dt = time.perf_counter() - t0
     full = dt * (w.B * w.Hkv) / len(pairs)
+    # the same on one thread, over a few slices
+    n1 = min(8, len(jobs))
+    t1 = time.perf_counter()
+    oracle.attend_slices_parallel(jobs[:n1], 1)
+    dt1 = time.perf_counter() - t1
+    full1 = dt1 * (w.B * w.Hkv) / n1
+    step_bytes = decode_bytes(w, w.N, gb)
     return {
-        "value": round(decode_bytes(w, w.N, gb) / full / 1e9, 3),
+        "value": round(step_bytes / full / 1e9, 3),
         "unit": "GB/s",
         "us_per_step": round(full * 1e6, 1),
         "cores": threads,
         "kind": "oracle",
         "sample": f"decode step (fp64 dequant + attention) over {len(pairs)} of {w.B * w.Hkv} (batch, kv-head) "
                   f"slices at {w.N} tokens, {dt:.2f} s wall on {threads} threads, scaled by slice count",
+        "one_core": {"value": round(step_bytes / full1 / 1e9, 4), "unit": "GB/s", "us_per_step": round(full1 * 1e6, 1),
+                     "sample": f"the same over {n1} slices on 1 thread ({dt1:.2f} s), scaled by slice count"},
+        "quantize": {"s_per_prefill": round(t_enc * (w.B * w.Hkv) / len(pairs), 2), "cores": threads,
+                     "sample": f"the oracle's encoder (O1-O6) over the {len(pairs)} sampled slices' {w.N} tokens "
+                               f"({t_enc:.2f} s), scaled by slice count"},
     }
 
 
