@@ -803,3 +803,17 @@ def test_drift_check_on_encoded_caches(orc):
     kl_k, kl_v, flags = orc.drift_check(enc["k_codes"], enc["v_codes"], G, D, 4, 2, cal_k, cal_v, 0.1)
     assert (kl_k[:30] < 0.05).all() and (kl_v[:30] < 0.05).all() and (flags[:30] == 0).all()
     assert (kl_k[30:] > 0.1).all() and (kl_v[30:] > 0.1).all() and (flags[30:] == 3).all()
+
+
+def test_input_widening_matches_torch(orc):
+    """input_to_f64 widens stored f32 values and f16 / bf16 bit patterns exactly
+    (checked against torch's own conversions of the same bits)."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(4096) * 30).astype(np.float32)
+    assert np.array_equal(orc.input_to_f64(x, "f32"), x.astype(np.float64))
+    for dt, tdt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        t = torch.from_numpy(x).to(tdt)
+        bits = t.view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(orc.input_to_f64(bits, dt), t.to(torch.float64).numpy()), dt
