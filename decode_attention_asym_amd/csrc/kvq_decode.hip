@@ -384,11 +384,32 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       for (int e = 0; e < 8; ++e)
         qm[kb][e] = hv ? qsh[(hv ? h : 0) * D + 32 * kb + 8 * j + e] * rs : 0.0f;
   } else {
+    // the lane's 8 channels of each kb are contiguous: one 16-byte load for
+    // 2-byte inputs, two for f32 (rows are 16-byte aligned: D is 64 or 128)
     const int64_t base = (static_cast<int64_t>(b) * a.Hq + hq) * D;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int64_t o = base + 32 * kb + 8 * j;
+      float x[8];
+      if (a.in_dtype == 0) {
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(static_cast<const float*>(a.q) + o);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(static_cast<const float*>(a.q) + o + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qm[kb][e] = hv ? load_q(a.q, a.in_dtype, base + 32 * kb + 8 * j + e) * qscale : 0.0f;
+        for (int e = 0; e < 4; ++e) {
+          x[e] = __uint_as_float(x0[e]);
+          x[4 + e] = __uint_as_float(x1[e]);
+        }
+      } else {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t u = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          x[e] = a.in_dtype == 1 ? __half2float(__ushort_as_half(static_cast<uint16_t>(u))) : __uint_as_float(u << 16);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qm[kb][e] = hv ? x[e] * qscale : 0.0f;
+    }
   }
   // Per-split fp16 parts of the query (part 1 = fp16(x - part 0)):
   //   qz: q itself, the B operand of the key zero-point bias and of the window;
