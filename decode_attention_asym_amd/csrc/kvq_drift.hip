@@ -219,7 +219,10 @@ __global__ __launch_bounds__(64) void drift_kernel(DriftArgs a) {
 #pragma unroll
     for (int i = 0; i < NBV; ++i) sv += qv[i];
     const bool kk = kslot >= 0;
-    q = static_cast<double>(kk ? qk[bk] : qv[bv]) / static_cast<double>(kk ? sk : sv);
+    const uint64_t cq = kk ? qk[bk] : qv[bv];
+    // a bin without calibration counts (all of them, for an empty
+    // calibration) has q = 0, so any count there makes the KL +inf
+    q = cq == 0 ? 0.0 : static_cast<double>(cq) / static_cast<double>(kk ? sk : sv);
   }
 
   uint32_t hk[NBK], hv[NBV];  // per-lane totals over the wave's groups (histogram mode)

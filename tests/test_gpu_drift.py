@@ -190,3 +190,23 @@ def test_drift_subranges_equal_full_range(g0, g1):
                                         w.kbits, w.vbits, ref_k[h], ref_v[h], THR)
         np.testing.assert_allclose(part[0][h], rk, rtol=1e-12, atol=1e-15)
         np.testing.assert_allclose(part[1][h], rv, rtol=1e-12, atol=1e-15)
+
+
+def test_drift_check_with_empty_calibration_is_infinite():
+    """A calibration histogram with no counts: every group's KL is +inf and
+    both flags are set (the oracle rejects such a calibration; the closed form
+    is KL = +inf since every group has counts where the calibration has none)."""
+    kvq = _lib()
+    w = DRIFT[0].replace(name="drift-empty-cal", B=1, Hq=4, Hkv=2, N=1500)
+    syn = Synth(w, "cuda")
+    K, V = syn.kv_all()
+    c = kvq.KVQCache(kvq.config_for(w))
+    c.append(K, V)
+    ng = c.num_groups()
+    kh = torch.zeros((w.Hkv, 1 << w.kbits), dtype=torch.int64, device="cuda")
+    vh = torch.zeros((w.Hkv, 1 << w.vbits), dtype=torch.int64, device="cuda")
+    kl_k, kl_v, flags = c.drift_check(kh, vh, 0, ng, THR)
+    torch.cuda.synchronize()
+    assert torch.isinf(kl_k).all() and (kl_k > 0).all()
+    assert torch.isinf(kl_v).all() and (kl_v > 0).all()
+    assert (flags == 3).all()
