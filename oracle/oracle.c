@@ -382,8 +382,11 @@ double orc_kl_divergence(const double* p, const double* q, int nb) {
  * k_codes / v_codes [ng * G][D].  The calibration histograms are counts
  * (cal_k[2^kbits], cal_v[2^vbits]), turned into probabilities by dividing by
  * their totals; a group's probabilities are its counts divided by G * D.
+ * A calibration with no counts at all has no mass in any bin (every q_i = 0,
+ * no division), so by the KL rule above every group's KL against it is +inf
+ * (a group always has G * D > 0 codes) and its flag is set.
  * Writes kl_k[g], kl_v[g] and flags[g] = (kl_k > thr) | (kl_v > thr) << 1.
- * Returns 0, or -1 on bad arguments. */
+ * Returns 0, or -1 on bad arguments (a negative count among them). */
 int orc_drift_check(const uint16_t* k_codes, const uint16_t* v_codes, int64_t ng, int G, int D, int kbits,
                     int vbits, const int64_t* cal_k, const int64_t* cal_v, double thr, double* kl_k,
                     double* kl_v, uint8_t* flags) {
@@ -391,11 +394,16 @@ int orc_drift_check(const uint16_t* k_codes, const uint16_t* v_codes, int64_t ng
   const int nbk = 1 << kbits, nbv = 1 << vbits;
   double qk[256], qv[256], pk[256], pv[256];
   int64_t tk = 0, tv = 0;
-  for (int i = 0; i < nbk; ++i) tk += cal_k[i];
-  for (int i = 0; i < nbv; ++i) tv += cal_v[i];
-  if (tk <= 0 || tv <= 0) return -1;
-  for (int i = 0; i < nbk; ++i) qk[i] = (double)cal_k[i] / (double)tk;
-  for (int i = 0; i < nbv; ++i) qv[i] = (double)cal_v[i] / (double)tv;
+  for (int i = 0; i < nbk; ++i) {
+    if (cal_k[i] < 0) return -1;
+    tk += cal_k[i];
+  }
+  for (int i = 0; i < nbv; ++i) {
+    if (cal_v[i] < 0) return -1;
+    tv += cal_v[i];
+  }
+  for (int i = 0; i < nbk; ++i) qk[i] = tk > 0 ? (double)cal_k[i] / (double)tk : 0.0;
+  for (int i = 0; i < nbv; ++i) qv[i] = tv > 0 ? (double)cal_v[i] / (double)tv : 0.0;
   const int64_t per = (int64_t)G * D;
   for (int64_t g = 0; g < ng; ++g) {
     int64_t hk[256] = {0}, hv[256] = {0};

@@ -192,21 +192,29 @@ def test_drift_subranges_equal_full_range(g0, g1):
         np.testing.assert_allclose(part[1][h], rv, rtol=1e-12, atol=1e-15)
 
 
-def test_drift_check_with_empty_calibration_is_infinite():
-    """A calibration histogram with no counts: every group's KL is +inf and
-    both flags are set (the oracle rejects such a calibration; the closed form
-    is KL = +inf since every group has counts where the calibration has none)."""
+def test_drift_check_with_empty_calibration_matches_oracle():
+    """A calibration histogram with no counts (on both sides, then on the key
+    side only): KL and flags equal the oracle's -- +inf against an empty
+    calibration, with the flag set -- and the non-empty side its KL."""
     kvq = _lib()
+    import oracle
+
     w = DRIFT[0].replace(name="drift-empty-cal", B=1, Hq=4, Hkv=2, N=1500)
     syn = Synth(w, "cuda")
     K, V = syn.kv_all()
     c = kvq.KVQCache(kvq.config_for(w))
     c.append(K, V)
     ng = c.num_groups()
+    encs = oracle_encode_slices(w, K, V, [(0, h) for h in range(w.Hkv)])
+    _, vh_full = c.code_histograms(0, ng)
     kh = torch.zeros((w.Hkv, 1 << w.kbits), dtype=torch.int64, device="cuda")
-    vh = torch.zeros((w.Hkv, 1 << w.vbits), dtype=torch.int64, device="cuda")
-    kl_k, kl_v, flags = c.drift_check(kh, vh, 0, ng, THR)
-    torch.cuda.synchronize()
-    assert torch.isinf(kl_k).all() and (kl_k > 0).all()
-    assert torch.isinf(kl_v).all() and (kl_v > 0).all()
-    assert (flags == 3).all()
+    for vh in (torch.zeros((w.Hkv, 1 << w.vbits), dtype=torch.int64, device="cuda"), vh_full):
+        kl_k, kl_v, flags = (x.cpu().numpy() for x in c.drift_check(kh, vh, 0, ng, THR))
+        vh_host = vh.cpu().numpy()
+        for (b, h), e in encs.items():
+            rk, rv, rf = oracle.drift_check(e["k_codes"], e["v_codes"], w.G, w.D, w.kbits, w.vbits,
+                                            np.zeros(1 << w.kbits, np.int64), vh_host[h], THR)
+            assert np.isposinf(rk).all()
+            assert np.array_equal(kl_k[h], rk)
+            np.testing.assert_allclose(kl_v[h], rv, rtol=1e-12, atol=1e-15)
+            assert np.array_equal(flags[h], rf)

@@ -781,6 +781,38 @@ def test_drift_check_flags_closed_forms(orc):
     assert (f[2] & 1) == 0
 
 
+def test_drift_check_empty_calibration_closed_form(orc):
+    """A calibration without counts has no mass in any bin, so every group
+    (which always has G * D codes) has KL = +inf against it and its flag set;
+    an empty key calibration leaves the value side as it is, and the reverse.
+    A negative count is rejected."""
+    G, D = 32, 64
+    per = G * D
+    kc = np.zeros((2, per), np.uint16)
+    vc = np.zeros((2, per), np.uint16)
+    kc[0] = np.arange(per) % 16
+    vc[0] = np.arange(per) % 4
+    kc[1] = 5
+    vc[1] = 2
+    zk, zv = np.zeros(16, np.int64), np.zeros(4, np.int64)
+    uk, uv = np.full(16, 10, np.int64), np.full(4, 10, np.int64)
+    kl_k, kl_v, flags = orc.drift_check(kc.reshape(-1, D), vc.reshape(-1, D), G, D, 4, 2, zk, zv, 0.1)
+    assert np.isposinf(kl_k).all() and np.isposinf(kl_v).all()
+    assert (flags == 3).all()
+    # empty keys only: key KL +inf, value KL = closed form against the uniform value calibration
+    kl_k, kl_v, flags = orc.drift_check(kc.reshape(-1, D), vc.reshape(-1, D), G, D, 4, 2, zk, uv, 0.1)
+    assert np.isposinf(kl_k).all()
+    assert kl_v[0] == 0.0 and kl_v[1] == pytest.approx(np.log(4), rel=1e-14)
+    assert list(flags) == [1, 3]
+    # empty values only
+    kl_k, kl_v, flags = orc.drift_check(kc.reshape(-1, D), vc.reshape(-1, D), G, D, 4, 2, uk, zv, 0.1)
+    assert np.isposinf(kl_v).all()
+    assert kl_k[0] == 0.0 and kl_k[1] == pytest.approx(np.log(16), rel=1e-14)
+    assert list(flags) == [2, 3]
+    with pytest.raises(ValueError):
+        orc.drift_check(kc.reshape(-1, D), vc.reshape(-1, D), G, D, 4, 2, np.array([-1] + [1] * 15), uv, 0.1)
+
+
 def test_drift_check_on_encoded_caches(orc):
     """Stationary Gaussian tokens stay far below the 0.1 threshold against a
     calibration taken from the first groups; tokens whose values turn heavy
