@@ -156,7 +156,41 @@ def _stream(stream) -> int:
     return int(stream)
 
 
+_TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+def _require(t, name: str, device, dtype, shape=None, min_numel: int | None = None):
+    """Raise ValueError unless t is a contiguous torch tensor on `device` with
+    `dtype` and exactly `shape` (or at least `min_numel` elements).  The C ABI
+    takes bare pointers, so a tensor on another device, of another dtype, a
+    strided view or a short buffer would be read or written out of bounds."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, the cache is on {device}")
+    want = dtype if isinstance(dtype, torch.dtype) else getattr(torch, dtype)
+    if t.dtype != want:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {want}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous (strides {tuple(t.stride())} for shape {tuple(t.shape)})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {min_numel} needed")
+
+
 def merge_partials(partials, out, rows: int, splits: int, head_dim: int, stream=None):
+    """out [rows, head_dim] float32 from split partials [rows, splits, head_dim + 4]
+    float32 (both contiguous, on one device)."""
+    if rows < 1 or splits < 1:
+        raise ValueError("rows and splits must be positive")
+    dev = getattr(partials, "device", None)
+    if dev is None or dev.type != "cuda":
+        raise ValueError(f"partials: expected a GPU tensor, got {dev}")
+    _require(partials, "partials", dev, "float32", min_numel=rows * splits * (head_dim + 4))
+    _require(out, "out", partials.device, "float32", min_numel=rows * head_dim)
     check(lib.kvq_merge_partials(_ptr(partials), _ptr(out), rows, splits, head_dim, _stream(stream)),
           "kvq_merge_partials")
     return out
@@ -173,6 +207,8 @@ class KVQCache:
         import torch
 
         self.cfg = cfg
+        if torch.device(device).type != "cuda":
+            raise ValueError(f"the cache lives in GPU memory; device {device!r} is not a GPU")
         nbytes = cache_bytes(cfg)
         if nbytes == 0:
             raise KVQError(KVQ_E_UNSUPPORTED if lib.kvq_last_error() else KVQ_E_ARG, "kvq_cache_bytes")
@@ -182,6 +218,33 @@ class KVQCache:
         c = cfg.c()
         check(lib.kvq_create(ctypes.byref(c), self.buf.data_ptr(), nbytes, ctypes.byref(h)), "kvq_create")
         self.h = h
+        self.device = self.buf.device
+
+    # ---- argument checks (before any call into the library)
+    def _in(self, t, name, shape):
+        _require(t, name, self.device, _TORCH_DTYPES[self.cfg.in_dtype], shape)
+
+    def _out(self, out, q):
+        import torch
+
+        c = self.cfg
+        if out is None:
+            return torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.float32, device=self.device)
+        _require(out, "out", self.device, "float32", (c.batch, c.num_q_heads, c.head_dim))
+        return out
+
+    def _q(self, q):
+        c = self.cfg
+        self._in(q, "q", (c.batch, c.num_q_heads, c.head_dim))
+
+    def _kv(self, k, v, T=None):
+        c = self.cfg
+        if T is None:
+            T = k.shape[2] if hasattr(k, "shape") and len(k.shape) == 4 else -1
+        shape = (c.batch, c.num_kv_heads, T, c.head_dim)
+        self._in(k, "k", shape)
+        self._in(v, "v", shape)
+        return T
 
     def __del__(self):
         h = getattr(self, "h", None)
@@ -201,15 +264,13 @@ class KVQCache:
         return int(lib.kvq_default_splits(self.h))
 
     def append(self, k, v, stream=None) -> None:
-        T = k.shape[2]
+        """k, v: [B, H_kv, T, D] contiguous, the config dtype, on the cache's device."""
+        T = self._kv(k, v)
         check(lib.kvq_append(self.h, _ptr(k), _ptr(v), T, _stream(stream)), "kvq_append")
 
     def decode(self, q, out=None, splits: int | None = None, stream=None):
-        import torch
-
-        if out is None:
-            out = torch.empty((self.cfg.batch, self.cfg.num_q_heads, self.cfg.head_dim), dtype=torch.float32,
-                              device=q.device)
+        self._q(q)
+        out = self._out(out, q)
         if splits is None:
             st = lib.kvq_decode_attn(self.h, _ptr(q), _ptr(out), _ptr(self.ws), self.ws.numel(), _stream(stream))
         else:
@@ -221,11 +282,9 @@ class KVQCache:
     def append_decode(self, k, v, q, out=None, stream=None):
         """One step: append one token (k, v [B, H_kv, 1, D]) and decode q,
         every argument checked before anything is enqueued."""
-        import torch
-
-        if out is None:
-            out = torch.empty((self.cfg.batch, self.cfg.num_q_heads, self.cfg.head_dim), dtype=torch.float32,
-                              device=q.device)
+        self._kv(k, v, 1)
+        self._q(q)
+        out = self._out(out, q)
         check(lib.kvq_append_decode_attn(self.h, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(self.ws), self.ws.numel(),
                                          _stream(stream)), "kvq_append_decode_attn")
         return out
@@ -235,8 +294,12 @@ class KVQCache:
         import torch
 
         rows, W = self.cfg.batch * self.cfg.num_q_heads, self.cfg.head_dim + 4
+        self._kv(k, v, 1)
+        self._q(q)
         if partials is None:
-            partials = torch.empty(self.ws.numel() // 4, dtype=torch.float32, device=q.device)
+            partials = torch.empty(self.ws.numel() // 4, dtype=torch.float32, device=self.device)
+        else:
+            _require(partials, "partials", self.device, "float32")
         S_req = splits if splits is not None else int(lib.kvq_default_splits(self.h))
         used = ctypes.c_int32(0)
         check(lib.kvq_append_decode_partials(self.h, _ptr(k), _ptr(v), _ptr(q), _ptr(partials), partials.numel() * 4,
@@ -248,13 +311,16 @@ class KVQCache:
         """Split partials [B*H_q, S, D+4] (o unnormalized, m, l in base 2); returns (partials, S)."""
         import torch
 
+        self._q(q)
         S_req = self.default_splits() if splits is None else splits
         rows, W = self.cfg.batch * self.cfg.num_q_heads, self.cfg.head_dim + 4
-        if partials is None:
+        if partials is not None:
+            _require(partials, "partials", self.device, "float32")
+        else:
             # a position-adaptive cache may use a few more splits than asked
             # (one per run of equal bit widths at least)
             cap = max(S_req, self.ws.numel() // (rows * W * 4))
-            partials = torch.empty((rows, cap, W), dtype=torch.float32, device=q.device)
+            partials = torch.empty((rows, cap, W), dtype=torch.float32, device=self.device)
         used = ctypes.c_int32(0)
         check(lib.kvq_decode_partials(self.h, _ptr(q), _ptr(partials), partials.numel() * 4, S_req,
                                       ctypes.byref(used), _stream(stream)), "kvq_decode_partials")
@@ -273,7 +339,7 @@ class KVQCache:
 
         c = self.cfg
         g1 = self.num_groups() if g1 is None else g1
-        dev = self.buf.device
+        dev = self.device
         kh = torch.empty((c.num_kv_heads, 1 << c.k_bits), dtype=torch.int64, device=dev)
         vh = torch.empty((c.num_kv_heads, 1 << c.v_bits), dtype=torch.int64, device=dev)
         check(lib.kvq_code_histograms(self.h, g0, g1, _ptr(kh), _ptr(vh), _stream(stream)), "kvq_code_histograms")
@@ -286,7 +352,11 @@ class KVQCache:
 
         c = self.cfg
         g1 = self.num_groups() if g1 is None else g1
-        dev = self.buf.device
+        dev = self.device
+        _require(cal_k, "cal_k", dev, "int64", (c.num_kv_heads, 1 << c.k_bits))
+        _require(cal_v, "cal_v", dev, "int64", (c.num_kv_heads, 1 << c.v_bits))
+        if g1 < g0:
+            raise ValueError(f"group range [{g0}, {g1}) is empty or reversed")
         shape = (c.batch * c.num_kv_heads, g1 - g0)
         kl_k = torch.empty(shape, dtype=torch.float64, device=dev)
         kl_v = torch.empty(shape, dtype=torch.float64, device=dev)
@@ -298,6 +368,12 @@ class KVQCache:
     def requantize(self, k, v, g0: int, g1: int, flags=None, stream=None) -> None:
         """Quantize groups [g0, g1) again from k, v [B, H_kv, (g1 - g0) * G, D]
         where flags (uint8 [B * H_kv, g1 - g0]) is nonzero (all if None)."""
+        c = self.cfg
+        if g1 < g0:
+            raise ValueError(f"group range [{g0}, {g1}) is reversed")
+        self._kv(k, v, (g1 - g0) * c.group_size)
+        if flags is not None:
+            _require(flags, "flags", self.device, "uint8", (c.batch * c.num_kv_heads, g1 - g0))
         check(lib.kvq_requantize(self.h, g0, g1, _ptr(k), _ptr(v), _ptr(flags), _stream(stream)), "kvq_requantize")
 
     def group_bits(self):
