@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -24,13 +25,47 @@ COMMON = [
 SOURCES = {
     "kvq_append.hip": ["-ffp-contract=off"],
     # MFMA accumulators in ArchVGPRs: the softmax rescale multiplies them with
-    # VALU, which otherwise costs AGPR<->VGPR copies every chunk
-    "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    # VALU, which otherwise costs AGPR<->VGPR copies every chunk; the resource
+    # remarks feed check_no_scratch
+    "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-Rpass-analysis=kernel-resource-usage"],
     "kvq_merge.hip": [],
     # KL terms are products and sums rounded one by one, as in the oracle
     "kvq_drift.hip": ["-ffp-contract=off"],
     "kvq_api.cpp": ["-ffp-contract=off"],
 }
+
+
+def resource_usage(remarks: str) -> dict:
+    """{kernel symbol: {field: value}} from hipcc's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+(.+?): (\S+) \[-Rpass-analysis=kernel-resource-usage\]", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = m.group(2)
+    return out
+
+
+def check_no_scratch(usage: dict) -> None:
+    """The decode kernels wait for their LDS copies with static vmcnt counts
+    that assume every vector-memory instruction in the chunk loop is one of
+    those copies; a register spill (scratch loads and stores) would break the
+    count and give wrong results without a fault.  Refuse such a build."""
+    bad = []
+    kernels = [k for k in usage if "decode_kernel" in k or "decode_mixed_kernel" in k]
+    if not kernels:
+        raise RuntimeError("no decode kernel resource remarks found (is -Rpass-analysis on?)")
+    for k in kernels:
+        u = usage[k]
+        if u.get("ScratchSize [bytes/lane]") != "0" or u.get("VGPRs Spill") != "0" or u.get("SGPRs Spill") != "0":
+            bad.append(f"{k}: scratch {u.get('ScratchSize [bytes/lane]')} B/lane, VGPR spill {u.get('VGPRs Spill')}, "
+                       f"SGPR spill {u.get('SGPRs Spill')}")
+    if bad:
+        raise RuntimeError("decode kernels must not use scratch (their vmcnt waits count only the LDS copies):\n"
+                           + "\n".join(bad))
 
 
 def _compile(src: str, extra: list[str], verbose: bool) -> str:
@@ -40,9 +75,13 @@ def _compile(src: str, extra: list[str], verbose: bool) -> str:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(x for x in r.stderr.splitlines() if noise not in x and x.strip())
+    lines = [x for x in r.stderr.splitlines() if noise not in x and x.strip()]
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+        raise RuntimeError(f"hipcc failed for {src}:\n" + "\n".join(lines))
+    if any("kernel-resource-usage" in x for x in lines):
+        check_no_scratch(resource_usage(r.stderr))
+        lines = [x for x in lines if "kernel-resource-usage" not in x]
+    err = "\n".join(lines)
     if err and verbose:
         print(err, flush=True)
     return obj

@@ -20,11 +20,12 @@
 //   values, per token t, group j:    sum_t p_t vhat_tc = sum_t (p_t s_tj) code_tc + sum_t p_t z_tj
 // so both products run on raw integer codes: (q_c s_gc) is the B operand of
 // QK^T once per token group, (p_t s_tj) the B operand of PV once per chunk,
-// and the zero-point sums are added as per-head biases.  Codes enter the MFMA
-// as fp16 subnormals 2^-24 * 2^p * code (see kvq_layout.h): the 2^p factors
-// are folded into the B operands and the 2^-24 into the scores and the final
-// output, all exact.  Softmax runs in the log2 domain (exp2), log2(e)/sqrt(D)
-// folded into q.
+// and the zero-point sums are added as per-head biases.  Key codes enter the
+// MFMA as fp16 subnormals 2^-24 * 2^p * code, value codes as the normal fp16
+// values 2^p * code (see kvq_layout.h and the precision note below): the 2^p
+// factors are folded into the B operands and the 2^-24 into the scores, all
+// exact.  Softmax runs in the log2 domain (exp2), log2(e)/sqrt(D) folded
+// into q.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -60,10 +61,20 @@ __device__ __forceinline__ uint32_t sgpr_const(uint32_t x) {
   return r;
 }
 
+// A constant held in a VGPR: lets (w & sgpr_mask) | c be one v_and_or_b32
+// (a VOP3 instruction reads at most one SGPR and no literal here).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t x) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(x));
+  return r;
+}
+
 template <int BITS>
 struct CodeMasks {
   uint32_t m[4];
+  uint32_t e1024;  // fp16 exponent field of 1024 in both halves (normal-range unpack)
   __device__ __forceinline__ CodeMasks() {
+    e1024 = vgpr_const(0x64006400u);
     if (BITS == 4) {
       m[0] = sgpr_const(0x000F000Fu);
       m[1] = sgpr_const(0x00F000F0u);
@@ -79,18 +90,20 @@ struct CodeMasks {
 };
 
 // A b-bit field at bit p of a 16-bit half, with every other bit of the half
-// clear, is the fp16 subnormal 2^(p - 24) * code exactly.
+// clear, is the fp16 subnormal 2^(p - 24) * code exactly.  With the exponent
+// field of 1024 set as well it is the normal value 1024 + 2^p * code, and
+// subtracting 1024 (exact) leaves 2^p * code as a normal fp16 value (or 0).
 //
-// Precision note (measured on gfx950): the matrix cores' fp32 result of a
-// 32-product sum is biased low by a few ulp (about -4e-6 relative) when an
-// input is a small subnormal, and equally so when a large offset is added
-// and cancelled (the 1024 + code encoding); only sums of normal-range inputs
-// are unbiased.  The PV code sum is then amplified by its cancellation
-// against the zero-point sum (|sum p s code| / |output| is 30-70 on long
-// diffuse contexts), which puts the attention output's relative error at
-// 1e-4 .. 1.5e-3 against exact arithmetic.  Normal-range code operands would
-// cost one more VALU operation per operand dword (about a quarter more VALU
-// work per chunk).
+// Precision (measured on gfx950 with chains of 64 MFMAs against exact sums):
+// the matrix cores' fp32 result is biased low by about 4.5 ulp per chain when
+// an A input is an fp16 subnormal, and the bias scales with the size of the
+// terms, not of the sum; with normal-range inputs the error has no measurable
+// bias (+0.02 ulp).  The value codes' product sum cancels against the
+// zero-point sum (|sum p s code| / |output| is 30-70 on long diffuse
+// contexts), so a bias there is amplified into the output: the PV operands
+// are therefore the normal-range form (one packed fp16 subtraction more per
+// operand dword).  The key codes keep the subnormal form: their bias moves a
+// score by ~1e-5 in log2 units, far below the tolerance.
 // 4-bit word -> 8 values 2^-24 * mult(e) * code_e, mult = 1, 1, 16, 16, 1, 1, 16, 16.
 __device__ __forceinline__ half8 unpack4(uint32_t w, const CodeMasks<4>& u) {
   const uint32_t w8 = w >> 8;
@@ -100,6 +113,27 @@ __device__ __forceinline__ half8 unpack4(uint32_t w, const CodeMasks<4>& u) {
 // 2^-24 * 4^(e>>1) * code_e.
 __device__ __forceinline__ half8 unpack2(uint32_t w, const CodeMasks<2>& u) {
   return __builtin_bit_cast(half8, u32x4{w & u.m[0], w & u.m[1], w & u.m[2], w & u.m[3]});
+}
+
+// Normal-range fp16 pair 2^p * code from the fields selected by m: the
+// exponent field of 1024 is set (v_and_or_b32), then 1024 is subtracted from
+// both halves (v_pk_add_f16); both steps are exact.
+__device__ __forceinline__ uint32_t norm_pair(uint32_t w, uint32_t m, uint32_t e1024) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 x = __builtin_bit_cast(h2, (w & m) | e1024);
+  const h2 off = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  return __builtin_bit_cast(uint32_t, x - off);
+}
+// 4-bit word -> 8 values mult(e) * code_e (normal range).
+__device__ __forceinline__ half8 unpack4n(uint32_t w, const CodeMasks<4>& u) {
+  const uint32_t w8 = w >> 8;
+  return __builtin_bit_cast(half8, u32x4{norm_pair(w, u.m[0], u.e1024), norm_pair(w, u.m[1], u.e1024),
+                                         norm_pair(w8, u.m[0], u.e1024), norm_pair(w8, u.m[1], u.e1024)});
+}
+// One 2-bit sub-block -> 8 values 4^(e>>1) * code_e (normal range).
+__device__ __forceinline__ half8 unpack2n(uint32_t w, const CodeMasks<2>& u) {
+  return __builtin_bit_cast(half8, u32x4{norm_pair(w, u.m[0], u.e1024), norm_pair(w, u.m[1], u.e1024),
+                                         norm_pair(w, u.m[2], u.e1024), norm_pair(w, u.m[3], u.e1024)});
 }
 
 template <int BITS>
@@ -115,6 +149,16 @@ __device__ __forceinline__ half8 a_operand(const uint32_t* words, int idx, const
   } else {
     const uint32_t w = words[idx >> 1];
     return unpack2((idx & 1) ? (w >> 8) : w, u);
+  }
+}
+// The same operand in the normal-range form (values mult(e) * code_e).
+template <int BITS>
+__device__ __forceinline__ half8 a_operand_n(const uint32_t* words, int idx, const CodeMasks<BITS>& u) {
+  if constexpr (BITS == 4) {
+    return unpack4n(words[idx], u);
+  } else {
+    const uint32_t w = words[idx >> 1];
+    return unpack2n((idx & 1) ? (w >> 8) : w, u);
   }
 }
 
@@ -456,9 +500,9 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   }
 
   // Online-softmax state (per head, uniform over replicas and j).  m is the
-  // running max in log2 units; acc holds the PV sums in units of 2^-24 while
-  // quantized chunks are processed (subnormal code operands), real units
-  // afterwards.  lsum and zacc are this lane's share (its value slots).
+  // running max in log2 units; acc holds the PV sums (the value codes enter
+  // as normal-range values mult * code, the weights as p * s / mult).  lsum
+  // and zacc are this lane's share (its value slots).
   float m = -INFINITY, mslack = -INFINITY, lsum = 0.0f;
   f32x4 acc[NMT];
 #pragma unroll
@@ -710,10 +754,10 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       uint32_t bp[NCG][4];
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) gather_pairs(bpc[cg], bp[cg]);
-      // PV on the subnormal code operands
+      // PV on the normal-range code operands
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
-        const half8 av = a_operand<VB>(vw, mt, uv);
+        const half8 av = a_operand_n<VB>(vw, mt, uv);
         const uint32_t* bw = bp[(16 * mt) / G];
         const half8 bb = __builtin_bit_cast(half8, u32x4{bw[0], bw[1], bw[2], bw[3]});
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bb, acc[mt], 0, 0, 0);
@@ -747,10 +791,6 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
     }
     wait_vmcnt<0>();  // no copy into LDS outlives the loop
   }
-  // quantized-chunk sums to real units
-#pragma unroll
-  for (int i = 0; i < NMT; ++i) acc[i] *= kTwo24;
-
   // ---- fp16 chunks (the attention-sink chunks, then the recent window's),
   // spread over the splits (split s takes chunks S - 1 - s, 2S - 1 - s, ...)
   // so that no wave adds more than its share of these latency-bound reads to

@@ -24,11 +24,12 @@
 //             = 16 + 4j + e - 4  for e >= 4
 //
 // Code unpack: a 32-bit word w holds fields for two fp16 lanes of a half8
-// (low half -> even e, high half -> odd e).  (w & mask) | 0x64006400 turns a
-// b-bit field at bit position p of each half into the fp16 value
-// 1024 + 2^p * code, exactly; a shift by 8 brings the upper byte of each half
-// down.  The 2^p factors are folded into the other operand (powers of two,
-// exact) and the 1024 offsets are removed by a per-group correction.
+// (low half -> even e, high half -> odd e).  w & mask turns a b-bit field at
+// bit position p of each half into the fp16 subnormal 2^(p - 24) * code
+// (key operands); (w & mask) | 0x64006400 is the fp16 value 1024 + 2^p * code,
+// and subtracting 1024 leaves the normal value 2^p * code (value operands),
+// both exactly; a shift by 8 brings the upper byte of each half down.  The
+// 2^p factors are folded into the other operand (powers of two, exact).
 //
 //   4-bit word, operand pair i = e >> 1: field at 4 * (i & 1) after shifting
 //     by 8 * (i >> 1); multiplier 16^(i & 1).  Bit of element e:

@@ -149,7 +149,12 @@ def test_requantize_partial_range_and_adaptive_cache():
     pairs = [(0, h) for h in range(w.Hkv)]
     assert oracle_group_bits(w, [w.N]) is not None
     assert_export_matches(w, c.export(), 0, oracle_encode_slices(w, K2, V2, pairs, calls=[w.N]))
+    # a range past the quantized groups is refused by the library (tensors of
+    # the range's size), a tensor not of the range's size by the binding
+    Kx = torch.zeros((w.B, w.Hkv, (ng + 1 - g0) * G, w.D), dtype=K.dtype, device="cuda")
     with pytest.raises(kvq.KVQError):
+        c.requantize(Kx, Kx, g0, ng + 1)
+    with pytest.raises(ValueError):
         c.requantize(Kn, Vn, g0, ng + 1)
     with pytest.raises(kvq.KVQError):
         c.code_histograms(0, 4)  # no drift detection on adaptive caches
