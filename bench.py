@@ -179,13 +179,53 @@ def copy_calibration(gib: float) -> int:
     return 0
 
 
+def cpu_info() -> dict:
+    """The CPU model and the cores this process may use: its affinity set,
+    bounded by a cgroup CPU quota if one is set."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+            if q != "max":
+                quota = max(1, int(int(q) / int(per)))
+    except (OSError, ValueError):
+        pass
+    return {"model": model, "affinity": usable, "cgroup_quota": quota,
+            "usable": min(usable, quota) if quota else usable}
+
+
+def percentiles(xs) -> dict:
+    import numpy as np
+
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 2), "median": round(float(np.median(a)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "mean": round(float(a.mean()), 2), "n": int(a.size)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64, help="timed steps (64 spans one group flush at G=64)")
-    ap.add_argument("--warmup", type=int, default=96,
-                    help="untimed steps first: after the prefill the step time settles over the first ~64 steps "
-                         "(measured 1012, 400, 373, 341, 335 .. 322 us per 8-step block on the 32k layer)")
+    ap.add_argument("--warmup", type=int, default=96, help="untimed steps before the timed ones")
+    ap.add_argument("--prefill-reps", type=int, default=8,
+                    help="timed prefills (reset + append of the whole context) right before the warmup steps; "
+                         "prefill_ms is their median.  They also keep the GPU busy up to the first step: after "
+                         "an idle stretch the step time takes ~60 steps to settle")
+    ap.add_argument("--dist-steps", type=int, default=64,
+                    help="steps after the timed ones, each between two events, for the step-time percentiles")
+    ap.add_argument("--evict-mall", type=float, default=0.0, metavar="GIB",
+                    help="write GIB GiB of scratch between the percentile steps (outside their events), so "
+                         "caches that fit the 256 MB MALL are read from HBM every step")
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS (default: the 32k K4/V2 layer)")
     ap.add_argument("--splits", type=int, default=0, help="split count (0: the library's default)")
     ap.add_argument("--sink", type=int, default=0, help="attention-sink tokens kept in fp16 (a multiple of the group size)")
@@ -233,45 +273,48 @@ def main() -> int:
                       + ("-tokennorm" if args.token_norm else "") + adapt,
                       sink=args.sink, hybrid=args.hybrid, token_norm=args.token_norm, adapt_delta=args.adapt_delta,
                       bits_low=lo if args.adapt_delta else (0, 0), bits_high=hi if args.adapt_delta else (0, 0))
-    total = args.warmup + args.steps + 2 * args.kernel_steps
+    total = args.warmup + args.steps + 2 * args.kernel_steps + args.dist_steps
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     syn = Synth(w, dev, positions=w.N + total + 1)
     cache = kvq.KVQCache(kvq.config_for(w, max_tokens=w.N + total), device=dev)
 
+    # every input and buffer exists before the prefill, so nothing but the
+    # prefills runs between the first prefill and the first step
     print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
     K, V = syn.kv_all()
     batches = list(range(min(args.cpu_sample_batches, w.B)))
     K_host = [K[b].cpu() for b in batches] if not args.no_cpu_baseline else None
     V_host = [V[b].cpu() for b in batches] if not args.no_cpu_baseline else None
-    torch.cuda.synchronize()
-    # the prefill, timed twice: the first call on a fresh cache buffer is
-    # slower (first touch of its pages), the second, after a reset, is the
-    # kernel's own rate; both write the same cache
-    prefill = []
-    for rep in range(2):
-        if rep:
-            cache.reset()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        cache.append(K, V)
-        e1.record()
-        torch.cuda.synchronize()
-        prefill.append(e0.elapsed_time(e1))
-    prefill_first_ms, prefill_ms = prefill
-    del K, V
-    torch.cuda.empty_cache()
-    print(f"[bench] prefill {w.N} tokens: {prefill_ms:.2f} ms (first call {prefill_first_ms:.2f} ms)", file=sys.stderr,
-          flush=True)
-
     step_kv = [syn.step_kv(i) for i in range(total)]
     qs = [syn.q(i) for i in range(total)]
     rows = w.B * w.Hq
-    S = args.splits or cache.default_splits()
+    cfg_full = kvq.config_for(w, max_tokens=w.N + total)
     # a position-adaptive cache may use a few more splits than asked (at least one per run of equal bits)
-    cap = max(S, kvq.workspace_bytes(kvq.config_for(w, max_tokens=w.N + total)) // (rows * (w.D + 4) * 4))
+    cap = max(args.splits, kvq.workspace_bytes(cfg_full) // (rows * (w.D + 4) * 4))
     partials = torch.empty(rows * cap * (w.D + 4), dtype=torch.float32, device=dev)
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    scratch = torch.empty(int(args.evict_mall * (1 << 30)) // 4, dtype=torch.float32, device=dev) \
+        if args.evict_mall > 0 else None
+    torch.cuda.synchronize()
+
+    # the prefill: the first call on the fresh cache buffer (first touch of its
+    # pages), then prefill_reps calls after a reset, each between two events;
+    # the last one leaves the cache prefilled for the steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cache.append(K, V)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_first_ms = e0.elapsed_time(e1)
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(1, args.prefill_reps))]
+    for a, b in pev:
+        cache.reset()
+        a.record()
+        cache.append(K, V)
+        b.record()
+    S = args.splits or cache.default_splits()  # host-side: the token count is known without the device
 
     def step(i):
         k, v = step_kv[i]
@@ -308,6 +351,29 @@ def main() -> int:
         merge_partials(partials, out, rows, used, w.D)  # the last decode's partials
     ev[4].record()
     torch.cuda.synchronize()
+    # per-step percentiles: each step between two events of its own (an event
+    # between kernels costs the next kernel a little, so these run slightly
+    # above the back-to-back steps), optionally with a MALL-evicting write
+    # between steps, outside the events
+    base = args.warmup + args.steps + 2 * nk
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.dist_steps)]
+    for i, (a, b) in enumerate(sev):
+        if scratch is not None:
+            scratch.fill_(float(i))
+        a.record()
+        step(base + i)
+        b.record()
+    torch.cuda.synchronize()
+    dist = percentiles([a.elapsed_time(b) * 1e3 for a, b in sev]) if sev else None
+    if dist is not None:
+        dist["evict_mall_gib"] = args.evict_mall
+    prefill_list = sorted(a.elapsed_time(b) for a, b in pev)
+    prefill_ms = prefill_list[len(prefill_list) // 2]
+    print(f"[bench] prefill {w.N} tokens: {prefill_ms:.2f} ms median of {len(pev)} (first call "
+          f"{prefill_first_ms:.2f} ms)", file=sys.stderr, flush=True)
+    del K, V
+
     ms_total = ev[0].elapsed_time(ev[1])
     ms_step = ms_total / args.steps
     gbits = cache.group_bits() if w.adapt_delta else None  # a group's bits never change once quantized
@@ -345,10 +411,15 @@ def main() -> int:
     if not args.no_cpu_baseline:
         from synth import to_oracle_input  # noqa: F401
 
-        threads = min(16, len(os.sched_getaffinity(0)))
-        print(f"[bench] cpu baseline on {threads} threads", file=sys.stderr, flush=True)
+        ci = cpu_info()
+        # every usable core, up to the 16-core CPU share a GPU gets on the
+        # measurement hosts (they show more cores than one GPU's share)
+        threads = min(16, ci["usable"])
+        print(f"[bench] cpu baseline on {threads} threads ({ci['model']})", file=sys.stderr, flush=True)
         q0 = syn.q(0).cpu()
         cpu = cpu_baseline(w, K_host, V_host, q0, batches, threads)
+        cpu["cpu_model"] = ci["model"]
+        cpu["host_cpus"] = {"affinity": ci["affinity"], "cgroup_quota": ci["cgroup_quota"]}
 
     res = {
         "metric": METRIC,
@@ -385,7 +456,9 @@ def main() -> int:
             "timing": "per launch: (span of nk steps) - (span of nk steps without the decode), after the timed steps",
             "bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes)),
         },
+        "step_us_percentiles": dist,
         "prefill_ms": round(prefill_ms, 2),
+        "prefill_reps": len(pev),
         "prefill_first_ms": round(prefill_first_ms, 2),
         **({"drift_check": drift} if drift else {}),
         "cpu_baseline": cpu,
