@@ -10,11 +10,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <new>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/kvq.h"
@@ -667,6 +669,38 @@ kvq_status kvq_requantize(kvq_cache* h, int64_t g0, int64_t g1, const void* k, c
 
 // ---------------------------------------------------------------- export / import
 
+}  // extern "C"
+
+namespace {
+// Runs fn(bi, hk, pages, ring, sink) for every (batch row bi < bc, kv head hk)
+// on up to 16 host threads, each with its own staging buffers of the given
+// sizes; returns the first device error any slice met (hipSuccess if none).
+template <typename F>
+hipError_t for_each_slice(int64_t bc, int64_t hkv, size_t page_bytes, size_t ring_bytes, size_t sink_bytes, F& fn) {
+  const int64_t total = bc * hkv;
+  const int64_t hw = std::max<int64_t>(1, std::thread::hardware_concurrency());
+  const int64_t nt = std::max<int64_t>(1, std::min<int64_t>({16, hw, total}));
+  std::atomic<int64_t> next{0};
+  std::atomic<int> err{static_cast<int>(hipSuccess)};
+  auto work = [&]() {
+    std::vector<uint8_t> pages(page_bytes), ring(ring_bytes), sink(sink_bytes);
+    for (int64_t i = next++; i < total; i = next++) {
+      if (err.load() != static_cast<int>(hipSuccess)) return;
+      const hipError_t e = fn(i / hkv, i % hkv, pages, ring, sink);
+      if (e != hipSuccess) err.store(static_cast<int>(e));
+    }
+  };
+  std::vector<std::thread> th;
+  for (int64_t t = 1; t < nt; ++t) th.emplace_back(work);
+  work();
+  for (auto& t : th) t.join();
+  return static_cast<hipError_t>(err.load());
+}
+}  // namespace
+
+extern "C" {
+
+
 kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void* k_scale, void* k_zero,
                       void* v_codes, void* v_scale, void* v_zero, void* k_resid, void* v_resid, void* stream) {
   kvq_status st = check_handle(h);
@@ -683,24 +717,24 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
   const int64_t ns = std::min<int64_t>(h->n, c.sink_tokens);  // fp16 index r < ns: sink token r
   const int64_t krow = D * kb / 8, vrow = D * vb / 8;
   const std::vector<Layout> GL = group_layouts(h, ng);
-  std::vector<uint8_t> pages(static_cast<size_t>(ng * L.page_bytes));
-  std::vector<uint8_t> ring(static_cast<size_t>(L.ring_chunks * L.ring_chunk_bytes));
-  std::vector<uint8_t> sink(static_cast<size_t>(L.sink_chunks * L.ring_chunk_bytes));
-  for (int64_t bi = 0; bi < bc; ++bi)
-    for (int64_t hk = 0; hk < c.num_kv_heads; ++hk) {
+  // one slice: copy its pages, window ring and sink to host buffers and
+  // write its canonical rows (slices are independent: threads take them in turn)
+  auto one = [&](int64_t bi, int64_t hk, std::vector<uint8_t>& pages, std::vector<uint8_t>& ring,
+                 std::vector<uint8_t>& sink) -> hipError_t {
+      hipError_t e = hipSuccess;
       const int64_t slice = (b0 + bi) * c.num_kv_heads + hk;
       const int64_t oi = bi * c.num_kv_heads + hk;  // output slice index
       if (ng > 0) {
         e = hipMemcpy(pages.data(), h->buf + kvq::page_offset(L, slice, 0), pages.size(), hipMemcpyDeviceToHost);
-        if (e != hipSuccess) return device_error(h, e, "export copy");
+        if (e != hipSuccess) return e;
       }
       e = hipMemcpy(ring.data(), h->buf + L.ring_offset + slice * L.ring_chunks * L.ring_chunk_bytes, ring.size(),
                     hipMemcpyDeviceToHost);
-      if (e != hipSuccess) return device_error(h, e, "export copy");
+      if (e != hipSuccess) return e;
       if (!sink.empty()) {
         e = hipMemcpy(sink.data(), h->buf + L.sink_offset + slice * L.sink_chunks * L.ring_chunk_bytes, sink.size(),
                       hipMemcpyDeviceToHost);
-        if (e != hipSuccess) return device_error(h, e, "export copy");
+        if (e != hipSuccess) return e;
       }
       for (int64_t t = 0; t < nq; ++t) {
         const uint8_t* page = pages.data() + (t / G) * L.page_bytes;
@@ -758,7 +792,12 @@ kvq_status kvq_export(kvq_cache* h, int32_t b0, int32_t bc, void* k_codes, void*
           if (v_resid) static_cast<uint16_t*>(v_resid)[(oi * nr + t) * D + cc] = vvb;
         }
       }
-    }
+      return hipSuccess;
+  };
+  e = for_each_slice(bc, c.num_kv_heads, static_cast<size_t>(ng * L.page_bytes),
+                     static_cast<size_t>(L.ring_chunks * L.ring_chunk_bytes),
+                     static_cast<size_t>(L.sink_chunks * L.ring_chunk_bytes), one);
+  if (e != hipSuccess) return device_error(h, e, "export copy");
   return ok();
 }
 

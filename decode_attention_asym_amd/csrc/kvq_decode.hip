@@ -103,7 +103,9 @@ struct CodeMasks {
 // contexts), so a bias there is amplified into the output: the PV operands
 // are therefore the normal-range form (one packed fp16 subtraction more per
 // operand dword).  The key codes keep the subnormal form: their bias moves a
-// score by ~1e-5 in log2 units, far below the tolerance.
+// score by ~1e-5 in log2 units, far below the tolerance (also with token
+// norms multiplied into the scores: normal-range key operands measured no
+// different there).
 // 4-bit word -> 8 values 2^-24 * mult(e) * code_e, mult = 1, 1, 16, 16, 1, 1, 16, 16.
 __device__ __forceinline__ half8 unpack4(uint32_t w, const CodeMasks<4>& u) {
   const uint32_t w8 = w >> 8;

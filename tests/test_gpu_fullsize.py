@@ -1,19 +1,67 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times (default split count): the oracle checks sampled (batch) rows one by
-one -- every kv head of those rows bit-exact, every query head's attention
-within relative L2 2e-3."""
+times (default split count), on every (batch, kv head) slice: every code,
+scale, zero and window value bit-exact against the oracle's encoding, and the
+attention output of every query head of every sequence against the oracle's
+fp64 attention on the same (exported) cache -- relative L2 over the whole
+output within 2e-3, and each head's row within the same bound, so that an
+error confined to one head or split cannot hide in the norm of the rest."""
 import numpy as np
 import pytest
 import torch
 
-from _parity import (TOL_REL_L2, assert_export_matches, log, oracle_encode_slices, oracle_rows, rel_l2)
+from _parity import (TOL_REL_L2, assert_export_matches, log, oracle_encode_slices, oracle_rows)
 from synth import WORKLOADS, Synth, to_oracle_input
 
 pytestmark = pytest.mark.gpu
 
+ROW_TOL = 2e-3  # relative L2 of any one (sequence, query head) output row
+SLICES_PER_PASS = 16
+
+
+class _Err:
+    """Accumulates the squared errors of output rows against the oracle."""
+
+    def __init__(self):
+        self.num = self.den = 0.0
+        self.rows = []
+
+    def add(self, got, ref):
+        d = got - ref
+        self.num += float((d ** 2).sum())
+        self.den += float((ref ** 2).sum())
+        self.rows.extend((np.linalg.norm(d, axis=-1) / np.linalg.norm(ref, axis=-1)).ravel().tolist())
+
+    def report(self, tag):
+        whole = (self.num / self.den) ** 0.5
+        r = np.asarray(self.rows)
+        log(f"[full] {tag}: rel L2 {whole:.3e} over {r.size} rows; per row median {np.median(r):.2e}, "
+            f"p99 {np.percentile(r, 99):.2e}, max {r.max():.2e}")
+        return whole, float(r.max())
+
+
+def check_every_slice(w, cache, K, V, q, out, calls=None, tag=""):
+    """Every slice's export against the oracle encoding of K, V, and every
+    output row against the oracle's attention on the export."""
+    q_host = to_oracle_input(q, w.dtype)
+    rows_per_pass = max(1, SLICES_PER_PASS // w.Hkv)
+    err = _Err()
+    for b0 in range(0, w.B, rows_per_pass):
+        bc = min(rows_per_pass, w.B - b0)
+        exp = cache.export(b0, bc)
+        batches = list(range(b0, b0 + bc))
+        encs = oracle_encode_slices(w, K, V, [(b, h) for b in batches for h in range(w.Hkv)], calls)
+        assert_export_matches(w, exp, b0, encs)
+        del encs
+        ref = oracle_rows(w, exp, b0, q_host, batches)
+        for b in batches:
+            err.add(out[b].double().cpu().numpy(), ref[b])
+    whole, worst = err.report(tag or w.name)
+    assert whole <= TOL_REL_L2, whole
+    assert worst <= ROW_TOL, worst
+
 
 @pytest.mark.parametrize("idx", [2, 3, 4], ids=["llama3-8b-32k-k4v2-drift", "70b-128k", "175b-mha-fwht"])
-def test_full_size_sampled_rows(idx):
+def test_full_size_every_slice(idx):
     import decode_attention_asym_amd as kvq
 
     w = WORKLOADS[idx]
@@ -26,23 +74,14 @@ def test_full_size_sampled_rows(idx):
     out = cache.decode(q)  # default split count, as timed by bench.py
     torch.cuda.synchronize()
     log(f"[full] {w.name}: splits {cache.default_splits()}")
-    q_host = to_oracle_input(q, w.dtype)
-    got, ref = [], []
-    for b in (0, w.B - 1):
-        exp = cache.export(b, 1)
-        encs = oracle_encode_slices(w, K, V, [(b, h) for h in range(w.Hkv)])
-        assert_export_matches(w, exp, b, encs)
-        ref.append(oracle_rows(w, exp, b, q_host, [b])[b])
-        got.append(out[b].double().cpu().numpy())
-    err, worst = rel_l2(np.stack(got), np.stack(ref))
-    log(f"[full] {w.name}: codes bit-exact on sampled rows; rel L2 {err:.3e} (worst row {worst:.3e})")
-    assert err <= TOL_REL_L2
+    check_every_slice(w, cache, K, V, q, out)
 
 
 def test_70b_append_decode_steps_cross_flushes():
     """The 70B-shaped 128k workload's step loop: 64 steps of append(1) +
-    decode, two group flushes (G = 32) on the way; decode checked at steps
-    that straddle a flush, cache contents bit-exact at the end."""
+    decode, two group flushes (G = 32) on the way; the decode of every
+    sequence checked at steps that straddle a flush, every slice's cache
+    contents bit-exact at those steps."""
     import decode_attention_asym_amd as kvq
 
     w = WORKLOADS[3]
@@ -52,7 +91,6 @@ def test_70b_append_decode_steps_cross_flushes():
     cache = kvq.KVQCache(kvq.config_for(w, max_tokens=w.N + steps))
     cache.append(K, V)
     ks, vs = [], []
-    errs = []
     for i in range(steps):
         k, v = syn.step_kv(i)
         ks.append(k)
@@ -62,13 +100,8 @@ def test_70b_append_decode_steps_cross_flushes():
         out = cache.decode(q)
         if i in (0, 30, 31, 32, 63):
             torch.cuda.synchronize()
-            exp = cache.export(0, 1)
-            ref = oracle_rows(w, exp, 0, to_oracle_input(q, w.dtype), [0])[0]
-            err, worst = rel_l2(out[0].double().cpu().numpy(), ref)
-            log(f"[steps] step {i}: n={cache.num_tokens} nq={cache.num_quantized} rel L2 {err:.3e}")
-            errs.append(err)
-    assert max(errs) <= TOL_REL_L2
-    Kall = torch.cat([K[:1]] + [k[:1] for k in ks], dim=2)
-    Vall = torch.cat([V[:1]] + [v[:1] for v in vs], dim=2)
-    encs = oracle_encode_slices(w, Kall, Vall, [(0, h) for h in range(w.Hkv)])
-    assert_export_matches(w, cache.export(0, 1), 0, encs)
+            log(f"[steps] step {i}: n={cache.num_tokens} nq={cache.num_quantized}")
+            Kall = torch.cat([K] + ks, dim=2)
+            Vall = torch.cat([V] + vs, dim=2)
+            check_every_slice(w, cache, Kall, Vall, q, out, tag=f"{w.name} step {i}")
+            del Kall, Vall
