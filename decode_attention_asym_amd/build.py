@@ -29,6 +29,7 @@ SOURCES = {
     # remarks feed check_no_scratch
     "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-Rpass-analysis=kernel-resource-usage"],
     "kvq_merge.hip": [],
+    "kvq_noalloc.hip": [],
     # KL terms are products and sums rounded one by one, as in the oracle
     "kvq_drift.hip": ["-ffp-contract=off"],
     "kvq_api.cpp": ["-ffp-contract=off"],

@@ -408,7 +408,7 @@ namespace {
 // bits); allow_final selects direct output
 // when the whole decode is one split.
 kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partials, size_t bytes, int32_t num_splits,
-                         bool allow_final, int32_t* splits_used, hipStream_t s) {
+                         bool allow_final, int32_t* splits_used, hipStream_t s, bool noalloc = false) {
   kvq_status st = check_handle(h);
   if (st != KVQ_OK) return st;
   if (h->n <= 0) return fail(KVQ_E_STATE, "decode on an empty cache");
@@ -447,6 +447,11 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
     if (!out || !aligned(out, 16)) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
   } else {
     size_t need = static_cast<size_t>(rows * S * (c.head_dim + 4) * sizeof(float));
+    if (noalloc && bytes < need)
+      return fail(KVQ_E_ARG,
+                  "this decode needs %zu bytes of split partials (%lld rows x %lld splits), above the %zu-byte "
+                  "no-allocation scratch; use kvq_decode_attn with a workspace",
+                  need, (long long)rows, (long long)S, bytes);
     if (!partials || !aligned(partials, 16) || bytes < need)
       return fail(KVQ_E_ARG, "workspace/partials NULL, misaligned or %zu < %zu bytes", bytes, need);
   }
@@ -576,6 +581,24 @@ kvq_status kvq_decode_attn(kvq_cache* h, const void* q, float* out, void* ws, si
   kvq_status st = check_handle(h);
   if (st != KVQ_OK) return st;
   return kvq_decode_attn_splits(h, q, out, ws, ws_bytes, choose_splits(h, h->n), stream);
+}
+
+kvq_status kvq_decode_attn_noalloc(kvq_cache* h, const void* q, float* out, void* stream) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  if (!out || !aligned(out, 16)) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
+  void* scratch = nullptr;
+  hipError_t e = kvq::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return fail(KVQ_E_DEVICE, "no-allocation scratch address: %s", hipGetErrorString(e));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t S = 0;
+  st = launch_splits(h, q, out, static_cast<float*>(scratch), kvq::kNoallocScratchBytes, choose_splits(h, h->n), true,
+                     &S, s, true);
+  if (st != KVQ_OK || S == 1) return st;
+  const int64_t rows = static_cast<int64_t>(h->cfg.batch) * h->cfg.num_q_heads;
+  e = kvq::launch_merge(static_cast<const float*>(scratch), out, static_cast<int>(rows), S, h->cfg.head_dim, s);
+  if (e != hipSuccess) return device_error(h, e, "merge kernel launch");
+  return ok();
 }
 
 // ---------------------------------------------------------------- drift detection

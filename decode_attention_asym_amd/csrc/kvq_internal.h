@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/kvq.h"
 #include "kvq_layout.h"
 
 namespace kvq {
@@ -86,6 +87,12 @@ struct MixedPlan {
   int npieces, nf16;
   MixedPiece p[kMaxPieces];
 };
+
+// Bytes of the per-device scratch array behind kvq_decode_attn_noalloc (split
+// partials), and its device address on the current device (looked up once per
+// device, with that device current).
+constexpr size_t kNoallocScratchBytes = KVQ_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
 
 // Both return hipSuccess or the launch error.
 hipError_t launch_flush(const AppendArgs& a, hipStream_t s);

@@ -54,6 +54,7 @@ SIGNATURES = {
     "kvq_append": (ctypes.c_int, [_P, _P, _P, _I32, _P]),
     "kvq_decode_attn": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _P]),
     "kvq_decode_attn_splits": (ctypes.c_int, [_P, _P, _P, _P, _SZ, _I32, _P]),
+    "kvq_decode_attn_noalloc": (ctypes.c_int, [_P, _P, _P, _P]),
     "kvq_default_splits": (_I32, [_P]),
     "kvq_decode_partials": (ctypes.c_int, [_P, _P, _P, _SZ, _I32, ctypes.POINTER(_I32), _P]),
     "kvq_merge_partials": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P]),
@@ -277,6 +278,15 @@ class KVQCache:
             st = lib.kvq_decode_attn_splits(self.h, _ptr(q), _ptr(out), _ptr(self.ws), self.ws.numel(), splits,
                                             _stream(stream))
         check(st, "kvq_decode_attn")
+        return out
+
+    def decode_noalloc(self, q, out=None, stream=None):
+        """decode(q) with the split partials in the library's per-device
+        scratch array instead of this cache's workspace (no device memory is
+        allocated by the call when `out` is given)."""
+        self._q(q)
+        out = self._out(out, q)
+        check(lib.kvq_decode_attn_noalloc(self.h, _ptr(q), _ptr(out), _stream(stream)), "kvq_decode_attn_noalloc")
         return out
 
     def append_decode(self, k, v, q, out=None, stream=None):

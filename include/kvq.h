@@ -135,6 +135,28 @@ kvq_status kvq_append(kvq_cache* cache, const void* k, const void* v, int32_t n_
 kvq_status kvq_decode_attn(kvq_cache* cache, const void* q, float* out, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/* Bytes of the device scratch array kvq_decode_attn_noalloc keeps its split
+ * partials in (one array per device, held until the process ends). */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* kvq_decode_attn for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the split partials live in a file-scope device
+ * array of KVQ_NOALLOC_SCRATCH_BYTES bytes that the library holds on every
+ * device it runs on, looked up once per device on the first call there.
+ * Same split count, kernels and result as kvq_decode_attn.
+ *   q:   device, [B][H_q][D] of in_dtype;  out: device, [B][H_q][D] float32
+ *        (16-byte aligned).
+ * Returns KVQ_E_ARG, enqueuing nothing, when this decode's partials
+ * (B * H_q * S * (D + 4) floats at the chosen split count S) exceed
+ * KVQ_NOALLOC_SCRATCH_BYTES; KVQ_E_DEVICE if the array's address cannot be
+ * obtained.  No device memory is allocated or freed.  Every call on one
+ * device shares that device's array, and every split record a call reads is
+ * written by the same call first (nothing needs clearing), so calls that
+ * overlap in time on one device -- on different streams or from different
+ * threads -- race and must be serialized by the caller. */
+kvq_status kvq_decode_attn_noalloc(kvq_cache* cache, const void* q, float* out, void* stream);
+
 /* As kvq_decode_attn with an explicit split count 1 <= num_splits <= the
  * S_max sized by kvq_workspace_bytes (values above the number of token
  * groups are clamped).  Any split count gives the same result up to
