@@ -384,8 +384,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
             int i = ch * kChunk + tau(j, e);
             const int pv = i * NCG + cg;
             uint32_t code = code_of<VB, HYB>(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB && vsym[pv]);
-            int bit = VB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
-            word |= code << bit;
+            word |= code << vcode_bit(VB, mt, e);
           }
         }
         *reinterpret_cast<uint32_t*>(page + L.off_vcodes + ch * L.vc_chunk_bytes + lane_dword_offset(VW, l, d)) = word;

@@ -61,20 +61,10 @@ __device__ __forceinline__ uint32_t sgpr_const(uint32_t x) {
   return r;
 }
 
-// A constant held in a VGPR: lets (w & sgpr_mask) | c be one v_and_or_b32
-// (a VOP3 instruction reads at most one SGPR and no literal here).
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t x) {
-  uint32_t r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(x));
-  return r;
-}
-
 template <int BITS>
 struct CodeMasks {
   uint32_t m[4];
-  uint32_t e1024;  // fp16 exponent field of 1024 in both halves (normal-range unpack)
   __device__ __forceinline__ CodeMasks() {
-    e1024 = vgpr_const(0x64006400u);
     if (BITS == 4) {
       m[0] = sgpr_const(0x000F000Fu);
       m[1] = sgpr_const(0x00F000F0u);
@@ -90,22 +80,20 @@ struct CodeMasks {
 };
 
 // A b-bit field at bit p of a 16-bit half, with every other bit of the half
-// clear, is the fp16 subnormal 2^(p - 24) * code exactly.  With the exponent
-// field of 1024 set as well it is the normal value 1024 + 2^p * code, and
-// subtracting 1024 (exact) leaves 2^p * code as a normal fp16 value (or 0).
+// clear, is the fp16 subnormal 2^(p - 24) * code exactly (key operands).
 //
-// Precision (measured on gfx950 with chains of 64 MFMAs against exact sums):
-// the matrix cores' fp32 result is biased low by about 4.5 ulp per chain when
-// an A input is an fp16 subnormal, and the bias scales with the size of the
-// terms, not of the sum; with normal-range inputs the error has no measurable
-// bias (+0.02 ulp).  The value codes' product sum cancels against the
+// Precision (measured on gfx950 with chains of MFMAs against exact sums): the
+// matrix cores' fp32 result is biased low when an input is an fp16 subnormal
+// (about -7e-6 relative over 128 MFMAs with weights spread like softmax
+// weights, in either operand), and the bias scales with the size of the
+// terms, not of the sum; with normal-range inputs the error has no
+// measurable bias.  The value codes' product sum cancels against the
 // zero-point sum (|sum p s code| / |output| is 30-70 on long diffuse
-// contexts), so a bias there is amplified into the output: the PV operands
-// are therefore the normal-range form (one packed fp16 subtraction more per
-// operand dword).  The key codes keep the subnormal form: their bias moves a
-// score by ~1e-5 in log2 units, far below the tolerance (also with token
-// norms multiplied into the scores: normal-range key operands measured no
-// different there).
+// contexts), so a bias there is amplified into the output: the value
+// operands are therefore normal-range (see v_operand).  The key codes keep
+// the subnormal form: their bias moves a score by ~1e-5 in log2 units, far
+// below the tolerance (also with token norms multiplied into the scores:
+// normal-range key operands measured no different there).
 // 4-bit word -> 8 values 2^-24 * mult(e) * code_e, mult = 1, 1, 16, 16, 1, 1, 16, 16.
 __device__ __forceinline__ half8 unpack4(uint32_t w, const CodeMasks<4>& u) {
   const uint32_t w8 = w >> 8;
@@ -115,27 +103,6 @@ __device__ __forceinline__ half8 unpack4(uint32_t w, const CodeMasks<4>& u) {
 // 2^-24 * 4^(e>>1) * code_e.
 __device__ __forceinline__ half8 unpack2(uint32_t w, const CodeMasks<2>& u) {
   return __builtin_bit_cast(half8, u32x4{w & u.m[0], w & u.m[1], w & u.m[2], w & u.m[3]});
-}
-
-// Normal-range fp16 pair 2^p * code from the fields selected by m: the
-// exponent field of 1024 is set (v_and_or_b32), then 1024 is subtracted from
-// both halves (v_pk_add_f16); both steps are exact.
-__device__ __forceinline__ uint32_t norm_pair(uint32_t w, uint32_t m, uint32_t e1024) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 x = __builtin_bit_cast(h2, (w & m) | e1024);
-  const h2 off = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
-  return __builtin_bit_cast(uint32_t, x - off);
-}
-// 4-bit word -> 8 values mult(e) * code_e (normal range).
-__device__ __forceinline__ half8 unpack4n(uint32_t w, const CodeMasks<4>& u) {
-  const uint32_t w8 = w >> 8;
-  return __builtin_bit_cast(half8, u32x4{norm_pair(w, u.m[0], u.e1024), norm_pair(w, u.m[1], u.e1024),
-                                         norm_pair(w8, u.m[0], u.e1024), norm_pair(w8, u.m[1], u.e1024)});
-}
-// One 2-bit sub-block -> 8 values 4^(e>>1) * code_e (normal range).
-__device__ __forceinline__ half8 unpack2n(uint32_t w, const CodeMasks<2>& u) {
-  return __builtin_bit_cast(half8, u32x4{norm_pair(w, u.m[0], u.e1024), norm_pair(w, u.m[1], u.e1024),
-                                         norm_pair(w, u.m[2], u.e1024), norm_pair(w, u.m[3], u.e1024)});
 }
 
 template <int BITS>
@@ -153,14 +120,29 @@ __device__ __forceinline__ half8 a_operand(const uint32_t* words, int idx, const
     return unpack2((idx & 1) ? (w >> 8) : w, u);
   }
 }
-// The same operand in the normal-range form (values mult(e) * code_e).
-template <int BITS>
-__device__ __forceinline__ half8 a_operand_n(const uint32_t* words, int idx, const CodeMasks<BITS>& u) {
-  if constexpr (BITS == 4) {
-    return unpack4n(words[idx], u);
+// Value operand of M-tile mt (16 channels x 32 tokens) from the lane's value
+// code words, as normal-range fp16 values equal to the codes: the words are
+// laid out (vcode_bit in kvq_layout.h) so that one mask leaves every code of
+// the tile in the low bits of a nibble of its own, which the fp4 (e2m1, 2-bit
+// codes: value code / 2, scaled by 2) or fp8 (e4m3, 4-bit codes: value
+// code * 2^-9, scaled by 2^9) -> fp16 conversions turn into code exactly, two
+// per instruction.
+template <int VB>
+__device__ __forceinline__ half8 v_operand(const uint32_t* words, int mt) {
+  if constexpr (VB == 2) {
+    const uint32_t w = words[mt >> 1];
+    const uint32_t m = ((mt & 1) ? (w >> 2) : w) & 0x33333333u;
+    return __builtin_bit_cast(half8, u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 0)),
+                                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 1)),
+                                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 2)),
+                                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, 3))});
   } else {
-    const uint32_t w = words[idx >> 1];
-    return unpack2n((idx & 1) ? (w >> 8) : w, u);
+    const uint32_t w = words[mt];
+    const uint32_t m0 = w & 0x0F0F0F0Fu, m1 = (w >> 4) & 0x0F0F0F0Fu;
+    return __builtin_bit_cast(half8, u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m0, 512.0f, false)),
+                                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m0, 512.0f, true)),
+                                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m1, 512.0f, false)),
+                                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(m1, 512.0f, true))});
   }
 }
 
@@ -489,32 +471,19 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
     }
 
   const CodeMasks<KB> uk;
-  const CodeMasks<VB> uv;
-
-  // Value-code multiplier of this lane's value pair pp (tokens e = NV rp + 2 pp
-  // and + 1 share it) and its log2.
-  float vmult[NPR], vmlog[NPR];
-#pragma unroll
-  for (int pp = 0; pp < NPR; ++pp) {
-    const int e = NV * rp + 2 * pp;
-    vmult[pp] = code_mult<VB>(e);
-    vmlog[pp] = VB == 4 ? 4.0f * ((e >> 1) & 1) : 2.0f * (e >> 1);
-  }
 
   // Online-softmax state (per head, uniform over replicas and j).  m is the
   // running max in log2 units; acc holds the PV sums (the value codes enter
-  // as normal-range values mult * code, the weights as p * s / mult).  lsum
-  // and zacc are this lane's share (its value slots).
+  // as normal-range fp16 values, the weights as fp16 p * s).  lsum and zacc
+  // are this lane's share (its value slots).
   float m = -INFINITY, mslack = -INFINITY, lsum = 0.0f;
   f32x4 acc[NMT];
 #pragma unroll
   for (int i = 0; i < NMT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // zero-point sums per value group and value pair, weighted by p / mult
-  float zacc[NCG][NPR];
+  // zero-point sums per value group, weighted by p
+  float zacc[NCG];
 #pragma unroll
-  for (int i = 0; i < NCG; ++i)
-#pragma unroll
-    for (int pp = 0; pp < NPR; ++pp) zacc[i][pp] = 0.0f;
+  for (int i = 0; i < NCG; ++i) zacc[i] = 0.0f;
 
   // (called wave-uniformly; mnew = max(m, chunk max) per head)
   auto rescale = [&](float mnew) __attribute__((always_inline)) {
@@ -522,9 +491,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
 #pragma unroll
     for (int i = 0; i < NMT; ++i) acc[i] *= al;
 #pragma unroll
-    for (int i = 0; i < NCG; ++i)
-#pragma unroll
-      for (int pp = 0; pp < NPR; ++pp) zacc[i][pp] *= al;
+    for (int i = 0; i < NCG; ++i) zacc[i] *= al;
     lsum *= al;
     m = mnew;
     mslack = mnew + kMaxSlack;
@@ -601,14 +568,10 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
 
     uint32_t bq[NP][NKB][4];  // B operand of QK^T (fp16 pairs), per part
     float cb = 0.0f;          // this group's zero-point score bias (log2 units)
-    // exponent offsets per value pair: exp2(score - m - log2(mult)) is p / mult,
-    // the weight the PV operand needs
-    float bmc[NPR];
+    // exponent offset: exp2(score + bias - m) is the softmax weight p
+    float bmc;
     // (with key token norms the bias is inside each score, so it is left out)
-    auto set_bmc = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int pp = 0; pp < NPR; ++pp) bmc[pp] = ((TN ? 0.0f : cb) - m) - vmlog[pp];
-    };
+    auto set_bmc = [&]() __attribute__((always_inline)) { bmc = (TN ? 0.0f : cb) - m; };
 
     auto process = [&](const uint8_t* sl, const uint8_t* pbk, int ch, auto&& refill) __attribute__((always_inline)) {
       if (ch == 0) {
@@ -729,15 +692,14 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
         rescale(fmax2(m, wave_max_j(replica_max<R>(lmax))));
         set_bmc();
       }
-      // pm = p / mult (the exponent offset per pair), lsum += pm * mult
+      // softmax weights p
       float pm[NV];
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        pm[k] = __builtin_amdgcn_exp2f(TN ? sc[k] + bmc[k >> 1] : __builtin_fmaf(u[k], kTwo24, bmc[k >> 1]));
-        lsum = __builtin_fmaf(pm[k], vmult[k >> 1], lsum);
+        pm[k] = __builtin_amdgcn_exp2f(TN ? sc[k] + bmc : __builtin_fmaf(u[k], kTwo24, bmc));
+        lsum += pm[k];
       }
-      // PV weights p * value scale / mult (one fp16 part: its rounding is far
-      // below the matrix cores' own error on these sums) and the zero-point sums
+      // PV weights p * value scale (one fp16 part) and the zero-point sums
       uint32_t bpc[NCG][NPR];
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
@@ -745,9 +707,8 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
         for (int pp = 0; pp < NPR; ++pp) {
           const uint32_t sp = vp[(pp * NCG + cg) * 2], zp = vp[(pp * NCG + cg) * 2 + 1];
           bpc[cg][pp] = mix_mul2(pm[2 * pp], pm[2 * pp + 1], sp);
-          float& z = zacc[cg][pp];
-          z = __builtin_fmaf(pm[2 * pp], h2f_lo(zp), z);
-          z = __builtin_fmaf(pm[2 * pp + 1], h2f_hi(zp), z);
+          zacc[cg] = __builtin_fmaf(pm[2 * pp], h2f_lo(zp), zacc[cg]);
+          zacc[cg] = __builtin_fmaf(pm[2 * pp + 1], h2f_hi(zp), zacc[cg]);
         }
       }
       // the slot's data has long been read into registers: refill it with a
@@ -759,7 +720,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       // PV on the normal-range code operands
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
-        const half8 av = a_operand_n<VB>(vw, mt, uv);
+        const half8 av = v_operand<VB>(vw, mt);
         const uint32_t* bw = bp[(16 * mt) / G];
         const half8 bb = __builtin_bit_cast(half8, u32x4{bw[0], bw[1], bw[2], bw[3]});
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bb, acc[mt], 0, 0, 0);
@@ -872,12 +833,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   lsum = wave_sum_j(replica_sum<R>(lsum));
   float zsum[NCG];
 #pragma unroll
-  for (int i = 0; i < NCG; ++i) {
-    float z = 0.0f;
-#pragma unroll
-    for (int pp = 0; pp < NPR; ++pp) z = __builtin_fmaf(zacc[i][pp], vmult[pp], z);
-    zsum[i] = wave_sum_j(replica_sum<R>(z));
-  }
+  for (int i = 0; i < NCG; ++i) zsum[i] = wave_sum_j(replica_sum<R>(zacc[i]));
   if (hv && rp == 0) {
     const int64_t row = static_cast<int64_t>(b) * a.Hq + hq;
     if (a.write_final) {

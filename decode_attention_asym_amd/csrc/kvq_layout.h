@@ -23,13 +23,13 @@
 //   tau(j, e) = 4j + e           for e < 4
 //             = 16 + 4j + e - 4  for e >= 4
 //
-// Code unpack: a 32-bit word w holds fields for two fp16 lanes of a half8
-// (low half -> even e, high half -> odd e).  w & mask turns a b-bit field at
-// bit position p of each half into the fp16 subnormal 2^(p - 24) * code
-// (key operands); (w & mask) | 0x64006400 is the fp16 value 1024 + 2^p * code,
-// and subtracting 1024 leaves the normal value 2^p * code (value operands),
-// both exactly; a shift by 8 brings the upper byte of each half down.  The
-// 2^p factors are folded into the other operand (powers of two, exact).
+// Key code unpack: a 32-bit word w holds fields for two fp16 lanes of a
+// half8 (low half -> even e, high half -> odd e).  w & mask turns a b-bit
+// field at bit position p of each half into the fp16 subnormal
+// 2^(p - 24) * code exactly; a shift by 8 brings the upper byte of each half
+// down.  The 2^p factors are folded into the other operand (powers of two,
+// exact).  Value codes are laid out for gfx950's fp4 / fp8 -> fp16
+// conversions instead (vcode_bit below), which give normal-range fp16 codes.
 //
 //   4-bit word, operand pair i = e >> 1: field at 4 * (i & 1) after shifting
 //     by 8 * (i >> 1); multiplier 16^(i & 1).  Bit of element e:
@@ -147,19 +147,30 @@ KVQ_HD void kcode_loc(const Layout& L, int t, int c, int64_t* byte, int* bit) {
   }
 }
 
+// Bit of element e (0..7) of value M-tile mt inside its code word (word mt
+// for 4-bit codes, mt / 2 for 2-bit).  The two elements of each operand pair
+// (e, e + 1 with e even) share a byte, each in the low bits of one nibble, so
+// a masked word is read by the fp4 / fp8 -> fp16 conversions:
+//   2-bit: byte e / 2, nibble e % 2, the nibble's low (mt even) or high
+//          (mt odd) two bits; (w >> 2 (mt odd)) & 0x33333333 leaves the
+//          tile's codes as fp4 e2m1 nibbles of value code / 2, byte k holding
+//          pair k.
+//   4-bit: elements 0..3 in the low nibbles of bytes 0..3, elements 4..7 in
+//          the high nibbles; w & 0x0F0F0F0F (and (w >> 4) & 0x0F0F0F0F) are
+//          four fp8 e4m3 bytes of value code * 2^-9, 16-bit half h holding
+//          pair h (pairs 2 + h).
+KVQ_HD int vcode_bit(int vbits, int mt, int e) {
+  return vbits == 4 ? 16 * ((e >> 1) & 1) + 8 * (e & 1) + 4 * (e >> 2) : 8 * (e >> 1) + 4 * (e & 1) + 2 * (mt & 1);
+}
+
 // Location of the value code of token t (0..31 within its chunk), channel c.
 KVQ_HD void vcode_loc(const Layout& L, int t, int c, int64_t* byte, int* bit) {
   int mt = c >> 4, c16 = c & 15;
   int j, e;
   tau_inv(t, &j, &e);
   int l = j * 16 + c16;
-  if (L.vbits == 4) {
-    *byte = lane_dword_offset(L.vw, l, mt);
-    *bit = 16 * (e & 1) + 4 * (e >> 1);
-  } else {
-    *byte = lane_dword_offset(L.vw, l, mt >> 1);
-    *bit = 16 * (e & 1) + 8 * (mt & 1) + 2 * (e >> 1);
-  }
+  *byte = lane_dword_offset(L.vw, l, L.vbits == 4 ? mt : mt >> 1);
+  *bit = vcode_bit(L.vbits, mt, e);
 }
 
 // Index (in fp16 elements) of channel c's key scale within a group's scale
