@@ -30,6 +30,14 @@ __device__ __forceinline__ float round_fp16(float x) { return __half2float(__flo
 
 __device__ __forceinline__ uint16_t fp16_bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
 
+// Two bf16 values (one dword) -> two fp16 values, each rounded to nearest even
+// from the exact binary32 value (one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 r = {static_cast<_Float16>(__uint_as_float(w << 16)), static_cast<_Float16>(__uint_as_float(w & 0xffff0000u))};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // rne(fl(n / s)) for |n / s| <= 16, given rs = fl(1 / s) (correctly
 // rounded).  fl(n * rs) is within 2^-19 of n / s (two roundings of relative
 // size 2^-24 on a quotient below 16) and fl(n / s) within 2^-20 of it, so the
@@ -48,20 +56,28 @@ __device__ __forceinline__ float rne_quotient(float n, float s, float rs) {
   return t;
 }
 
-// code = clamp(rne((x - mn) / s), 0, levels); 0 when the group is constant.
-__device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float rs, float levels) {
-  if (s == 0.0f) return 0u;
-  float q = rne_quotient(x - mn, s, rs);
-  q = fminf(fmaxf(q, 0.0f), levels);
-  return static_cast<uint32_t>(q);
+// code = clamp(rne((x - mn) / s), 0, levels) as a float; 0 when the group is
+// constant.  The clamp never acts, so it is left out: every x of the group
+// lies in [mn, mx], fl is monotonic, and s = fl(fl(mx - mn) / levels), so the
+// quotient is at most levels * (1 + 2^-22) and at least -0, which round to
+// levels and 0 (the same holds for the reciprocal product the rounding helper
+// forms first).
+__device__ __forceinline__ float quant_code_f(float x, float mn, float s, float rs) {
+  if (s == 0.0f) return 0.0f;
+  return rne_quotient(x - mn, s, rs);
+}
+__device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float rs, float) {
+  return static_cast<uint32_t>(quant_code_f(x, mn, s, rs));
 }
 
-// Symmetric code: clamp(rne(x / s), -c0, c0) + c0; c0 when s == 0.
+// Symmetric code: clamp(rne(x / s), -c0, c0) + c0 as a float; c0 when s == 0
+// (|x| <= max|x| and s = fl(max|x| / c0): the clamp never acts, as above).
+__device__ __forceinline__ float quant_code_sym_f(float x, float s, float rs, float c0) {
+  if (s == 0.0f) return c0;
+  return rne_quotient(x, s, rs) + c0;
+}
 __device__ __forceinline__ uint32_t quant_code_sym(float x, float s, float rs, float c0) {
-  if (s == 0.0f) return static_cast<uint32_t>(c0);
-  float q = rne_quotient(x, s, rs);
-  q = fminf(fmaxf(q, -c0), c0);
-  return static_cast<uint32_t>(q + c0);
+  return static_cast<uint32_t>(quant_code_sym_f(x, s, rs, c0));
 }
 
 __device__ __forceinline__ float recip(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
@@ -135,13 +151,31 @@ __device__ __forceinline__ GroupQ group_params_pair(F&& x) {
   return r;
 }
 
+// The code of x as a float (an integer in [0, 2^BITS - 1]).
 template <int BITS, bool HYB>
-__device__ __forceinline__ uint32_t code_of(float x, float mn, float s, float rs, bool sym) {
-  constexpr float levels = static_cast<float>((1 << BITS) - 1), c0 = static_cast<float>((1 << (BITS - 1)) - 1);
+__device__ __forceinline__ float code_of(float x, float mn, float s, float rs, bool sym) {
+  constexpr float c0 = static_cast<float>((1 << (BITS - 1)) - 1);
   if constexpr (HYB) {
-    if (sym) return quant_code_sym(x, s, rs, c0);
+    if (sym) return quant_code_sym_f(x, s, rs, c0);
   }
-  return quant_code(x, mn, s, rs, levels);
+  return quant_code_f(x, mn, s, rs);
+}
+
+// Packs codes into a dword: the code of field k goes to bit bit_of(k); the
+// fields of a byte are summed as floats (exact small integers) and each byte
+// is inserted by one v_cvt_pk_u8_f32.
+template <int N, typename BitF, typename CodeF>
+__device__ __forceinline__ uint32_t pack_codes(BitF&& bit_of, CodeF&& code) {
+  float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int bit = bit_of(k);
+    b[bit >> 3] = __builtin_fmaf(code(k), static_cast<float>(1 << (bit & 7)), b[bit >> 3]);
+  }
+  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(b[0], 0, 0u);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(b[1], 1, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(b[2], 2, w);
+  return __builtin_amdgcn_cvt_pk_u8_f32(b[3], 3, w);
 }
 
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // nearest binary32 to 1/sqrt(128)
@@ -229,13 +263,22 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
       const int e0 = (tid + 256 * r) * 8, i = e0 / D, c0 = e0 % D;
       const uint32_t kw[4] = {kv[r].x, kv[r].y, kv[r].z, kv[r].w}, vw[4] = {vv[r].x, vv[r].y, vv[r].z, vv[r].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t ku = static_cast<uint16_t>(kw[e >> 1] >> (16 * (e & 1)));
-        const uint16_t vu = static_cast<uint16_t>(vw[e >> 1] >> (16 * (e & 1)));
-        const float kf = a.in_dtype == 1 ? __half2float(__ushort_as_half(ku)) : __uint_as_float(static_cast<uint32_t>(ku) << 16);
-        const float vf = a.in_dtype == 1 ? __half2float(__ushort_as_half(vu)) : __uint_as_float(static_cast<uint32_t>(vu) << 16);
-        kput(i * KS + c0 + e, kf);
-        vx[i * VS + c0 + e] = __float2half_rn(vf);
+      for (int p = 0; p < 4; ++p) {
+        // an fp16 pair as it is, a bf16 pair converted to fp16 (nearest even)
+        // two at a time; stored as one dword (rows are 4-byte aligned)
+        const uint32_t vh = a.in_dtype == 1 ? vw[p] : bf16x2_to_f16x2(vw[p]);
+        if constexpr (F32K) {
+          // binary32 keys are staged as given (rotation and norms come first,
+          // the fp16 rounding after them)
+          const uint32_t w = kw[p];
+          kx[i * KS + c0 + 2 * p] = a.in_dtype == 1 ? __half2float(__ushort_as_half(static_cast<uint16_t>(w)))
+                                                    : __uint_as_float(w << 16);
+          kx[i * KS + c0 + 2 * p + 1] = a.in_dtype == 1 ? __half2float(__ushort_as_half(static_cast<uint16_t>(w >> 16)))
+                                                        : __uint_as_float(w & 0xffff0000u);
+        } else {
+          *reinterpret_cast<uint32_t*>(&kx[i * KS + c0 + 2 * p]) = a.in_dtype == 1 ? kw[p] : bf16x2_to_f16x2(kw[p]);
+        }
+        *reinterpret_cast<uint32_t*>(&vx[i * VS + c0 + 2 * p]) = vh;
       }
     }
   } else {
@@ -350,19 +393,19 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         int l = (task / KW) % kLanes;
         int d = task % KW;
         int l16 = l & 15, j = l >> 4;
-        uint32_t word = 0;
+        // field k: element e = k % 8 of sub-block k / 8
         constexpr int SUBS = KB == 4 ? 1 : 2;
-        for (int sub = 0; sub < SUBS; ++sub) {
-          int combo = KB == 4 ? d : 2 * d + sub;
-          int mt = combo / NKB, kb = combo % NKB;
-          int i = ch * kChunk + 16 * mt + l16;  // token within the group
-          for (int e = 0; e < 8; ++e) {
-            int c = 32 * kb + 8 * j + e;
-            uint32_t code = code_of<KB, HYB>(kget(i * KS + c), kmn[c], ks[c], krs[c], HYB && ksym[c]);
-            int bit = KB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1);
-            word |= code << bit;
-          }
-        }
+        const uint32_t word = pack_codes<8 * SUBS>(
+            [&](int k) { const int e = k & 7, sub = k >> 3;
+                         return KB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1); },
+            [&](int k) {
+              const int e = k & 7, sub = k >> 3;
+              const int combo = KB == 4 ? d : 2 * d + sub;
+              const int mt = combo / NKB, kb = combo % NKB;
+              const int i = ch * kChunk + 16 * mt + l16;  // token within the group
+              const int c = 32 * kb + 8 * j + e;
+              return code_of<KB, HYB>(kget(i * KS + c), kmn[c], ks[c], krs[c], HYB && ksym[c]);
+            });
         *reinterpret_cast<uint32_t*>(page + L.off_kcodes + ch * L.kc_chunk_bytes + lane_dword_offset(KW, l, d)) = word;
       }
     }
@@ -374,19 +417,16 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         int l = (task / VW) % kLanes;
         int d = task % VW;
         int l16 = l & 15, j = l >> 4;
-        uint32_t word = 0;
         constexpr int SUBS = VB == 4 ? 1 : 2;
-        for (int sub = 0; sub < SUBS; ++sub) {
-          int mt = VB == 4 ? d : 2 * d + sub;
-          int c = 16 * mt + l16;
-          int cg = c / G;
-          for (int e = 0; e < 8; ++e) {
-            int i = ch * kChunk + tau(j, e);
-            const int pv = i * NCG + cg;
-            uint32_t code = code_of<VB, HYB>(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB && vsym[pv]);
-            word |= code << vcode_bit(VB, mt, e);
-          }
-        }
+        const uint32_t word = pack_codes<8 * SUBS>(
+            [&](int k) { return vcode_bit(VB, VB == 4 ? d : 2 * d + (k >> 3), k & 7); },
+            [&](int k) {
+              const int e = k & 7, mt = VB == 4 ? d : 2 * d + (k >> 3);
+              const int c = 16 * mt + l16, cg = c / G;
+              const int i = ch * kChunk + tau(j, e);
+              const int pv = i * NCG + cg;
+              return code_of<VB, HYB>(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB && vsym[pv]);
+            });
         *reinterpret_cast<uint32_t*>(page + L.off_vcodes + ch * L.vc_chunk_bytes + lane_dword_offset(VW, l, d)) = word;
       }
     }
