@@ -315,13 +315,15 @@ def main() -> int:
         cache.append(K, V)
         b.record()
     S = args.splits or cache.default_splits()  # host-side: the token count is known without the device
+    # (split count, splits merged inside the decode kernel): with the merge in
+    # the kernel a step is two launches (append, decode), else three (append,
+    # decode, merge kernel)
+    S_used, merged = cache.decode_plan(S)
 
     def step(i):
         k, v = step_kv[i]
         cache.append(k, v)
-        _, used = cache.decode_partials(qs[i], partials, splits=S)
-        merge_partials(partials, out, rows, used, w.D)
-        return used
+        cache.decode(qs[i], out, splits=S)
 
     for i in range(args.warmup):
         step(i)
@@ -340,15 +342,19 @@ def main() -> int:
     # the decode kernel's average launch duration, by difference, right after
     # (an idle GPU restarts slower: the first ~60 steps after a pause of a few
     # ms run up to 3x the settled step time): nk more steps, then nk steps
-    # without the decode (append and merge only), each span between two events
+    # without the decode launch (the append, and the merge kernel when the
+    # decode does not merge its splits itself), each span between two events
+    if not merged:
+        cache.decode_partials(qs[0], partials, splits=S)  # partials for the merge-only steps
     ev[2].record()
     for i in range(nk):
-        used = step(args.warmup + args.steps + i)
+        step(args.warmup + args.steps + i)
     ev[3].record()
     for i in range(nk):
         k, v = step_kv[args.warmup + args.steps + nk + i]
         cache.append(k, v)
-        merge_partials(partials, out, rows, used, w.D)  # the last decode's partials
+        if not merged:
+            merge_partials(partials, out, rows, S_used, w.D)
     ev[4].record()
     torch.cuda.synchronize()
     # per-step percentiles: each step between two events of its own (an event
@@ -439,12 +445,14 @@ def main() -> int:
         "config": {
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
             "context": w.N, "k_bits": w.kbits, "v_bits": w.vbits, "group": w.G, "residual": w.R,
-            "rotate": w.rotate, "sink": w.sink, "hybrid": w.hybrid, "token_norm": w.token_norm, "splits": S,
+            "rotate": w.rotate, "sink": w.sink, "hybrid": w.hybrid, "token_norm": w.token_norm, "splits": S_used,
+            "splits_merged_in_kernel": merged,
             "adapt_delta": w.adapt_delta, "bits_low": list(w.bits_low), "bits_high": list(w.bits_high),
             "parallelism": "single-gpu",
         },
         "roofline": {
-            "kernel": "decode_kernel (split dequant-attention)",
+            "kernel": ("decode_fused_kernel (split dequant-attention, splits merged in the workgroup)" if merged
+                       else "decode_kernel (split dequant-attention)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -453,7 +461,8 @@ def main() -> int:
             "traffic": measured_traffic(w.name),
             "avg_us": round(dec_avg_ms * 1e3, 2),
             "launches_timed": nk,
-            "timing": "per launch: (span of nk steps) - (span of nk steps without the decode), after the timed steps",
+            "timing": "per launch: (span of nk steps) - (span of nk steps without the decode launch), after the "
+                      "timed steps",
             "bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes)),
         },
         "step_us_percentiles": dist,

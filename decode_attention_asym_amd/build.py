@@ -56,7 +56,7 @@ def check_no_scratch(usage: dict) -> None:
     those copies; a register spill (scratch loads and stores) would break the
     count and give wrong results without a fault.  Refuse such a build."""
     bad = []
-    kernels = [k for k in usage if "decode_kernel" in k or "decode_mixed_kernel" in k]
+    kernels = [k for k in usage if any(n in k for n in ("decode_kernel", "decode_mixed_kernel", "decode_fused_kernel"))]
     if not kernels:
         raise RuntimeError("no decode kernel resource remarks found (is -Rpass-analysis on?)")
     for k in kernels:

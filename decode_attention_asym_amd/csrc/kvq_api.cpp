@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <new>
 #include <string>
 #include <thread>
@@ -32,6 +33,9 @@ struct kvq_cache {
   bool poisoned;
   int cu_count;
   std::vector<uint8_t> gk, gv;  // key / value bits of each quantized group
+  // dynamic LDS of the workgroup-merged decode per (key bits, value bits,
+  // splits), 0 where it does not apply (kvq::decode_fused_lds, asked once)
+  std::map<int, size_t> fused_lds;
 };
 
 namespace {
@@ -149,6 +153,24 @@ int64_t nquant_of(const kvq_cache* h, int64_t n) {
 }
 int64_t ngroups_of(const kvq_cache* h) { return nquant_of(h, h->n) / h->cfg.group_size; }
 
+// Whether a decode of one run of (kb, vb) groups at S splits per slice may
+// merge its splits inside the decode kernel (asked of the kernels once per
+// bit widths and split count).
+bool fused_allowed(kvq_cache* h, int kb, int vb, int64_t S) {
+  if (S < 2 || S > kvq::kMaxFusedSplits) return false;
+  const int key = (kb << 16) | (vb << 8) | static_cast<int>(S);
+  auto it = h->fused_lds.find(key);
+  if (it == h->fused_lds.end()) {
+    kvq::DecodeArgs a{};
+    a.L = layout_for(h, kb, vb);
+    a.rotate = h->cfg.rotate;
+    a.gqa = h->cfg.num_q_heads / h->cfg.num_kv_heads;
+    a.splits = static_cast<int>(S);
+    it = h->fused_lds.emplace(key, kvq::decode_fused_lds(a)).first;
+  }
+  return it->second > 0;
+}
+
 // Split count for a decode over n tokens.
 int choose_splits(kvq_cache* h, int64_t n) {
   if (h->cu_count <= 0) {
@@ -168,6 +190,11 @@ int choose_splits(kvq_cache* h, int64_t n) {
   const int64_t per_cu = h->cfg.num_q_heads / h->cfg.num_kv_heads > 8 ? 8 : 12;
   const int64_t target = static_cast<int64_t>(h->cu_count) * per_cu;
   int64_t s = std::max<int64_t>(2, (target + slices - 1) / slices);
+  // where one pass takes 4 to 6 splits, 4 splits merged inside the decode
+  // kernel (one workgroup of four waves per slice) save the merge launch:
+  // measured on the 32k K4/V2 layer, 301.5 us against 306.2 us for 6 splits
+  // and the merge kernel (4 and 6 splits stream the cache equally fast)
+  if (s >= 4 && s <= 6 && h->cfg.adapt_delta == 0 && fused_allowed(h, h->cfg.k_bits, h->cfg.v_bits, 4)) s = 4;
   int64_t ng = nquant_of(h, n) / h->cfg.group_size;
   s = std::min<int64_t>(s, std::max<int64_t>(1, ng / 2));
   s = std::min<int64_t>(s, max_splits(&h->cfg));
@@ -404,57 +431,21 @@ int32_t kvq_default_splits(const kvq_cache* h) {
 
 namespace {
 
-// Validate and launch the split kernels (one per run of groups with equal
-// bits); allow_final selects direct output
-// when the whole decode is one split.
-kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partials, size_t bytes, int32_t num_splits,
-                         bool allow_final, int32_t* splits_used, hipStream_t s, bool noalloc = false) {
-  kvq_status st = check_handle(h);
-  if (st != KVQ_OK) return st;
-  if (h->n <= 0) return fail(KVQ_E_STATE, "decode on an empty cache");
-  if (!q || !aligned(q, 16)) return fail(KVQ_E_ARG, "q NULL or not 16-byte aligned");
-  if (num_splits < 1) return fail(KVQ_E_ARG, "num_splits %d < 1", num_splits);
-  if (num_splits > max_splits(&h->cfg))
-    return fail(KVQ_E_ARG, "num_splits %d above the workspace maximum %d", num_splits, max_splits(&h->cfg));
+// How a decode of the cache's tokens is cut: the runs of groups with equal
+// bits, their splits (or the piece table of a one-launch mixed decode), and
+// whether the splits are merged inside the decode kernel.
+struct SplitPlan {
+  std::vector<Run> runs;
+  bool mixed = false;
+  kvq::MixedPlan pieces{};
+  std::vector<int64_t> sp, gps;  // splits and groups per split of each run
+  int64_t S = 0;                 // split slots per row
+  bool fused = false;            // one run, its splits merged in the workgroup
+};
+
+// Arguments of every decode launch over the cache's current tokens.
+kvq::DecodeArgs decode_args(const kvq_cache* h, const void* q, float* out, float* partials) {
   const kvq_config& c = h->cfg;
-  const int64_t ng = ngroups_of(h);
-  std::vector<Run> runs = runs_of(h, 0, ng);
-  if (runs.empty()) runs.push_back({0, 0, c.k_bits, c.v_bits});
-  if (static_cast<int64_t>(runs.size()) > max_splits(&c))
-    return fail(KVQ_E_UNSUPPORTED, "%zu runs of equal bit widths exceed the split maximum %d", runs.size(),
-                max_splits(&c));
-  kvq::MixedPlan plan{};
-  const bool mixed = runs.size() > 1 && runs.size() <= static_cast<size_t>(kvq::kMaxRuns) &&
-                     plan_pieces(h, runs, std::min<int64_t>(num_splits, ng), &plan);
-  std::vector<int64_t> sp(runs.size(), 1), gps(runs.size(), 0);
-  int64_t S = 0;
-  if (mixed) {
-    S = plan.npieces;
-  } else {
-    if (ng > 0) sp = run_splits(h, runs, std::min<int64_t>(num_splits, ng));
-    for (size_t i = 0; i < runs.size(); ++i) {
-      const int64_t len = runs[i].g1 - runs[i].g0;
-      if (len > 0) {
-        gps[i] = (len + sp[i] - 1) / sp[i];
-        sp[i] = (len + gps[i] - 1) / gps[i];  // no empty split
-      }
-      S += sp[i];
-    }
-  }
-  const int64_t rows = static_cast<int64_t>(c.batch) * c.num_q_heads;
-  const bool final = allow_final && S == 1;
-  if (final) {
-    if (!out || !aligned(out, 16)) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
-  } else {
-    size_t need = static_cast<size_t>(rows * S * (c.head_dim + 4) * sizeof(float));
-    if (noalloc && bytes < need)
-      return fail(KVQ_E_ARG,
-                  "this decode needs %zu bytes of split partials (%lld rows x %lld splits), above the %zu-byte "
-                  "no-allocation scratch; use kvq_decode_attn with a workspace",
-                  need, (long long)rows, (long long)S, bytes);
-    if (!partials || !aligned(partials, 16) || bytes < need)
-      return fail(KVQ_E_ARG, "workspace/partials NULL, misaligned or %zu < %zu bytes", bytes, need);
-  }
   kvq::DecodeArgs a{};
   a.cache = h->buf;
   a.q = q;
@@ -469,31 +460,105 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
   a.nsc = (std::min<int64_t>(h->n, c.sink_tokens) + kvq::kChunk - 1) / kvq::kChunk;
   a.partial = partials;
   a.out = out;
-  a.write_final = final ? 1 : 0;
-  a.splits_total = S;
-  // the fp16 chunks go with the run that has the most splits
-  const size_t fp16_run = static_cast<size_t>(std::max_element(sp.begin(), sp.end()) - sp.begin());
-  if (mixed) {
-    a.L = h->L;
-    hipError_t e = kvq::launch_decode_mixed(a, plan, s);
-    if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
-    if (splits_used) *splits_used = static_cast<int32_t>(S);
+  return a;
+}
+
+// Validate a split count against the cache and plan the decode; allow_fused
+// lets one run with 2 .. kMaxFusedSplits splits per slice merge them in the
+// workgroup, when that launch fits as many waves per CU as the one-wave
+// launch (asked of the kernels once per bit widths and split count).
+kvq_status plan_splits(kvq_cache* h, int32_t num_splits, bool allow_fused, SplitPlan* p) {
+  kvq_status st = check_handle(h);
+  if (st != KVQ_OK) return st;
+  if (h->n <= 0) return fail(KVQ_E_STATE, "decode on an empty cache");
+  if (num_splits < 1) return fail(KVQ_E_ARG, "num_splits %d < 1", num_splits);
+  if (num_splits > max_splits(&h->cfg))
+    return fail(KVQ_E_ARG, "num_splits %d above the workspace maximum %d", num_splits, max_splits(&h->cfg));
+  const kvq_config& c = h->cfg;
+  const int64_t ng = ngroups_of(h);
+  p->runs = runs_of(h, 0, ng);
+  if (p->runs.empty()) p->runs.push_back({0, 0, c.k_bits, c.v_bits});
+  if (static_cast<int64_t>(p->runs.size()) > max_splits(&c))
+    return fail(KVQ_E_UNSUPPORTED, "%zu runs of equal bit widths exceed the split maximum %d", p->runs.size(),
+                max_splits(&c));
+  const std::vector<Run>& runs = p->runs;
+  p->mixed = runs.size() > 1 && runs.size() <= static_cast<size_t>(kvq::kMaxRuns) &&
+             plan_pieces(h, runs, std::min<int64_t>(num_splits, ng), &p->pieces);
+  p->sp.assign(runs.size(), 1);
+  p->gps.assign(runs.size(), 0);
+  p->S = 0;
+  p->fused = false;
+  if (p->mixed) {
+    p->S = p->pieces.npieces;
     return ok();
   }
-  int64_t off = 0;
+  if (ng > 0) p->sp = run_splits(h, runs, std::min<int64_t>(num_splits, ng));
   for (size_t i = 0; i < runs.size(); ++i) {
-    a.L = layout_for(h, runs[i].kb, runs[i].vb);
-    a.g_base = runs[i].g0;
-    a.ngroups = runs[i].g1 - runs[i].g0;
-    a.splits = static_cast<int>(sp[i]);
-    a.groups_per_split = gps[i];
-    a.split_off = off;
-    a.do_fp16 = i == fp16_run ? 1 : 0;
-    hipError_t e = kvq::launch_decode(a, s);
+    const int64_t len = runs[i].g1 - runs[i].g0;
+    if (len > 0) {
+      p->gps[i] = (len + p->sp[i] - 1) / p->sp[i];
+      p->sp[i] = (len + p->gps[i] - 1) / p->gps[i];  // no empty split
+    }
+    p->S += p->sp[i];
+  }
+  p->fused = allow_fused && runs.size() == 1 && fused_allowed(h, runs[0].kb, runs[0].vb, p->S);
+  return ok();
+}
+
+// Validate and launch the split kernels (one per run of groups with equal
+// bits).  allow_final selects direct output when the whole decode is one
+// split, or one run whose few splits per slice are merged inside the
+// workgroup; *merged tells the caller that `out` is written (no merge left).
+kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partials, size_t bytes, int32_t num_splits,
+                         bool allow_final, int32_t* splits_used, bool* merged, hipStream_t s, bool noalloc = false) {
+  if (merged) *merged = false;
+  SplitPlan p;
+  kvq_status st = plan_splits(h, num_splits, allow_final, &p);
+  if (st != KVQ_OK) return st;
+  if (!q || !aligned(q, 16)) return fail(KVQ_E_ARG, "q NULL or not 16-byte aligned");
+  const kvq_config& c = h->cfg;
+  const int64_t rows = static_cast<int64_t>(c.batch) * c.num_q_heads;
+  const int64_t S = p.S;
+  const bool final = allow_final && (S == 1 || p.fused);
+  if (final) {
+    if (!out || !aligned(out, 16)) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
+  } else {
+    size_t need = static_cast<size_t>(rows * S * (c.head_dim + 4) * sizeof(float));
+    if (noalloc && bytes < need)
+      return fail(KVQ_E_ARG,
+                  "this decode needs %zu bytes of split partials (%lld rows x %lld splits), above the %zu-byte "
+                  "no-allocation scratch; use kvq_decode_attn with a workspace",
+                  need, (long long)rows, (long long)S, bytes);
+    if (!partials || !aligned(partials, 16) || bytes < need)
+      return fail(KVQ_E_ARG, "workspace/partials NULL, misaligned or %zu < %zu bytes", bytes, need);
+  }
+  kvq::DecodeArgs a = decode_args(h, q, out, partials);
+  a.write_final = final && !p.fused ? 1 : 0;
+  a.splits_total = static_cast<int>(S);
+  hipError_t e = hipSuccess;
+  if (p.mixed) {
+    a.L = h->L;
+    e = kvq::launch_decode_mixed(a, p.pieces, s);
     if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
-    off += sp[i];
+  } else {
+    // the fp16 chunks go with the run that has the most splits
+    const size_t fp16_run = static_cast<size_t>(std::max_element(p.sp.begin(), p.sp.end()) - p.sp.begin());
+    int64_t off = 0;
+    for (size_t i = 0; i < p.runs.size(); ++i) {
+      a.L = layout_for(h, p.runs[i].kb, p.runs[i].vb);
+      a.g_base = p.runs[i].g0;
+      a.ngroups = p.runs[i].g1 - p.runs[i].g0;
+      a.splits = static_cast<int>(p.sp[i]);
+      a.groups_per_split = p.gps[i];
+      a.split_off = static_cast<int>(off);
+      a.do_fp16 = i == fp16_run ? 1 : 0;
+      e = p.fused ? kvq::launch_decode_fused(a, s) : kvq::launch_decode(a, s);
+      if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
+      off += p.sp[i];
+    }
   }
   if (splits_used) *splits_used = static_cast<int32_t>(S);
+  if (merged) *merged = final;
   return ok();
 }
 
@@ -504,24 +569,36 @@ kvq_status kvq_decode_attn_splits(kvq_cache* h, const void* q, float* out, void*
   if (!out || !aligned(out, 16)) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t S = 0;
-  kvq_status st = launch_splits(h, q, out, static_cast<float*>(ws), ws_bytes, num_splits, true, &S, s);
-  if (st != KVQ_OK || S == 1) return st;
+  bool merged = false;
+  kvq_status st = launch_splits(h, q, out, static_cast<float*>(ws), ws_bytes, num_splits, true, &S, &merged, s);
+  if (st != KVQ_OK || merged) return st;
   const int64_t rows = static_cast<int64_t>(h->cfg.batch) * h->cfg.num_q_heads;
   hipError_t e = kvq::launch_merge(static_cast<float*>(ws), out, static_cast<int>(rows), S, h->cfg.head_dim, s);
   if (e != hipSuccess) return device_error(h, e, "merge kernel launch");
   return ok();
 }
 
+kvq_status kvq_decode_plan(kvq_cache* h, int32_t num_splits, int32_t* splits_used, int32_t* merged_in_kernel) {
+  SplitPlan p;
+  kvq_status st = plan_splits(h, num_splits, true, &p);
+  if (st != KVQ_OK) return st;
+  if (splits_used) *splits_used = static_cast<int32_t>(p.S);
+  if (merged_in_kernel) *merged_in_kernel = p.S == 1 || p.fused ? 1 : 0;
+  return ok();
+}
+
 kvq_status kvq_decode_partials(kvq_cache* h, const void* q, float* partials, size_t bytes, int32_t num_splits,
                                int32_t* splits_used, void* stream) {
-  return launch_splits(h, q, nullptr, partials, bytes, num_splits, false, splits_used, static_cast<hipStream_t>(stream));
+  return launch_splits(h, q, nullptr, partials, bytes, num_splits, false, splits_used, nullptr,
+                       static_cast<hipStream_t>(stream));
 }
 
 namespace {
 // Append one token and decode.  Everything a launch could reject is checked
 // before the first launch.
 kvq_status append_decode(kvq_cache* h, const void* k, const void* v, const void* q, float* out, float* partials,
-                         size_t bytes, int32_t num_splits, bool allow_final, int32_t* splits_used, hipStream_t s) {
+                         size_t bytes, int32_t num_splits, bool allow_final, int32_t* splits_used, bool* merged,
+                         hipStream_t s) {
   kvq_status st = check_handle(h);
   if (st != KVQ_OK) return st;
   const kvq_config& c = h->cfg;
@@ -540,7 +617,7 @@ kvq_status append_decode(kvq_cache* h, const void* k, const void* v, const void*
     return fail(KVQ_E_UNSUPPORTED, "runs of equal bit widths exceed the split maximum %d", max_splits(&c));
   st = append_impl(h, k, v, 1, s);
   if (st != KVQ_OK) return st;
-  return launch_splits(h, q, out, partials, bytes, num_splits, allow_final, splits_used, s);
+  return launch_splits(h, q, out, partials, bytes, num_splits, allow_final, splits_used, merged, s);
 }
 }  // namespace
 
@@ -551,8 +628,9 @@ kvq_status kvq_append_decode_attn(kvq_cache* h, const void* k, const void* v, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t S_req = choose_splits(h, h->n + 1);  // as kvq_decode_attn after the append
   int32_t S = 0;
-  st = append_decode(h, k, v, q, out, static_cast<float*>(ws), ws_bytes, S_req, true, &S, s);
-  if (st != KVQ_OK || S == 1) return st;
+  bool merged = false;
+  st = append_decode(h, k, v, q, out, static_cast<float*>(ws), ws_bytes, S_req, true, &S, &merged, s);
+  if (st != KVQ_OK || merged) return st;
   const int64_t rows = static_cast<int64_t>(h->cfg.batch) * h->cfg.num_q_heads;
   hipError_t e = kvq::launch_merge(static_cast<float*>(ws), out, static_cast<int>(rows), S, h->cfg.head_dim, s);
   if (e != hipSuccess) return device_error(h, e, "merge kernel launch");
@@ -561,7 +639,7 @@ kvq_status kvq_append_decode_attn(kvq_cache* h, const void* k, const void* v, co
 
 kvq_status kvq_append_decode_partials(kvq_cache* h, const void* k, const void* v, const void* q, float* partials,
                                       size_t bytes, int32_t num_splits, int32_t* splits_used, void* stream) {
-  return append_decode(h, k, v, q, nullptr, partials, bytes, num_splits, false, splits_used,
+  return append_decode(h, k, v, q, nullptr, partials, bytes, num_splits, false, splits_used, nullptr,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -592,9 +670,10 @@ kvq_status kvq_decode_attn_noalloc(kvq_cache* h, const void* q, float* out, void
   if (e != hipSuccess) return fail(KVQ_E_DEVICE, "no-allocation scratch address: %s", hipGetErrorString(e));
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t S = 0;
+  bool merged = false;
   st = launch_splits(h, q, out, static_cast<float*>(scratch), kvq::kNoallocScratchBytes, choose_splits(h, h->n), true,
-                     &S, s, true);
-  if (st != KVQ_OK || S == 1) return st;
+                     &S, &merged, s, true);
+  if (st != KVQ_OK || merged) return st;
   const int64_t rows = static_cast<int64_t>(h->cfg.batch) * h->cfg.num_q_heads;
   e = kvq::launch_merge(static_cast<const float*>(scratch), out, static_cast<int>(rows), S, h->cfg.head_dim, s);
   if (e != hipSuccess) return device_error(h, e, "merge kernel launch");

@@ -355,10 +355,15 @@ __device__ __forceinline__ float replica_sum(float x) {
 // the PV weights of the other replicas by DPP row rotation and owns the
 // output; the other replicas' PV columns are never read.
 //
-// decode_split is one workgroup's work: split s of slice `slice`, with the
-// LDS ring at `ring` (ring_bytes<...>() bytes).
-template <int D, int KB, int VB, int G, int GQC, bool TN>
-__device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t slice, const int s, uint8_t* ring) {
+// decode_split is one wave's work: split s of slice `slice`, with the LDS
+// ring at `ring` (ring_bytes<...>() bytes) and, for rotated keys, gqa * D
+// floats at qsh for the query's transform, shared by the workgroup's waves
+// (all of them work on the same slice).  With FUSED the split's (o, m, l)
+// goes to the start of its ring instead of global memory, for the
+// workgroup's own merge (decode_fused_kernel).
+template <int D, int KB, int VB, int G, int GQC, bool TN, bool FUSED = false>
+__device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t slice, const int s, uint8_t* ring,
+                                             float* qsh) {
   using PS = PageShape<D, KB, VB, G, TN>;
   constexpr int NKB = D / 32, NMT = D / 16, NCG = PS::NCG, CPG = PS::CPG;
   constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4;
@@ -370,7 +375,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   // MFMA) when GQC < 16, else as two MFMAs.
   constexpr int NP = GQC < 16 ? 1 : 2;
   const Layout& L = a.L;
-  const int l = threadIdx.x, l16 = l & 15, j = l >> 4;
+  const int l = threadIdx.x & (kLanes - 1), l16 = l & 15, j = l >> 4;
   const int S = a.splits;
   const int b = static_cast<int>(slice / a.Hkv), hkv = static_cast<int>(slice % a.Hkv);
   const int h = l16 % GQC, rp = l16 / GQC;
@@ -391,12 +396,13 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   float qm[NKB][8];
   const float qscale = kLog2e * (D == 128 ? 0.08838834764831845f : 0.125f);
   if (a.rotate) {
-    extern __shared__ float qsh[];  // gqa * D floats, sized at launch
+    // every element and butterfly once per workgroup, spread over its threads
     const int64_t base = (static_cast<int64_t>(b) * a.Hq + hkv * a.gqa) * D;
-    for (int idx = l; idx < a.gqa * D; idx += kLanes) qsh[idx] = load_q(a.q, a.in_dtype, base + idx);
+    const int tid = threadIdx.x, nth = blockDim.x;
+    for (int idx = tid; idx < a.gqa * D; idx += nth) qsh[idx] = load_q(a.q, a.in_dtype, base + idx);
     __syncthreads();
     for (int hh = 1; hh < D; hh <<= 1) {
-      for (int k = l; k < a.gqa * (D / 2); k += kLanes) {
+      for (int k = tid; k < a.gqa * (D / 2); k += nth) {
         int r = k / (D / 2), p = k % (D / 2);
         int i0 = r * D + (p / hh) * 2 * hh + (p % hh);
         float x0 = qsh[i0], x1 = qsh[i0 + hh];
@@ -834,6 +840,23 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   float zsum[NCG];
 #pragma unroll
   for (int i = 0; i < NCG; ++i) zsum[i] = wave_sum_j(replica_sum<R>(zacc[i]));
+  if constexpr (FUSED) {
+    // record [head slot h][D + 4] floats: o, then m and l (the ring's copies
+    // have all landed: the main loop ends with no copy in flight)
+    if (hv && rp == 0) {
+      float* pr = reinterpret_cast<float*>(ring) + h * (D + 4);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int c0 = 16 * mt + 4 * j;
+        *reinterpret_cast<f32x4*>(pr + c0) = acc[mt] + zsum[c0 / G];
+      }
+      if (j == 0) {
+        pr[D] = m;
+        pr[D + 1] = lsum;
+      }
+    }
+    return;
+  }
   if (hv && rp == 0) {
     const int64_t row = static_cast<int64_t>(b) * a.Hq + hq;
     if (a.write_final) {
@@ -864,7 +887,58 @@ template <int D, int KB, int VB, int G, int GQC, bool TN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
 void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[ring_bytes<D, KB, VB, G, TN>()];
-  decode_split<D, KB, VB, G, GQC, TN>(a, blockIdx.x / a.splits, static_cast<int>(blockIdx.x % a.splits), ring);
+  extern __shared__ float qsh[];  // gqa * D floats for rotated keys, sized at launch
+  decode_split<D, KB, VB, G, GQC, TN>(a, blockIdx.x / a.splits, static_cast<int>(blockIdx.x % a.splits), ring, qsh);
+}
+
+// ---- splits merged inside the workgroup --------------------------------------
+// With few splits per slice, the slice's splits run as the waves of one
+// workgroup (wave w = split w), each streaming its range through its own LDS
+// ring; after one barrier the workgroup merges the splits' (o, m, l) records
+// from LDS with the log-sum-exp combination of the merge kernel and writes
+// the output, so the partials never go to memory and no merge launch
+// follows.  The dynamic LDS holds S regions of fused_region_bytes (ring,
+// then the split's record at its start) and the rotated query's gqa * D
+// floats after them.
+template <int D, int KB, int VB, int G, int GQC, bool TN>
+constexpr int fused_region_bytes() {
+  constexpr int rb = ring_bytes<D, KB, VB, G, TN>(), rec = GQC * (D + 4) * 4;
+  return ((rb > rec ? rb : rec) + 15) / 16 * 16;
+}
+
+template <int D, int KB, int VB, int G, int GQC, bool TN>
+__global__ __launch_bounds__(kLanes * kMaxFusedSplits) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
+void decode_fused_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int RW = fused_region_bytes<D, KB, VB, G, GQC, TN>(), Q = D / 4, W = D + 4;
+  const int S = a.splits;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kLanes);
+  float* qsh = reinterpret_cast<float*>(lds + S * RW);
+  const int64_t slice = blockIdx.x;
+  decode_split<D, KB, VB, G, GQC, TN, true>(a, slice, w, lds + w * RW, qsh);
+  __syncthreads();
+  // thread t: channels 4q .. 4q + 3 of head slot hh; M = max_s m_s,
+  // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, and a split with no
+  // tokens (m = -inf) contributes nothing (its o is never read)
+  const int b = static_cast<int>(slice / a.Hkv), hkv = static_cast<int>(slice % a.Hkv);
+  for (int t = threadIdx.x; t < a.gqa * Q; t += blockDim.x) {
+    const int hh = t / Q, q = t % Q;
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, reinterpret_cast<const float*>(lds + sp * RW)[hh * W + D]);
+    float L = 0.0f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < S; ++sp) {
+      const float* pr = reinterpret_cast<const float*>(lds + sp * RW) + hh * W;
+      const float ms = pr[D];
+      if (ms != -INFINITY) {
+        const float ws = __builtin_amdgcn_exp2f(ms - M);
+        L += ws * pr[D + 1];
+        acc += ws * *reinterpret_cast<const f32x4*>(pr + 4 * q);
+      }
+    }
+    const int64_t row = static_cast<int64_t>(b) * a.Hq + hkv * a.gqa + hh;
+    *reinterpret_cast<f32x4*>(a.out + row * D + 4 * q) = acc / L;
+  }
 }
 
 // Groups of several bit widths in one launch: each block looks up its piece
@@ -885,6 +959,7 @@ template <int D, int G, int GQC, bool TN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
 void decode_mixed_kernel(DecodeArgs a, MixedPlan mp) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[mixed_ring_bytes<D, G>()];
+  extern __shared__ float qsh[];  // gqa * D floats for rotated keys, sized at launch
   const int64_t slice = blockIdx.x % a.L.slices;
   const MixedPiece pc = mp.p[blockIdx.x / a.L.slices];
   // the piece's range and slot through the split arithmetic of decode_split:
@@ -900,10 +975,10 @@ void decode_mixed_kernel(DecodeArgs a, MixedPlan mp) {
   r.split_off = pc.slot - s;
   r.do_fp16 = pc.f16 >= 0 ? 1 : 0;
   switch (pc.bits) {
-    case 0x22: decode_split<D, 2, 2, G, GQC, TN>(r, slice, s, ring); break;
-    case 0x24: decode_split<D, 2, 4, G, GQC, TN>(r, slice, s, ring); break;
-    case 0x42: decode_split<D, 4, 2, G, GQC, TN>(r, slice, s, ring); break;
-    default: decode_split<D, 4, 4, G, GQC, TN>(r, slice, s, ring); break;
+    case 0x22: decode_split<D, 2, 2, G, GQC, TN>(r, slice, s, ring, qsh); break;
+    case 0x24: decode_split<D, 2, 4, G, GQC, TN>(r, slice, s, ring, qsh); break;
+    case 0x42: decode_split<D, 4, 2, G, GQC, TN>(r, slice, s, ring, qsh); break;
+    default: decode_split<D, 4, 4, G, GQC, TN>(r, slice, s, ring, qsh); break;
   }
 }
 
@@ -936,7 +1011,87 @@ hipError_t decode_k(const DecodeArgs& a, hipStream_t s) {
   return a.L.kbits == 2 ? decode_v<D, 2>(a, s) : decode_v<D, 4>(a, s);
 }
 
+// The fused launch: one workgroup of S waves per slice.  fused_plan gives
+// its dynamic LDS bytes, or 0 when it does not apply: S not a multiple of 4
+// up to kMaxFusedSplits, more LDS than a workgroup may hold, or fewer waves
+// per CU than the one-wave launch of the same decode (by the runtime's
+// occupancy calculator), so that merging in the workgroup never costs the
+// stream its waves in flight.  Measured on MI355X, workgroups of 2, 3 or 6
+// waves ran 1-33% slower than the one-wave launch at the same split count
+// (175B-shaped MHA layer at 2 splits 973 against 855 us; 32k K4/V2 layer at
+// 6 splits 330 against 302 us): a workgroup's waves do not spread evenly over
+// a CU's four SIMDs unless they come in fours; at 4 splits the 32k layer
+// decodes in 301.5 us merged against 304.2 us with the merge kernel.
+template <int D, int KB, int VB, int G, int GQC, bool TN>
+size_t fused_plan_i(const DecodeArgs& a) {
+  const int S = a.splits;
+  if (S < 4 || S > kMaxFusedSplits || S % 4 != 0) return 0;
+  const size_t qb = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
+  const size_t lds = static_cast<size_t>(S) * fused_region_bytes<D, KB, VB, G, GQC, TN>() + qb;
+  int dev = 0, max_lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      lds > static_cast<size_t>(max_lds))
+    return 0;
+  int nf = 0, n1 = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, decode_fused_kernel<D, KB, VB, G, GQC, TN>, kLanes * S, lds) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n1, decode_kernel<D, KB, VB, G, GQC, TN>, kLanes, qb) != hipSuccess)
+    return 0;
+  return nf * S >= n1 ? lds : 0;
+}
+
+template <int D, int KB, int VB, int G, int GQC, bool TN>
+hipError_t fused_launch_i(const DecodeArgs& a, hipStream_t s) {
+  const size_t lds = fused_plan_i<D, KB, VB, G, GQC, TN>(a);
+  if (lds == 0) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_fused_kernel<D, KB, VB, G, GQC, TN>), dim3(static_cast<unsigned>(a.L.slices)),
+                     dim3(kLanes * a.splits), lds, s, a);
+  return hipGetLastError();
+}
+
+// Calls F<D, KB, VB, G, GQC, TN>::run(a, x...) for the instance that serves a.
+template <template <int, int, int, int, int, bool> class F, typename... X>
+auto instance_of(const DecodeArgs& a, X... x) {
+  auto gq = [&](auto d, auto kb, auto vb, auto g, auto tn) {
+    constexpr int D_ = decltype(d)::value, KB_ = decltype(kb)::value, VB_ = decltype(vb)::value;
+    constexpr int G_ = decltype(g)::value;
+    constexpr bool TN_ = decltype(tn)::value;
+    if (a.gqa <= 4) return F<D_, KB_, VB_, G_, 4, TN_>::run(a, x...);
+    if (a.gqa <= 8) return F<D_, KB_, VB_, G_, 8, TN_>::run(a, x...);
+    return F<D_, KB_, VB_, G_, 16, TN_>::run(a, x...);
+  };
+  using std::integral_constant;
+  auto tn = [&](auto d, auto kb, auto vb, auto g) {
+    return a.L.token_norm ? gq(d, kb, vb, g, integral_constant<bool, true>{})
+                          : gq(d, kb, vb, g, integral_constant<bool, false>{});
+  };
+  auto gg = [&](auto d, auto kb, auto vb) {
+    return a.L.G == 32 ? tn(d, kb, vb, integral_constant<int, 32>{}) : tn(d, kb, vb, integral_constant<int, 64>{});
+  };
+  auto vv = [&](auto d, auto kb) {
+    return a.L.vbits == 2 ? gg(d, kb, integral_constant<int, 2>{}) : gg(d, kb, integral_constant<int, 4>{});
+  };
+  auto kk = [&](auto d) {
+    return a.L.kbits == 2 ? vv(d, integral_constant<int, 2>{}) : vv(d, integral_constant<int, 4>{});
+  };
+  return a.L.D == 64 ? kk(integral_constant<int, 64>{}) : kk(integral_constant<int, 128>{});
+}
+
+template <int D, int KB, int VB, int G, int GQC, bool TN>
+struct FusedPlan {
+  static size_t run(const DecodeArgs& a) { return fused_plan_i<D, KB, VB, G, GQC, TN>(a); }
+};
+template <int D, int KB, int VB, int G, int GQC, bool TN>
+struct FusedLaunch {
+  static hipError_t run(const DecodeArgs& a, hipStream_t s) { return fused_launch_i<D, KB, VB, G, GQC, TN>(a, s); }
+};
+
 }  // namespace
+
+size_t decode_fused_lds(const DecodeArgs& a) { return instance_of<FusedPlan>(a); }
+
+hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t s) { return instance_of<FusedLaunch>(a, s); }
 
 bool decode_supported(int D, int kbits, int vbits, int G) {
   return (D == 64 || D == 128) && (kbits == 2 || kbits == 4) && (vbits == 2 || vbits == 4) &&

@@ -98,6 +98,14 @@ hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_flush(const AppendArgs& a, hipStream_t s);
 hipError_t launch_window_write(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// A decode of one launch (every group of one width) whose slices have 4 or
+// 8 splits can run each slice's splits as the waves of one workgroup, merged
+// in LDS, writing `out` directly (partial unused).  decode_fused_lds: that
+// launch's dynamic LDS bytes, 0 when it does not apply or would hold fewer
+// waves per CU than launch_decode.
+constexpr int kMaxFusedSplits = 8;
+size_t decode_fused_lds(const DecodeArgs& a);
+hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t s);
 // a: splits_total (= npieces), L (any of the widths' layouts) and the common fields
 hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedPlan& mp, hipStream_t s);
 hipError_t launch_merge(const float* partial, float* out, int rows, int splits, int D, hipStream_t s);

@@ -57,6 +57,7 @@ SIGNATURES = {
     "kvq_decode_attn_noalloc": (ctypes.c_int, [_P, _P, _P, _P]),
     "kvq_default_splits": (_I32, [_P]),
     "kvq_decode_partials": (ctypes.c_int, [_P, _P, _P, _SZ, _I32, ctypes.POINTER(_I32), _P]),
+    "kvq_decode_plan": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "kvq_merge_partials": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P]),
     "kvq_num_tokens": (_I64, [_P]),
     "kvq_num_quantized": (_I64, [_P]),
@@ -263,6 +264,14 @@ class KVQCache:
 
     def default_splits(self) -> int:
         return int(lib.kvq_default_splits(self.h))
+
+    def decode_plan(self, splits: int | None = None) -> tuple[int, bool]:
+        """(split count, merged inside the decode kernel) of decode(q, splits=splits)
+        on the current tokens; nothing is launched."""
+        S_req = self.default_splits() if splits is None else splits
+        used, merged = ctypes.c_int32(0), ctypes.c_int32(0)
+        check(lib.kvq_decode_plan(self.h, S_req, ctypes.byref(used), ctypes.byref(merged)), "kvq_decode_plan")
+        return int(used.value), bool(merged.value)
 
     def append(self, k, v, stream=None) -> None:
         """k, v: [B, H_kv, T, D] contiguous, the config dtype, on the cache's device."""

@@ -130,7 +130,12 @@ kvq_status kvq_append(kvq_cache* cache, const void* k, const void* v, int32_t n_
  *   workspace: device scratch of ws_bytes >= kvq_workspace_bytes(cfg); its
  *        contents on entry do not matter and are clobbered.
  * The split count over the token axis is chosen from the cache shape and the
- * number of compute units.  Requires at least one cached token
+ * number of compute units.  When every group has the same bits and a slice
+ * has 4 or 8 splits, the splits of a slice run as the waves of one workgroup
+ * and are merged there (the cross-split combination of kvq_merge_partials,
+ * in LDS), unless that launch would hold fewer waves per compute unit; the
+ * workspace is then not touched and no merge kernel follows
+ * (kvq_decode_plan tells which).  Requires at least one cached token
  * (KVQ_E_STATE otherwise). */
 kvq_status kvq_decode_attn(kvq_cache* cache, const void* q, float* out, void* workspace, size_t ws_bytes,
                            void* stream);
@@ -163,6 +168,15 @@ kvq_status kvq_decode_attn_noalloc(kvq_cache* cache, const void* q, float* out, 
  * floating-point summation order. */
 kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, void* workspace, size_t ws_bytes,
                                   int32_t num_splits, void* stream);
+
+/* How kvq_decode_attn_splits(num_splits) would run on the cache's current
+ * tokens, without launching anything: *splits_used receives the split count
+ * S, *merged_in_kernel 1 when the decode writes `out` itself (one split, or
+ * the splits of each slice merged inside the decode kernel) and 0 when a
+ * merge of S partials per row follows.  Either pointer may be NULL.
+ * KVQ_E_STATE on an empty cache, KVQ_E_ARG for a split count outside
+ * [1, S_max]; the split count of kvq_decode_attn is kvq_default_splits. */
+kvq_status kvq_decode_plan(kvq_cache* cache, int32_t num_splits, int32_t* splits_used, int32_t* merged_in_kernel);
 
 /* The two halves of kvq_decode_attn, for callers that merge partial results
  * themselves (e.g. several caches holding disjoint token ranges of the same
