@@ -356,7 +356,13 @@ int64_t kvq_num_quantized(const kvq_cache* h) {
 
 namespace {
 
-kvq_status append_impl(kvq_cache* h, const void* k, const void* v, int32_t n_tokens, void* stream) {
+// deferred: when not null and the call appends one token that goes to the
+// fp16 window (not the sink, not flushed) of a cache without key rotation or
+// position-adaptive widths, the window write is left to the decode that
+// follows (the token's position is returned; the decode must run), else -1.
+kvq_status append_impl(kvq_cache* h, const void* k, const void* v, int32_t n_tokens, void* stream,
+                       int64_t* deferred = nullptr) {
+  if (deferred) *deferred = -1;
   kvq_status st = check_handle(h);
   if (st != KVQ_OK) return st;
   if (n_tokens < 0) return fail(KVQ_E_ARG, "n_tokens %d < 0", n_tokens);
@@ -410,8 +416,13 @@ kvq_status append_impl(kvq_cache* h, const void* k, const void* v, int32_t n_tok
     e = kvq::launch_flush(ar, s);
     if (e != hipSuccess) return device_error(h, e, "flush kernel launch");
   }
-  e = kvq::launch_window_write(a, s);
-  if (e != hipSuccess) return device_error(h, e, "window write kernel launch");
+  if (deferred && n_tokens == 1 && !c.rotate && c.adapt_delta == 0 && a.n_sink_write == 0 && a.n_write == 1 &&
+      a.w_first == h->n) {
+    *deferred = h->n;
+  } else {
+    e = kvq::launch_window_write(a, s);
+    if (e != hipSuccess) return device_error(h, e, "window write kernel launch");
+  }
   h->n = n_new;
   return ok();
 }
@@ -509,8 +520,10 @@ kvq_status plan_splits(kvq_cache* h, int32_t num_splits, bool allow_fused, Split
 // bits).  allow_final selects direct output when the whole decode is one
 // split, or one run whose few splits per slice are merged inside the
 // workgroup; *merged tells the caller that `out` is written (no merge left).
+using kvq::NewToken;
 kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partials, size_t bytes, int32_t num_splits,
-                         bool allow_final, int32_t* splits_used, bool* merged, hipStream_t s, bool noalloc = false) {
+                         bool allow_final, int32_t* splits_used, bool* merged, hipStream_t s, bool noalloc = false,
+                         NewToken nt = NewToken{}) {
   if (merged) *merged = false;
   SplitPlan p;
   kvq_status st = plan_splits(h, num_splits, allow_final, &p);
@@ -552,7 +565,7 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
       a.groups_per_split = p.gps[i];
       a.split_off = static_cast<int>(off);
       a.do_fp16 = i == fp16_run ? 1 : 0;
-      e = p.fused ? kvq::launch_decode_fused(a, s) : kvq::launch_decode(a, s);
+      e = p.fused ? kvq::launch_decode_fused(a, nt, s) : kvq::launch_decode(a, nt, s);
       if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
       off += p.sp[i];
     }
@@ -615,9 +628,15 @@ kvq_status append_decode(kvq_cache* h, const void* k, const void* v, const void*
   if (allow_final && (!out || !aligned(out, 16))) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
   if (static_cast<int64_t>(runs_of(h, 0, ngroups_of(h)).size()) + 1 > max_splits(&c))
     return fail(KVQ_E_UNSUPPORTED, "runs of equal bit widths exceed the split maximum %d", max_splits(&c));
-  st = append_impl(h, k, v, 1, s);
+  // the token's window write goes with the decode when it can (one launch
+  // fewer per step); the decode below then must run, and everything it could
+  // reject was checked above
+  int64_t deferred = -1;
+  st = append_impl(h, k, v, 1, s, &deferred);
   if (st != KVQ_OK) return st;
-  return launch_splits(h, q, out, partials, bytes, num_splits, allow_final, splits_used, merged, s);
+  NewToken nt;
+  if (deferred >= 0) nt = NewToken{k, v, deferred};
+  return launch_splits(h, q, out, partials, bytes, num_splits, allow_final, splits_used, merged, s, false, nt);
 }
 }  // namespace
 

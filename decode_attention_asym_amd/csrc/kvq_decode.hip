@@ -273,13 +273,17 @@ constexpr int kp_after(int ch) {
 template <int CPG>
 constexpr int param_buffers(int n) { return CPG == 1 ? n : n / CPG + 1; }
 // Chunks in flight per wave: as many as fit, with their parameter buffers, in
-// 12800 bytes of LDS, so that twelve waves (three per SIMD) fit in a CU's
-// 160 KiB: measured on gfx950, 13312 bytes per workgroup already cost a
-// workgroup slot per CU (allocation is rounded up beyond the byte count).
-template <int SLOT, int PB, int CPG>
+// BUDGET bytes of LDS.  The one-wave launches take 12800 bytes, so that
+// twelve waves (three per SIMD) fit in a CU's 160 KiB: measured on gfx950,
+// 13312 bytes per workgroup already cost a workgroup slot per CU (allocation
+// is rounded up beyond the byte count).
+constexpr int kRingBudget = 12800;
+// LDS ring budget per wave of the workgroup-merged launch
+constexpr int kFusedRingBudget = 12800;
+template <int SLOT, int PB, int CPG, int BUDGET = kRingBudget>
 constexpr int ring_depth() {
   int n = 2;
-  while ((n + 1) * SLOT + param_buffers<CPG>(n + 1) * PB <= 12800) ++n;
+  while ((n + 1) * SLOT + param_buffers<CPG>(n + 1) * PB <= BUDGET) ++n;
   return n;
 }
 template <int N>
@@ -303,11 +307,11 @@ struct PageShape {
 };
 
 // LDS bytes of the chunk ring and parameter buffers of one page shape.
-template <int D, int KB, int VB, int G, bool TN>
+template <int D, int KB, int VB, int G, bool TN, int BUDGET = kRingBudget>
 constexpr int ring_bytes() {
   using PS = PageShape<D, KB, VB, G, TN>;
   constexpr int SLOT = PS::KC + PS::VC;
-  constexpr int n = ring_depth<SLOT, PS::PB, PS::CPG>();
+  constexpr int n = ring_depth<SLOT, PS::PB, PS::CPG, BUDGET>();
   return n * SLOT + param_buffers<PS::CPG>(n) * PS::PB;
 }
 
@@ -341,6 +345,58 @@ __device__ __forceinline__ float replica_sum(float x) {
   return x;
 }
 
+// The token this step appends when its fp16 window write is left to the
+// decode (kvq_append_decode_attn): the wave whose window chunks include its
+// position first stages its key and value rows in its LDS ring (free once the
+// ring's copies are done), as fp16 rounded to nearest even from binary32 like
+// the window write does: lane l converts elements 2l and 2l + 1 of each row
+// (rows of new_k / new_v are [B][H_kv][1][D]).  In that chunk the lanes whose
+// key or value elements belong to the token then take them from LDS instead
+// of the cache and store them to the window (take_new_keys, take_new_value).
+template <int D>
+__device__ __forceinline__ void stage_new_token(const NewToken& nt, int in_dtype, int64_t slice, uint8_t* ring) {
+  const int l = threadIdx.x & (kLanes - 1);
+  if (2 * l < D) {
+    const int64_t i = slice * D + 2 * l;
+    uint32_t kh, vh;
+    if (in_dtype == 0) {
+      const float* k = static_cast<const float*>(nt.k) + i;
+      const float* v = static_cast<const float*>(nt.v) + i;
+      kh = pack_h2(k[0], k[1]);
+      vh = pack_h2(v[0], v[1]);
+    } else {
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(nt.k) + i);
+      const uint32_t vw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(nt.v) + i);
+      kh = in_dtype == 1 ? kw : pack_h2(__uint_as_float(kw << 16), __uint_as_float(kw & 0xffff0000u));
+      vh = in_dtype == 1 ? vw : pack_h2(__uint_as_float(vw << 16), __uint_as_float(vw & 0xffff0000u));
+    }
+    *reinterpret_cast<uint32_t*>(ring + 4 * l) = kh;
+    *reinterpret_cast<uint32_t*>(ring + 2 * D + 4 * l) = vh;
+  }
+}
+// Keys: the lanes of token column t % 16 hold channels 32 kb + 8 j .. + 7 of
+// tile t / 16 in one 16-byte operand.
+template <int D>
+__device__ __forceinline__ void take_new_keys(const uint8_t* staged, uint8_t* rch, int t, int l, int kb, u32x4& k0,
+                                              u32x4& k1) {
+  constexpr int NKB = D / 32;
+  const int tile = t >> 4, j = l >> 4;
+  const u32x4 w = *reinterpret_cast<const u32x4*>(staged + 2 * (32 * kb + 8 * j));
+  if (tile == 0) k0 = w; else k1 = w;
+  *reinterpret_cast<u32x4*>(rch + ((tile * NKB + kb) * kLanes + l) * 16) = w;
+}
+// Values: lane group j with tau(j, e) = t holds element e of channel
+// 16 mt + l % 16 in operand mt.
+template <int D>
+__device__ __forceinline__ void take_new_value(const uint8_t* staged, uint8_t* rch, int e, int l, int mt, u32x4& vw) {
+  const uint32_t h = *reinterpret_cast<const uint16_t*>(staged + 2 * D + 2 * (16 * mt + (l & 15)));
+  const int hi = e & 1, dw = e >> 1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (k == dw) vw[k] = hi ? ((vw[k] & 0xffffu) | (h << 16)) : ((vw[k] & 0xffff0000u) | h);
+  *reinterpret_cast<uint16_t*>(rch + kChunk * D * 2 + (mt * kLanes + l) * 16 + 2 * e) = static_cast<uint16_t>(h);
+}
+
 // Column layout.  Lane l holds MFMA column l16 = l % 16 and lane group
 // j = l / 16.  The gqa query heads of the slice take head slots 0..GQC-1
 // (GQC = 4 for gqa <= 4, 8 for gqa = 8, 16 for gqa = 16); the 16 columns hold
@@ -360,10 +416,12 @@ __device__ __forceinline__ float replica_sum(float x) {
 // floats at qsh for the query's transform, shared by the workgroup's waves
 // (all of them work on the same slice).  With FUSED the split's (o, m, l)
 // goes to the start of its ring instead of global memory, for the
-// workgroup's own merge (decode_fused_kernel).
-template <int D, int KB, int VB, int G, int GQC, bool TN, bool FUSED = false>
+// workgroup's own merge (decode_fused_kernel).  NEWTOK: the window pass takes
+// a deferred appended token from the step's input (DecodeArgs::new_pos); the
+// mixed-width kernel, whose caches never defer it, is built without it.
+template <int D, int KB, int VB, int G, int GQC, bool TN, bool FUSED = false, bool NEWTOK = true>
 __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t slice, const int s, uint8_t* ring,
-                                             float* qsh) {
+                                             float* qsh, const NewToken& nt) {
   using PS = PageShape<D, KB, VB, G, TN>;
   constexpr int NKB = D / 32, NMT = D / 16, NCG = PS::NCG, CPG = PS::CPG;
   constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4;
@@ -534,9 +592,10 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   constexpr int SLOT = KC + VC;
   // NBUF chunks are in flight; a group's parameters stay until its last chunk
   // has read them, and the refill that reuses a buffer comes after that read.
-  constexpr int NBUF = ring_depth<SLOT, PB, CPG>(), NPB = param_buffers<CPG>(NBUF);
+  constexpr int BUDGET = FUSED ? kFusedRingBudget : kRingBudget;
+  constexpr int NBUF = ring_depth<SLOT, PB, CPG, BUDGET>(), NPB = param_buffers<CPG>(NBUF);
   constexpr int NBASE = dma_count<KC>() + dma_count<VC>(), NKP = dma_count<PB>();
-  static_assert(NBUF * SLOT + NPB * PB == ring_bytes<D, KB, VB, G, TN>(), "ring size");
+  static_assert(NBUF * SLOT + NPB * PB == ring_bytes<D, KB, VB, G, TN, BUDGET>(), "ring size");
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((KVQ_AS3 uint8_t*)ring));
   const uint32_t pbuf_lds = ring_lds + NBUF * SLOT;
   const uint32_t lane16 = static_cast<uint32_t>(l) * 16, lane4 = static_cast<uint32_t>(l) * 4;
@@ -766,14 +825,35 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   // the end of the kernel
   {
     const int64_t nfc = a.do_fp16 ? a.nsc + (a.rc1 - a.rc0) : 0;
+    // the deferred appended token, when one of this split's window chunks
+    // holds it: staged in the ring (its copies are done: the loop above ends
+    // with none in flight)
+    int64_t new_rc = -1;
+    if constexpr (NEWTOK) {
+      if (nt.pos >= 0) {
+        const int64_t fcn = a.nsc + (nt.pos / kChunk - a.rc0), f0 = S - 1 - s;
+        if (fcn >= f0 && fcn < nfc && (fcn - f0) % S == 0) {
+          new_rc = nt.pos / kChunk;
+          stage_new_token<D>(nt, a.in_dtype, slice, ring);
+        }
+      }
+    }
     for (int64_t fc = S - 1 - s; fc < nfc; fc += S) {
       const int64_t rc = fc < a.nsc ? fc : a.rc0 + (fc - a.nsc);  // absolute chunk index
-      const uint8_t* rch = a.cache + fp16_chunk_offset(L, slice, rc * kChunk);
+      uint8_t* rch = a.cache + fp16_chunk_offset(L, slice, rc * kChunk);
+      const int64_t pos0 = rc * kChunk;
+      // the step's appended token, when its window write was left to the
+      // decode and it falls in this chunk: token tn of the chunk
+      const int tn = NEWTOK && rc == new_rc ? static_cast<int>(nt.pos - pos0) : -1;
+      const bool new_keys = tn >= 0 && l16 == (tn & 15);
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const half8 a0 = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(rch + ((0 * NKB + kb) * kLanes + l) * 16));
-        const half8 a1 = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(rch + ((1 * NKB + kb) * kLanes + l) * 16));
+        u32x4 k0 = *reinterpret_cast<const u32x4*>(rch + ((0 * NKB + kb) * kLanes + l) * 16);
+        u32x4 k1 = *reinterpret_cast<const u32x4*>(rch + ((1 * NKB + kb) * kLanes + l) * 16);
+        if (new_keys) take_new_keys<D>(ring, rch, tn, l, kb, k0, k1);
+        const half8 a0 = __builtin_bit_cast(half8, k0);
+        const half8 a1 = __builtin_bit_cast(half8, k1);
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp) {
           const half8 bb = __builtin_bit_cast(half8, u32x4{qz[pp][kb][0], qz[pp][kb][1], qz[pp][kb][2], qz[pp][kb][3]});
@@ -781,7 +861,6 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
           c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bb, c1, 0, 0, 0);
         }
       }
-      const int64_t pos0 = rc * kChunk;
       const bool partial = pos0 + kChunk > a.n;
       float sc[8];
 #pragma unroll
@@ -822,9 +901,13 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       uint32_t bpr[2][4];
       gather_pairs(ph, bpr[0]);
       gather_pairs(pl, bpr[1]);
+      int jv = -1, ev = 0;
+      if (tn >= 0) tau_inv(tn, &jv, &ev);
+      const bool new_values = j == jv;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         u32x4 vwd = *reinterpret_cast<const u32x4*>(rch + kChunk * D * 2 + (mt * kLanes + l) * 16);
+        if (new_values) take_new_value<D>(ring, rch, ev, l, mt, vwd);
         vwd[0] &= vmask[0]; vwd[1] &= vmask[1]; vwd[2] &= vmask[2]; vwd[3] &= vmask[3];
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
@@ -885,10 +968,10 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
 
 template <int D, int KB, int VB, int G, int GQC, bool TN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
-void decode_kernel(DecodeArgs a) {
+void decode_kernel(DecodeArgs a, NewToken nt) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[ring_bytes<D, KB, VB, G, TN>()];
   extern __shared__ float qsh[];  // gqa * D floats for rotated keys, sized at launch
-  decode_split<D, KB, VB, G, GQC, TN>(a, blockIdx.x / a.splits, static_cast<int>(blockIdx.x % a.splits), ring, qsh);
+  decode_split<D, KB, VB, G, GQC, TN>(a, blockIdx.x / a.splits, static_cast<int>(blockIdx.x % a.splits), ring, qsh, nt);
 }
 
 // ---- splits merged inside the workgroup --------------------------------------
@@ -902,20 +985,20 @@ void decode_kernel(DecodeArgs a) {
 // floats after them.
 template <int D, int KB, int VB, int G, int GQC, bool TN>
 constexpr int fused_region_bytes() {
-  constexpr int rb = ring_bytes<D, KB, VB, G, TN>(), rec = GQC * (D + 4) * 4;
+  constexpr int rb = ring_bytes<D, KB, VB, G, TN, kFusedRingBudget>(), rec = GQC * (D + 4) * 4;
   return ((rb > rec ? rb : rec) + 15) / 16 * 16;
 }
 
 template <int D, int KB, int VB, int G, int GQC, bool TN>
 __global__ __launch_bounds__(kLanes * kMaxFusedSplits) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
-void decode_fused_kernel(DecodeArgs a) {
+void decode_fused_kernel(DecodeArgs a, NewToken nt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int RW = fused_region_bytes<D, KB, VB, G, GQC, TN>(), Q = D / 4, W = D + 4;
   const int S = a.splits;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kLanes);
   float* qsh = reinterpret_cast<float*>(lds + S * RW);
   const int64_t slice = blockIdx.x;
-  decode_split<D, KB, VB, G, GQC, TN, true>(a, slice, w, lds + w * RW, qsh);
+  decode_split<D, KB, VB, G, GQC, TN, true>(a, slice, w, lds + w * RW, qsh, nt);
   __syncthreads();
   // thread t: channels 4q .. 4q + 3 of head slot hh; M = max_s m_s,
   // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, and a split with no
@@ -975,48 +1058,28 @@ void decode_mixed_kernel(DecodeArgs a, MixedPlan mp) {
   r.split_off = pc.slot - s;
   r.do_fp16 = pc.f16 >= 0 ? 1 : 0;
   switch (pc.bits) {
-    case 0x22: decode_split<D, 2, 2, G, GQC, TN>(r, slice, s, ring, qsh); break;
-    case 0x24: decode_split<D, 2, 4, G, GQC, TN>(r, slice, s, ring, qsh); break;
-    case 0x42: decode_split<D, 4, 2, G, GQC, TN>(r, slice, s, ring, qsh); break;
-    default: decode_split<D, 4, 4, G, GQC, TN>(r, slice, s, ring, qsh); break;
+    case 0x22: decode_split<D, 2, 2, G, GQC, TN, false, false>(r, slice, s, ring, qsh, NewToken{}); break;
+    case 0x24: decode_split<D, 2, 4, G, GQC, TN, false, false>(r, slice, s, ring, qsh, NewToken{}); break;
+    case 0x42: decode_split<D, 4, 2, G, GQC, TN, false, false>(r, slice, s, ring, qsh, NewToken{}); break;
+    default: decode_split<D, 4, 4, G, GQC, TN, false, false>(r, slice, s, ring, qsh, NewToken{}); break;
   }
 }
 
-template <int D, int KB, int VB, int G, bool TN>
-hipError_t decode_tn(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(a.L.slices * a.splits));
+// The one-wave launch: one workgroup of one wave per (slice, split).
+template <int D, int KB, int VB, int G, int GQC, bool TN>
+hipError_t one_wave_launch_i(const DecodeArgs& a, const NewToken& nt, hipStream_t s) {
   const size_t lds = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
-  if (a.gqa <= 4)
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 4, TN>), grid, dim3(kLanes), lds, s, a);
-  else if (a.gqa <= 8)
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 8, TN>), grid, dim3(kLanes), lds, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, 16, TN>), grid, dim3(kLanes), lds, s, a);
+  hipLaunchKernelGGL((decode_kernel<D, KB, VB, G, GQC, TN>), dim3(static_cast<unsigned>(a.L.slices * a.splits)),
+                     dim3(kLanes), lds, s, a, nt);
   return hipGetLastError();
-}
-template <int D, int KB, int VB, int G>
-hipError_t decode_t(const DecodeArgs& a, hipStream_t s) {
-  return a.L.token_norm ? decode_tn<D, KB, VB, G, true>(a, s) : decode_tn<D, KB, VB, G, false>(a, s);
-}
-template <int D, int KB, int VB>
-hipError_t decode_g(const DecodeArgs& a, hipStream_t s) {
-  return a.L.G == 32 ? decode_t<D, KB, VB, 32>(a, s) : decode_t<D, KB, VB, 64>(a, s);
-}
-template <int D, int KB>
-hipError_t decode_v(const DecodeArgs& a, hipStream_t s) {
-  return a.L.vbits == 2 ? decode_g<D, KB, 2>(a, s) : decode_g<D, KB, 4>(a, s);
-}
-template <int D>
-hipError_t decode_k(const DecodeArgs& a, hipStream_t s) {
-  return a.L.kbits == 2 ? decode_v<D, 2>(a, s) : decode_v<D, 4>(a, s);
 }
 
 // The fused launch: one workgroup of S waves per slice.  fused_plan gives
 // its dynamic LDS bytes, or 0 when it does not apply: S not a multiple of 4
-// up to kMaxFusedSplits, more LDS than a workgroup may hold, or fewer waves
-// per CU than the one-wave launch of the same decode (by the runtime's
-// occupancy calculator), so that merging in the workgroup never costs the
-// stream its waves in flight.  Measured on MI355X, workgroups of 2, 3 or 6
+// up to kMaxFusedSplits, more LDS than a workgroup may hold, or (by the
+// runtime's occupancy calculator) neither one pass of the CUs for all slices
+// nor as many waves per CU as the one-wave launch of the same decode, so that
+// merging in the workgroup never costs the stream its waves in flight.  Measured on MI355X, workgroups of 2, 3 or 6
 // waves ran 1-33% slower than the one-wave launch at the same split count
 // (175B-shaped MHA layer at 2 splits 973 against 855 us; 32k K4/V2 layer at
 // 6 splits 330 against 302 us): a workgroup's waves do not spread evenly over
@@ -1028,9 +1091,10 @@ size_t fused_plan_i(const DecodeArgs& a) {
   if (S < 4 || S > kMaxFusedSplits || S % 4 != 0) return 0;
   const size_t qb = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
   const size_t lds = static_cast<size_t>(S) * fused_region_bytes<D, KB, VB, G, GQC, TN>() + qb;
-  int dev = 0, max_lds = 0;
+  int dev = 0, max_lds = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       lds > static_cast<size_t>(max_lds))
     return 0;
   int nf = 0, n1 = 0;
@@ -1038,15 +1102,16 @@ size_t fused_plan_i(const DecodeArgs& a) {
           hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&n1, decode_kernel<D, KB, VB, G, GQC, TN>, kLanes, qb) != hipSuccess)
     return 0;
-  return nf * S >= n1 ? lds : 0;
+  const bool one_pass = static_cast<int64_t>(nf) * cus >= a.L.slices;
+  return one_pass || nf * S >= n1 ? lds : 0;
 }
 
 template <int D, int KB, int VB, int G, int GQC, bool TN>
-hipError_t fused_launch_i(const DecodeArgs& a, hipStream_t s) {
+hipError_t fused_launch_i(const DecodeArgs& a, const NewToken& nt, hipStream_t s) {
   const size_t lds = fused_plan_i<D, KB, VB, G, GQC, TN>(a);
   if (lds == 0) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_fused_kernel<D, KB, VB, G, GQC, TN>), dim3(static_cast<unsigned>(a.L.slices)),
-                     dim3(kLanes * a.splits), lds, s, a);
+                     dim3(kLanes * a.splits), lds, s, a, nt);
   return hipGetLastError();
 }
 
@@ -1084,22 +1149,32 @@ struct FusedPlan {
 };
 template <int D, int KB, int VB, int G, int GQC, bool TN>
 struct FusedLaunch {
-  static hipError_t run(const DecodeArgs& a, hipStream_t s) { return fused_launch_i<D, KB, VB, G, GQC, TN>(a, s); }
+  static hipError_t run(const DecodeArgs& a, const NewToken& nt, hipStream_t s) {
+    return fused_launch_i<D, KB, VB, G, GQC, TN>(a, nt, s);
+  }
+};
+template <int D, int KB, int VB, int G, int GQC, bool TN>
+struct OneWaveLaunch {
+  static hipError_t run(const DecodeArgs& a, const NewToken& nt, hipStream_t s) {
+    return one_wave_launch_i<D, KB, VB, G, GQC, TN>(a, nt, s);
+  }
 };
 
 }  // namespace
 
 size_t decode_fused_lds(const DecodeArgs& a) { return instance_of<FusedPlan>(a); }
 
-hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t s) { return instance_of<FusedLaunch>(a, s); }
+hipError_t launch_decode_fused(const DecodeArgs& a, const NewToken& nt, hipStream_t s) {
+  return instance_of<FusedLaunch>(a, nt, s);
+}
 
 bool decode_supported(int D, int kbits, int vbits, int G) {
   return (D == 64 || D == 128) && (kbits == 2 || kbits == 4) && (vbits == 2 || vbits == 4) &&
          (G == 32 || G == 64) && G <= D;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  return a.L.D == 64 ? decode_k<64>(a, s) : decode_k<128>(a, s);
+hipError_t launch_decode(const DecodeArgs& a, const NewToken& nt, hipStream_t s) {
+  return instance_of<OneWaveLaunch>(a, nt, s);
 }
 
 namespace {

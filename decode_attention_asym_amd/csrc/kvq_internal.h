@@ -50,7 +50,7 @@ struct DriftArgs {
 };
 
 struct DecodeArgs {
-  const uint8_t* cache;
+  uint8_t* cache;       // the decode writes only the window slots of a NewToken
   Layout L;
   const void* q;        // [B][H_q][D] in_dtype
   int in_dtype;
@@ -97,7 +97,16 @@ hipError_t noalloc_scratch(void** ptr);
 // Both return hipSuccess or the launch error.
 hipError_t launch_flush(const AppendArgs& a, hipStream_t s);
 hipError_t launch_window_write(const AppendArgs& a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// The token appended by a step whose fp16 window write is left to the decode
+// (pos >= 0: its position, a window position): k and v ([B][H_kv][1][D],
+// in_dtype) hold it; the wave whose window chunk holds the position takes it
+// from there instead of the cache and stores it to the window.
+struct NewToken {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int64_t pos = -1;
+};
+hipError_t launch_decode(const DecodeArgs& a, const NewToken& nt, hipStream_t s);
 // A decode of one launch (every group of one width) whose slices have 4 or
 // 8 splits can run each slice's splits as the waves of one workgroup, merged
 // in LDS, writing `out` directly (partial unused).  decode_fused_lds: that
@@ -105,7 +114,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // waves per CU than launch_decode.
 constexpr int kMaxFusedSplits = 8;
 size_t decode_fused_lds(const DecodeArgs& a);
-hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_fused(const DecodeArgs& a, const NewToken& nt, hipStream_t s);
 // a: splits_total (= npieces), L (any of the widths' layouts) and the common fields
 hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedPlan& mp, hipStream_t s);
 hipError_t launch_merge(const float* partial, float* out, int rows, int splits, int D, hipStream_t s);

@@ -78,9 +78,10 @@ def test_full_size_every_slice(idx):
 
 
 def test_70b_append_decode_steps_cross_flushes():
-    """The 70B-shaped 128k workload's step loop: 64 steps of append(1) +
-    decode, two group flushes (G = 32) on the way; the decode of every
-    sequence checked at steps that straddle a flush, every slice's cache
+    """The 70B-shaped 128k workload's step loop: 64 one-call steps
+    (kvq_append_decode_attn: append one token, whose window write the decode
+    does, then decode), two group flushes (G = 32) on the way; the decode of
+    every sequence checked at steps that straddle a flush, every slice's cache
     contents bit-exact at those steps."""
     import decode_attention_asym_amd as kvq
 
@@ -95,9 +96,8 @@ def test_70b_append_decode_steps_cross_flushes():
         k, v = syn.step_kv(i)
         ks.append(k)
         vs.append(v)
-        cache.append(k, v)
         q = syn.q(i)
-        out = cache.decode(q)
+        out = cache.append_decode(k, v, q)
         if i in (0, 30, 31, 32, 63):
             torch.cuda.synchronize()
             log(f"[steps] step {i}: n={cache.num_tokens} nq={cache.num_quantized}")
