@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the quantized-KV decode attention path on one MI355X.
 
-A step is one pass of the whole hot path on one batch: append one token per
-sequence (entry conversion, fp16 window write, and a group flush whenever the
-window fills) and decode attention of one query per head over the whole
-cache (split kernel + cross-split merge).  Inputs are seeded synthetic
-tensors already resident in HBM; the cache is prefilled before timing.
+A step is one pass of the whole hot path on one batch, one call of
+kvq_append_decode_attn: append one token per sequence (entry conversion, the
+fp16 window write -- done by the decode kernel when the token goes to the
+window -- and a group flush whenever the window fills) and decode attention
+of one query per head over the whole cache (split kernel and cross-split
+merge, inside the kernel's workgroups or by a merge kernel).  Inputs are
+seeded synthetic tensors already resident in HBM; the cache is prefilled
+before timing.
 
 Prints one JSON line.  `value` is achieved HBM throughput of the whole step
 (algorithmic bytes: packed codes + fp16 scales/zeros + fp16 window + q + out
@@ -321,6 +324,17 @@ def main() -> int:
     S_used, merged = cache.decode_plan(S)
 
     def step(i):
+        # one decode step: kvq_append_decode_attn (append one token, whose
+        # window write the decode kernel does, then decode); with an explicit
+        # --splits, kvq_append then kvq_decode_attn_splits
+        k, v = step_kv[i]
+        if args.splits:
+            cache.append(k, v)
+            cache.decode(qs[i], out, splits=S)
+        else:
+            cache.append_decode(k, v, qs[i], out)
+
+    def step_separate(i):
         k, v = step_kv[i]
         cache.append(k, v)
         cache.decode(qs[i], out, splits=S)
@@ -341,14 +355,15 @@ def main() -> int:
     torch.cuda.synchronize()
     # the decode kernel's average launch duration, by difference, right after
     # (an idle GPU restarts slower: the first ~60 steps after a pause of a few
-    # ms run up to 3x the settled step time): nk more steps, then nk steps
-    # without the decode launch (the append, and the merge kernel when the
-    # decode does not merge its splits itself), each span between two events
+    # ms run up to 3x the settled step time): nk more steps as kvq_append +
+    # kvq_decode_attn_splits, then nk steps without the decode launch (the
+    # append, and the merge kernel when the decode does not merge its splits
+    # itself), each span between two events
     if not merged:
         cache.decode_partials(qs[0], partials, splits=S)  # partials for the merge-only steps
     ev[2].record()
     for i in range(nk):
-        step(args.warmup + args.steps + i)
+        step_separate(args.warmup + args.steps + i)
     ev[3].record()
     for i in range(nk):
         k, v = step_kv[args.warmup + args.steps + nk + i]
@@ -461,8 +476,8 @@ def main() -> int:
             "traffic": measured_traffic(w.name),
             "avg_us": round(dec_avg_ms * 1e3, 2),
             "launches_timed": nk,
-            "timing": "per launch: (span of nk steps) - (span of nk steps without the decode launch), after the "
-                      "timed steps",
+            "timing": "per launch: (span of nk steps of append + decode) - (span of nk steps without the decode "
+                      "launch), after the timed steps",
             "bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes)),
         },
         "step_us_percentiles": dist,

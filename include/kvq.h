@@ -213,8 +213,11 @@ kvq_status kvq_decode_partials(kvq_cache* cache, const void* q, float* partials,
  * are those of the two calls.  The workspace / partials must hold
  * kvq_workspace_bytes (all splits the library may use).  Every argument is
  * checked before any work is enqueued, so on an error nothing has been
- * appended.  (Writing the new token inside the decode kernel instead of by
- * the window-write kernel was measured slower by 6-16 us per step.) */
+ * appended.  When the token goes to the fp16 window (not the sink, not
+ * quantized by this append) of a cache without key rotation or
+ * position-adaptive widths, the decode kernel writes its window slots itself
+ * (one launch fewer per step); k and v are read by that kernel, so they must
+ * stay unchanged until the work enqueued on `stream` has completed. */
 kvq_status kvq_append_decode_attn(kvq_cache* cache, const void* k, const void* v, const void* q, float* out,
                                   void* workspace, size_t ws_bytes, void* stream);
 kvq_status kvq_append_decode_partials(kvq_cache* cache, const void* k, const void* v, const void* q,
