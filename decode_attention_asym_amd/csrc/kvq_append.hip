@@ -151,26 +151,59 @@ __device__ __forceinline__ GroupQ group_params_pair(F&& x) {
   return r;
 }
 
-// The code of x as a float (an integer in [0, 2^BITS - 1]).
+// The operands of one code: the quotient's numerator n (fl(x - min) for the
+// asymmetric quantizer, x for the symmetric one), its scale s, rs = fl(1/s)
+// (0 when s = 0) and the offset added to the rounded quotient (0, or c0 for
+// the symmetric quantizer).  fl(x - min) is formed as fma(x, 1, -min): the
+// exact difference rounded once, as a binary32 subtraction rounds it, and
+// with x an fp16 value the conversion folds into the fma.
+struct QOp {
+  float n, s, rs, off;
+};
 template <int BITS, bool HYB>
-__device__ __forceinline__ float code_of(float x, float mn, float s, float rs, bool sym) {
+__device__ __forceinline__ QOp quant_op(float x, float mn, float s, float rs, bool sym) {
   constexpr float c0 = static_cast<float>((1 << (BITS - 1)) - 1);
   if constexpr (HYB) {
-    if (sym) return quant_code_sym_f(x, s, rs, c0);
+    if (sym) return QOp{x, s, rs, c0};
   }
-  return quant_code_f(x, mn, s, rs);
+  return QOp{__builtin_fmaf(x, 1.0f, -mn), s, rs, 0.0f};
 }
 
-// Packs codes into a dword: the code of field k goes to bit bit_of(k); the
-// fields of a byte are summed as floats (exact small integers) and each byte
-// is inserted by one v_cvt_pk_u8_f32.
-template <int N, typename BitF, typename CodeF>
-__device__ __forceinline__ uint32_t pack_codes(BitF&& bit_of, CodeF&& code) {
+// Packs N codes into a dword: the code of field k (its operands op(k)) goes
+// to bit bit_of(k); the fields of a byte are summed as floats (exact small
+// integers) and each byte is inserted by one v_cvt_pk_u8_f32.  A code is
+// rne(fl(n / s)) + off, formed as rint(fl(n * rs)) (rne_quotient's rule): the
+// quotients of all N fields are rounded first and one ballot over them tells
+// whether any lane has a field within 2^-12 of a half-integer; only then are
+// the operands formed again and those fields take the correctly rounded
+// division.  A group with s = 0 has n = 0 (every x equals the minimum, or is
+// zero for the symmetric quantizer) and rs = 0, so its quotient is 0 without
+// a test.  OFF: some operands carry an offset (the hybrid quantizer).
+template <int N, bool OFF, typename BitF, typename OpF>
+__device__ __forceinline__ uint32_t pack_codes(BitF&& bit_of, OpF&& op) {
+  float t[N], off[N];
+  uint64_t near = 0;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const QOp q = op(k);
+    const float f = q.n * q.rs;
+    t[k] = rintf(f);
+    off[k] = q.off;
+    near |= __builtin_amdgcn_ballot_w64(fabsf(f - t[k]) > kTieGuard);
+  }
+  if (near != 0) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const QOp q = op(k);
+      const float f = q.n * q.rs;
+      if (fabsf(f - rintf(f)) > kTieGuard) t[k] = rintf(q.n / q.s);
+    }
+  }
   float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const int bit = bit_of(k);
-    b[bit >> 3] = __builtin_fmaf(code(k), static_cast<float>(1 << (bit & 7)), b[bit >> 3]);
+    b[bit >> 3] = __builtin_fmaf(OFF ? t[k] + off[k] : t[k], static_cast<float>(1 << (bit & 7)), b[bit >> 3]);
   }
   uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(b[0], 0, 0u);
   w = __builtin_amdgcn_cvt_pk_u8_f32(b[1], 1, w);
@@ -395,7 +428,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         int l16 = l & 15, j = l >> 4;
         // field k: element e = k % 8 of sub-block k / 8
         constexpr int SUBS = KB == 4 ? 1 : 2;
-        const uint32_t word = pack_codes<8 * SUBS>(
+        const uint32_t word = pack_codes<8 * SUBS, HYB>(
             [&](int k) { const int e = k & 7, sub = k >> 3;
                          return KB == 4 ? 16 * (e & 1) + 4 * (e >> 1) : 16 * (e & 1) + 8 * sub + 2 * (e >> 1); },
             [&](int k) {
@@ -404,7 +437,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
               const int mt = combo / NKB, kb = combo % NKB;
               const int i = ch * kChunk + 16 * mt + l16;  // token within the group
               const int c = 32 * kb + 8 * j + e;
-              return code_of<KB, HYB>(kget(i * KS + c), kmn[c], ks[c], krs[c], HYB && ksym[c]);
+              return quant_op<KB, HYB>(kget(i * KS + c), kmn[c], ks[c], krs[c], HYB && ksym[c]);
             });
         *reinterpret_cast<uint32_t*>(page + L.off_kcodes + ch * L.kc_chunk_bytes + lane_dword_offset(KW, l, d)) = word;
       }
@@ -418,14 +451,14 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         int d = task % VW;
         int l16 = l & 15, j = l >> 4;
         constexpr int SUBS = VB == 4 ? 1 : 2;
-        const uint32_t word = pack_codes<8 * SUBS>(
+        const uint32_t word = pack_codes<8 * SUBS, HYB>(
             [&](int k) { return vcode_bit(VB, VB == 4 ? d : 2 * d + (k >> 3), k & 7); },
             [&](int k) {
               const int e = k & 7, mt = VB == 4 ? d : 2 * d + (k >> 3);
               const int c = 16 * mt + l16, cg = c / G;
               const int i = ch * kChunk + tau(j, e);
               const int pv = i * NCG + cg;
-              return code_of<VB, HYB>(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB && vsym[pv]);
+              return quant_op<VB, HYB>(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB && vsym[pv]);
             });
         *reinterpret_cast<uint32_t*>(page + L.off_vcodes + ch * L.vc_chunk_bytes + lane_dword_offset(VW, l, d)) = word;
       }

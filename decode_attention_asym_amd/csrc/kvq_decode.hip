@@ -13,7 +13,12 @@
 // Per wave: one (batch, kv head) slice and one contiguous range of token
 // groups (a split).  The GQA query heads of the slice are columns of the MFMA
 // B operand, replicated across the 16 columns so that the per-score softmax
-// work is shared out over the replicas (see decode_kernel).
+// work is shared out over the replicas (see decode_split).  Launches:
+// decode_kernel (one wave per workgroup; the splits' partials go to memory
+// for the merge kernel), decode_fused_kernel (a slice's 4 or 8 splits as the
+// waves of one workgroup, merged in LDS) and decode_mixed_kernel (groups of
+// several bit widths).  In a one-call decode step the wave whose window chunk
+// holds the appended token also writes that token's window slots.
 //
 // Scale folding (exact in real arithmetic):
 //   keys, per channel c of group g:  q . khat_t = sum_c (q_c s_gc) code_tc + sum_c q_c z_gc
