@@ -61,3 +61,17 @@ def test_symmetric_quotients():
         M = np.abs(x).max(axis=1, keepdims=True)
         s = M / np.float32(c0)
         _check(x, np.broadcast_to(s, x.shape))
+
+
+def test_quotients_around_the_guard_band():
+    """Quotients planted 2^-19 .. 2^-14 from half-integers, inside and outside
+    the band where the division decides: everywhere the rule must give the
+    correctly rounded quotient's integer (the bound behind the band is
+    2^-18)."""
+    rng = np.random.default_rng(5)
+    s = rng.uniform(1e-4, 1e3, 100000).astype(np.float32)
+    k = rng.integers(0, 15, s.size).astype(np.float32)
+    for e in (-19, -18, -17, -16, -15, -14):
+        for sign in (-1.0, 1.0):
+            q = (k + np.float32(0.5) + np.float32(sign * 2.0 ** e)).astype(np.float32)
+            _check((q * s).astype(np.float32), s)
