@@ -251,8 +251,9 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   // channel of 16 or 32 consecutive tokens hit different LDS banks
   using KT = typename std::conditional<F32K, float, __half>::type;
   constexpr int KS = F32K ? D + 1 : D + 2, VS = D + 2;
-  __shared__ KT kx[G * KS];
-  __shared__ __half vx[G * VS];  // values are fp16 after entry conversion
+  // (rows are written as dwords: 4-byte aligned rows, 16-byte aligned bases)
+  __shared__ __attribute__((aligned(16))) KT kx[G * KS];
+  __shared__ __attribute__((aligned(16))) __half vx[G * VS];  // values are fp16 after entry conversion
   // a staged key as binary32, and the store of an entry-converted key (fp16
   // staging rounds it to fp16 here, as the entry conversion does anyway)
   auto kget = [&](int i) __attribute__((always_inline)) -> float {
