@@ -300,7 +300,9 @@ class KVQCache:
 
     def append_decode(self, k, v, q, out=None, stream=None):
         """One step: append one token (k, v [B, H_kv, 1, D]) and decode q,
-        every argument checked before anything is enqueued."""
+        every argument checked before anything is enqueued.  The decode kernel
+        may read k and v itself (it writes the token's window slots), so they
+        must stay unchanged until the work enqueued on the stream is done."""
         self._kv(k, v, 1)
         self._q(q)
         out = self._out(out, q)

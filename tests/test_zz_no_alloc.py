@@ -39,6 +39,18 @@ def test_noalloc_equals_workspace_decode_twice():
         _run(kvq, w)
 
 
+def test_noalloc_equals_workspace_decode_merged_in_kernel():
+    """A decode whose splits merge inside the kernel (the 32k layer's slice
+    count) uses no partials: the no-allocation entry point gives the same
+    output, and does not need the scratch array."""
+    import decode_attention_asym_amd as kvq
+
+    w = WORKLOADS[2].replace(name="noalloc-merged", N=64 * 16 + 128 + 5)
+    c = _run(kvq, w)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert c.decode_plan() == (4, True)
+
+
 def test_noalloc_refuses_partials_beyond_the_scratch():
     import decode_attention_asym_amd as kvq
 
