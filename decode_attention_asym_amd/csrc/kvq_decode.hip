@@ -516,6 +516,28 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   //   in first-part columns) and qh is zero in first-part columns, so the same
   //   three instructions produce either part: x = qh s, y = qh s - x (exact),
   //   part = fp16(ql s + y).
+  //   With key token norms the keys' scales are at most 1 (normalized rows lie
+  //   in [-1, 1]) and often far below it, so q * scale / mult would sit in
+  //   the fp16 subnormals with few bits left; q / mult is then scaled by 2^E,
+  //   E per split such that max |q| 2^E < 2^14, and the scores by 2^(24 - E)
+  //   instead of 2^24 (exact powers of two).
+  float qup = 1.0f, kscale = kTwo24;
+  if constexpr (TN) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qm[kb][e]));
+    // over the wave: the 16 columns of each row, then the four rows
+    mx = fmax2(mx, row_from<8>(mx));
+    mx = fmax2(mx, row_from<4>(mx));
+    mx = fmax2(mx, row_from<2>(mx));
+    mx = fmax2(mx, row_from<1>(mx));
+    mx = wave_max_j(mx);
+    const int E = mx > 0.0f ? min(40, max(-24, 14 - __builtin_amdgcn_frexp_expf(mx))) : 40;
+    qup = __builtin_ldexpf(1.0f, E);
+    kscale = __builtin_ldexpf(kTwo24, -E);
+  }
   uint32_t qz[NP][NKB][4], qh[NKB][4], ql[NKB][4];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -524,7 +546,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       const float x0 = qm[kb][2 * i], x1 = qm[kb][2 * i + 1];
       const float h0 = static_cast<float>(static_cast<_Float16>(x0)), h1 = static_cast<float>(static_cast<_Float16>(x1));
       const uint32_t z_hi = pack_h2(x0, x1), z_lo = pack_h2(x0 - h0, x1 - h1);
-      const float d0 = x0 * (1.0f / code_mult<KB>(2 * i)), d1 = x1 * (1.0f / code_mult<KB>(2 * i + 1));
+      const float d0 = (x0 * qup) * (1.0f / code_mult<KB>(2 * i)), d1 = (x1 * qup) * (1.0f / code_mult<KB>(2 * i + 1));
       const float e0 = static_cast<float>(static_cast<_Float16>(d0)), e1 = static_cast<float>(static_cast<_Float16>(d1));
       const uint32_t d_hi = pack_h2(d0, d1), d_lo = pack_h2(d0 - e0, d1 - e1);
       if constexpr (NP == 1) {
@@ -752,7 +774,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       if constexpr (TN) {
 #pragma unroll
         for (int k = 0; k < NV; ++k)
-          sc[k] = __builtin_fmaf(u[k], kTwo24, cb) * ((k & 1) ? h2f_hi(kn[k >> 1]) : h2f_lo(kn[k >> 1]));
+          sc[k] = __builtin_fmaf(u[k], kscale, cb) * ((k & 1) ? h2f_hi(kn[k >> 1]) : h2f_lo(kn[k >> 1]));
       }
       float tmax = TN ? sc[0] : u[0];
 #pragma unroll
