@@ -318,10 +318,11 @@ def main() -> int:
         cache.append(K, V)
         b.record()
     S = args.splits or cache.default_splits()  # host-side: the token count is known without the device
-    # (split count, splits merged inside the decode kernel): with the merge in
-    # the kernel a step is two launches (append, decode), else three (append,
-    # decode, merge kernel)
-    S_used, merged = cache.decode_plan(S)
+    # (split count, splits merged inside the decode kernel, partial records
+    # per row the merge kernel combines): with the merge in the kernel a step
+    # is one launch (the decode also writes the token's window slots), else
+    # two (decode, merge kernel)
+    S_used, merged, records = cache.decode_plan(S)
 
     def step(i):
         # one decode step: kvq_append_decode_attn (append one token, whose
@@ -360,7 +361,10 @@ def main() -> int:
     # append, and the merge kernel when the decode does not merge its splits
     # itself), each span between two events
     if not merged:
-        cache.decode_partials(qs[0], partials, splits=S)  # partials for the merge-only steps
+        # valid records (o = 0, m = 0, l = 1) for the merge-only steps
+        pv = partials[: rows * records * (w.D + 4)].view(rows * records, w.D + 4)
+        pv.zero_()
+        pv[:, w.D + 1] = 1.0
     ev[2].record()
     for i in range(nk):
         step_separate(args.warmup + args.steps + i)
@@ -369,7 +373,7 @@ def main() -> int:
         k, v = step_kv[args.warmup + args.steps + nk + i]
         cache.append(k, v)
         if not merged:
-            merge_partials(partials, out, rows, S_used, w.D)
+            merge_partials(partials, out, rows, records, w.D)
     ev[4].record()
     torch.cuda.synchronize()
     # per-step percentiles: each step between two events of its own (an event
@@ -461,13 +465,15 @@ def main() -> int:
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
             "context": w.N, "k_bits": w.kbits, "v_bits": w.vbits, "group": w.G, "residual": w.R,
             "rotate": w.rotate, "sink": w.sink, "hybrid": w.hybrid, "token_norm": w.token_norm, "splits": S_used,
-            "splits_merged_in_kernel": merged,
+            "splits_merged_in_kernel": merged, "merge_records": records,
             "adapt_delta": w.adapt_delta, "bits_low": list(w.bits_low), "bits_high": list(w.bits_high),
             "parallelism": "single-gpu",
         },
         "roofline": {
-            "kernel": ("decode_fused_kernel (split dequant-attention, splits merged in the workgroup)" if merged
-                       else "decode_kernel (split dequant-attention)"),
+            "kernel": ("decode_fused_kernel (split dequant-attention, splits merged in the workgroup)"
+                       if merged and S_used > 1 else
+                       "decode_fused_kernel (split dequant-attention, each four splits merged in the workgroup)"
+                       if 0 < records < S_used else "decode_kernel (split dequant-attention)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

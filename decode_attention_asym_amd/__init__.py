@@ -5,6 +5,7 @@ C ABI in include/kvq.h); this package is the ctypes binding over it.
 """
 from .kvq import (  # noqa: F401
     Config,
+    DecodePlan,
     KVQCache,
     KVQError,
     cache_bytes,

@@ -33,9 +33,10 @@ struct kvq_cache {
   bool poisoned;
   int cu_count;
   std::vector<uint8_t> gk, gv;  // key / value bits of each quantized group
-  // dynamic LDS of the workgroup-merged decode per (key bits, value bits,
-  // splits), 0 where it does not apply (kvq::decode_fused_lds, asked once)
-  std::map<int, size_t> fused_lds;
+  // dynamic LDS of the workgroup-merged decode per (splits, key bits, value
+  // bits, group size), 0 where it does not apply (kvq::decode_fused_lds,
+  // asked once)
+  std::map<int64_t, size_t> fused_lds;
 };
 
 namespace {
@@ -154,11 +155,11 @@ int64_t nquant_of(const kvq_cache* h, int64_t n) {
 int64_t ngroups_of(const kvq_cache* h) { return nquant_of(h, h->n) / h->cfg.group_size; }
 
 // Whether a decode of one run of (kb, vb) groups at S splits per slice may
-// merge its splits inside the decode kernel (asked of the kernels once per
-// bit widths and split count).
-bool fused_allowed(kvq_cache* h, int kb, int vb, int64_t S) {
-  if (S < 2 || S > kvq::kMaxFusedSplits) return false;
-  const int key = (kb << 16) | (vb << 8) | static_cast<int>(S);
+// run them in groups of W as the waves of one workgroup, merged there (asked
+// of the kernels once per bit widths, split count and group size).
+bool fused_allowed(kvq_cache* h, int kb, int vb, int64_t S, int W) {
+  if (W < 2 || W > kvq::kMaxFusedSplits || S < W || S % W != 0 || S > INT32_MAX) return false;
+  const int64_t key = (static_cast<int64_t>(S) << 24) | (kb << 16) | (vb << 8) | W;
   auto it = h->fused_lds.find(key);
   if (it == h->fused_lds.end()) {
     kvq::DecodeArgs a{};
@@ -166,7 +167,7 @@ bool fused_allowed(kvq_cache* h, int kb, int vb, int64_t S) {
     a.rotate = h->cfg.rotate;
     a.gqa = h->cfg.num_q_heads / h->cfg.num_kv_heads;
     a.splits = static_cast<int>(S);
-    it = h->fused_lds.emplace(key, kvq::decode_fused_lds(a)).first;
+    it = h->fused_lds.emplace(key, kvq::decode_fused_lds(a, W)).first;
   }
   return it->second > 0;
 }
@@ -194,7 +195,7 @@ int choose_splits(kvq_cache* h, int64_t n) {
   // kernel (one workgroup of four waves per slice) save the merge launch:
   // measured on the 32k K4/V2 layer, 301.5 us against 306.2 us for 6 splits
   // and the merge kernel (4 and 6 splits stream the cache equally fast)
-  if (s >= 4 && s <= 6 && h->cfg.adapt_delta == 0 && fused_allowed(h, h->cfg.k_bits, h->cfg.v_bits, 4)) s = 4;
+  if (s >= 4 && s <= 6 && h->cfg.adapt_delta == 0 && fused_allowed(h, h->cfg.k_bits, h->cfg.v_bits, 4, 4)) s = 4;
   int64_t ng = nquant_of(h, n) / h->cfg.group_size;
   s = std::min<int64_t>(s, std::max<int64_t>(1, ng / 2));
   s = std::min<int64_t>(s, max_splits(&h->cfg));
@@ -450,8 +451,9 @@ struct SplitPlan {
   bool mixed = false;
   kvq::MixedPlan pieces{};
   std::vector<int64_t> sp, gps;  // splits and groups per split of each run
-  int64_t S = 0;                 // split slots per row
-  bool fused = false;            // one run, its splits merged in the workgroup
+  int64_t S = 0;                 // splits per slice
+  int W = 0;                     // one run whose splits are merged in workgroups of W (0: none)
+  int64_t slots = 0;             // partial records per row for the merge kernel (0: none)
 };
 
 // Arguments of every decode launch over the cache's current tokens.
@@ -475,9 +477,13 @@ kvq::DecodeArgs decode_args(const kvq_cache* h, const void* q, float* out, float
 }
 
 // Validate a split count against the cache and plan the decode; allow_fused
-// lets one run with 2 .. kMaxFusedSplits splits per slice merge them in the
-// workgroup, when that launch fits as many waves per CU as the one-wave
-// launch (asked of the kernels once per bit widths and split count).
+// lets one run merge its splits in the decode kernel's workgroups: all of a
+// slice's when it has 4 or 8, in groups of four when it has more (the count
+// rounded up to a multiple of four, trailing splits possibly empty but no
+// workgroup without groups, and the groups' records merged by the merge
+// kernel); each when that launch fits as
+// many waves per CU as the one-wave launch or all its workgroups at once
+// (asked of the kernels once per bit widths, split count and group size).
 kvq_status plan_splits(kvq_cache* h, int32_t num_splits, bool allow_fused, SplitPlan* p) {
   kvq_status st = check_handle(h);
   if (st != KVQ_OK) return st;
@@ -498,9 +504,10 @@ kvq_status plan_splits(kvq_cache* h, int32_t num_splits, bool allow_fused, Split
   p->sp.assign(runs.size(), 1);
   p->gps.assign(runs.size(), 0);
   p->S = 0;
-  p->fused = false;
+  p->W = 0;
   if (p->mixed) {
     p->S = p->pieces.npieces;
+    p->slots = p->S;
     return ok();
   }
   if (ng > 0) p->sp = run_splits(h, runs, std::min<int64_t>(num_splits, ng));
@@ -512,17 +519,35 @@ kvq_status plan_splits(kvq_cache* h, int32_t num_splits, bool allow_fused, Split
     }
     p->S += p->sp[i];
   }
-  p->fused = allow_fused && runs.size() == 1 && fused_allowed(h, runs[0].kb, runs[0].vb, p->S);
+  p->slots = p->S;
+  if (allow_fused && runs.size() == 1) {
+    if (fused_allowed(h, runs[0].kb, runs[0].vb, p->S, static_cast<int>(p->S))) {
+      p->W = static_cast<int>(p->S);
+      p->slots = 0;
+    } else if (p->S > kvq::kMaxFusedSplits) {
+      // every workgroup keeps some groups (trailing splits may be empty)
+      const int64_t len = runs[0].g1 - runs[0].g0, S4 = (p->S + 3) / 4 * 4, gps = (len + S4 - 1) / S4;
+      if (len > 0 && (len + gps - 1) / gps > S4 - 4 && fused_allowed(h, runs[0].kb, runs[0].vb, S4, 4)) {
+        p->S = S4;
+        p->sp[0] = S4;
+        p->gps[0] = gps;
+        p->W = 4;
+        p->slots = S4 / 4;
+      }
+    }
+  }
   return ok();
 }
 
 // Validate and launch the split kernels (one per run of groups with equal
 // bits).  allow_final selects direct output when the whole decode is one
-// split, or one run whose few splits per slice are merged inside the
-// workgroup; *merged tells the caller that `out` is written (no merge left).
+// split, or one run whose 4 or 8 splits per slice are merged inside the
+// workgroup, and the grouped in-workgroup merge of more splits; *merged tells
+// the caller that `out` is written (no merge left), else *records is the
+// number of partial records per row the merge kernel reads.
 using kvq::NewToken;
 kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partials, size_t bytes, int32_t num_splits,
-                         bool allow_final, int32_t* splits_used, bool* merged, hipStream_t s, bool noalloc = false,
+                         bool allow_final, int32_t* records, bool* merged, hipStream_t s, bool noalloc = false,
                          NewToken nt = NewToken{}) {
   if (merged) *merged = false;
   SplitPlan p;
@@ -532,21 +557,21 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
   const kvq_config& c = h->cfg;
   const int64_t rows = static_cast<int64_t>(c.batch) * c.num_q_heads;
   const int64_t S = p.S;
-  const bool final = allow_final && (S == 1 || p.fused);
+  const bool final = allow_final && (S == 1 || p.W == S);
   if (final) {
     if (!out || !aligned(out, 16)) return fail(KVQ_E_ARG, "out NULL or not 16-byte aligned");
   } else {
-    size_t need = static_cast<size_t>(rows * S * (c.head_dim + 4) * sizeof(float));
+    size_t need = static_cast<size_t>(rows * p.slots * (c.head_dim + 4) * sizeof(float));
     if (noalloc && bytes < need)
       return fail(KVQ_E_ARG,
-                  "this decode needs %zu bytes of split partials (%lld rows x %lld splits), above the %zu-byte "
+                  "this decode needs %zu bytes of split partials (%lld rows x %lld records), above the %zu-byte "
                   "no-allocation scratch; use kvq_decode_attn with a workspace",
-                  need, (long long)rows, (long long)S, bytes);
+                  need, (long long)rows, (long long)p.slots, bytes);
     if (!partials || !aligned(partials, 16) || bytes < need)
       return fail(KVQ_E_ARG, "workspace/partials NULL, misaligned or %zu < %zu bytes", bytes, need);
   }
   kvq::DecodeArgs a = decode_args(h, q, out, partials);
-  a.write_final = final && !p.fused ? 1 : 0;
+  a.write_final = final && p.W == 0 ? 1 : 0;
   a.splits_total = static_cast<int>(S);
   hipError_t e = hipSuccess;
   if (p.mixed) {
@@ -565,12 +590,12 @@ kvq_status launch_splits(kvq_cache* h, const void* q, float* out, float* partial
       a.groups_per_split = p.gps[i];
       a.split_off = static_cast<int>(off);
       a.do_fp16 = i == fp16_run ? 1 : 0;
-      e = p.fused ? kvq::launch_decode_fused(a, nt, s) : kvq::launch_decode(a, nt, s);
+      e = p.W > 0 ? kvq::launch_decode_fused(a, nt, p.W, s) : kvq::launch_decode(a, nt, s);
       if (e != hipSuccess) return device_error(h, e, "decode kernel launch");
       off += p.sp[i];
     }
   }
-  if (splits_used) *splits_used = static_cast<int32_t>(S);
+  if (records) *records = static_cast<int32_t>(final ? 0 : p.slots);
   if (merged) *merged = final;
   return ok();
 }
@@ -591,12 +616,12 @@ kvq_status kvq_decode_attn_splits(kvq_cache* h, const void* q, float* out, void*
   return ok();
 }
 
-kvq_status kvq_decode_plan(kvq_cache* h, int32_t num_splits, int32_t* splits_used, int32_t* merged_in_kernel) {
+kvq_status kvq_decode_plan(kvq_cache* h, int32_t num_splits, int32_t* splits_used, int32_t* merge_records) {
   SplitPlan p;
   kvq_status st = plan_splits(h, num_splits, true, &p);
   if (st != KVQ_OK) return st;
   if (splits_used) *splits_used = static_cast<int32_t>(p.S);
-  if (merged_in_kernel) *merged_in_kernel = p.S == 1 || p.fused ? 1 : 0;
+  if (merge_records) *merge_records = p.S == 1 || p.W == p.S ? 0 : static_cast<int32_t>(p.slots);
   return ok();
 }
 

@@ -1002,14 +1002,17 @@ void decode_kernel(DecodeArgs a, NewToken nt) {
 }
 
 // ---- splits merged inside the workgroup --------------------------------------
-// With few splits per slice, the slice's splits run as the waves of one
-// workgroup (wave w = split w), each streaming its range through its own LDS
-// ring; after one barrier the workgroup merges the splits' (o, m, l) records
-// from LDS with the log-sum-exp combination of the merge kernel and writes
-// the output, so the partials never go to memory and no merge launch
-// follows.  The dynamic LDS holds S regions of fused_region_bytes (ring,
-// then the split's record at its start) and the rotated query's gqa * D
-// floats after them.
+// A slice's splits run in groups of W = 4 or 8 as the waves of one workgroup
+// (workgroup gi of the slice, wave w = split W gi + w), each streaming its
+// range through its own LDS ring; after one barrier the workgroup merges its
+// W splits' (o, m, l) records from LDS with the log-sum-exp combination of
+// the merge kernel.  With one group per slice it writes the output, so the
+// partials never go to memory and no merge launch follows; with NG = S / W
+// groups it writes the group's merged record (o relative to the group's
+// maximum, that maximum, l) to partial slot gi of NG, for the merge kernel.
+// The dynamic LDS holds W regions of fused_region_bytes (ring, then the
+// split's record at its start) and the rotated query's gqa * D floats after
+// them.
 template <int D, int KB, int VB, int G, int GQC, bool TN>
 constexpr int fused_region_bytes() {
   constexpr int rb = ring_bytes<D, KB, VB, G, TN, kFusedRingBudget>(), rec = GQC * (D + 4) * 4;
@@ -1020,12 +1023,13 @@ template <int D, int KB, int VB, int G, int GQC, bool TN>
 __global__ __launch_bounds__(kLanes * kMaxFusedSplits) __attribute__((amdgpu_waves_per_eu(GQC < 16 ? 3 : 2)))
 void decode_fused_kernel(DecodeArgs a, NewToken nt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr int RW = fused_region_bytes<D, KB, VB, G, GQC, TN>(), Q = D / 4, W = D + 4;
-  const int S = a.splits;
+  constexpr int RW = fused_region_bytes<D, KB, VB, G, GQC, TN>(), Q = D / 4, RS = D + 4;
+  const int W = static_cast<int>(blockDim.x) / kLanes, NG = a.splits / W;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kLanes);
-  float* qsh = reinterpret_cast<float*>(lds + S * RW);
-  const int64_t slice = blockIdx.x;
-  decode_split<D, KB, VB, G, GQC, TN, true>(a, slice, w, lds + w * RW, qsh, nt);
+  float* qsh = reinterpret_cast<float*>(lds + W * RW);
+  const int64_t slice = blockIdx.x / NG;
+  const int gi = static_cast<int>(blockIdx.x % NG);
+  decode_split<D, KB, VB, G, GQC, TN, true>(a, slice, gi * W + w, lds + w * RW, qsh, nt);
   __syncthreads();
   // thread t: channels 4q .. 4q + 3 of head slot hh; M = max_s m_s,
   // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, and a split with no
@@ -1034,11 +1038,11 @@ void decode_fused_kernel(DecodeArgs a, NewToken nt) {
   for (int t = threadIdx.x; t < a.gqa * Q; t += blockDim.x) {
     const int hh = t / Q, q = t % Q;
     float M = -INFINITY;
-    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, reinterpret_cast<const float*>(lds + sp * RW)[hh * W + D]);
+    for (int sp = 0; sp < W; ++sp) M = fmaxf(M, reinterpret_cast<const float*>(lds + sp * RW)[hh * RS + D]);
     float L = 0.0f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < S; ++sp) {
-      const float* pr = reinterpret_cast<const float*>(lds + sp * RW) + hh * W;
+    for (int sp = 0; sp < W; ++sp) {
+      const float* pr = reinterpret_cast<const float*>(lds + sp * RW) + hh * RS;
       const float ms = pr[D];
       if (ms != -INFINITY) {
         const float ws = __builtin_amdgcn_exp2f(ms - M);
@@ -1047,7 +1051,16 @@ void decode_fused_kernel(DecodeArgs a, NewToken nt) {
       }
     }
     const int64_t row = static_cast<int64_t>(b) * a.Hq + hkv * a.gqa + hh;
-    *reinterpret_cast<f32x4*>(a.out + row * D + 4 * q) = acc / L;
+    if (NG == 1) {
+      *reinterpret_cast<f32x4*>(a.out + row * D + 4 * q) = acc / L;
+    } else {
+      float* pr = a.partial + (row * NG + gi) * RS;
+      *reinterpret_cast<f32x4*>(pr + 4 * q) = acc;
+      if (q == 0) {
+        pr[D] = M;
+        pr[D + 1] = L;
+      }
+    }
   }
 }
 
@@ -1113,11 +1126,11 @@ hipError_t one_wave_launch_i(const DecodeArgs& a, const NewToken& nt, hipStream_
 // a CU's four SIMDs unless they come in fours; at 4 splits the 32k layer
 // decodes in 301.5 us merged against 304.2 us with the merge kernel.
 template <int D, int KB, int VB, int G, int GQC, bool TN>
-size_t fused_plan_i(const DecodeArgs& a) {
+size_t fused_plan_i(const DecodeArgs& a, int W) {
   const int S = a.splits;
-  if (S < 4 || S > kMaxFusedSplits || S % 4 != 0) return 0;
+  if ((W != 4 && W != 8) || W > kMaxFusedSplits || S < W || S % W != 0) return 0;
   const size_t qb = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
-  const size_t lds = static_cast<size_t>(S) * fused_region_bytes<D, KB, VB, G, GQC, TN>() + qb;
+  const size_t lds = static_cast<size_t>(W) * fused_region_bytes<D, KB, VB, G, GQC, TN>() + qb;
   int dev = 0, max_lds = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
@@ -1125,20 +1138,20 @@ size_t fused_plan_i(const DecodeArgs& a) {
       lds > static_cast<size_t>(max_lds))
     return 0;
   int nf = 0, n1 = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, decode_fused_kernel<D, KB, VB, G, GQC, TN>, kLanes * S, lds) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nf, decode_fused_kernel<D, KB, VB, G, GQC, TN>, kLanes * W, lds) !=
           hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&n1, decode_kernel<D, KB, VB, G, GQC, TN>, kLanes, qb) != hipSuccess)
     return 0;
-  const bool one_pass = static_cast<int64_t>(nf) * cus >= a.L.slices;
-  return one_pass || nf * S >= n1 ? lds : 0;
+  const bool one_pass = static_cast<int64_t>(nf) * cus >= a.L.slices * (S / W);
+  return one_pass || nf * W >= n1 ? lds : 0;
 }
 
 template <int D, int KB, int VB, int G, int GQC, bool TN>
-hipError_t fused_launch_i(const DecodeArgs& a, const NewToken& nt, hipStream_t s) {
-  const size_t lds = fused_plan_i<D, KB, VB, G, GQC, TN>(a);
+hipError_t fused_launch_i(const DecodeArgs& a, const NewToken& nt, int W, hipStream_t s) {
+  const size_t lds = fused_plan_i<D, KB, VB, G, GQC, TN>(a, W);
   if (lds == 0) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_fused_kernel<D, KB, VB, G, GQC, TN>), dim3(static_cast<unsigned>(a.L.slices)),
-                     dim3(kLanes * a.splits), lds, s, a, nt);
+  hipLaunchKernelGGL((decode_fused_kernel<D, KB, VB, G, GQC, TN>),
+                     dim3(static_cast<unsigned>(a.L.slices * (a.splits / W))), dim3(kLanes * W), lds, s, a, nt);
   return hipGetLastError();
 }
 
@@ -1172,12 +1185,12 @@ auto instance_of(const DecodeArgs& a, X... x) {
 
 template <int D, int KB, int VB, int G, int GQC, bool TN>
 struct FusedPlan {
-  static size_t run(const DecodeArgs& a) { return fused_plan_i<D, KB, VB, G, GQC, TN>(a); }
+  static size_t run(const DecodeArgs& a, int W) { return fused_plan_i<D, KB, VB, G, GQC, TN>(a, W); }
 };
 template <int D, int KB, int VB, int G, int GQC, bool TN>
 struct FusedLaunch {
-  static hipError_t run(const DecodeArgs& a, const NewToken& nt, hipStream_t s) {
-    return fused_launch_i<D, KB, VB, G, GQC, TN>(a, nt, s);
+  static hipError_t run(const DecodeArgs& a, const NewToken& nt, int W, hipStream_t s) {
+    return fused_launch_i<D, KB, VB, G, GQC, TN>(a, nt, W, s);
   }
 };
 template <int D, int KB, int VB, int G, int GQC, bool TN>
@@ -1189,10 +1202,10 @@ struct OneWaveLaunch {
 
 }  // namespace
 
-size_t decode_fused_lds(const DecodeArgs& a) { return instance_of<FusedPlan>(a); }
+size_t decode_fused_lds(const DecodeArgs& a, int W) { return instance_of<FusedPlan>(a, W); }
 
-hipError_t launch_decode_fused(const DecodeArgs& a, const NewToken& nt, hipStream_t s) {
-  return instance_of<FusedLaunch>(a, nt, s);
+hipError_t launch_decode_fused(const DecodeArgs& a, const NewToken& nt, int W, hipStream_t s) {
+  return instance_of<FusedLaunch>(a, nt, W, s);
 }
 
 bool decode_supported(int D, int kbits, int vbits, int G) {

@@ -107,14 +107,16 @@ struct NewToken {
   int64_t pos = -1;
 };
 hipError_t launch_decode(const DecodeArgs& a, const NewToken& nt, hipStream_t s);
-// A decode of one launch (every group of one width) whose slices have 4 or
-// 8 splits can run each slice's splits as the waves of one workgroup, merged
-// in LDS, writing `out` directly (partial unused).  decode_fused_lds: that
-// launch's dynamic LDS bytes, 0 when it does not apply or would hold fewer
-// waves per CU than launch_decode.
+// A decode of one launch (every group of one width) whose split count S per
+// slice is a multiple of W (4 or 8) can run each slice's splits in groups of
+// W as the waves of one workgroup, merged in LDS: with S = W the workgroup
+// writes `out` (partial unused); otherwise each writes its group's merged
+// record to partial slot gi of S / W per row, for the merge kernel.
+// decode_fused_lds: that launch's dynamic LDS bytes, 0 when it does not apply
+// or would hold fewer waves per CU than launch_decode and not fit one pass.
 constexpr int kMaxFusedSplits = 8;
-size_t decode_fused_lds(const DecodeArgs& a);
-hipError_t launch_decode_fused(const DecodeArgs& a, const NewToken& nt, hipStream_t s);
+size_t decode_fused_lds(const DecodeArgs& a, int W);
+hipError_t launch_decode_fused(const DecodeArgs& a, const NewToken& nt, int W, hipStream_t s);
 // a: splits_total (= npieces), L (any of the widths' layouts) and the common fields
 hipError_t launch_decode_mixed(const DecodeArgs& a, const MixedPlan& mp, hipStream_t s);
 hipError_t launch_merge(const float* partial, float* out, int rows, int splits, int D, hipStream_t s);

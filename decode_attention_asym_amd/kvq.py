@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
+from typing import NamedTuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
@@ -198,6 +199,14 @@ def merge_partials(partials, out, rows: int, splits: int, head_dim: int, stream=
     return out
 
 
+class DecodePlan(NamedTuple):
+    """How a decode runs (kvq_decode_plan)."""
+
+    splits: int  # splits per slice
+    merged: bool  # the decode kernel writes the output itself
+    records: int  # partial records per row the merge kernel combines (0 when merged)
+
+
 class KVQCache:
     """A quantized KV cache in a torch-allocated device buffer.
 
@@ -265,13 +274,14 @@ class KVQCache:
     def default_splits(self) -> int:
         return int(lib.kvq_default_splits(self.h))
 
-    def decode_plan(self, splits: int | None = None) -> tuple[int, bool]:
-        """(split count, merged inside the decode kernel) of decode(q, splits=splits)
-        on the current tokens; nothing is launched."""
+    def decode_plan(self, splits: int | None = None) -> DecodePlan:
+        """(split count, merged inside the decode kernel, partial records per
+        row the merge kernel combines) of decode(q, splits=splits) on the
+        current tokens; nothing is launched."""
         S_req = self.default_splits() if splits is None else splits
-        used, merged = ctypes.c_int32(0), ctypes.c_int32(0)
-        check(lib.kvq_decode_plan(self.h, S_req, ctypes.byref(used), ctypes.byref(merged)), "kvq_decode_plan")
-        return int(used.value), bool(merged.value)
+        used, records = ctypes.c_int32(0), ctypes.c_int32(0)
+        check(lib.kvq_decode_plan(self.h, S_req, ctypes.byref(used), ctypes.byref(records)), "kvq_decode_plan")
+        return DecodePlan(int(used.value), records.value == 0, int(records.value))
 
     def append(self, k, v, stream=None) -> None:
         """k, v: [B, H_kv, T, D] contiguous, the config dtype, on the cache's device."""

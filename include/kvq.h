@@ -134,8 +134,12 @@ kvq_status kvq_append(kvq_cache* cache, const void* k, const void* v, int32_t n_
  * has 4 or 8 splits, the splits of a slice run as the waves of one workgroup
  * and are merged there (the cross-split combination of kvq_merge_partials,
  * in LDS), unless that launch would hold fewer waves per compute unit; the
- * workspace is then not touched and no merge kernel follows
- * (kvq_decode_plan tells which).  Requires at least one cached token
+ * workspace is then not touched and no merge kernel follows.  With more than
+ * 8 splits the count is rounded up to a multiple of 4 and each 4 consecutive
+ * splits of a slice are merged in one workgroup into one partial record, the
+ * merge kernel combining S/4 records per row (under the same occupancy rule,
+ * and only when no workgroup is left without token groups).
+ * kvq_decode_plan tells which.  Requires at least one cached token
  * (KVQ_E_STATE otherwise). */
 kvq_status kvq_decode_attn(kvq_cache* cache, const void* q, float* out, void* workspace, size_t ws_bytes,
                            void* stream);
@@ -153,7 +157,8 @@ kvq_status kvq_decode_attn(kvq_cache* cache, const void* q, float* out, void* wo
  *   q:   device, [B][H_q][D] of in_dtype;  out: device, [B][H_q][D] float32
  *        (16-byte aligned).
  * Returns KVQ_E_ARG, enqueuing nothing, when this decode's partials
- * (B * H_q * S * (D + 4) floats at the chosen split count S) exceed
+ * (B * H_q * R * (D + 4) floats, R the merge records per row that
+ * kvq_decode_plan gives for the default split count) exceed
  * KVQ_NOALLOC_SCRATCH_BYTES; KVQ_E_DEVICE if the array's address cannot be
  * obtained.  No device memory is allocated or freed.  Every call on one
  * device shares that device's array, and every split record a call reads is
@@ -171,12 +176,14 @@ kvq_status kvq_decode_attn_splits(kvq_cache* cache, const void* q, float* out, v
 
 /* How kvq_decode_attn_splits(num_splits) would run on the cache's current
  * tokens, without launching anything: *splits_used receives the split count
- * S, *merged_in_kernel 1 when the decode writes `out` itself (one split, or
- * the splits of each slice merged inside the decode kernel) and 0 when a
- * merge of S partials per row follows.  Either pointer may be NULL.
- * KVQ_E_STATE on an empty cache, KVQ_E_ARG for a split count outside
- * [1, S_max]; the split count of kvq_decode_attn is kvq_default_splits. */
-kvq_status kvq_decode_plan(kvq_cache* cache, int32_t num_splits, int32_t* splits_used, int32_t* merged_in_kernel);
+ * S per slice, *merge_records 0 when the decode writes `out` itself (one
+ * split, or all splits of each slice merged inside the decode kernel), else
+ * the partial records per row the merge kernel then combines (S, or S/4 when
+ * groups of four splits are merged inside the decode kernel).  Either
+ * pointer may be NULL.  KVQ_E_STATE on an empty cache, KVQ_E_ARG for a split
+ * count outside [1, S_max]; the split count of kvq_decode_attn is
+ * kvq_default_splits. */
+kvq_status kvq_decode_plan(kvq_cache* cache, int32_t num_splits, int32_t* splits_used, int32_t* merge_records);
 
 /* The two halves of kvq_decode_attn, for callers that merge partial results
  * themselves (e.g. several caches holding disjoint token ranges of the same

@@ -60,6 +60,9 @@ def check_every_slice(w, cache, K, V, q, out, calls=None, tag=""):
     assert worst <= ROW_TOL, worst
 
 
+# the oracle's encoding and fp64 attention of every slice take one to two
+# minutes of host time per workload on a 16-core share
+@pytest.mark.timeout(480)
 @pytest.mark.parametrize("idx", [2, 3, 4], ids=["llama3-8b-32k-k4v2-drift", "70b-128k", "175b-mha-fwht"])
 def test_full_size_every_slice(idx):
     import decode_attention_asym_amd as kvq
@@ -77,6 +80,7 @@ def test_full_size_every_slice(idx):
     check_every_slice(w, cache, K, V, q, out)
 
 
+@pytest.mark.timeout(480)
 def test_70b_append_decode_steps_cross_flushes():
     """The 70B-shaped 128k workload's step loop: 64 one-call steps
     (kvq_append_decode_attn: append one token, whose window write the decode

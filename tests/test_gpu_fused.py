@@ -1,10 +1,12 @@
 """GPU parity of the decode whose splits are merged inside the workgroup: at 4
-and 8 splits per slice (the counts it serves) over the kernel instances (head
-dim, key/value bits, group size, query heads per kv head, rotation, key token
-norms, sink window, hybrid quantizer), its output against the oracle's fp64
-attention on the exported cache, and against the split kernel + merge kernel
-at the same split count; the default split choice on the 32k K4/V2 layer
-shape."""
+and 8 splits per slice (all of a slice's splits in one workgroup) and at 10,
+12 and 16 (groups of four splits per workgroup, the count rounded up to a
+multiple of four, the groups' records merged by the merge kernel), over the
+kernel instances (head dim, key/value bits, group size, query heads per kv
+head, rotation, key token norms, sink window, hybrid quantizer): its output
+against the oracle's fp64 attention on the exported cache, and against the
+split kernel + merge kernel at the same split count; the default split
+choice on the 32k K4/V2 layer shape."""
 import pytest
 import torch
 
@@ -41,21 +43,28 @@ def test_fused_merge_matches_oracle_and_merge_kernel(w):
     exp = cache.export()
     q_host = to_oracle_input(q, w.dtype)
     ref = oracle_rows(w, exp, 0, q_host, list(range(w.B)))
-    fused_seen = False
-    for S in (4, 8):
-        S_used, merged = cache.decode_plan(S)
+    fused_seen = grouped_seen = False
+    for S in (4, 8, 10, 12, 16):
+        S_used, merged, records = cache.decode_plan(S)
         out = cache.decode(q, splits=S)
         partials, S_p = cache.decode_partials(q, splits=S)
         out_m = torch.empty_like(out)
         kvq.merge_partials(partials, out_m, w.B * w.Hq, S_p, w.D)
         torch.cuda.synchronize()
-        assert S_p == S_used
-        fused_seen |= merged
+        # the decode takes the split partials' count, or rounds it up to a
+        # multiple of four for the grouped merge
+        grouped = 0 < records < S_used
+        if grouped:
+            assert not merged and S_used % 4 == 0 and S_p <= S_used < S_p + 4 and records == S_used // 4
+        else:
+            assert S_p == S_used and records == (0 if merged else S_used)
+        fused_seen |= merged and S_used > 1
+        grouped_seen |= grouped
         err_m, _ = rel_l2(out.double().cpu().numpy(), out_m.double().cpu().numpy())
         got = out.double().cpu().numpy()
         err, worst = rel_l2(got, [ref[b] for b in range(w.B)])
-        log(f"[fused] {w.name} splits {S} -> {S_used} merged in kernel {merged}: vs merge kernel {err_m:.2e}, "
-            f"vs oracle {err:.3e} (worst row {worst:.3e})")
+        log(f"[fused] {w.name} splits {S} -> {S_used} (partials {S_p}) merged in kernel {merged}: "
+            f"vs merge kernel {err_m:.2e}, vs oracle {err:.3e} (worst row {worst:.3e})")
         assert err_m <= 1e-6
         assert err <= TOL_REL_L2 and worst <= TOL_REL_L2
     # with head dim 128 the one-wave launch is held to 12 waves per CU by its
@@ -63,6 +72,7 @@ def test_fused_merge_matches_oracle_and_merge_kernel(w):
     # lets 13 in, and the in-kernel merge may be refused for holding fewer
     if w.D == 128:
         assert fused_seen, "no split count took the in-kernel merge"
+        assert grouped_seen, "no split count took the grouped in-kernel merge"
 
 
 def test_default_splits_of_the_32k_layer_shape_merge_in_kernel():
@@ -79,7 +89,7 @@ def test_default_splits_of_the_32k_layer_shape_merge_in_kernel():
     plan = cache.decode_plan()
     log(f"[fused] {w.name}: {cus} CUs, default plan {plan}")
     if cus == 256:
-        assert plan == (4, True)
+        assert plan == (4, True, 0)
     q = syn.q()
     out = cache.decode(q)
     partials, S = cache.decode_partials(q)

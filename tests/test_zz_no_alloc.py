@@ -48,7 +48,7 @@ def test_noalloc_equals_workspace_decode_merged_in_kernel():
     w = WORKLOADS[2].replace(name="noalloc-merged", N=64 * 16 + 128 + 5)
     c = _run(kvq, w)
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert c.decode_plan() == (4, True)
+        assert c.decode_plan() == (4, True, 0)
 
 
 def test_noalloc_refuses_partials_beyond_the_scratch():
