@@ -257,12 +257,17 @@ __device__ __forceinline__ void dma_block(const uint8_t* g, uint32_t lane16, uin
 }
 template <int BYTES>
 constexpr int dma_count() { return BYTES / 1024 + (BYTES % 1024) / 256 + (BYTES % 256 != 0 ? 1 : 0); }
-// N copy instructions of 256 bytes each (global [g + 256 k, +256) to LDS
-// [lds + 256 k, +256)): stands in for N copies whose data is not needed.
+// N copy instructions issued by lane 0 alone, 4 bytes each (global
+// [g + 256 k, +4) to LDS [lds + 256 k, +4)): they stand in for N copies whose
+// data is not needed, keeping the count of copy instructions (which the
+// waits count; a copy counts once whatever lanes are active) at one memory
+// line each instead of 256 bytes or 1 KiB.
 template <int N>
 __device__ __forceinline__ void dma_filler(const uint8_t* g, uint32_t lane4, uint32_t lds) {
+  if (lane4 == 0) {
 #pragma unroll
-  for (int k = 0; k < N; ++k) dma_256(g + 256 * k, lane4, lds + 256 * k);
+    for (int k = 0; k < N; ++k) dma_256(g + 256 * k, 0u, lds + 256 * k);
+  }
 }
 // Number of chunks among the NBUF - 1 issued after chunk position ch (mod
 // CPG) that start a group, i.e. that also carry key parameters.
@@ -639,10 +644,11 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       return pbuf_lds + static_cast<uint32_t>((gi - g0) % NPB) * PB;
     };
     // Copies for positions past the split's end keep the per-chunk copy count
-    // fixed (the waits count copies): their code part is the same number of
-    // copy instructions, each only 256 bytes of the split's last page, into a
-    // slot nobody reads; their parameter part repeats the split's last group
-    // into that group's own buffer (identical bytes).
+    // fixed (the waits count copies): the same number of copy instructions,
+    // each 4 bytes from one lane: their code part from the split's last page
+    // into a slot nobody reads, their parameter part from the split's last
+    // group's parameter block into that group's own buffer (identical bytes
+    // at the same offsets).
     auto issue = [&](int gi, auto chi_c, uint32_t sl) __attribute__((always_inline)) {
       constexpr int chi = decltype(chi_c)::value;
       const bool real = gi < g1;
@@ -655,7 +661,13 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       } else {
         dma_filler<dma_count<KC>() + dma_count<VC>()>(page, lane4, sl);
       }
-      if constexpr (chi == 0) dma_block<PB>(page + PS::OFF_KP, lane16, lane4, pbuf_of(gp));
+      if constexpr (chi == 0) {
+        if (real) {
+          dma_block<PB>(page + PS::OFF_KP, lane16, lane4, pbuf_of(gp));
+        } else {
+          dma_filler<dma_count<PB>()>(page + PS::OFF_KP, lane4, pbuf_of(gp));
+        }
+      }
     };
 
     uint32_t bq[NP][NKB][4];  // B operand of QK^T (fp16 pairs), per part
