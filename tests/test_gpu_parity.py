@@ -184,10 +184,13 @@ def test_decode_partials_per_split_match_oracle(base, sink, tn, S_req):
                 assert err <= TOL_REL_L2 and worst <= TOL_REL_L2, (b, h, s, err, worst)
 
 
-@pytest.mark.parametrize("D,S", [(128, 1), (128, 8), (64, 13), (128, 100), (64, 256), (128, 256)])
+@pytest.mark.parametrize("D,S", [(128, 1), (128, 6), (128, 8), (64, 13), (128, 17), (128, 24), (128, 33), (64, 37),
+                                 (64, 64), (128, 64), (128, 65), (128, 100), (64, 256), (128, 256)])
 def test_merge_partials_against_oracle(D, S):
     """kvq_merge_partials on seeded partials (wide score ranges, empty splits
-    whose o and l hold NaN) against the oracle's split merge."""
+    whose o and l hold NaN) against the oracle's split merge; up to 64
+    records per row the merge runs one wave per row (37 rows: a partial
+    block of four rows at the end), above that one block per row."""
     kvq = _lib()
     import oracle
 
