@@ -362,7 +362,9 @@ __device__ __forceinline__ float replica_sum(float x) {
 // the window write does: lane l converts elements 2l and 2l + 1 of each row
 // (rows of new_k / new_v are [B][H_kv][1][D]).  In that chunk the lanes whose
 // key or value elements belong to the token then take them from LDS instead
-// of the cache and store them to the window (take_new_keys, take_new_value).
+// of the cache (take_new_keys, take_new_value), and after the window pass
+// the same lanes store them to the window (put_new_token): no store comes
+// between the pass's loads, which therefore all go out at once.
 template <int D>
 __device__ __forceinline__ void stage_new_token(const NewToken& nt, int in_dtype, int64_t slice, uint8_t* ring) {
   const int l = threadIdx.x & (kLanes - 1);
@@ -387,24 +389,40 @@ __device__ __forceinline__ void stage_new_token(const NewToken& nt, int in_dtype
 // Keys: the lanes of token column t % 16 hold channels 32 kb + 8 j .. + 7 of
 // tile t / 16 in one 16-byte operand.
 template <int D>
-__device__ __forceinline__ void take_new_keys(const uint8_t* staged, uint8_t* rch, int t, int l, int kb, u32x4& k0,
-                                              u32x4& k1) {
-  constexpr int NKB = D / 32;
+__device__ __forceinline__ void take_new_keys(const uint8_t* staged, int t, int l, int kb, u32x4& k0, u32x4& k1) {
   const int tile = t >> 4, j = l >> 4;
   const u32x4 w = *reinterpret_cast<const u32x4*>(staged + 2 * (32 * kb + 8 * j));
   if (tile == 0) k0 = w; else k1 = w;
-  *reinterpret_cast<u32x4*>(rch + ((tile * NKB + kb) * kLanes + l) * 16) = w;
 }
 // Values: lane group j with tau(j, e) = t holds element e of channel
 // 16 mt + l % 16 in operand mt.
 template <int D>
-__device__ __forceinline__ void take_new_value(const uint8_t* staged, uint8_t* rch, int e, int l, int mt, u32x4& vw) {
+__device__ __forceinline__ void take_new_value(const uint8_t* staged, int e, int l, int mt, u32x4& vw) {
   const uint32_t h = *reinterpret_cast<const uint16_t*>(staged + 2 * D + 2 * (16 * mt + (l & 15)));
   const int hi = e & 1, dw = e >> 1;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     if (k == dw) vw[k] = hi ? ((vw[k] & 0xffffu) | (h << 16)) : ((vw[k] & 0xffff0000u) | h);
-  *reinterpret_cast<uint16_t*>(rch + kChunk * D * 2 + (mt * kLanes + l) * 16 + 2 * e) = static_cast<uint16_t>(h);
+}
+// The token's window slots from the staged rows: key token t (tile t / 16)
+// by the four lanes of column t % 16 (16 bytes per kb each), value element e
+// of every channel by the lanes of group jv with tau(jv, e) = t.
+template <int D>
+__device__ __forceinline__ void put_new_token(const uint8_t* staged, uint8_t* rch, int t, int l, int jv, int e) {
+  constexpr int NKB = D / 32, NMT = D / 16;
+  const int tile = t >> 4, j = l >> 4;
+  if ((l & 15) == (t & 15)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      *reinterpret_cast<u32x4*>(rch + ((tile * NKB + kb) * kLanes + l) * 16) =
+          *reinterpret_cast<const u32x4*>(staged + 2 * (32 * kb + 8 * j));
+  }
+  if (j == jv) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      *reinterpret_cast<uint16_t*>(rch + kChunk * D * 2 + (mt * kLanes + l) * 16 + 2 * e) =
+          *reinterpret_cast<const uint16_t*>(staged + 2 * D + 2 * (16 * mt + (l & 15)));
+  }
 }
 
 // Column layout.  Lane l holds MFMA column l16 = l % 16 and lane group
@@ -885,12 +903,21 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       // decode and it falls in this chunk: token tn of the chunk
       const int tn = NEWTOK && rc == new_rc ? static_cast<int>(nt.pos - pos0) : -1;
       const bool new_keys = tn >= 0 && l16 == (tn & 15);
+      // every load of the chunk first (keys, then values): one memory latency
+      u32x4 kq[2][NKB], vq[NMT];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        kq[0][kb] = *reinterpret_cast<const u32x4*>(rch + ((0 * NKB + kb) * kLanes + l) * 16);
+        kq[1][kb] = *reinterpret_cast<const u32x4*>(rch + ((1 * NKB + kb) * kLanes + l) * 16);
+      }
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        vq[mt] = *reinterpret_cast<const u32x4*>(rch + kChunk * D * 2 + (mt * kLanes + l) * 16);
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        u32x4 k0 = *reinterpret_cast<const u32x4*>(rch + ((0 * NKB + kb) * kLanes + l) * 16);
-        u32x4 k1 = *reinterpret_cast<const u32x4*>(rch + ((1 * NKB + kb) * kLanes + l) * 16);
-        if (new_keys) take_new_keys<D>(ring, rch, tn, l, kb, k0, k1);
+        u32x4 k0 = kq[0][kb], k1 = kq[1][kb];
+        if (new_keys) take_new_keys<D>(ring, tn, l, kb, k0, k1);
         const half8 a0 = __builtin_bit_cast(half8, k0);
         const half8 a1 = __builtin_bit_cast(half8, k1);
 #pragma unroll
@@ -945,8 +972,8 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       const bool new_values = j == jv;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
-        u32x4 vwd = *reinterpret_cast<const u32x4*>(rch + kChunk * D * 2 + (mt * kLanes + l) * 16);
-        if (new_values) take_new_value<D>(ring, rch, ev, l, mt, vwd);
+        u32x4 vwd = vq[mt];
+        if (new_values) take_new_value<D>(ring, ev, l, mt, vwd);
         vwd[0] &= vmask[0]; vwd[1] &= vmask[1]; vwd[2] &= vmask[2]; vwd[3] &= vmask[3];
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
@@ -954,6 +981,14 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, vwd), bb, acc[mt], 0, 0, 0);
         }
       }
+    }
+    // the appended token's window slots, after every load of the pass (and
+    // before a workgroup record overwrites the staged rows)
+    if (NEWTOK && new_rc >= 0) {
+      const int tn = static_cast<int>(nt.pos - new_rc * kChunk);
+      int jv = -1, ev = 0;
+      tau_inv(tn, &jv, &ev);
+      put_new_token<D>(ring, a.cache + fp16_chunk_offset(L, slice, new_rc * kChunk), tn, l, jv, ev);
     }
   }
 
