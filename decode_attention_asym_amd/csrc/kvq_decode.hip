@@ -505,30 +505,36 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
         qm[kb][e] = hv ? qsh[(hv ? h : 0) * D + 32 * kb + 8 * j + e] * rs : 0.0f;
   } else {
     // the lane's 8 channels of each kb are contiguous: one 16-byte load for
-    // 2-byte inputs, two for f32 (rows are 16-byte aligned: D is 64 or 128)
-    const int64_t base = (static_cast<int64_t>(b) * a.Hq + hq) * D;
+    // 2-byte inputs, two for f32 (rows are 16-byte aligned: D is 64 or 128);
+    // every load of the lane is issued before the first conversion, so the
+    // query costs one memory latency (with the dtype tested per kb, each kb's
+    // load waited for the previous one)
+    const int64_t base = (static_cast<int64_t>(b) * a.Hq + hq) * D + 8 * j;
+    if (a.in_dtype == 0) {
+      u32x4 x[NKB][2];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int64_t o = base + 32 * kb + 8 * j;
-      float x[8];
-      if (a.in_dtype == 0) {
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(static_cast<const float*>(a.q) + o);
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(static_cast<const float*>(a.q) + o + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = __uint_as_float(x0[e]);
-          x[4 + e] = __uint_as_float(x1[e]);
-        }
-      } else {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + o);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t u = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          x[e] = a.in_dtype == 1 ? __half2float(__ushort_as_half(static_cast<uint16_t>(u))) : __uint_as_float(u << 16);
-        }
+      for (int kb = 0; kb < NKB; ++kb) {
+        x[kb][0] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(a.q) + base + 32 * kb);
+        x[kb][1] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(a.q) + base + 32 * kb + 4);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qm[kb][e] = hv ? x[e] * qscale : 0.0f;
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qm[kb][e] = hv ? __uint_as_float(x[kb][e >> 2][e & 3]) * qscale : 0.0f;
+    } else {
+      u32x4 w[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        w[kb] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + base + 32 * kb);
+      const bool f16 = a.in_dtype == 1;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t u = (w[kb][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          const float x = f16 ? __half2float(__ushort_as_half(static_cast<uint16_t>(u))) : __uint_as_float(u << 16);
+          qm[kb][e] = hv ? x * qscale : 0.0f;
+        }
     }
   }
   // Per-split fp16 parts of the query (part 1 = fp16(x - part 0)):
