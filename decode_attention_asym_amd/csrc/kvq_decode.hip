@@ -439,6 +439,16 @@ __device__ __forceinline__ void put_new_token(const uint8_t* staged, uint8_t* rc
 // the PV weights of the other replicas by DPP row rotation and owns the
 // output; the other replicas' PV columns are never read.
 //
+// GQC = 1 (one query head per kv head, multi-head attention): the query head
+// takes all four head slots of the GQC = 4 layout, so every column carries a
+// live score, and head slot h serves value group h % NCG: its lanes form the
+// PV weights and zero-point sums of that group only, the PV B operand is the
+// same for every M-tile, and the output of a tile is read from the column of
+// its group's slot.  Per chunk a lane then forms one group's weights instead
+// of NCG (for D = 128, G = 32 a quarter of the weight, zero-sum and gather
+// work), where the four-slot layout with one live slot left three quarters
+// of the lanes computing a softmax nobody read.
+//
 // decode_split is one wave's work: split s of slice `slice`, with the LDS
 // ring at `ring` (ring_bytes<...>() bytes) and, for rotated keys, gqa * D
 // floats at qsh for the query's transform, shared by the workgroup's waves
@@ -453,26 +463,35 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   using PS = PageShape<D, KB, VB, G, TN>;
   constexpr int NKB = D / 32, NMT = D / 16, NCG = PS::NCG, CPG = PS::CPG;
   constexpr int KW = 2 * NKB * KB / 4, VW = NMT * VB / 4;
-  constexpr int R = 16 / GQC, NV = 8 / R, NPR = NV / 2;  // replicas, values and value pairs per lane
-  constexpr int VPL = NV * NCG;                           // value-parameter dwords a lane reads per chunk
-  static_assert(GQC == 4 || GQC == 8 || GQC == 16, "head slots per replica");
+  static_assert(GQC == 1 || GQC == 4 || GQC == 8 || GQC == 16, "head slots per replica");
+  constexpr bool MHA = GQC == 1;                          // one query head in every slot
+  constexpr int GS = MHA ? 4 : GQC;                       // head slots
+  constexpr int R = 16 / GS, NV = 8 / R, NPR = NV / 2;    // replicas, values and value pairs per lane
+  constexpr int NCGL = MHA ? 1 : NCG;                     // value groups a lane forms weights for
+  constexpr int VPL = NV * NCGL;                          // value-parameter dwords a lane reads per chunk
+  static_assert(!MHA || NCG <= GS, "a value group per head slot");
   // B operands of QK^T carry each value as two fp16 parts (hi + lo) so the
   // folded products keep ~22 bits: in the columns of odd replicas (NP = 1
-  // MFMA) when GQC < 16, else as two MFMAs.
-  constexpr int NP = GQC < 16 ? 1 : 2;
+  // MFMA) when GS < 16, else as two MFMAs.
+  constexpr int NP = GS < 16 ? 1 : 2;
   const Layout& L = a.L;
   const int l = threadIdx.x & (kLanes - 1), l16 = l & 15, j = l >> 4;
   const int S = a.splits;
   const int b = static_cast<int>(slice / a.Hkv), hkv = static_cast<int>(slice % a.Hkv);
-  const int h = l16 % GQC, rp = l16 / GQC;
-  const bool hv = h < a.gqa;
-  const int hq = hkv * a.gqa + (hv ? h : 0);
+  const int h = l16 % GS, rp = l16 / GS;
+  // hv: the slot carries a query head (all slots with MHA, whose head is 0)
+  const bool hv = MHA || h < a.gqa;
+  const int hh = MHA ? 0 : (hv ? h : 0);                  // the slot's query head within the slice
+  const int hq = hkv * a.gqa + hh;
+  // MHA: the value group of this slot, and whether it writes that group's tiles
+  const int cgh = h % NCG;
+  const bool owner = !MHA || h < NCG;
 
   const bool lo_cols = NP == 1 && (rp & 1);               // this lane's columns hold the second part
   // full QK^T sum from the two parts' columns
   auto combine = [&](float x) __attribute__((always_inline)) {
     if constexpr (NP == 1) {
-      return x + row_from<GQC>(x);
+      return x + row_from<GS>(x);
     } else {
       return x;
     }
@@ -502,7 +521,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        qm[kb][e] = hv ? qsh[(hv ? h : 0) * D + 32 * kb + 8 * j + e] * rs : 0.0f;
+        qm[kb][e] = hv ? qsh[hh * D + 32 * kb + 8 * j + e] * rs : 0.0f;
   } else {
     // the lane's 8 channels of each kb are contiguous: one 16-byte load for
     // 2-byte inputs, two for f32 (rows are 16-byte aligned: D is 64 or 128);
@@ -600,10 +619,10 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   f32x4 acc[NMT];
 #pragma unroll
   for (int i = 0; i < NMT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // zero-point sums per value group, weighted by p
-  float zacc[NCG];
+  // zero-point sums per value group, weighted by p (MHA: this slot's group)
+  float zacc[NCGL];
 #pragma unroll
-  for (int i = 0; i < NCG; ++i) zacc[i] = 0.0f;
+  for (int i = 0; i < NCGL; ++i) zacc[i] = 0.0f;
 
   // (called wave-uniformly; mnew = max(m, chunk max) per head)
   auto rescale = [&](float mnew) __attribute__((always_inline)) {
@@ -611,7 +630,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
 #pragma unroll
     for (int i = 0; i < NMT; ++i) acc[i] *= al;
 #pragma unroll
-    for (int i = 0; i < NCG; ++i) zacc[i] *= al;
+    for (int i = 0; i < NCGL; ++i) zacc[i] *= al;
     lsum *= al;
     m = mnew;
     mslack = mnew + kMaxSlack;
@@ -633,7 +652,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       if constexpr (r == 0) {
         o[i] = c[i % NPR];
       } else {
-        o[i] = row_from<GQC * r>(c[i % NPR]);
+        o[i] = row_from<GS * r>(c[i % NPR]);
       }
     });
   };
@@ -657,7 +676,8 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
   const uint32_t lane16 = static_cast<uint32_t>(l) * 16, lane4 = static_cast<uint32_t>(l) * 4;
   // byte offset of this lane's value parameters inside a chunk's part of the
   // parameter block (layout [j][pair][group][scale, zero] dwords, see kvq_layout.h)
-  const int vp_off = KPB + (j * 4 + NPR * rp) * NCG * 8;
+  // (MHA: the NPR = 1 pair's scale and zero of group cgh only)
+  const int vp_off = KPB + ((j * 4 + NPR * rp) * NCG + (MHA ? cgh : 0)) * 8;
 
   if (g1 > g0) {
     const uint8_t* slice_pages = a.cache + page_offset(L, slice, 0);
@@ -828,12 +848,12 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
         lsum += pm[k];
       }
       // PV weights p * value scale (one fp16 part) and the zero-point sums
-      uint32_t bpc[NCG][NPR];
+      uint32_t bpc[NCGL][NPR];
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
+      for (int cg = 0; cg < NCGL; ++cg) {
 #pragma unroll
         for (int pp = 0; pp < NPR; ++pp) {
-          const uint32_t sp = vp[(pp * NCG + cg) * 2], zp = vp[(pp * NCG + cg) * 2 + 1];
+          const uint32_t sp = vp[(pp * NCGL + cg) * 2], zp = vp[(pp * NCGL + cg) * 2 + 1];
           bpc[cg][pp] = mix_mul2(pm[2 * pp], pm[2 * pp + 1], sp);
           zacc[cg] = __builtin_fmaf(pm[2 * pp], h2f_lo(zp), zacc[cg]);
           zacc[cg] = __builtin_fmaf(pm[2 * pp + 1], h2f_hi(zp), zacc[cg]);
@@ -842,14 +862,14 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
       // the slot's data has long been read into registers: refill it with a
       // later chunk before the PV products
       refill();
-      uint32_t bp[NCG][4];
+      uint32_t bp[NCGL][4];
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) gather_pairs(bpc[cg], bp[cg]);
+      for (int cg = 0; cg < NCGL; ++cg) gather_pairs(bpc[cg], bp[cg]);
       // PV on the normal-range code operands
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const half8 av = v_operand<VB>(vw, mt);
-        const uint32_t* bw = bp[(16 * mt) / G];
+        const uint32_t* bw = bp[MHA ? 0 : (16 * mt) / G];
         const half8 bb = __builtin_bit_cast(half8, u32x4{bw[0], bw[1], bw[2], bw[3]});
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bb, acc[mt], 0, 0, 0);
       }
@@ -1000,45 +1020,48 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, const int64_t 
 
   // ---- finalize: reduce the lane shares over replicas and lane groups, write
   lsum = wave_sum_j(replica_sum<R>(lsum));
-  float zsum[NCG];
+  float zsum[NCGL];
 #pragma unroll
-  for (int i = 0; i < NCG; ++i) zsum[i] = wave_sum_j(replica_sum<R>(zacc[i]));
+  for (int i = 0; i < NCGL; ++i) zsum[i] = wave_sum_j(replica_sum<R>(zacc[i]));
+  // tile mt's output: o = acc + the zero-point sum of its value group, held by
+  // this lane (MHA: only the lanes of the group's slot hold the tile's column)
+  auto tile_mine = [&](int mt) __attribute__((always_inline)) { return !MHA || (16 * mt) / G == cgh; };
+  auto tile_o = [&](int mt) __attribute__((always_inline)) { return acc[mt] + zsum[MHA ? 0 : (16 * mt) / G]; };
+  const bool ml_writer = j == 0 && (!MHA || h == 0);  // one lane per head writes m and l
   if constexpr (FUSED) {
     // record [head slot h][D + 4] floats: o, then m and l (the ring's copies
     // have all landed: the main loop ends with no copy in flight)
-    if (hv && rp == 0) {
-      float* pr = reinterpret_cast<float*>(ring) + h * (D + 4);
+    if (hv && owner && rp == 0) {
+      float* pr = reinterpret_cast<float*>(ring) + hh * (D + 4);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int c0 = 16 * mt + 4 * j;
-        *reinterpret_cast<f32x4*>(pr + c0) = acc[mt] + zsum[c0 / G];
+        if (tile_mine(mt)) *reinterpret_cast<f32x4*>(pr + c0) = tile_o(mt);
       }
-      if (j == 0) {
+      if (ml_writer) {
         pr[D] = m;
         pr[D + 1] = lsum;
       }
     }
     return;
   }
-  if (hv && rp == 0) {
+  if (hv && owner && rp == 0) {
     const int64_t row = static_cast<int64_t>(b) * a.Hq + hq;
     if (a.write_final) {
       const float inv = 1.0f / lsum;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int c0 = 16 * mt + 4 * j;
-        f32x4 o = (acc[mt] + zsum[c0 / G]) * inv;
-        *reinterpret_cast<f32x4*>(a.out + row * D + c0) = o;
+        if (tile_mine(mt)) *reinterpret_cast<f32x4*>(a.out + row * D + c0) = tile_o(mt) * inv;
       }
     } else {
       float* pr = a.partial + (row * a.splits_total + a.split_off + s) * (D + 4);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int c0 = 16 * mt + 4 * j;
-        f32x4 o = acc[mt] + zsum[c0 / G];
-        *reinterpret_cast<f32x4*>(pr + c0) = o;
+        if (tile_mine(mt)) *reinterpret_cast<f32x4*>(pr + c0) = tile_o(mt);
       }
-      if (j == 0) {
+      if (ml_writer) {
         pr[D] = m;
         pr[D + 1] = lsum;
       }
@@ -1215,6 +1238,7 @@ auto instance_of(const DecodeArgs& a, X... x) {
     constexpr int D_ = decltype(d)::value, KB_ = decltype(kb)::value, VB_ = decltype(vb)::value;
     constexpr int G_ = decltype(g)::value;
     constexpr bool TN_ = decltype(tn)::value;
+    if (a.gqa == 1) return F<D_, KB_, VB_, G_, 1, TN_>::run(a, x...);
     if (a.gqa <= 4) return F<D_, KB_, VB_, G_, 4, TN_>::run(a, x...);
     if (a.gqa <= 8) return F<D_, KB_, VB_, G_, 8, TN_>::run(a, x...);
     return F<D_, KB_, VB_, G_, 16, TN_>::run(a, x...);

@@ -424,11 +424,13 @@ def test_capacity_and_empty_errors():
     assert torch.isfinite(out).all()
 
 
-@pytest.mark.parametrize("kb,vb,G,hq", [(kb, vb, G, hq) for kb in (2, 4) for vb in (2, 4) for G in (32, 64) for hq in (4, 8, 16)],
+@pytest.mark.parametrize("kb,vb,G,hq", [(kb, vb, G, hq) for kb in (2, 4) for vb in (2, 4) for G in (32, 64)
+                                        for hq in (1, 4, 8, 16)],
                          ids=lambda v: str(v))
 def test_bits_group_gqa_matrix(kb, vb, G, hq):
     """Every decode kernel instantiation at D=128 (bit widths x group size x
-    head-slot replica modes: gqa 4, 8, 16), one kv head, ragged length."""
+    head-slot modes: gqa 1 with the head in every slot and a value group per
+    slot, gqa 4, 8, 16), one kv head, ragged length."""
     w = WORKLOADS[1].replace(name=f"k{kb}v{vb}g{G}h{hq}", B=1, Hq=hq, Hkv=1, N=1000 + 7, kbits=kb, vbits=vb, G=G, R=64)
     _check_full(w, splits=1)
 
