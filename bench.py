@@ -353,13 +353,15 @@ def main() -> int:
     for i in range(args.steps):
         step(args.warmup + i)
     ev[1].record()
-    torch.cuda.synchronize()
     # the decode kernel's average launch duration, by difference, right after
+    # and with no host synchronization in between, so the GPU never idles
     # (an idle GPU restarts slower: the first ~60 steps after a pause of a few
-    # ms run up to 3x the settled step time): nk more steps as kvq_append +
-    # kvq_decode_attn_splits, then nk steps without the decode launch (the
-    # append, and the merge kernel when the decode does not merge its splits
-    # itself), each span between two events
+    # ms run up to 3x the settled step time; with a synchronization here the
+    # 175B-shaped MHA layer's first decode launches after it ran ~15% slower
+    # in the trace): nk more steps as kvq_append + kvq_decode_attn_splits,
+    # then nk steps without the decode launch (the append, and the merge
+    # kernel when the decode does not merge its splits itself), each span
+    # between two events
     if not merged:
         # valid records (o = 0, m = 0, l = 1) for the merge-only steps
         pv = partials[: rows * records * (w.D + 4)].view(rows * records, w.D + 4)
