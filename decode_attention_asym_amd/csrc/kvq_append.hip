@@ -160,13 +160,22 @@ __device__ __forceinline__ GroupQ group_params_pair(F&& x) {
 struct QOp {
   float n, s, rs, off;
 };
+// `one` is 1.0f taken from an SGPR (opaque_one): with a literal 1.0 the
+// compiler rewrites the fma as a subtraction and converts x from fp16 in an
+// instruction of its own; with an operand it cannot see it keeps the fma and
+// selects one v_fma_mix_f32 (fp16 input, exact product, one rounding).
 template <int BITS, bool HYB>
-__device__ __forceinline__ QOp quant_op(float x, float mn, float s, float rs, bool sym) {
+__device__ __forceinline__ QOp quant_op(float x, float mn, float s, float rs, bool sym, float one) {
   constexpr float c0 = static_cast<float>((1 << (BITS - 1)) - 1);
   if constexpr (HYB) {
     if (sym) return QOp{x, s, rs, c0};
   }
-  return QOp{__builtin_fmaf(x, 1.0f, -mn), s, rs, 0.0f};
+  return QOp{__builtin_fmaf(x, one, -mn), s, rs, 0.0f};
+}
+__device__ __forceinline__ float opaque_one() {
+  uint32_t r;
+  asm("s_mov_b32 %0, 0x3f800000" : "=s"(r));
+  return __uint_as_float(r);
 }
 
 // Packs N codes into a dword: the code of field k (its operands op(k)) goes
@@ -199,11 +208,16 @@ __device__ __forceinline__ uint32_t pack_codes(BitF&& bit_of, OpF&& op) {
       if (fabsf(f - rintf(f)) > kTieGuard) t[k] = rintf(q.n / q.s);
     }
   }
+  // a byte's first field starts its sum (an fma onto +0 would cost an add)
   float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  bool started[4] = {false, false, false, false};
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    const int bit = bit_of(k);
-    b[bit >> 3] = __builtin_fmaf(OFF ? t[k] + off[k] : t[k], static_cast<float>(1 << (bit & 7)), b[bit >> 3]);
+    const int bit = bit_of(k), by = bit >> 3;
+    const float code = OFF ? t[k] + off[k] : t[k];
+    const float mult = static_cast<float>(1 << (bit & 7));
+    b[by] = started[by] ? __builtin_fmaf(code, mult, b[by]) : code * mult;
+    started[by] = true;
   }
   uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(b[0], 0, 0u);
   w = __builtin_amdgcn_cvt_pk_u8_f32(b[1], 1, w);
@@ -243,8 +257,12 @@ __device__ void fwht_rows(float* x, int rows, int tid, int nthreads) {
 // norms, which round to fp16 only after their arithmetic); without either,
 // keys are fp16 from entry conversion on and staged as fp16, which halves
 // their LDS and lets four blocks share a CU at G = 64 instead of three.
+// Threads of a flush block.  The loops below stride by this constant rather
+// than blockDim.x, so the compiler unrolls them and folds their per-task index
+// and address arithmetic (the launch always uses this many).
+constexpr int kFlushThreads = 256;
 template <int D, int KB, int VB, int G, bool F32K>
-__global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
+__global__ __launch_bounds__(kFlushThreads) void flush_kernel(AppendArgs a) {
   constexpr int NKB = D / 32, NCG = D / G;
   constexpr int CPG = G / kChunk;
   // token rows padded by one bank (4 bytes) so that the lanes reading one
@@ -316,7 +334,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
       }
     }
   } else {
-  for (int idx = tid; idx < G * D; idx += blockDim.x) {
+  for (int idx = tid; idx < G * D; idx += kFlushThreads) {
     int i = idx / D, c = idx % D;
     int64_t p = pos0 + i;
     if (p >= a.n_old) {
@@ -337,8 +355,8 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
     // rows [first_new, G) come from the input: rotate (keys) then round to fp16
     int first_new = a.n_old > pos0 ? static_cast<int>(a.n_old - pos0) : 0;
     if constexpr (F32K) {
-      if (a.rotate) fwht_rows<D, KS>(kx + first_new * KS, G - first_new, tid, blockDim.x);
-      for (int idx = first_new * D + tid; idx < G * D; idx += blockDim.x)
+      if (a.rotate) fwht_rows<D, KS>(kx + first_new * KS, G - first_new, tid, kFlushThreads);
+      for (int idx = first_new * D + tid; idx < G * D; idx += kFlushThreads)
         kx[(idx / D) * KS + idx % D] = round_fp16(kx[(idx / D) * KS + idx % D]);
     }
     __syncthreads();
@@ -355,7 +373,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
       // (or, for D = 64, lanes 0..31), then each tree level adds pairs (2t,
       // 2t + 1) of the level below: a fixed order, so the norm does not depend
       // on how the work is shared; then a correctly rounded square root
-      const int lane = tid % kLanes, wave = tid / kLanes, nwaves = blockDim.x / kLanes;
+      const int lane = tid % kLanes, wave = tid / kLanes, nwaves = kFlushThreads / kLanes;
       for (int i = wave; i < G; i += nwaves) {
         const float* row = kx + i * KS;
         float t = 0.0f;
@@ -372,7 +390,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         }
       }
       __syncthreads();
-      for (int idx = tid; idx < G * D; idx += blockDim.x) {
+      for (int idx = tid; idx < G * D; idx += kFlushThreads) {
         const float nrm = knrm[idx / D];
         const int k = (idx / D) * KS + idx % D;
         kput(k, nrm == 0.0f ? 0.0f : round_fp16(kget(k) / nrm));
@@ -385,7 +403,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   // channels; two adjacent lanes per group, each over half of it
   auto params = [&](auto hyb_c) __attribute__((always_inline)) {
     constexpr bool HYB = decltype(hyb_c)::value;
-    for (int t = tid; t < 2 * D; t += blockDim.x) {
+    for (int t = tid; t < 2 * D; t += kFlushThreads) {
       const int c = t >> 1, h = t & 1;
       const GroupQ q = group_params_pair<G, KB, HYB>([&](int i) { return kget((h * (G / 2) + i) * KS + c); });
       if (h == 0) {
@@ -399,7 +417,7 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
         kp[D + pi] = q.zero16;
       }
     }
-    for (int t = tid; t < 2 * G * NCG; t += blockDim.x) {
+    for (int t = tid; t < 2 * G * NCG; t += kFlushThreads) {
       const int task = t >> 1, h = t & 1;
       const int i = task / NCG, cg = task % NCG;
       const __half* row = vx + i * VS + cg * G + h * (G / 2);
@@ -420,9 +438,14 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
   // 4. value codes, likewise
   auto codes = [&](auto hyb_c) __attribute__((always_inline)) {
     constexpr bool HYB = decltype(hyb_c)::value;
+    const float one = opaque_one();
+    // the page's code blocks: uniform bases, 32-bit offsets within the page
+    uint8_t* const kcodes = page + L.off_kcodes;
+    uint8_t* const vcodes = page + L.off_vcodes;
+    const uint32_t kc_chunk = static_cast<uint32_t>(L.kc_chunk_bytes), vc_chunk = static_cast<uint32_t>(L.vc_chunk_bytes);
     {
       constexpr int KW = 2 * NKB * KB / 4;
-      for (int task = tid; task < CPG * kLanes * KW; task += blockDim.x) {
+      for (int task = tid; task < CPG * kLanes * KW; task += kFlushThreads) {
         int ch = task / (kLanes * KW);
         int l = (task / KW) % kLanes;
         int d = task % KW;
@@ -438,15 +461,16 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
               const int mt = combo / NKB, kb = combo % NKB;
               const int i = ch * kChunk + 16 * mt + l16;  // token within the group
               const int c = 32 * kb + 8 * j + e;
-              return quant_op<KB, HYB>(kget(i * KS + c), kmn[c], ks[c], krs[c], HYB && ksym[c]);
+              return quant_op<KB, HYB>(kget(i * KS + c), kmn[c], ks[c], krs[c], HYB && ksym[c], one);
             });
-        *reinterpret_cast<uint32_t*>(page + L.off_kcodes + ch * L.kc_chunk_bytes + lane_dword_offset(KW, l, d)) = word;
+        *reinterpret_cast<uint32_t*>(kcodes + (static_cast<uint32_t>(ch) * kc_chunk +
+                                               static_cast<uint32_t>(lane_dword_offset(KW, l, d)))) = word;
       }
     }
     {
       constexpr int NMT = D / 16;
       constexpr int VW = NMT * VB / 4;
-      for (int task = tid; task < CPG * kLanes * VW; task += blockDim.x) {
+      for (int task = tid; task < CPG * kLanes * VW; task += kFlushThreads) {
         int ch = task / (kLanes * VW);
         int l = (task / VW) % kLanes;
         int d = task % VW;
@@ -459,9 +483,10 @@ __global__ __launch_bounds__(256) void flush_kernel(AppendArgs a) {
               const int c = 16 * mt + l16, cg = c / G;
               const int i = ch * kChunk + tau(j, e);
               const int pv = i * NCG + cg;
-              return quant_op<VB, HYB>(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB && vsym[pv]);
+              return quant_op<VB, HYB>(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB && vsym[pv], one);
             });
-        *reinterpret_cast<uint32_t*>(page + L.off_vcodes + ch * L.vc_chunk_bytes + lane_dword_offset(VW, l, d)) = word;
+        *reinterpret_cast<uint32_t*>(vcodes + (static_cast<uint32_t>(ch) * vc_chunk +
+                                               static_cast<uint32_t>(lane_dword_offset(VW, l, d)))) = word;
       }
     }
   };
@@ -498,9 +523,9 @@ template <int D, int KB, int VB, int G>
 hipError_t flush_t(const AppendArgs& a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(a.n_flush), static_cast<unsigned>(a.L.slices));
   if (a.rotate || a.L.token_norm)
-    hipLaunchKernelGGL((flush_kernel<D, KB, VB, G, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((flush_kernel<D, KB, VB, G, true>), grid, dim3(kFlushThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((flush_kernel<D, KB, VB, G, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((flush_kernel<D, KB, VB, G, false>), grid, dim3(kFlushThreads), 0, s, a);
   return hipGetLastError();
 }
 
