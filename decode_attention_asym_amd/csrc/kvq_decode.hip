@@ -1299,7 +1299,9 @@ template <int D, int G, bool TN>
 hipError_t mixed_t(const DecodeArgs& a, const MixedPlan& mr, hipStream_t s) {
   dim3 grid(static_cast<unsigned>(a.L.slices * mr.npieces));
   const size_t lds = a.rotate ? static_cast<size_t>(a.gqa) * D * sizeof(float) : 0;
-  if (a.gqa <= 4)
+  if (a.gqa == 1)
+    hipLaunchKernelGGL((decode_mixed_kernel<D, G, 1, TN>), grid, dim3(kLanes), lds, s, a, mr);
+  else if (a.gqa <= 4)
     hipLaunchKernelGGL((decode_mixed_kernel<D, G, 4, TN>), grid, dim3(kLanes), lds, s, a, mr);
   else if (a.gqa <= 8)
     hipLaunchKernelGGL((decode_mixed_kernel<D, G, 8, TN>), grid, dim3(kLanes), lds, s, a, mr);

@@ -93,6 +93,11 @@ SMALL = [
                          bits_low=(4, 2), bits_high=(4, 4)),
     WORKLOADS[1].replace(name="adapt-delta-covers-all", B=2, N=700 + 3, adapt_delta=4096, bits_low=(2, 2),
                          bits_high=(4, 4)),
+    # gqa 1 (the head in every slot, a value group per slot) on the mixed-width kernel
+    WORKLOADS[4].replace(name="mha-fwht-adapt-lo22-hi44", B=1, Hq=6, Hkv=6, N=2000 + 11, adapt_delta=512,
+                         bits_low=(2, 2), bits_high=(4, 4)),
+    WORKLOADS[0].replace(name="d64-mha-adapt-g64-tokennorm", B=2, Hq=3, Hkv=3, N=1200 + 5, G=64, R=64,
+                         token_norm=True, adapt_delta=256, bits_low=(4, 2), bits_high=(2, 4)),
 ]
 
 
