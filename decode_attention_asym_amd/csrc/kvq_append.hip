@@ -156,7 +156,11 @@ __device__ __forceinline__ GroupQ group_params_pair(F&& x) {
 // (0 when s = 0) and the offset added to the rounded quotient (0, or c0 for
 // the symmetric quantizer).  fl(x - min) is formed as fma(x, 1, -min): the
 // exact difference rounded once, as a binary32 subtraction rounds it, and
-// with x an fp16 value the conversion folds into the fma.
+// with x an fp16 value the conversion folds into the fma.  The group's
+// quantizer choice is folded into its stored operands: a symmetric group
+// stores min = 0 (fma(x, 1, -0) is x exactly, signed zeros included) and
+// offset c0, an asymmetric one its minimum and offset 0, so no code selects
+// between the two.
 struct QOp {
   float n, s, rs, off;
 };
@@ -164,13 +168,8 @@ struct QOp {
 // compiler rewrites the fma as a subtraction and converts x from fp16 in an
 // instruction of its own; with an operand it cannot see it keeps the fma and
 // selects one v_fma_mix_f32 (fp16 input, exact product, one rounding).
-template <int BITS, bool HYB>
-__device__ __forceinline__ QOp quant_op(float x, float mn, float s, float rs, bool sym, float one) {
-  constexpr float c0 = static_cast<float>((1 << (BITS - 1)) - 1);
-  if constexpr (HYB) {
-    if (sym) return QOp{x, s, rs, c0};
-  }
-  return QOp{__builtin_fmaf(x, one, -mn), s, rs, 0.0f};
+__device__ __forceinline__ QOp quant_op(float x, float mn, float s, float rs, float off, float one) {
+  return QOp{__builtin_fmaf(x, one, -mn), s, rs, off};
 }
 __device__ __forceinline__ float opaque_one() {
   uint32_t r;
@@ -282,7 +281,9 @@ __global__ __launch_bounds__(kFlushThreads) void flush_kernel(AppendArgs a) {
   };
   __shared__ float ks[D], kmn[D], krs[D];
   __shared__ float vs[G * NCG], vmn[G * NCG], vrs[G * NCG];
-  __shared__ bool ksym[D], vsym[G * NCG];
+  // hybrid quantizer: the offset added to a group's rounded quotients (c0 for
+  // a symmetric group, whose stored minimum is then 0; 0 otherwise)
+  __shared__ float koff[D], voff[G * NCG];
   __shared__ float knrm[G];
 
   const Layout& L = a.L;
@@ -409,8 +410,8 @@ __global__ __launch_bounds__(kFlushThreads) void flush_kernel(AppendArgs a) {
       if (h == 0) {
         ks[c] = q.s;
         krs[c] = q.rs;
-        kmn[c] = q.mn;
-        ksym[c] = q.sym;
+        kmn[c] = HYB && q.sym ? 0.0f : q.mn;
+        if constexpr (HYB) koff[c] = q.sym ? static_cast<float>((1 << (KB - 1)) - 1) : 0.0f;
         uint16_t* kp = reinterpret_cast<uint16_t*>(page + L.off_kparams);
         const int pi = kparam_index(L, c);
         kp[pi] = q.scale16;
@@ -425,8 +426,8 @@ __global__ __launch_bounds__(kFlushThreads) void flush_kernel(AppendArgs a) {
       if (h == 0) {
         vs[task] = q.s;
         vrs[task] = q.rs;
-        vmn[task] = q.mn;
-        vsym[task] = q.sym;
+        vmn[task] = HYB && q.sym ? 0.0f : q.mn;
+        if constexpr (HYB) voff[task] = q.sym ? static_cast<float>((1 << (VB - 1)) - 1) : 0.0f;
         uint16_t* vp = reinterpret_cast<uint16_t*>(page + L.off_vparams + (i / kChunk) * L.vp_chunk_bytes);
         vp[vparam_scale_elem(L, i % kChunk, cg)] = q.scale16;
         vp[vparam_zero_elem(L, i % kChunk, cg)] = q.zero16;
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(kFlushThreads) void flush_kernel(AppendArgs a) {
               const int mt = combo / NKB, kb = combo % NKB;
               const int i = ch * kChunk + 16 * mt + l16;  // token within the group
               const int c = 32 * kb + 8 * j + e;
-              return quant_op<KB, HYB>(kget(i * KS + c), kmn[c], ks[c], krs[c], HYB && ksym[c], one);
+              return quant_op(kget(i * KS + c), kmn[c], ks[c], krs[c], HYB ? koff[c] : 0.0f, one);
             });
         *reinterpret_cast<uint32_t*>(kcodes + (static_cast<uint32_t>(ch) * kc_chunk +
                                                static_cast<uint32_t>(lane_dword_offset(KW, l, d)))) = word;
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(kFlushThreads) void flush_kernel(AppendArgs a) {
               const int c = 16 * mt + l16, cg = c / G;
               const int i = ch * kChunk + tau(j, e);
               const int pv = i * NCG + cg;
-              return quant_op<VB, HYB>(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB && vsym[pv], one);
+              return quant_op(__half2float(vx[i * VS + c]), vmn[pv], vs[pv], vrs[pv], HYB ? voff[pv] : 0.0f, one);
             });
         *reinterpret_cast<uint32_t*>(vcodes + (static_cast<uint32_t>(ch) * vc_chunk +
                                                static_cast<uint32_t>(lane_dword_offset(VW, l, d)))) = word;
